@@ -1,0 +1,305 @@
+"""Pins of the CPU oracle to things other than itself: hand-worked cases, closed forms,
+brute force on tiny inputs, invariants and special cases. CPU only."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")))
+
+
+def logistic(z):
+    return 1.0 / (1.0 + math.exp(-z))
+
+
+# ------------------------------------------------------------------ hand-worked route
+def test_hand_route_case():
+    g = GOLD["route"]
+    L = O.gate_logits(np.array(g["x"]), np.array(g["w_router"]))
+    np.testing.assert_array_equal(L, np.array(g["expected_logits"]))
+    idx, flags = O.select_experts(L, g["top_k"])
+    assert flags == 0
+    np.testing.assert_array_equal(idx, np.array(g["expected_idx"]))
+    w = O.topk_weights(L, idx, renormalize=True)
+    want = np.array([[logistic(z) for z in row] for row in g["weights_logistic_args"]])
+    np.testing.assert_allclose(w, want, rtol=1e-15, atol=0)
+
+
+def test_hand_capacity_case():
+    g, c = GOLD["route"], GOLD["capacity"]
+    L = O.gate_logits(np.array(g["x"]), np.array(g["w_router"]))
+    idx, _ = O.select_experts(L, 2)
+    cap = O.capacity(c["capacity_factor"], 2, 2, 3)
+    assert cap == c["expected_capacity"]
+    p = O.permute_indices(idx, 3, cap)
+    for key in ("counts", "kept", "offsets", "row_token", "slot_row"):
+        np.testing.assert_array_equal(p[key], np.array(c["expected_" + key]), err_msg=key)
+    assert p["flags"] == 0
+
+
+# ------------------------------------------------------------------ brute-force top-k
+def _beats(a, b, ia, ib):
+    """Does (value a, index ia) rank ahead of (b, ib)? NaN lowest, lower index wins ties."""
+    na, nb = math.isnan(a), math.isnan(b)
+    if na and nb:
+        return ia < ib
+    if na:
+        return False
+    if nb:
+        return True
+    if a == b:
+        return ia < ib
+    return a > b
+
+
+def brute_topk(L, k):
+    T, E = L.shape
+    out = np.full((T, k), -1, dtype=np.int64)
+    for t in range(T):
+        for e in range(E):
+            rank = sum(1 for f in range(E) if f != e and _beats(L[t, f], L[t, e], f, e))
+            if rank < k:
+                out[t, rank] = e
+    return out
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_select_matches_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    T, E = 40, 9
+    if seed % 2 == 0:
+        L = rng.standard_normal((T, E))
+    else:  # tie-heavy, with signed zeros, infinities and NaN
+        pool = np.array([-1.0, -0.0, 0.0, 1.0, 2.0, np.inf, -np.inf, np.nan])
+        L = pool[rng.integers(0, len(pool), (T, E))]
+    for k in (1, 2, 3, E):
+        idx, flags = O.select_experts(L, k)
+        np.testing.assert_array_equal(idx, brute_topk(L, k))
+        assert ((idx >= 0) & (idx < E)).all()
+        assert bool(flags & O.FLAG_NONFINITE_LOGIT) == (not np.isfinite(L).all())
+
+
+def test_signed_zero_ties_by_index():
+    L = np.array([[-0.0, 0.0, -1.0], [0.0, -0.0, -1.0]])
+    idx, _ = O.select_experts(L, 1)
+    np.testing.assert_array_equal(idx[:, 0], [0, 0])
+
+
+def test_zero_router_selects_first_k_with_equal_weights():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((16, 8))
+    for E, k in ((4, 2), (8, 3), (5, 5)):
+        L = O.gate_logits(x, np.zeros((8, E)))
+        idx, _ = O.select_experts(L, k)
+        np.testing.assert_array_equal(idx, np.tile(np.arange(k), (16, 1)))
+        np.testing.assert_allclose(O.topk_weights(L, idx, True), 1.0 / k, rtol=1e-15)
+
+
+# ------------------------------------------------------------------ weights
+def test_weight_invariants():
+    rng = np.random.default_rng(2)
+    L = rng.standard_normal((50, 7)) * 3
+    for k in (1, 2, 4, 7):
+        idx, _ = O.select_experts(L, k)
+        w = O.topk_weights(L, idx, True)
+        np.testing.assert_allclose(w.sum(1), 1.0, rtol=0, atol=1e-15)
+        assert (np.diff(w, axis=1) <= 0).all()          # slots are in descending weight
+    idx, _ = O.select_experts(L, 1)
+    np.testing.assert_array_equal(O.topk_weights(L, idx, True), 1.0)
+    idx, _ = O.select_experts(L, 7)
+    np.testing.assert_allclose(O.topk_weights(L, idx, False).sum(1), 1.0, atol=1e-15)
+    # two experts without renormalisation: the softmax probability is logistic(L0 - L1)
+    L2 = np.array([[0.7, -1.3]])
+    idx, _ = O.select_experts(L2, 1)
+    assert O.topk_weights(L2, idx, False)[0, 0] == pytest.approx(logistic(2.0), rel=1e-15)
+
+
+def test_nonfinite_weights_are_nan():
+    L = np.array([[np.nan, 1.0, 0.0], [np.inf, 1.0, 0.0], [-np.inf, -np.inf, -np.inf]])
+    idx, flags = O.select_experts(L, 2)
+    assert flags & O.FLAG_NONFINITE_LOGIT
+    np.testing.assert_array_equal(idx, [[1, 2], [0, 1], [0, 1]])
+    assert np.isnan(O.topk_weights(L, idx, True)).all()
+
+
+# ------------------------------------------------------------------ capacity
+def test_capacity_formula():
+    assert O.capacity(1.2, 8192, 2, 32) == 615           # ceil(614.4)
+    assert O.capacity(1.0, 8192, 2, 32) == 512           # exact: no spurious round-up
+    assert O.capacity(0.0, 100, 2, 8) == 100
+    assert O.capacity(-1.0, 100, 2, 8) == 100
+    assert O.capacity(1.25, 10, 1, 4) == 4               # ceil(3.125)
+
+
+def sequential_permute(idx, E, cap):
+    """Walk tokens in order with one counter per expert (a second, independent algorithm)."""
+    T, k = idx.shape
+    lists = [[] for _ in range(E)]
+    counts = [0] * E
+    for t in range(T):
+        seen = set()
+        for j in range(k):
+            e = int(idx[t, j])
+            if e < 0 or e >= E or e in seen:
+                continue
+            seen.add(e)
+            counts[e] += 1
+            if len(lists[e]) < cap:
+                lists[e].append((t, j))
+    offsets = [0]
+    for e in range(E):
+        offsets.append(offsets[-1] + len(lists[e]))
+    slot_row = -np.ones((T, k), dtype=np.int64)
+    row_token = []
+    for e in range(E):
+        for r, (t, j) in enumerate(lists[e]):
+            slot_row[t, j] = offsets[e] + r
+            row_token.append(t)
+    return np.array(counts), np.array(offsets), slot_row, np.array(row_token, dtype=np.int64)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_permute_matches_sequential_walk(seed):
+    rng = np.random.default_rng(10 + seed)
+    T, E, k = 200, 6, 2
+    L = rng.standard_normal((T, E)) + np.array([2.0, 1.0, 0, 0, -1, -2])
+    idx, _ = O.select_experts(L, k)
+    for cap in (1, 7, 50, 67, T):
+        p = O.permute_indices(idx, E, cap)
+        counts, offsets, slot_row, row_token = sequential_permute(idx, E, cap)
+        np.testing.assert_array_equal(p["counts"], counts)
+        np.testing.assert_array_equal(p["offsets"], offsets)
+        np.testing.assert_array_equal(p["slot_row"], slot_row)
+        np.testing.assert_array_equal(p["row_token"], row_token)
+        assert p["counts"].sum() == T * k
+        np.testing.assert_array_equal(p["kept"], np.minimum(counts, cap))
+
+
+def test_invalid_and_repeated_ids_are_dropped_and_flagged():
+    idx = np.array([[0, 5], [1, 1], [-1, 2], [2, 0]])
+    p = O.permute_indices(idx, 3, 10)
+    assert p["flags"] & O.FLAG_BAD_INDEX
+    counts, offsets, slot_row, row_token = sequential_permute(idx, 3, 10)
+    np.testing.assert_array_equal(p["slot_row"], slot_row)
+    np.testing.assert_array_equal(p["counts"], [2, 1, 2])
+    assert (p["slot_row"][[0, 1, 2], [1, 1, 0]] == -1).all()
+
+
+# ------------------------------------------------------------------ permutation
+def test_permutation_invariants_and_unpermute_identity():
+    rng = np.random.default_rng(3)
+    T, H, E, k = 120, 5, 8, 3
+    x = rng.standard_normal((T, H))
+    L = rng.standard_normal((T, E))
+    idx, _ = O.select_experts(L, k)
+    for cap in (T, 20):
+        p = O.permute_indices(idx, E, cap)
+        sr, rt, off = p["slot_row"], p["row_token"], p["offsets"]
+        t_of = np.repeat(np.arange(T)[:, None], k, 1)
+        m = sr >= 0
+        np.testing.assert_array_equal(rt[sr[m]], t_of[m])
+        for e in range(E):
+            seg = rt[off[e]:off[e + 1]]
+            assert (np.diff(seg) > 0).all()
+            assert (idx[seg] == e).any(axis=1).all()
+        x_perm = O.gather_rows(x, rt)
+        back = O.combine(x_perm, sr, np.ones((T, k)), H)
+        np.testing.assert_array_equal(back, m.sum(1)[:, None] * x)
+
+
+# ------------------------------------------------------------------ expert FFN
+def test_scalar_ffn_closed_forms():
+    ln3 = math.log(3.0)
+    x = np.array([[1.0]])
+    y = O.expert_ffn(x, np.array([[ln3]]), np.array([[2.0]]), np.array([[0.5]]), "swiglu")
+    assert y[0, 0] == pytest.approx(0.75 * ln3, rel=1e-15)
+    # gate and up are not interchangeable
+    y2 = O.expert_ffn(x, np.array([[2.0]]), np.array([[ln3]]), np.array([[0.5]]), "swiglu")
+    assert abs(y2[0, 0] - 0.75 * ln3) > 0.1
+    assert O.gelu(np.array([1.0]))[0] == pytest.approx(GOLD["scalar_ffn"]["gelu_at_1"], rel=1e-15)
+    z = np.linspace(-4, 4, 17)
+    np.testing.assert_allclose(O.gelu(z) - O.gelu(-z), z, atol=1e-15)
+    assert O.silu(np.array([0.0]))[0] == 0.0 and O.gelu(np.array([0.0]))[0] == 0.0
+    zero = O.expert_ffn(np.zeros((1, 3)), np.ones((3, 2)), np.ones((3, 2)), np.ones((2, 3)), "swiglu")
+    np.testing.assert_array_equal(zero, 0.0)
+
+
+def _dense_ffn(x, wg, wu, wd, act):
+    # written from the textbook definitions: silu(z) = z * logistic(z), gelu(z) = z * Phi(z)
+    vlog = np.vectorize(logistic)
+    vphi = np.vectorize(lambda z: 0.5 * math.erfc(-z / math.sqrt(2.0)))
+    if act == "swiglu":
+        a = x @ wg
+        h = a * vlog(a) * (x @ wu)
+    else:
+        a = x @ wu
+        h = a * vphi(a)
+    return h @ wd
+
+
+@pytest.mark.parametrize("act", ["swiglu", "gelu"])
+def test_single_expert_k1_is_dense_ffn(act):
+    rng = np.random.default_rng(4)
+    T, H, I = 33, 6, 10
+    x = rng.standard_normal((T, H))
+    wr = rng.standard_normal((H, 1))
+    wg = rng.standard_normal((1, H, I)) if act == "swiglu" else None
+    wu = rng.standard_normal((1, H, I))
+    wd = rng.standard_normal((1, I, H))
+    r = O.forward(x, wr, None, wg, wu, wd, top_k=1, activation=act)
+    want = _dense_ffn(x, None if wg is None else wg[0], wu[0], wd[0], act)
+    np.testing.assert_allclose(r["out"], want, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(r["topk_w"], 1.0)
+    # linear in the down projection
+    r2 = O.forward(x, wr, None, wg, wu, 2.5 * wd, top_k=1, activation=act)
+    np.testing.assert_allclose(r2["out"], 2.5 * r["out"], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("act", ["swiglu", "gelu"])
+def test_k_equals_E_is_dense_mixture(act):
+    rng = np.random.default_rng(5)
+    T, H, I, E = 9, 4, 6, 5
+    x = rng.standard_normal((T, H))
+    wr = rng.standard_normal((H, E))
+    bias = rng.standard_normal(E)
+    wg = rng.standard_normal((E, H, I))
+    wu = rng.standard_normal((E, H, I))
+    wd = rng.standard_normal((E, I, H))
+    r = O.forward(x, wr, bias, wg, wu, wd, top_k=E, activation=act)
+    want = np.zeros((T, H))
+    for t in range(T):
+        logit = [sum(x[t, h] * wr[h, e] for h in range(H)) + bias[e] for e in range(E)]
+        mx = max(logit)
+        z = [math.exp(v - mx) for v in logit]
+        s = sum(z)
+        for e in range(E):
+            want[t] += (z[e] / s) * _dense_ffn(x[t:t + 1], wg[e], wu[e], wd[e], act)[0]
+    np.testing.assert_allclose(r["out"], want, rtol=1e-12, atol=1e-12)
+
+
+def test_token_subset_matches_full_forward():
+    rng = np.random.default_rng(6)
+    T, H, I, E, k = 50, 8, 12, 6, 2
+    args = [rng.standard_normal(s) for s in ((T, H), (H, E), (E,), (E, H, I), (E, H, I), (E, I, H))]
+    full = O.forward(*args, top_k=k, activation="swiglu", capacity_factor=0.7)
+    ts = np.array([0, 7, 31, 49])
+    sub = O.forward(*args, top_k=k, activation="swiglu", capacity_factor=0.7, tokens=ts)
+    np.testing.assert_allclose(sub["out"], full["out"][ts], rtol=1e-13, atol=1e-13)
+    assert full["capacity"] == math.ceil(0.7 * T * k / E)
+
+
+def test_all_slots_dropped_gives_zero():
+    T, H, E = 6, 3, 2
+    x = np.ones((T, H))
+    wr = np.zeros((H, E))
+    bias = np.array([1.0, 0.0])          # every token prefers expert 0, then 1
+    w = np.ones((E, H, 4))
+    r = O.forward(x, wr, bias, w, w, np.ones((E, 4, H)), top_k=2, activation="swiglu",
+                  capacity_factor=0.5)   # C = ceil(0.5*12/2) = 3
+    assert r["capacity"] == 3
+    np.testing.assert_array_equal(r["kept"], [3, 3])
+    assert (r["out"][3:] == 0).all() and (r["out"][:3] != 0).all()
