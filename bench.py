@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Throughput of the MoE layer forward on one MI355X, plus its roofline and a CPU baseline.
+
+A step is one pass of the whole path -- route, permute, grouped GEMM 1 (gate/up + SwiGLU),
+grouped GEMM 2 (down), combine -- over one batch of seeded synthetic inputs already in
+HBM, through the library's C ABI on torch's current stream. HIP events recorded on that
+stream between the stages give per-stage times; the dominant kernel (GEMM 1) is reported
+against the bf16 dense MFMA peak. The CPU oracle is timed on a bounded token sample.
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer fwd tokens/s at 1 GPU; grouped-GEMM % bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_up_mixtral_traffic.txt")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="mixtral")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=256)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_source_digest() -> str:
+    p = os.path.join(ROOT, "mixture_experts_layer_37_amd", "csrc", "gemm.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(per_launch_flops_unused=None):
+    """HBM bytes per GEMM-1 launch from the committed rocprofv3 counter summary, or None when
+    the summary is missing or was taken on a different GEMM source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        m = re.match(r"^\s*([a-z_]+)\s*:\s*(\S+)", line)
+        if m:
+            kv[m.group(1)] = m.group(2)
+    if kv.get("gemm_source_sha256_16") != kernel_source_digest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU layout "
+              "is described in the design notes and is not run here.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from mixture_experts_layer_37_amd import _lib as L
+    from mixture_experts_layer_37_amd import configs as C
+    from mixture_experts_layer_37_amd.inputs import make_inputs
+    from mixture_experts_layer_37_amd.layer import MoELayer, to_device
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    cfg = C.get(args.config)
+    T, H, I, E, k = cfg.tokens, cfg.hidden, cfg.inter, cfg.experts, cfg.top_k
+    print(f"[bench] {cfg.name}: generating inputs", file=sys.stderr, flush=True)
+    inp = make_inputs(cfg, seed=args.seed, threads=16)
+    layer = MoELayer(cfg, inp)
+    x = to_device(cfg, inp["x"])
+    dev = x.device
+    c = layer.c
+    ws = layer.ws
+    edt = x.dtype
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    xp = torch.empty((T * k, H), dtype=edt, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offs = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    rt = torch.empty(T * k, dtype=torch.int32, device=dev)
+    sr = torch.empty((T, k), dtype=torch.int32, device=dev)
+    h = torch.empty((T * k, I), dtype=edt, device=dev)
+    y = torch.empty((T * k, H), dtype=edt, device=dev)
+    out = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+    names = ["route", "permute", "gemm_up", "gemm_down", "combine"]
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        L.moe_route(c, x, layer.w_router, layer.bias, logits, idx, w, ws, stream)
+        if ev: ev[1].record(stream)
+        L.moe_permute(c, x, idx, xp, counts, offs, rt, sr, ws, stream)
+        if ev: ev[2].record(stream)
+        L.moe_expert_up(c, xp, offs, layer.w_gate, layer.w_up, h, stream)
+        if ev: ev[3].record(stream)
+        L.moe_expert_down(c, h, offs, layer.w_down, y, stream)
+        if ev: ev[4].record(stream)
+        L.moe_combine(c, y, sr, w, out, stream)
+        if ev: ev[5].record(stream)
+
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty(n, dtype=torch.uint8, device=dev)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    stage_ms = {n: float(np.mean([events[s][i].elapsed_time(events[s][i + 1])
+                                  for s in range(args.steps)])) for i, n in enumerate(names)}
+
+    n_kept = int(offs[-1].item())
+    up_flops = (4 if cfg.activation == C.SWIGLU else 2) * n_kept * H * I
+    down_flops = 2 * n_kept * H * I
+    ffn_flops = up_flops + down_flops
+    total_flops = 2 * T * H * E + ffn_flops
+    up_tflops = up_flops / (stage_ms["gemm_up"] * 1e-3) / 1e12
+    ffn_tflops = ffn_flops / ((stage_ms["gemm_up"] + stage_ms["gemm_down"]) * 1e-3) / 1e12
+    es = 2 if cfg.dtype == C.BF16 else 4
+    # algorithmic bytes of the bandwidth-bound steps
+    route_bytes = T * H * es + H * E * es + T * E * 4 + T * k * 8
+    permute_bytes = T * H * es + n_kept * H * es + T * k * 4 * 4
+    combine_bytes = n_kept * H * es + T * H * es + T * k * 8
+    traffic = measured_traffic()
+    result = {
+        "metric": METRIC,
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == C.BF16 else "f32",
+        "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) weights)",
+        "config": {"workload": cfg.description, "tokens": T, "hidden": H, "inter": I,
+                   "experts": E, "top_k": k, "capacity_factor": cfg.capacity_factor,
+                   "activation": cfg.activation, "kept_rows": n_kept},
+        "roofline": {"kernel": "grouped_gemm_bf16_kernel<SwiGLU> (moe_expert_up)",
+                     "bound": "mfma", "achieved": up_tflops, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": up_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": traffic, "algorithmic_flops": up_flops},
+        "grouped_gemm_frac_of_peak": ffn_tflops / PEAK_BF16_TFLOPS,
+        "layer_tflops": total_flops / (ms_per_step * 1e-3) / 1e12,
+        "stages_us": {n: v * 1e3 for n, v in stage_ms.items()},
+        "hbm_frac": {"route": route_bytes / (stage_ms["route"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                     "permute": permute_bytes / (stage_ms["permute"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                     "combine": combine_bytes / (stage_ms["combine"] * 1e-3) / 1e9 / PEAK_HBM_GBS},
+    }
+
+    result["device_flags"] = L.moe_read_device_status(c, ws, 3, stream)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, inp, out, logits, idx, args.cpu_sample_tokens,
+                                              result)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(cfg, inp, out_dev, logits_dev, idx_dev, n_tok, result):
+    """The oracle, as it is, on the first n_tok tokens of the same layer (its expert weights
+    widened to float64 one expert at a time). The same leg re-checks the timed outputs:
+    routing bit-exact from the GPU's own logits on every token, and the sampled tokens'
+    layer outputs against the oracle's."""
+    import numpy as np
+
+    import oracle as O
+    from mixture_experts_layer_37_amd.inputs import ExpertView, as_float, bf16_bits_to_f32
+    from mixture_experts_layer_37_amd.layer import from_device
+
+    ridx, _ = O.select_experts(logits_dev.cpu().numpy().astype(np.float64), cfg.top_k)
+    result["parity"] = {"routing_bit_exact": bool(np.array_equal(ridx, idx_dev.cpu().numpy()))}
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    n_tok = min(n_tok, cfg.tokens)
+    xs = as_float(cfg, inp["x"][:n_tok])
+    wg = ExpertView(cfg, inp["w_gate"]) if cfg.activation == "swiglu" else None
+    t0 = time.perf_counter()
+    ref = O.forward(xs, as_float(cfg, inp["w_router"]), inp["bias"], wg,
+                    ExpertView(cfg, inp["w_up"]), ExpertView(cfg, inp["w_down"]),
+                    top_k=cfg.top_k, activation=cfg.activation,
+                    capacity_factor=cfg.capacity_factor, renormalize=cfg.renormalize)
+    dt = time.perf_counter() - t0
+    rep = {"value": n_tok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"first {n_tok} of {cfg.tokens} tokens of the same layer, all experts; "
+                     f"{dt:.1f} s", "host_cpus": len(os.sched_getaffinity(0))}
+    if cfg.capacity_factor <= 0:      # a token prefix routes exactly as in the full batch
+        got = from_device(out_dev[:n_tok])
+        got = (bf16_bits_to_f32(got) if got.dtype == np.uint16 else got).astype(np.float64)
+        use = ref["margin"] >= 1e-4
+        err = np.abs(got[use] - ref["out"][use])
+        result["parity"]["sample_max_rel"] = float(err.max() / np.abs(ref["out"][use]).max())
+        result["parity"]["sample_mean_rel"] = float(err.sum() / np.abs(ref["out"][use]).sum())
+    return rep
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,190 @@
+/*
+ * moe.h -- C ABI of an MI355X (gfx950) Mixture-of-Experts FFN layer forward.
+ *
+ * The layer (intelliparadigm.com, "MoE模型高效推理：CANN算子库优化实践", section 2.1,
+ * the moe_layer pseudo-code; gitcode.csdn.net, "ops-transformer 仓库 - MoE 算子优化实战",
+ * section "核心代码解析", MoEOperator::Forward):
+ *
+ *   logits = x @ W_router (+ gate_bias)             gate GEMM
+ *   p      = softmax(logits)                          per token, over E experts
+ *   idx, w = top-k of p, renormalised over the k      lower expert index wins ties
+ *   rows   = tokens grouped by expert, token order    capacity clamp, then gather
+ *   h      = silu(x_e Wg[e]) * (x_e Wu[e])            grouped GEMM 1 (GELU: gelu(x_e Wu[e]))
+ *   y      = h Wd[e]                                  grouped GEMM 2
+ *   out[t] = sum_j w[t,j] * y[row(t,j)]               combine, one write per row, no atomics
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a device pointer owned by the caller; the library never
+ *     allocates, frees or keeps a pointer after returning. All scratch memory comes from
+ *     the caller's workspace `ws` of `ws_bytes` bytes (size it with moe_workspace_size);
+ *     it is sized for the worst case of T*k routed rows, so no routing outcome can
+ *     overflow it.
+ *   - Layouts are dense and row-major: x[T,H], W_router[H,E], W_gate/W_up[E,H,I],
+ *     W_down[E,I,H] (the pages' x[tokens,hidden] and expert weights
+ *     [num_experts,hidden,intermediate]: lshu.cn/news/82007, section 3). Element type is
+ *     cfg->dtype for x, the weights, x_perm, h, y_perm and out; logits and gate weights
+ *     are float32; expert ids and row indices are int32 (lshu.cn page, section 5.2).
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null stream), do no
+ *     device->host synchronisation (moe_read_device_status excepted) and keep no global
+ *     mutable state, so they are safe to call from several host threads. Calls that share
+ *     one workspace must be ordered on one stream.
+ *   - Argument errors are reported synchronously, before any HIP call, as a moe_status;
+ *     nothing aborts or prints. A failed kernel launch returns MOE_ERR_HIP and the HIP
+ *     error code is kept per host thread (moe_last_hip_error).
+ *   - Data errors found on the device (an expert id outside [0,E) or repeated within a
+ *     token, a non-finite logit) never cause an out-of-bounds access: the offending slot
+ *     is dropped and a flag is raised, to be read with moe_read_device_status. Ids are
+ *     never clamped silently.
+ *   - tokens == 0 is a valid empty call: once the configuration is valid, MOE_OK is
+ *     returned without inspecting any pointer and nothing is launched.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad size, k outside [1, E] ... */
+  MOE_ERR_UNSUPPORTED = 2,   /* valid but not supported: E or k above the maximum, a dtype /
+                                activation value outside the enums, bf16 sizes that are not
+                                multiples of the GEMM tiles */
+  MOE_ERR_WORKSPACE = 3,     /* ws_bytes smaller than moe_workspace_size() */
+  MOE_ERR_HIP = 4            /* a HIP call or kernel launch failed */
+} moe_status;
+
+enum { MOE_DTYPE_BF16 = 0, MOE_DTYPE_F32 = 1 };
+enum { MOE_ACT_SWIGLU = 0, MOE_ACT_GELU = 1 };
+/* device status flags (moe_read_device_status) */
+enum { MOE_FLAG_BAD_INDEX = 1, MOE_FLAG_NONFINITE_LOGIT = 2 };
+enum { MOE_MAX_EXPERTS = 256, MOE_MAX_TOPK = 16 };
+
+typedef struct moe_config {
+  int32_t tokens;            /* T >= 0 */
+  int32_t hidden;            /* H >= 1; bf16: multiple of 256 */
+  int32_t inter;             /* I >= 1; bf16: multiple of 128 (SwiGLU), 256 (GELU) */
+  int32_t experts;           /* E in [1, MOE_MAX_EXPERTS] */
+  int32_t top_k;             /* k in [1, min(E, MOE_MAX_TOPK)] */
+  int32_t activation;        /* MOE_ACT_SWIGLU or MOE_ACT_GELU */
+  int32_t dtype;             /* MOE_DTYPE_BF16 or MOE_DTYPE_F32 (f32: H multiple of 8) */
+  int32_t renormalize;       /* nonzero: weights renormalised over the k selected experts
+                                (mhpn.cn/news/871594 chapter 8, normalize_scores=True);
+                                zero: the raw softmax probabilities (intelliparadigm.com
+                                page, section 2.1) */
+  double capacity_factor;    /* <= 0: no limit. Otherwise each expert keeps at most
+                                C = ceil(capacity_factor * (T*k) / E) assignments, lowest
+                                token index first (hnwysp.cn/news/132341, section 3.2) */
+} moe_config;
+
+typedef void* moe_stream_t;  /* hipStream_t */
+
+/* Workspace bytes needed by every entry point below for this configuration. */
+moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes);
+
+/* The capacity C the kernels use: ceil(cf * (T*k) / E) evaluated in IEEE double, or T
+ * when cf <= 0. */
+moe_status moe_capacity(const moe_config* cfg, int32_t* capacity);
+
+/* Gate GEMM + softmax + top-k + weights (gitcode page, "核心代码解析": routing_module_,
+ * TopKRouting; hnwysp.cn page, section 2.1: top-k routing; section 4.1: softmax first).
+ *   x         [T,H] dtype, or NULL: then `logits` is an INPUT and only top-k runs
+ *   w_router  [H,E] dtype (ignored when x == NULL)
+ *   gate_bias [E] float32 or NULL, added to the logits before softmax and selection
+ *   logits    [T,E] float32: output (input when x == NULL)
+ *   topk_idx  [T,k] int32 out: experts in descending logit order, lower index first on ties
+ *   topk_w    [T,k] float32 out: softmax weights of those experts (renormalised if set);
+ *             NaN for a token with a NaN logit
+ * Non-finite logits raise MOE_FLAG_NONFINITE_LOGIT; NaN ranks below -inf. */
+moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
+                     const float* gate_bias, float* logits, int32_t* topk_idx, float* topk_w,
+                     void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* Histogram + scan + capacity clamp + gather of token rows by expert (gitcode page,
+ * SparseGather and the CSR storage of "MoE 算子核心原理"; lshu.cn page, section 4,
+ * npu_moe_token_preprocess).
+ *   x              [T,H] dtype
+ *   topk_idx       [T,k] int32 expert ids (invalid or repeated ids are dropped + flagged)
+ *   x_perm         [T*k,H] dtype out: rows grouped by expert, token order inside an expert;
+ *                  rows >= expert_offsets[E] are left untouched
+ *   expert_counts  [E] int32 out: assignments per expert before the capacity clamp
+ *   expert_offsets [E+1] int32 out: first row of each expert after the clamp
+ *   row_token      [T*k] int32 out: source token of each row (rows < expert_offsets[E])
+ *   slot_row       [T,k] int32 out: row of slot (t,j), -1 if dropped or invalid */
+moe_status moe_permute(const moe_config* cfg, const void* x, const int32_t* topk_idx,
+                       void* x_perm, int32_t* expert_counts, int32_t* expert_offsets,
+                       int32_t* row_token, int32_t* slot_row, void* ws, size_t ws_bytes,
+                       moe_stream_t stream);
+
+/* Grouped GEMM 1 with the activation fused: for the rows of each expert e,
+ * h = silu(x_perm Wg[e]) * (x_perm Wu[e])  (SwiGLU)   or   h = gelu(x_perm Wu[e])  (GELU)
+ * (lshu.cn page, section 3: npu_moe_final_optimizer_mm is this up-projection; the
+ * activation and the down-projection follow it).
+ *   x_perm [rows,H], expert_offsets [E+1] (device; values are clamped to [0, T*k] and an
+ *   empty or reversed range counts as empty), w_gate [E,H,I] (NULL for GELU),
+ *   w_up [E,H,I], h [T*k,I] out (rows >= expert_offsets[E] untouched). */
+moe_status moe_expert_up(const moe_config* cfg, const void* x_perm,
+                         const int32_t* expert_offsets, const void* w_gate, const void* w_up,
+                         void* h, moe_stream_t stream);
+
+/* Grouped GEMM 2: y_perm = h Wd[e] for the rows of each expert (lshu.cn page, section 4,
+ * npu_moe_matmul). h [rows,I], w_down [E,I,H], y_perm [T*k,H] out. */
+moe_status moe_expert_down(const moe_config* cfg, const void* h, const int32_t* expert_offsets,
+                           const void* w_down, void* y_perm, moe_stream_t stream);
+
+/* moe_expert_up followed by moe_expert_down, with h kept in the workspace. */
+moe_status moe_grouped_ffn(const moe_config* cfg, const void* x_perm,
+                           const int32_t* expert_offsets, const void* w_gate, const void* w_up,
+                           const void* w_down, void* y_perm, void* ws, size_t ws_bytes,
+                           moe_stream_t stream);
+
+/* Weighted combine back to token order (lshu.cn page, section 4,
+ * npu_moe_token_postprocess; the pages aggregate with an atomic scatter-add, this library
+ * gathers instead): out[t] = sum over kept slots of topk_w[t,j] * y_perm[slot_row[t,j]]
+ * (a slot is kept when 0 <= slot_row[t,j] < T*k),
+ * accumulated in float32 in slot order and written once per row; a token whose slots were
+ * all dropped gets zeros. y_perm [rows,H], slot_row [T,k], topk_w [T,k], out [T,H]. */
+moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* slot_row,
+                       const float* topk_w, void* out, moe_stream_t stream);
+
+/* The whole layer: moe_route -> moe_permute -> moe_grouped_ffn -> moe_combine, with every
+ * intermediate in `ws` (readable with moe_workspace_view until the next call). */
+moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_router,
+                       const float* gate_bias, const void* w_gate, const void* w_up,
+                       const void* w_down, void* out, void* ws, size_t ws_bytes,
+                       moe_stream_t stream);
+
+/* Where moe_forward keeps an intermediate inside `ws` (device address and byte size). */
+enum {
+  MOE_WS_LOGITS = 0,      /* [T,E] float32 */
+  MOE_WS_TOPK_IDX = 1,    /* [T,k] int32 */
+  MOE_WS_TOPK_W = 2,      /* [T,k] float32 */
+  MOE_WS_COUNTS = 3,      /* [E] int32 */
+  MOE_WS_OFFSETS = 4,     /* [E+1] int32 */
+  MOE_WS_SLOT_ROW = 5,    /* [T,k] int32 */
+  MOE_WS_ROW_TOKEN = 6,   /* [T*k] int32 */
+  MOE_WS_X_PERM = 7,      /* [T*k,H] dtype */
+  MOE_WS_H = 8,           /* [T*k,I] dtype */
+  MOE_WS_Y_PERM = 9,      /* [T*k,H] dtype */
+  MOE_WS_NUM_VIEWS = 10
+};
+moe_status moe_workspace_view(const moe_config* cfg, void* ws, int32_t which, void** dev_ptr,
+                              size_t* bytes);
+
+/* OR of the device flags raised by the last moe_route (which = 1), the last moe_permute
+ * (which = 2) or both (which = 3) that used this workspace; moe_forward runs both.
+ * Synchronises `stream`. */
+moe_status moe_read_device_status(const moe_config* cfg, void* ws, int32_t which,
+                                  moe_stream_t stream, int32_t* flags);
+
+const char* moe_status_string(moe_status status);
+int32_t moe_last_hip_error(void);   /* hipError_t of this thread's last MOE_ERR_HIP */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,50 @@
+// Shared device helpers for the gfx950 MoE kernels: bf16 conversion, vector types and the
+// MFMA operand types. Internal to the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kMaxExperts = 256;
+constexpr int kMaxTopK = 16;
+constexpr int kCountBlockTokens = 1024;   // tokens per permute histogram block
+constexpr int kRouteFlagGroup = 16;       // tokens per route flag word
+
+typedef uint16_t bf16_t;                  // raw bfloat16 bits
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// float -> bfloat16, round to nearest, ties to even; NaN -> quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// Element storage helpers: bf16 is stored as raw 16-bit patterns.
+template <typename T> struct Elem;
+template <> struct Elem<bf16_t> {
+  static __device__ __forceinline__ float load(const bf16_t* p) { return bf16_to_f32(*p); }
+  static __device__ __forceinline__ bf16_t from_f32(float f) { return (bf16_t)f32_to_bf16(f); }
+  static __device__ __forceinline__ float to_f32(bf16_t v) { return bf16_to_f32(v); }
+};
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ float from_f32(float f) { return f; }
+  static __device__ __forceinline__ float to_f32(float v) { return v; }
+};
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+}  // namespace moe

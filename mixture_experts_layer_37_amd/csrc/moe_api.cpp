@@ -1,0 +1,377 @@
+// Host side of the C ABI declared in include/moe.h: argument validation (before any HIP
+// call), workspace layout, the capacity formula and the launch sequence on the caller's
+// stream. No allocation, no global mutable state apart from the per-thread last HIP error.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "moe.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+enum Region {
+  R_WT, R_LOGITS, R_TOPK_IDX, R_TOPK_W, R_ROUTE_FLAGS, R_HIST, R_PERM_FLAGS, R_COUNTS,
+  R_OFFSETS, R_SLOT_ROW, R_ROW_TOKEN, R_X_PERM, R_H, R_Y_PERM, R_NUM
+};
+
+struct Layout {
+  size_t off[R_NUM];
+  size_t size[R_NUM];
+  size_t total;
+};
+
+constexpr size_t kAlign = 256;
+
+size_t esize(const moe_config* c) { return c->dtype == MOE_DTYPE_BF16 ? 2 : 4; }
+
+Layout layout_of(const moe_config* c) {
+  const size_t T = (size_t)c->tokens, H = (size_t)c->hidden, I = (size_t)c->inter;
+  const size_t E = (size_t)c->experts, k = (size_t)c->top_k, es = esize(c);
+  const size_t N = T * k;
+  const size_t NB = (size_t)moe::permute_count_blocks(c->tokens);
+  Layout L;
+  L.size[R_WT] = c->dtype == MOE_DTYPE_BF16 ? (size_t)moe::route_padded_experts(c->experts) * H * 2 : 0;
+  L.size[R_LOGITS] = T * E * 4;
+  L.size[R_TOPK_IDX] = N * 4;
+  L.size[R_TOPK_W] = N * 4;
+  L.size[R_ROUTE_FLAGS] = ((T + moe::kRouteFlagGroup - 1) / moe::kRouteFlagGroup) * 4;
+  L.size[R_HIST] = NB * E * 4;
+  L.size[R_PERM_FLAGS] = NB * 4;
+  L.size[R_COUNTS] = E * 4;
+  L.size[R_OFFSETS] = (E + 1) * 4;
+  L.size[R_SLOT_ROW] = N * 4;
+  L.size[R_ROW_TOKEN] = N * 4;
+  L.size[R_X_PERM] = N * H * es;
+  L.size[R_H] = N * I * es;
+  L.size[R_Y_PERM] = N * H * es;
+  size_t o = 0;
+  for (int r = 0; r < R_NUM; ++r) {
+    L.off[r] = o;
+    o += (L.size[r] + kAlign - 1) / kAlign * kAlign;
+  }
+  L.total = o;
+  return L;
+}
+
+template <typename P> P* region(void* ws, const Layout& L, Region r) {
+  return reinterpret_cast<P*>(static_cast<char*>(ws) + L.off[r]);
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+moe_status check_cfg(const moe_config* c) {
+  if (c == nullptr) return MOE_ERR_INVALID_ARG;
+  if (c->tokens < 0 || c->hidden < 1 || c->inter < 1 || c->experts < 1 || c->top_k < 1)
+    return MOE_ERR_INVALID_ARG;
+  if (c->top_k > c->experts) return MOE_ERR_INVALID_ARG;
+  if (std::isnan(c->capacity_factor)) return MOE_ERR_INVALID_ARG;
+  if (c->dtype != MOE_DTYPE_BF16 && c->dtype != MOE_DTYPE_F32) return MOE_ERR_UNSUPPORTED;
+  if (c->activation != MOE_ACT_SWIGLU && c->activation != MOE_ACT_GELU) return MOE_ERR_UNSUPPORTED;
+  if (c->experts > MOE_MAX_EXPERTS || c->top_k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
+  if (c->dtype == MOE_DTYPE_BF16) {
+    if (c->hidden % 256 != 0) return MOE_ERR_UNSUPPORTED;
+    if (c->inter % (c->activation == MOE_ACT_SWIGLU ? 128 : 256) != 0) return MOE_ERR_UNSUPPORTED;
+  } else if (c->hidden % 8 != 0) {
+    return MOE_ERR_UNSUPPORTED;
+  }
+  const long long T = c->tokens, k = c->top_k;
+  const long long wide = (long long)(c->hidden > c->inter ? c->hidden : c->inter);
+  if (T * k > INT_MAX || T * c->experts > INT_MAX || T * k * wide > (1LL << 40))
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int capacity_of(const moe_config* c) {
+  if (!(c->capacity_factor > 0.0)) return c->tokens;
+  const double v = std::ceil((c->capacity_factor * (double)((long long)c->tokens * c->top_k)) /
+                             (double)c->experts);
+  return v >= (double)INT_MAX ? INT_MAX : (int)v;
+}
+
+moe_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  g_last_hip_error = (int)e;
+  return MOE_ERR_HIP;
+}
+
+#define MOE_TRY(expr)                              \
+  do {                                             \
+    const moe_status st_ = (expr);                 \
+    if (st_ != MOE_OK) return st_;                 \
+  } while (0)
+
+moe_status check_ws(const moe_config* c, void* ws, size_t ws_bytes) {
+  if (ws == nullptr || !aligned(ws, 16)) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < layout_of(c).total) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+moe_status need(const void* p, size_t align) {
+  return (p != nullptr && aligned(p, align)) ? MOE_OK : MOE_ERR_INVALID_ARG;
+}
+
+// ---- the steps, arguments already validated
+moe_status do_route(const moe_config* c, const void* x, const void* w_router, const float* bias,
+                    float* logits, int32_t* idx, float* w, void* ws, hipStream_t s) {
+  const Layout L = layout_of(c);
+  int32_t* flags = region<int32_t>(ws, L, R_ROUTE_FLAGS);
+  const int T = c->tokens, H = c->hidden, E = c->experts, k = c->top_k;
+  const int renorm = c->renormalize != 0;
+  if (x == nullptr)
+    return hip_status(moe::launch_route_topk(logits, idx, w, flags, T, E, k, renorm, s));
+  if (c->dtype == MOE_DTYPE_BF16) {
+    moe::bf16_t* wt = region<moe::bf16_t>(ws, L, R_WT);
+    MOE_TRY(hip_status(moe::launch_router_transpose((const moe::bf16_t*)w_router, wt, H, E, s)));
+    return hip_status(moe::launch_route_bf16((const moe::bf16_t*)x, wt, bias, logits, idx, w,
+                                             flags, T, H, E, k, renorm, s));
+  }
+  MOE_TRY(hip_status(moe::launch_route_logits_f32((const float*)x, (const float*)w_router, bias,
+                                                  logits, T, H, E, s)));
+  return hip_status(moe::launch_route_topk(logits, idx, w, flags, T, E, k, renorm, s));
+}
+
+moe_status do_permute(const moe_config* c, const void* x, const int32_t* idx, void* x_perm,
+                      int32_t* counts, int32_t* offsets, int32_t* row_token, int32_t* slot_row,
+                      void* ws, hipStream_t s) {
+  const Layout L = layout_of(c);
+  const int cap = capacity_of(c);
+  return hip_status(moe::launch_permute(
+      x, (int)esize(c), idx, x_perm, counts, offsets, row_token, slot_row,
+      region<int32_t>(ws, L, R_HIST), region<int32_t>(ws, L, R_PERM_FLAGS), c->tokens, c->hidden,
+      c->experts, c->top_k, cap < c->tokens ? cap : c->tokens, s));
+}
+
+moe_status do_up(const moe_config* c, const void* x_perm, const int32_t* offsets,
+                 const void* w_gate, const void* w_up, void* h, hipStream_t s) {
+  const int swiglu = c->activation == MOE_ACT_SWIGLU;
+  const int epi = swiglu ? moe::EPI_SWIGLU : moe::EPI_GELU;
+  const int rows = c->tokens * c->top_k;
+  if (c->dtype == MOE_DTYPE_BF16)
+    return hip_status(moe::launch_gemm_bf16(
+        epi, (const moe::bf16_t*)x_perm, offsets,
+        (const moe::bf16_t*)(swiglu ? w_gate : w_up), (const moe::bf16_t*)w_up,
+        (moe::bf16_t*)h, c->experts, c->hidden, c->inter, rows, s));
+  return hip_status(moe::launch_gemm_f32(epi, (const float*)x_perm, offsets,
+                                         (const float*)(swiglu ? w_gate : w_up),
+                                         (const float*)w_up, (float*)h, c->experts, c->hidden,
+                                         c->inter, rows, s));
+}
+
+moe_status do_down(const moe_config* c, const void* h, const int32_t* offsets,
+                   const void* w_down, void* y, hipStream_t s) {
+  const int rows = c->tokens * c->top_k;
+  if (c->dtype == MOE_DTYPE_BF16)
+    return hip_status(moe::launch_gemm_bf16(moe::EPI_NONE, (const moe::bf16_t*)h, offsets,
+                                            (const moe::bf16_t*)w_down, nullptr,
+                                            (moe::bf16_t*)y, c->experts, c->inter, c->hidden,
+                                            rows, s));
+  return hip_status(moe::launch_gemm_f32(moe::EPI_NONE, (const float*)h, offsets,
+                                         (const float*)w_down, nullptr, (float*)y, c->experts,
+                                         c->inter, c->hidden, rows, s));
+}
+
+moe_status do_combine(const moe_config* c, const void* y, const int32_t* slot_row,
+                      const float* w, void* out, hipStream_t s) {
+  return hip_status(moe::launch_combine(c->dtype == MOE_DTYPE_BF16, y, slot_row, w, out,
+                                        c->tokens, c->hidden, c->top_k, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes) {
+  MOE_TRY(check_cfg(cfg));
+  if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
+  *bytes = layout_of(cfg).total;
+  return MOE_OK;
+}
+
+moe_status moe_capacity(const moe_config* cfg, int32_t* capacity) {
+  MOE_TRY(check_cfg(cfg));
+  if (capacity == nullptr) return MOE_ERR_INVALID_ARG;
+  *capacity = capacity_of(cfg);
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
+                     const float* gate_bias, float* logits, int32_t* topk_idx, float* topk_w,
+                     void* ws, size_t ws_bytes, moe_stream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  if (cfg->tokens == 0) return MOE_OK;   // empty batch: nothing to read or write
+  if (x != nullptr) {
+    MOE_TRY(need(x, 16));
+    MOE_TRY(need(w_router, cfg->dtype == MOE_DTYPE_BF16 ? 2 : 4));
+    if (gate_bias != nullptr) MOE_TRY(need(gate_bias, 4));
+  }
+  MOE_TRY(need(logits, 4));
+  MOE_TRY(need(topk_idx, 4));
+  MOE_TRY(need(topk_w, 4));
+  MOE_TRY(check_ws(cfg, ws, ws_bytes));
+  return do_route(cfg, x, w_router, gate_bias, logits, topk_idx, topk_w, ws,
+                  (hipStream_t)stream);
+}
+
+moe_status moe_permute(const moe_config* cfg, const void* x, const int32_t* topk_idx,
+                       void* x_perm, int32_t* expert_counts, int32_t* expert_offsets,
+                       int32_t* row_token, int32_t* slot_row, void* ws, size_t ws_bytes,
+                       moe_stream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  if (cfg->tokens == 0) return MOE_OK;   // empty batch: nothing to read or write
+  MOE_TRY(need(x, 16));
+  MOE_TRY(need(topk_idx, 4));
+  MOE_TRY(need(x_perm, 16));
+  MOE_TRY(need(expert_counts, 4));
+  MOE_TRY(need(expert_offsets, 4));
+  MOE_TRY(need(row_token, 4));
+  MOE_TRY(need(slot_row, 4));
+  MOE_TRY(check_ws(cfg, ws, ws_bytes));
+  return do_permute(cfg, x, topk_idx, x_perm, expert_counts, expert_offsets, row_token, slot_row,
+                    ws, (hipStream_t)stream);
+}
+
+moe_status moe_expert_up(const moe_config* cfg, const void* x_perm,
+                         const int32_t* expert_offsets, const void* w_gate, const void* w_up,
+                         void* h, moe_stream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  if (cfg->tokens == 0) return MOE_OK;   // empty batch: nothing to read or write
+  MOE_TRY(need(x_perm, 16));
+  MOE_TRY(need(expert_offsets, 4));
+  if (cfg->activation == MOE_ACT_SWIGLU) MOE_TRY(need(w_gate, 16));
+  MOE_TRY(need(w_up, 16));
+  MOE_TRY(need(h, 16));
+  return do_up(cfg, x_perm, expert_offsets, w_gate, w_up, h, (hipStream_t)stream);
+}
+
+moe_status moe_expert_down(const moe_config* cfg, const void* h, const int32_t* expert_offsets,
+                           const void* w_down, void* y_perm, moe_stream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  if (cfg->tokens == 0) return MOE_OK;   // empty batch: nothing to read or write
+  MOE_TRY(need(h, 16));
+  MOE_TRY(need(expert_offsets, 4));
+  MOE_TRY(need(w_down, 16));
+  MOE_TRY(need(y_perm, 16));
+  return do_down(cfg, h, expert_offsets, w_down, y_perm, (hipStream_t)stream);
+}
+
+moe_status moe_grouped_ffn(const moe_config* cfg, const void* x_perm,
+                           const int32_t* expert_offsets, const void* w_gate, const void* w_up,
+                           const void* w_down, void* y_perm, void* ws, size_t ws_bytes,
+                           moe_stream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  if (cfg->tokens == 0) return MOE_OK;   // empty batch: nothing to read or write
+  MOE_TRY(need(x_perm, 16));
+  MOE_TRY(need(expert_offsets, 4));
+  if (cfg->activation == MOE_ACT_SWIGLU) MOE_TRY(need(w_gate, 16));
+  MOE_TRY(need(w_up, 16));
+  MOE_TRY(need(w_down, 16));
+  MOE_TRY(need(y_perm, 16));
+  MOE_TRY(check_ws(cfg, ws, ws_bytes));
+  const Layout L = layout_of(cfg);
+  void* h = region<void>(ws, L, R_H);
+  const hipStream_t s = (hipStream_t)stream;
+  MOE_TRY(do_up(cfg, x_perm, expert_offsets, w_gate, w_up, h, s));
+  return do_down(cfg, h, expert_offsets, w_down, y_perm, s);
+}
+
+moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* slot_row,
+                       const float* topk_w, void* out, moe_stream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  if (cfg->tokens == 0) return MOE_OK;   // empty batch: nothing to read or write
+  MOE_TRY(need(y_perm, 16));
+  MOE_TRY(need(slot_row, 4));
+  MOE_TRY(need(topk_w, 4));
+  MOE_TRY(need(out, 16));
+  return do_combine(cfg, y_perm, slot_row, topk_w, out, (hipStream_t)stream);
+}
+
+moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_router,
+                       const float* gate_bias, const void* w_gate, const void* w_up,
+                       const void* w_down, void* out, void* ws, size_t ws_bytes,
+                       moe_stream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  if (cfg->tokens == 0) return MOE_OK;   // empty batch: nothing to read or write
+  MOE_TRY(need(x, 16));
+  MOE_TRY(need(w_router, cfg->dtype == MOE_DTYPE_BF16 ? 2 : 4));
+  if (gate_bias != nullptr) MOE_TRY(need(gate_bias, 4));
+  if (cfg->activation == MOE_ACT_SWIGLU) MOE_TRY(need(w_gate, 16));
+  MOE_TRY(need(w_up, 16));
+  MOE_TRY(need(w_down, 16));
+  MOE_TRY(need(out, 16));
+  MOE_TRY(check_ws(cfg, ws, ws_bytes));
+  const Layout L = layout_of(cfg);
+  const hipStream_t s = (hipStream_t)stream;
+  float* logits = region<float>(ws, L, R_LOGITS);
+  int32_t* idx = region<int32_t>(ws, L, R_TOPK_IDX);
+  float* w = region<float>(ws, L, R_TOPK_W);
+  int32_t* counts = region<int32_t>(ws, L, R_COUNTS);
+  int32_t* offsets = region<int32_t>(ws, L, R_OFFSETS);
+  int32_t* slot_row = region<int32_t>(ws, L, R_SLOT_ROW);
+  int32_t* row_token = region<int32_t>(ws, L, R_ROW_TOKEN);
+  void* x_perm = region<void>(ws, L, R_X_PERM);
+  void* h = region<void>(ws, L, R_H);
+  void* y = region<void>(ws, L, R_Y_PERM);
+  MOE_TRY(do_route(cfg, x, w_router, gate_bias, logits, idx, w, ws, s));
+  MOE_TRY(do_permute(cfg, x, idx, x_perm, counts, offsets, row_token, slot_row, ws, s));
+  MOE_TRY(do_up(cfg, x_perm, offsets, w_gate, w_up, h, s));
+  MOE_TRY(do_down(cfg, h, offsets, w_down, y, s));
+  return do_combine(cfg, y, slot_row, w, out, s);
+}
+
+moe_status moe_workspace_view(const moe_config* cfg, void* ws, int32_t which, void** dev_ptr,
+                              size_t* bytes) {
+  MOE_TRY(check_cfg(cfg));
+  if (ws == nullptr || dev_ptr == nullptr) return MOE_ERR_INVALID_ARG;
+  static const Region map[MOE_WS_NUM_VIEWS] = {R_LOGITS,   R_TOPK_IDX, R_TOPK_W,  R_COUNTS,
+                                               R_OFFSETS,  R_SLOT_ROW, R_ROW_TOKEN, R_X_PERM,
+                                               R_H,        R_Y_PERM};
+  if (which < 0 || which >= MOE_WS_NUM_VIEWS) return MOE_ERR_INVALID_ARG;
+  const Layout L = layout_of(cfg);
+  *dev_ptr = static_cast<char*>(ws) + L.off[map[which]];
+  if (bytes != nullptr) *bytes = L.size[map[which]];
+  return MOE_OK;
+}
+
+moe_status moe_read_device_status(const moe_config* cfg, void* ws, int32_t which,
+                                  moe_stream_t stream, int32_t* flags) {
+  MOE_TRY(check_cfg(cfg));
+  if (ws == nullptr || flags == nullptr || which < 1 || which > 3) return MOE_ERR_INVALID_ARG;
+  *flags = 0;
+  if (cfg->tokens == 0) return MOE_OK;
+  const Layout L = layout_of(cfg);
+  const hipStream_t s = (hipStream_t)stream;
+  std::vector<int32_t> host;
+  int32_t acc = 0;
+  for (int part = 1; part <= 2; ++part) {
+    if (!(which & part)) continue;
+    const Region r = part == 1 ? R_ROUTE_FLAGS : R_PERM_FLAGS;
+    host.assign(L.size[r] / 4, 0);
+    MOE_TRY(hip_status(hipMemcpyAsync(host.data(), region<void>(ws, L, r), L.size[r],
+                                      hipMemcpyDeviceToHost, s)));
+    MOE_TRY(hip_status(hipStreamSynchronize(s)));
+    for (int32_t v : host) acc |= v;
+  }
+  *flags = acc;
+  return MOE_OK;
+}
+
+const char* moe_status_string(moe_status status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+int32_t moe_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,194 @@
+// Permute: group the (token, slot) assignments by expert, in token order, apply the
+// capacity clamp and gather the token rows (gitcode.csdn.net, "ops-transformer 仓库 - MoE
+// 算子优化实战": a per-expert mask feeds SparseGather, and sparse data is kept CSR-style;
+// lshu.cn/news/82007, section 4: npu_moe_token_preprocess reorders the tokens).
+//
+// Three launches, no float and no global atomics:
+//   count  -- 1024 tokens per block. Per wave and expert a 64-bit lane mask (LDS OR);
+//             popcounts give the block's per-expert histogram and each assignment's rank
+//             inside the block in token order. Invalid or repeated ids are dropped, flagged.
+//   scan   -- one block: per expert, exclusive prefix over the count blocks (in place),
+//             pre-capacity counts, kept = min(count, C), and the kept offsets (a scan over E).
+//   gather -- one wave per token: row = offsets[e] + block prefix + in-block rank, kept iff
+//             below C; writes slot_row / row_token and copies the token row once into each
+//             of its kept rows with 16-byte loads and stores.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+int permute_count_blocks(int T) { return (T + kCountBlockTokens - 1) / kCountBlockTokens; }
+
+__global__ __launch_bounds__(1024) void permute_count_kernel(const int32_t* __restrict__ idx,
+                                                             int32_t* __restrict__ hist,
+                                                             int32_t* __restrict__ slot_row,
+                                                             int32_t* __restrict__ flags, int T,
+                                                             int E, int k) {
+  constexpr int NW = kCountBlockTokens / kWave;   // 16 waves
+  __shared__ unsigned long long masks[NW * kMaxExperts];
+  __shared__ int wpre[NW * kMaxExperts];
+  __shared__ int sbad;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int i = tid; i < NW * E; i += blockDim.x) masks[i] = 0ull;
+  if (tid == 0) sbad = 0;
+  __syncthreads();
+
+  const int t = blockIdx.x * kCountBlockTokens + tid;
+  int ev[kMaxTopK];
+  unsigned valid = 0u;
+  bool bad = false;
+  if (t < T) {
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (j < k) {
+        const int e = idx[(size_t)t * k + j];
+        bool ok = (unsigned)e < (unsigned)E;
+#pragma unroll
+        for (int jj = 0; jj < j; ++jj) ok &= (ev[jj] != e);
+        ev[j] = e;
+        if (ok) {
+          valid |= 1u << j;
+          atomicOr(&masks[wave * E + e], 1ull << lane);
+        } else {
+          bad = true;
+        }
+      }
+    }
+  }
+  if (bad) sbad = 1;
+  __syncthreads();
+  for (int e = tid; e < E; e += blockDim.x) {
+    int run = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      wpre[w * E + e] = run;
+      run += __popcll(masks[w * E + e]);
+    }
+    hist[(size_t)blockIdx.x * E + e] = run;
+  }
+  __syncthreads();
+  if (t < T) {
+    const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (j < k) {
+        int r = -1;
+        if (valid & (1u << j)) {
+          const int e = ev[j];
+          r = wpre[wave * E + e] + __popcll(masks[wave * E + e] & below);
+        }
+        slot_row[(size_t)t * k + j] = r;
+      }
+    }
+  }
+  if (tid == 0) flags[blockIdx.x] = sbad ? 1 /* MOE_FLAG_BAD_INDEX */ : 0;
+}
+
+__global__ __launch_bounds__(256) void permute_scan_kernel(int32_t* __restrict__ hist,
+                                                           int32_t* __restrict__ counts,
+                                                           int32_t* __restrict__ offsets, int NB,
+                                                           int E, int cap) {
+  __shared__ int wsum[4];
+  const int e = threadIdx.x, wave = e >> 6, lane = e & 63;
+  int run = 0;
+  if (e < E) {
+    int b = 0;
+    for (; b + 8 <= NB; b += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = hist[(size_t)(b + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        hist[(size_t)(b + u) * E + e] = run;
+        run += v[u];
+      }
+    }
+    for (; b < NB; ++b) {
+      const int v = hist[(size_t)b * E + e];
+      hist[(size_t)b * E + e] = run;
+      run += v;
+    }
+    counts[e] = run;
+  }
+  const int kept = e < E ? min(run, cap) : 0;
+  int incl = kept;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int n = __shfl_up(incl, o);
+    if (lane >= o) incl += n;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int pre = 0;
+  for (int w = 0; w < wave; ++w) pre += wsum[w];
+  incl += pre;
+  if (e < E) offsets[e] = incl - kept;
+  if (e == E - 1) offsets[E] = incl;
+}
+
+template <int U>
+__global__ __launch_bounds__(256) void permute_gather_kernel(
+    const uint4* __restrict__ x, const int32_t* __restrict__ idx, int32_t* __restrict__ slot_row,
+    int32_t* __restrict__ row_token, const int32_t* __restrict__ prefix,
+    const int32_t* __restrict__ offsets, uint4* __restrict__ x_perm, int T, int E, int k, int cap,
+    int row_vecs) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  int row = -1;
+  if (lane < k) {
+    const int r = slot_row[(size_t)t * k + lane];
+    if (r >= 0) {
+      const int e = idx[(size_t)t * k + lane];
+      const int pos = prefix[(size_t)(t / kCountBlockTokens) * E + e] + r;
+      if (pos < cap) row = offsets[e] + pos;
+    }
+    slot_row[(size_t)t * k + lane] = row;
+    if (row >= 0) row_token[row] = t;
+  }
+  int rows[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) rows[j] = __shfl(row, j);
+  const uint4* src = x + (size_t)t * row_vecs;
+  for (int base = 0; base < row_vecs; base += 64 * U) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = base + u * 64 + lane;
+      if (c < row_vecs) v[u] = src[c];
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (j < k && rows[j] >= 0) {
+        uint4* dst = x_perm + (size_t)rows[j] * row_vecs;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int c = base + u * 64 + lane;
+          if (c < row_vecs) dst[c] = v[u];
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_permute(const void* x, int elem_bytes, const int32_t* topk_idx, void* x_perm,
+                          int32_t* counts, int32_t* offsets, int32_t* row_token,
+                          int32_t* slot_row, int32_t* hist, int32_t* flags, int T, int H, int E,
+                          int k, int cap, hipStream_t s) {
+  const int NB = permute_count_blocks(T);
+  hipLaunchKernelGGL(permute_count_kernel, dim3(NB), dim3(kCountBlockTokens), 0, s, topk_idx,
+                     hist, slot_row, flags, T, E, k);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(256), 0, s, hist, counts, offsets, NB, E,
+                     cap);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int row_vecs = (int)((size_t)H * elem_bytes / 16);
+  hipLaunchKernelGGL((permute_gather_kernel<8>), dim3((T + 3) / 4), dim3(256), 0, s,
+                     (const uint4*)x, topk_idx, slot_row, row_token, hist, offsets,
+                     (uint4*)x_perm, T, E, k, cap, row_vecs);
+  return hipGetLastError();
+}
+
+}  // namespace moe

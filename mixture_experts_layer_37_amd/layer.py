@@ -1,0 +1,79 @@
+"""Device-side plumbing around the C ABI: moving seeded inputs into torch tensors, owning a
+workspace and exposing its intermediates as tensor views. No layer arithmetic here."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import _lib as L
+from .configs import BF16, SWIGLU, MoEConfig
+
+_VIEW_DTYPES = {
+    L.MOE_WS_LOGITS: torch.float32, L.MOE_WS_TOPK_IDX: torch.int32, L.MOE_WS_TOPK_W: torch.float32,
+    L.MOE_WS_COUNTS: torch.int32, L.MOE_WS_OFFSETS: torch.int32, L.MOE_WS_SLOT_ROW: torch.int32,
+    L.MOE_WS_ROW_TOKEN: torch.int32,
+}
+
+
+def elem_dtype(cfg: MoEConfig) -> torch.dtype:
+    return torch.bfloat16 if cfg.dtype == BF16 else torch.float32
+
+
+def to_device(cfg: MoEConfig, a, device="cuda") -> torch.Tensor | None:
+    """numpy input (bf16 bits as uint16, or float32) -> device tensor of the layer dtype."""
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def from_device(t: torch.Tensor) -> np.ndarray:
+    """device tensor -> numpy (bf16 as uint16 bits, others as is)."""
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+class MoELayer:
+    """Holds device weights and one workspace; ``forward`` calls moe_forward."""
+
+    def __init__(self, cfg: MoEConfig, inputs: dict, device="cuda", tokens: int | None = None):
+        self.cfg = cfg
+        self.tokens = cfg.tokens if tokens is None else tokens
+        self.c = L.cconfig(cfg, self.tokens)
+        self.device = device
+        self.w_router = to_device(cfg, inputs["w_router"], device)
+        self.bias = to_device(cfg, inputs.get("bias"), device)
+        self.w_gate = to_device(cfg, inputs.get("w_gate"), device) if cfg.activation == SWIGLU else None
+        self.w_up = to_device(cfg, inputs["w_up"], device)
+        self.w_down = to_device(cfg, inputs["w_down"], device)
+        self.ws = torch.empty(L.moe_workspace_size(self.c), dtype=torch.uint8, device=device)
+
+    def forward(self, x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        if out is None:
+            out = torch.empty_like(x)
+        L.moe_forward(self.c, x, self.w_router, self.bias, self.w_gate, self.w_up, self.w_down,
+                      out, self.ws, stream)
+        return out
+
+    def view(self, which: int) -> torch.Tensor:
+        """Tensor aliasing one intermediate of the last forward inside the workspace."""
+        ptr, nbytes = L.moe_workspace_view(self.c, self.ws, which)
+        off = ptr - self.ws.data_ptr()
+        raw = self.ws[off:off + nbytes]
+        cfg, T, k = self.cfg, self.tokens, self.cfg.top_k
+        if which in _VIEW_DTYPES:
+            t = raw.view(_VIEW_DTYPES[which])
+            if which in (L.MOE_WS_LOGITS,):
+                return t.view(T, cfg.experts)
+            if which in (L.MOE_WS_TOPK_IDX, L.MOE_WS_TOPK_W, L.MOE_WS_SLOT_ROW):
+                return t.view(T, k)
+            return t
+        t = raw.view(elem_dtype(cfg))
+        width = cfg.inter if which == L.MOE_WS_H else cfg.hidden
+        return t.view(T * k, width)
+
+    def device_status(self, which: int = 3) -> int:
+        return L.moe_read_device_status(self.c, self.ws, which)

@@ -1,0 +1,166 @@
+"""The C ABI on the host: the library loads, exports every function include/moe.h declares,
+and rejects bad arguments before any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle as O
+from mixture_experts_layer_37_amd import _lib as L
+from mixture_experts_layer_37_amd import configs as C
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "moe.h")
+FAKE = 1 << 20          # an aligned, never dereferenced address
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.skip("libmoe.so not built")
+    return L.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:moe_status|const char\*|int32_t)\s+(moe_\w+)\(", text,
+                                 re.M)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(L.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def cfg_of(**kw):
+    base = dict(tokens=64, hidden=256, inter=256, experts=8, top_k=2, activation=0, dtype=0,
+                renormalize=1, capacity_factor=0.0)
+    base.update(kw)
+    return L.CConfig(**base)
+
+
+def ws_size(lib, c):
+    n = ctypes.c_size_t()
+    st = lib.moe_workspace_size(ctypes.byref(c), ctypes.byref(n))
+    return st, n.value
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(top_k=0), L.MOE_ERR_INVALID_ARG),
+    (dict(top_k=9), L.MOE_ERR_INVALID_ARG),
+    (dict(experts=0), L.MOE_ERR_INVALID_ARG),
+    (dict(tokens=-1), L.MOE_ERR_INVALID_ARG),
+    (dict(hidden=0), L.MOE_ERR_INVALID_ARG),
+    (dict(capacity_factor=float("nan")), L.MOE_ERR_INVALID_ARG),
+    (dict(experts=257, top_k=2), L.MOE_ERR_UNSUPPORTED),
+    (dict(experts=64, top_k=17), L.MOE_ERR_UNSUPPORTED),
+    (dict(dtype=7), L.MOE_ERR_UNSUPPORTED),
+    (dict(activation=3), L.MOE_ERR_UNSUPPORTED),
+    (dict(hidden=200), L.MOE_ERR_UNSUPPORTED),                 # bf16 hidden % 256
+    (dict(inter=192), L.MOE_ERR_UNSUPPORTED),                  # bf16 SwiGLU inter % 128
+    (dict(inter=384, activation=1), L.MOE_ERR_UNSUPPORTED),    # bf16 GELU inter % 256
+    (dict(dtype=1, hidden=20), L.MOE_ERR_UNSUPPORTED),         # f32 hidden % 8
+    (dict(), L.MOE_OK),
+    (dict(dtype=1, hidden=24, inter=7, experts=3, top_k=3), L.MOE_OK),
+    (dict(tokens=0), L.MOE_OK),
+])
+def test_config_validation(lib, kw, status):
+    assert ws_size(lib, cfg_of(**kw))[0] == status
+
+
+def test_null_config_and_outputs(lib):
+    n = ctypes.c_size_t()
+    assert lib.moe_workspace_size(None, ctypes.byref(n)) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_workspace_size(ctypes.byref(cfg_of()), None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_capacity(ctypes.byref(cfg_of()), None) == L.MOE_ERR_INVALID_ARG
+
+
+def test_workspace_size_grows_with_tokens(lib):
+    sizes = [ws_size(lib, cfg_of(tokens=t))[1] for t in (1, 100, 1000, 10000)]
+    assert sizes == sorted(sizes) and sizes[0] > 0
+    assert ws_size(lib, cfg_of(tokens=0))[1] > 0
+
+
+@pytest.mark.parametrize("cfg", list(C.CONFIGS.values()), ids=list(C.CONFIGS))
+def test_capacity_matches_oracle_formula(lib, cfg):
+    assert L.moe_capacity(cfg) == O.capacity(cfg.capacity_factor, cfg.tokens, cfg.top_k,
+                                             cfg.experts)
+
+
+def test_capacity_boundaries(lib):
+    for cf, T, k, E in [(1.2, 8192, 2, 32), (1.0, 8192, 2, 32), (0.5, 2, 2, 3), (1.25, 10, 1, 4),
+                        (0.0, 77, 2, 8), (-2.0, 77, 2, 8), (3.0, 5, 1, 1)]:
+        c = cfg_of(tokens=T, top_k=k, experts=E, capacity_factor=cf)
+        got = ctypes.c_int32()
+        assert lib.moe_capacity(ctypes.byref(c), ctypes.byref(got)) == L.MOE_OK
+        assert got.value == O.capacity(cf, T, k, E)
+
+
+def call_forward(lib, c, ws_bytes, **over):
+    p = dict(x=FAKE, wr=FAKE, bias=None, wg=FAKE, wu=FAKE, wd=FAKE, out=FAKE, ws=FAKE)
+    p.update(over)
+    return lib.moe_forward(ctypes.byref(c), p["x"], p["wr"], p["bias"], p["wg"], p["wu"], p["wd"],
+                           p["out"], p["ws"], ws_bytes, None)
+
+
+def test_forward_argument_errors(lib):
+    c = cfg_of()
+    _, need = ws_size(lib, c)
+    assert call_forward(lib, c, need - 1) == L.MOE_ERR_WORKSPACE
+    assert call_forward(lib, c, need, x=None) == L.MOE_ERR_INVALID_ARG
+    assert call_forward(lib, c, need, x=FAKE + 8) == L.MOE_ERR_INVALID_ARG      # misaligned
+    assert call_forward(lib, c, need, wg=None) == L.MOE_ERR_INVALID_ARG         # SwiGLU needs it
+    assert call_forward(lib, c, need, ws=None) == L.MOE_ERR_INVALID_ARG
+    assert call_forward(lib, c, need, out=None) == L.MOE_ERR_INVALID_ARG
+    c0 = cfg_of(tokens=0)
+    _, need0 = ws_size(lib, c0)
+    assert call_forward(lib, c0, need0) == L.MOE_OK                              # empty batch
+    g = cfg_of(tokens=0, activation=1, inter=512)
+    _, needg = ws_size(lib, g)
+    assert call_forward(lib, g, needg, wg=None) == L.MOE_OK                      # GELU: no gate
+
+
+def test_stage_argument_errors(lib):
+    c = cfg_of()
+    cp = ctypes.byref(c)
+    _, need = ws_size(lib, c)
+    assert lib.moe_route(cp, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, need, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(cp, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 16, None) == L.MOE_ERR_WORKSPACE
+    assert lib.moe_permute(cp, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_up(cp, FAKE, FAKE, None, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_down(cp, FAKE, None, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_grouped_ffn(cp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == L.MOE_ERR_WORKSPACE
+    assert lib.moe_combine(cp, FAKE, FAKE, None, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine(ctypes.byref(cfg_of(top_k=0)), FAKE, FAKE, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    f = ctypes.c_int32(5)
+    assert lib.moe_read_device_status(cp, FAKE, 0, None, ctypes.byref(f)) == L.MOE_ERR_INVALID_ARG
+    c0 = cfg_of(tokens=0)
+    assert lib.moe_read_device_status(ctypes.byref(c0), FAKE, 3, None, ctypes.byref(f)) == L.MOE_OK
+    assert f.value == 0
+
+
+def test_workspace_views(lib):
+    c = cfg_of(tokens=100)
+    _, need = ws_size(lib, c)
+    ptrs = []
+    for which in range(10):
+        p, n = ctypes.c_void_p(), ctypes.c_size_t()
+        assert lib.moe_workspace_view(ctypes.byref(c), FAKE, which, ctypes.byref(p), ctypes.byref(n)) == L.MOE_OK
+        assert p.value % 256 == 0 and FAKE <= p.value and p.value + n.value <= FAKE + need
+        ptrs.append((p.value, n.value))
+    ptrs.sort()
+    for (a, na), (b, _) in zip(ptrs, ptrs[1:]):
+        assert a + na <= b                      # views never overlap
+    p = ctypes.c_void_p()
+    assert lib.moe_workspace_view(ctypes.byref(c), FAKE, 10, ctypes.byref(p), None) == L.MOE_ERR_INVALID_ARG
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.moe_status_string(s)
+    assert lib.moe_status_string(99) == b"unknown status"

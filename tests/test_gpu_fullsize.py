@@ -1,0 +1,30 @@
+"""GPU parity at the full sizes of the five workloads, in the launch configuration the
+bench times: routing and the permutation on every token, expert outputs and the layer
+output on sampled tokens."""
+import pytest
+import torch
+
+from mixture_experts_layer_37_amd import configs as C
+from mixture_experts_layer_37_amd.inputs import make_inputs
+
+import parity as P
+
+pytestmark = pytest.mark.gpu
+
+SAMPLE = {"tiny": None, "small": 48, "mixtral": 24, "cap32": 12, "fine": 16}
+
+
+@pytest.mark.parametrize("name", list(SAMPLE))
+def test_full_size_workload(name):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    cfg = C.get(name)
+    print(f"[fullsize] {name}: generating inputs", flush=True)
+    inputs = make_inputs(cfg, seed=0, threads=16)
+    print(f"[fullsize] {name}: running", flush=True)
+    rep, layer = P.full_check(cfg, inputs, tokens_sample=SAMPLE[name])
+    print(f"[fullsize] {name}: {rep}", flush=True)
+    if cfg.capacity_factor > 0:
+        assert rep["dropped"] > 0
+    del layer
+    torch.cuda.empty_cache()
