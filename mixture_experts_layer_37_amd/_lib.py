@@ -14,7 +14,8 @@ import torch  # noqa: F401  (loads the process's HIP runtime before libmoe.so)
 
 from .configs import BF16, GELU, MoEConfig
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+LIB_PATH = os.environ.get("MOE_LIB_PATH") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_DTYPE_BF16, MOE_DTYPE_F32 = 0, 1

@@ -12,12 +12,17 @@
 //
 // gfx950 design (bf16):
 //   - block tile 256 x 256 x 64, 4 waves in 2 x 2, each wave 128 x 128 of output computed
-//     with v_mfma_f32_32x32x16_bf16 (fp32 accumulators);
-//   - A (x_perm rows, K-contiguous) and B (weights [K,N], N-contiguous) are staged through
-//     double-buffered LDS (2 x 64 KB); B is transposed in registers (8x8 bf16 blocks) on its
-//     way into LDS so that every MFMA operand is one 16-byte K-contiguous LDS read;
-//   - LDS rows are 128 B (64 bf16 of K); 16-byte chunks are XOR-swizzled with
-//     (row ^ row>>3) & 7, which keeps both the stores and the MFMA reads conflict-free;
+//     with v_mfma_f32_32x32x16_bf16 (fp32 accumulators in AGPRs);
+//   - both operands go global -> LDS by DMA (global_load_lds_dwordx4: lane l's 16 bytes land
+//     at base + 16 l), double-buffered, one barrier per k-step, no register staging;
+//   - A (x_perm rows, K-contiguous) sits in LDS as [m][64 k], 16-byte chunks XOR-swizzled
+//     with (m ^ m>>3) & 7; MFMA fragments are single ds_read_b128;
+//   - B (weights [K,N], N-contiguous) stays in its own layout, [64 k][256 n], 32-byte chunks
+//     XOR-swizzled with (k & 3) | (k & 1) << 2; MFMA fragments (8 consecutive k of one n
+//     per lane) come from two ds_read_b64_tr_b16, the gfx950 transposing LDS read: in each
+//     16-lane group lane L reads row L/4, columns 4(L%4)..+3 of a 4 x 16 block and
+//     receives column L, rows 0..3. Both swizzles keep reads conflict-free for 32 and 64
+//     banks;
 //   - operands are issued as (W, x) so each lane's accumulators hold 4 consecutive output
 //     columns of one row, written straight to global memory as 8-byte stores;
 //   - persistent grid of one block per CU; tiles are ordered (expert, n-tile, m-tile) and
@@ -83,9 +88,24 @@ __device__ __forceinline__ float gelu_f(float z) {
   return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
 }
 
-// Lower/upper 16-bit halves of two words interleaved: element j of rows p and q.
-__device__ __forceinline__ uint32_t pair_col(uint32_t p, uint32_t q, int odd) {
-  return odd ? ((p >> 16) | (q & 0xffff0000u)) : ((p & 0xffffu) | (q << 16));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) char lds_char;
+
+// B-tile swizzle of 32-byte chunks for row k (a row is 128 columns = 256 bytes).
+__device__ __forceinline__ int bswz(int k) { return (k & 3) | ((k & 1) << 2); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_char*)p;
+}
+
+// 16 bytes per lane global -> LDS (lane l lands at lds + 16 l). Issued through asm so the
+// compiler does not make every later LDS read wait for it; the kernel waits explicitly
+// (s_waitcnt vmcnt(0) + barrier) before it reads a stage.
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(lds) : "memory", "m0");
 }
 
 template <int EPI>
@@ -94,12 +114,15 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     const bf16_t* __restrict__ W0, const bf16_t* __restrict__ W1, bf16_t* __restrict__ C, int E,
     int K, int N, int max_rows) {
   constexpr int OUTN = (EPI == EPI_SWIGLU) ? 128 : 256;   // output columns per tile
-  __shared__ __attribute__((aligned(16))) bf16_t smem[2][2][BM * BK];
+  constexpr int HALF = BK * 128;                           // elements of one B half
+  constexpr int STAGE = BM * BK + 2 * HALF;                // elements per LDS stage
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[2 * STAGE];
   __shared__ int s_start[kMaxExperts + 1];
   __shared__ int s_off[kMaxExperts + 1];
   __shared__ int s_wsum[4];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int NT = N / OUTN;
   const int total = build_tile_starts<BM>(offsets, E, NT, max_rows, s_start, s_off, s_wsum);
 
@@ -107,13 +130,32 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   const int nper = gridDim.x / kXcds;
   const int per = (total + kXcds - 1) / kXcds;
   const int KT = K / BK;
+  const uint32_t lds0 = lds_addr(smem);
 
-  // global->LDS staging coordinates
-  const int a_c = tid & 7, a_r = tid >> 3;           // A: chunk a_c of rows a_r + 32 i
-  const int b_nc = tid & 31, b_kc = tid >> 5;        // B: 8x8 block (n chunk, k chunk)
-  // MFMA fragment coordinates
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, lhi = lane >> 5;
+
+  // Per-lane LDS read offsets (bytes). A: fragment (kk, i) at a_rd[kk & 1 ...] -- the
+  // XOR swizzle makes the kk dependence non-additive, so keep one offset per kk.
+  uint32_t a_rd[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int m = wm * 128 + l32;                 // + i*32: swz flips bit 2 with i & 1
+    a_rd[kk] = (uint32_t)(m * BK * 2 + (((kk * 2 + lhi) ^ swz(m)) << 4));
+  }
+  // B: fragment (kk, j, r): row krow = kk*16 + 8*lhi + 4r + (lane&15)/4; the swizzle
+  // depends on krow & 3 only, so kk and r are immediate offsets.
+  uint32_t b_rd[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    int h, nb;
+    if (EPI == EPI_SWIGLU) { h = j >> 1; nb = wn * 64 + (j & 1) * 32; }
+    else { h = wn; nb = j * 32; }
+    const int krow0 = 8 * lhi + ((lane & 15) >> 2);
+    const int c32 = (nb >> 4) + ((lane >> 4) & 1);
+    b_rd[j] = (uint32_t)((BM * BK + h * HALF) * 2 + krow0 * 256 + ((c32 ^ bswz(krow0)) << 5) +
+                         8 * (lane & 3));
+  }
 
   for (int it = li; it < per; it += nper) {
     const int tile = xcd * per + it;
@@ -126,23 +168,52 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     const int n_t = rem / mt_e, m_t = rem - n_t * mt_e;
     const int row0 = row_beg + m_t * BM;
     const int mrows = min(BM, m_e - m_t * BM);
+    const char* Ab = (const char*)(A + (size_t)row0 * K);
+    // B halves: base pointers (uniform) of columns [0,128) and [128,256) of the tile
+    const bf16_t* Bh0;
+    const bf16_t* Bh1;
+    if (EPI == EPI_SWIGLU) {
+      Bh0 = W0 + (size_t)e * K * N + n_t * 128;
+      Bh1 = W1 + (size_t)e * K * N + n_t * 128;
+    } else {
+      Bh0 = W0 + (size_t)e * K * N + n_t * 256;
+      Bh1 = Bh0 + 128;
+    }
 
-    // A row offsets (rows past the expert's end re-read its last row; results discarded)
-    int a_off[8];
+    // DMA source offsets (bytes, relative to Ab / Bh at k0 = 0) of this lane.
+    // A: instruction i of wave w fills chunks [(w*8+i)*64, +64) of [256 m][8 chunks].
+    uint32_t a_src[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int r = min(a_r + 32 * i, mrows - 1);
-      a_off[i] = r * K + a_c * 8;
+      const int r = wave * 64 + i * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ swz(r);
+      a_src[i] = (uint32_t)(min(r, mrows - 1) * K * 2 + c * 16);
     }
-    const bf16_t* Ab = A + (size_t)row0 * K;
-    const bf16_t* Bb;
-    if (EPI == EPI_SWIGLU) {
-      const int col = n_t * 128 + (b_nc & 15) * 8;
-      Bb = (b_nc < 16 ? W0 : W1) + (size_t)e * K * N + col;
-    } else {
-      Bb = W0 + (size_t)e * K * N + n_t * 256 + b_nc * 8;
+    // B: instruction i (half i >> 2) of wave w fills units [(w*4 + (i&3))*64, +64) of
+    // [64 k][16 units]: row k = (w*4 + (i&3))*4 + lane/16.
+    uint32_t b_src[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = (wave * 4 + i) * 4 + (lane >> 4);
+      const int u = lane & 15;
+      const int ncol = (((u >> 1) ^ bswz(k)) << 4) + ((u & 1) << 3);
+      b_src[i] = (uint32_t)(k * N * 2 + ncol * 2);
     }
-    Bb += (size_t)(b_kc * 8) * N;
+
+    auto dma = [&](int kt, int st) {
+      const uint32_t kA = (uint32_t)(kt * BK * 2);
+      const size_t kB = (size_t)kt * BK * N * 2;
+      const uint32_t sA = lds0 + st * STAGE * 2;
+      const uint32_t sB = sA + BM * BK * 2;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        lds_dma16(Ab + (a_src[i] + kA), sA + (wave * 8 + i) * 1024);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lds_dma16((const char*)Bh0 + kB + b_src[i], sB + (wave * 4 + i) * 1024);
+        lds_dma16((const char*)Bh1 + kB + b_src[i], sB + HALF * 2 + (wave * 4 + i) * 1024);
+      }
+    };
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -152,73 +223,53 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    uint4 ra[8], rb[8];
-    auto gload = [&](int kt) {
-      const int k0 = kt * BK;
+    auto load_frags = [&](const char* st, int kk, bf16x8 (&xa)[4], bf16x8 (&wb)[4]) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ra[i] = *(const uint4*)(Ab + a_off[i] + k0);
-      const bf16_t* bp = Bb + (size_t)k0 * N;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) rb[r] = *(const uint4*)(bp + (size_t)r * N);
-    };
-    auto sstore = [&](int buf) {
-      bf16_t* As = smem[buf][0];
-      bf16_t* Bs = smem[buf][1];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = a_r + 32 * i;
-        *(uint4*)(As + r * BK + ((a_c ^ swz(r)) << 3)) = ra[i];
+      for (int i = 0; i < 4; ++i) {
+        // rows m + 32 i: the chunk swizzle alternates with i & 1 (bit 2 of swz)
+        const uint32_t off = a_rd[kk] ^ ((i & 1) << 6);
+        xa[i] = *(const bf16x8*)(st + off + i * 32 * BK * 2);
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int n = b_nc * 8 + j;
-        const int w = j >> 1, odd = j & 1;
-        uint4 o;
-        o.x = pair_col((&rb[0].x)[w], (&rb[1].x)[w], odd);
-        o.y = pair_col((&rb[2].x)[w], (&rb[3].x)[w], odd);
-        o.z = pair_col((&rb[4].x)[w], (&rb[5].x)[w], odd);
-        o.w = pair_col((&rb[6].x)[w], (&rb[7].x)[w], odd);
-        *(uint4*)(Bs + n * BK + ((b_kc ^ swz(n)) << 3)) = o;
+      for (int j = 0; j < 4; ++j) {
+        const char* p = st + b_rd[j] + kk * 16 * 256;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const lds_char*)p);
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const lds_char*)(p + 4 * 256));
+        const v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        wb[j] = __builtin_bit_cast(bf16x8, v);
       }
     };
-    auto compute = [&](int buf) {
-      const bf16_t* As = smem[buf][0];
-      const bf16_t* Bs = smem[buf][1];
+
+    dma(0, 0);
+    for (int kt = 0; kt < KT; ++kt) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (kt + 1 < KT) dma(kt + 1, (kt + 1) & 1);
+      const char* st = (const char*)smem + (kt & 1) * STAGE * 2;
+      bf16x8 xa[2][4], wb[2][4];
+      load_frags(st, 0, xa[0], wb[0]);
 #pragma unroll
       for (int kk = 0; kk < BK / 16; ++kk) {
-        const int ch = kk * 2 + lhi;
-        bf16x8 xa[4], wb[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = wm * 128 + i * 32 + l32;
-          xa[i] = *(const bf16x8*)(As + m * BK + ((ch ^ swz(m)) << 3));
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          int nb;
-          if (EPI == EPI_SWIGLU) nb = (j < 2 ? 0 : 128) + wn * 64 + (j & 1) * 32;
-          else nb = wn * 128 + j * 32;
-          const int n = nb + l32;
-          wb[j] = *(const bf16x8*)(Bs + n * BK + ((ch ^ swz(n)) << 3));
-        }
+        if (kk + 1 < BK / 16) load_frags(st, kk + 1, xa[(kk + 1) & 1], wb[(kk + 1) & 1]);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wb[j], xa[i], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wb[kk & 1][j], xa[kk & 1][i],
+                                                                acc[i][j], 0, 0, 0);
+        // Interleave the next slice's 12 LDS reads with this slice's 16 MFMAs so their
+        // latency hides under MFMA execution.
+        if (kk + 1 < BK / 16) {
+#pragma unroll
+          for (int x = 0; x < 12; ++x) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        }
       }
-    };
-
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < KT) gload(kt + 1);
-      compute(cur);
-      if (kt + 1 < KT) sstore(cur ^ 1);
-      __syncthreads();
     }
+    __syncthreads();   // every wave is done with both stages before the next tile's DMA
 
     // Epilogue. acc[i][j][4q+s]: row m = wm*128 + i*32 + l32,
     // column (within the wave's block j) = 8q + 4*lhi + s.
