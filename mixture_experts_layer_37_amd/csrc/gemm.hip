@@ -14,7 +14,12 @@
 //   - block tile 256 x 256 x 64, 4 waves in 2 x 2, each wave 128 x 128 of output computed
 //     with v_mfma_f32_32x32x16_bf16 (fp32 accumulators in AGPRs);
 //   - both operands go global -> LDS by DMA (global_load_lds_dwordx4: lane l's 16 bytes land
-//     at base + 16 l), double-buffered, one barrier per k-step, no register staging;
+//     at base + 16 l), double-buffered in two distinct LDS objects, one barrier per k-step,
+//     no register staging. The DMA of step kt + 2 is issued right after the barrier of step
+//     kt, under the MFMAs of that step's last k slice;
+//   - inside a k-step, each 16-wide k slice first issues the next slice's 12 LDS reads, then
+//     runs its 16 MFMAs on fragments read one slice earlier, so LDS latency hides under MFMA
+//     execution (fragments double-buffered in VGPRs, accumulators in AGPRs, no spills);
 //   - A (x_perm rows, K-contiguous) sits in LDS as [m][64 k], 16-byte chunks XOR-swizzled
 //     with (m ^ m>>3) & 7; MFMA fragments are single ds_read_b128;
 //   - B (weights [K,N], N-contiguous) stays in its own layout, [64 k][256 n], 32-byte chunks
@@ -28,6 +33,8 @@
 //   - persistent grid of one block per CU; tiles are ordered (expert, n-tile, m-tile) and
 //     each of the 8 XCDs walks its own contiguous range, so the blocks sharing an XCD's L2
 //     work on the same weight columns at the same time.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -92,37 +99,45 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void global_void;
 
 // B-tile swizzle of 32-byte chunks for row k (a row is 128 columns = 256 bytes).
 __device__ __forceinline__ int bswz(int k) { return (k & 3) | ((k & 1) << 2); }
 
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const lds_char*)p;
+// 16 bytes per lane global -> LDS: lane l's bytes land at lds + 16 l (lds is wave-uniform).
+__device__ __forceinline__ void lds_dma16(const void* src, bf16_t* lds) {
+  __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)lds, 16, 0, 0);
 }
 
-// 16 bytes per lane global -> LDS (lane l lands at lds + 16 l). Issued through asm so the
-// compiler does not make every later LDS read wait for it; the kernel waits explicitly
-// (s_waitcnt vmcnt(0) + barrier) before it reads a stage.
-__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(src), "s"(lds) : "memory", "m0");
-}
+// MFMA operand fragments of one 16-wide k slice of a wave's 128 x 128 output block.
+struct Frags {
+  bf16x8 a[4];   // token rows   wm*128 + 32 i + (lane & 31)
+  bf16x8 b[4];   // weight columns of the wave's four 32-column blocks
+};
+
+// s_waitcnt immediate: lgkmcnt(0), vmcnt and expcnt left at their maxima (no wait).
+constexpr int kWaitLgkm0 = 0xC07F;
+
+constexpr int kHalf = BK * 128;                  // elements of one B half [64 k][128 n]
+constexpr int kStage = BM * BK + 2 * kHalf;      // elements of one LDS stage (64 KB)
 
 template <int EPI>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets,
     const bf16_t* __restrict__ W0, const bf16_t* __restrict__ W1, bf16_t* __restrict__ C, int E,
     int K, int N, int max_rows) {
-  constexpr int OUTN = (EPI == EPI_SWIGLU) ? 128 : 256;   // output columns per tile
-  constexpr int HALF = BK * 128;                           // elements of one B half
-  constexpr int STAGE = BM * BK + 2 * HALF;                // elements per LDS stage
-  __shared__ __attribute__((aligned(1024))) bf16_t smem[2 * STAGE];
+  // Two stages in two distinct LDS objects: the compiler can then tell a DMA into one
+  // stage from reads of the other and does not make those reads wait for the DMA.
+  __shared__ __attribute__((aligned(1024))) bf16_t stage0[kStage];
+  __shared__ __attribute__((aligned(1024))) bf16_t stage1[kStage];
   __shared__ int s_start[kMaxExperts + 1];
   __shared__ int s_off[kMaxExperts + 1];
   __shared__ int s_wsum[4];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  constexpr int OUTN = (EPI == EPI_SWIGLU) ? 128 : 256;   // output columns per tile
   const int NT = N / OUTN;
   const int total = build_tile_starts<BM>(offsets, E, NT, max_rows, s_start, s_off, s_wsum);
 
@@ -130,21 +145,22 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   const int nper = gridDim.x / kXcds;
   const int per = (total + kXcds - 1) / kXcds;
   const int KT = K / BK;
-  const uint32_t lds0 = lds_addr(smem);
 
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, lhi = lane >> 5;
 
-  // Per-lane LDS read offsets (bytes). A: fragment (kk, i) at a_rd[kk & 1 ...] -- the
-  // XOR swizzle makes the kk dependence non-additive, so keep one offset per kk.
+  // Per-lane LDS read offsets (bytes within a stage). A fragment (kk, i): row
+  // m = wm*128 + 32 i + l32, 16-byte chunk 2 kk + lhi, stored at chunk ^ swz(m); swz
+  // changes only in bit 2 with i & 1, applied as an XOR below.
   uint32_t a_rd[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    const int m = wm * 128 + l32;                 // + i*32: swz flips bit 2 with i & 1
+    const int m = wm * 128 + l32;
     a_rd[kk] = (uint32_t)(m * BK * 2 + (((kk * 2 + lhi) ^ swz(m)) << 4));
   }
-  // B: fragment (kk, j, r): row krow = kk*16 + 8*lhi + 4r + (lane&15)/4; the swizzle
-  // depends on krow & 3 only, so kk and r are immediate offsets.
+  // B fragment (kk, j): 8 consecutive k of one weight column per lane from two
+  // ds_read_b64_tr_b16 (rows krow0 + 16 kk and krow0 + 16 kk + 4). The swizzle depends on
+  // k & 3 only, so kk is an immediate offset.
   uint32_t b_rd[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -153,9 +169,27 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     else { h = wn; nb = j * 32; }
     const int krow0 = 8 * lhi + ((lane & 15) >> 2);
     const int c32 = (nb >> 4) + ((lane >> 4) & 1);
-    b_rd[j] = (uint32_t)((BM * BK + h * HALF) * 2 + krow0 * 256 + ((c32 ^ bswz(krow0)) << 5) +
+    b_rd[j] = (uint32_t)((BM * BK + h * kHalf) * 2 + krow0 * 256 + ((c32 ^ bswz(krow0)) << 5) +
                          8 * (lane & 3));
   }
+
+  auto load_frags = [&](const bf16_t* stg, int kk, Frags& f) {
+    const char* st = (const char*)stg;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t off = a_rd[kk] ^ ((i & 1) << 6);
+      f.a[i] = *(const bf16x8*)(st + off + i * 32 * BK * 2);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const char* p = st + b_rd[j] + kk * 16 * 256;
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const lds_char*)p);
+      const v4i16 hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const lds_char*)(p + 4 * 256));
+      const v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      f.b[j] = __builtin_bit_cast(bf16x8, v);
+    }
+  };
 
   for (int it = li; it < per; it += nper) {
     const int tile = xcd * per + it;
@@ -181,7 +215,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     }
 
     // DMA source offsets (bytes, relative to Ab / Bh at k0 = 0) of this lane.
-    // A: instruction i of wave w fills chunks [(w*8+i)*64, +64) of [256 m][8 chunks].
+    // A: instruction i of wave w fills chunks [(w*8+i)*64, +64) of [256 m][8 chunks];
+    // rows past the expert's last row re-read its last row (never written back).
     uint32_t a_src[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -189,8 +224,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
       const int c = (lane & 7) ^ swz(r);
       a_src[i] = (uint32_t)(min(r, mrows - 1) * K * 2 + c * 16);
     }
-    // B: instruction i (half i >> 2) of wave w fills units [(w*4 + (i&3))*64, +64) of
-    // [64 k][16 units]: row k = (w*4 + (i&3))*4 + lane/16.
+    // B: instruction i of wave w fills units [(w*4 + i)*64, +64) of one half's
+    // [64 k][16 units]: row k = (w*4 + i)*4 + lane/16.
     uint32_t b_src[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -200,18 +235,15 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
       b_src[i] = (uint32_t)(k * N * 2 + ncol * 2);
     }
 
-    auto dma = [&](int kt, int st) {
+    auto dma = [&](int kt, bf16_t* stg) {
       const uint32_t kA = (uint32_t)(kt * BK * 2);
       const size_t kB = (size_t)kt * BK * N * 2;
-      const uint32_t sA = lds0 + st * STAGE * 2;
-      const uint32_t sB = sA + BM * BK * 2;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        lds_dma16(Ab + (a_src[i] + kA), sA + (wave * 8 + i) * 1024);
+      for (int i = 0; i < 8; ++i) lds_dma16(Ab + (a_src[i] + kA), stg + (wave * 8 + i) * 512);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        lds_dma16((const char*)Bh0 + kB + b_src[i], sB + (wave * 4 + i) * 1024);
-        lds_dma16((const char*)Bh1 + kB + b_src[i], sB + HALF * 2 + (wave * 4 + i) * 1024);
+        lds_dma16((const char*)Bh0 + kB + b_src[i], stg + BM * BK + (wave * 4 + i) * 512);
+        lds_dma16((const char*)Bh1 + kB + b_src[i], stg + BM * BK + kHalf + (wave * 4 + i) * 512);
       }
     };
 
@@ -223,52 +255,60 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    auto load_frags = [&](const char* st, int kk, bf16x8 (&xa)[4], bf16x8 (&wb)[4]) {
+    auto mfma16 = [&](const Frags& f) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // rows m + 32 i: the chunk swizzle alternates with i & 1 (bit 2 of swz)
-        const uint32_t off = a_rd[kk] ^ ((i & 1) << 6);
-        xa[i] = *(const bf16x8*)(st + off + i * 32 * BK * 2);
-      }
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const char* p = st + b_rd[j] + kk * 16 * 256;
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const lds_char*)p);
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const lds_char*)(p + 4 * 256));
-        const v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        wb[j] = __builtin_bit_cast(bf16x8, v);
-      }
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
     };
-
-    dma(0, 0);
-    for (int kt = 0; kt < KT; ++kt) {
-      __builtin_amdgcn_s_waitcnt(0);
+    // One 16-wide k slice: the next slice's 12 LDS reads go out first, then the 16 MFMAs
+    // of the current slice run while they are in flight. The reads issued one slice earlier
+    // are drained first (they have had a whole slice to land): the 4-bit LDS counter cannot
+    // track 24 outstanding reads, and without this wait the compiler waits for all of them
+    // after issuing the new ones.
+    auto phase = [&](const bf16_t* stg, int kk_next, Frags& nxt, const Frags& cur) {
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      load_frags(stg, kk_next, nxt);
+      mfma16(cur);
+      __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);   // the LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);   // then the MFMAs
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    Frags f0, f1;
+    // One k-step on stage `cur` while stage `nxt` is in flight. After its last LDS read of
+    // `cur`, the wave waits for its own DMA into `nxt`; the barrier then publishes `nxt`
+    // and frees `cur`, which is refilled with step kt + 2 under the last slice's MFMAs.
+    // `refill` / `next` are compile-time at every call site: the steady-state loop carries
+    // no branches, which keeps the fragments in VGPRs and the accumulators in AGPRs.
+    auto kstep = [&](int kt, bf16_t* cur, bf16_t* nxt, auto refill, auto next) {
+      phase(cur, 1, f1, f0);
+      phase(cur, 2, f0, f1);
+      phase(cur, 3, f1, f0);
+      __builtin_amdgcn_s_waitcnt(0);   // f1 has landed; this wave's DMA into nxt is done
       __syncthreads();
-      if (kt + 1 < KT) dma(kt + 1, (kt + 1) & 1);
-      const char* st = (const char*)smem + (kt & 1) * STAGE * 2;
-      bf16x8 xa[2][4], wb[2][4];
-      load_frags(st, 0, xa[0], wb[0]);
-#pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        if (kk + 1 < BK / 16) load_frags(st, kk + 1, xa[(kk + 1) & 1], wb[(kk + 1) & 1]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wb[kk & 1][j], xa[kk & 1][i],
-                                                                acc[i][j], 0, 0, 0);
-        // Interleave the next slice's 12 LDS reads with this slice's 16 MFMAs so their
-        // latency hides under MFMA execution.
-        if (kk + 1 < BK / 16) {
-#pragma unroll
-          for (int x = 0; x < 12; ++x) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-          }
-          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        }
-      }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (decltype(refill)::value) dma(kt + 2, cur);
+      if constexpr (decltype(next)::value) load_frags(nxt, 0, f0);
+      mfma16(f1);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    using yes = std::true_type;
+    using no = std::false_type;
+
+    // K / 64 is even (K is a multiple of 128), so the steps pair up as (stage0, stage1).
+    dma(0, stage0);
+    __builtin_amdgcn_s_waitcnt(0);
+    dma(1, stage1);
+    __syncthreads();
+    load_frags(stage0, 0, f0);
+    int kt = 0;
+    for (; kt + 2 < KT; kt += 2) {
+      kstep(kt, stage0, stage1, yes{}, yes{});
+      kstep(kt + 1, stage1, stage0, yes{}, yes{});
     }
+    kstep(kt, stage0, stage1, no{}, yes{});
+    kstep(kt + 1, stage1, stage0, no{}, no{});
     __syncthreads();   // every wave is done with both stages before the next tile's DMA
 
     // Epilogue. acc[i][j][4q+s]: row m = wm*128 + i*32 + l32,
