@@ -11,7 +11,8 @@
 //             pre-capacity counts, kept = min(count, C), and the kept offsets (a scan over E).
 //   gather -- one wave per token: row = offsets[e] + block prefix + in-block rank, kept iff
 //             below C; writes slot_row / row_token and copies the token row once into each
-//             of its kept rows with 16-byte loads and stores.
+//             of its kept rows with 16-byte loads and stores, all loads of a chunk in
+//             flight together.
 #include "common.h"
 #include "kernels.h"
 
@@ -146,27 +147,28 @@ __global__ __launch_bounds__(256) void permute_gather_kernel(
     slot_row[(size_t)t * k + lane] = row;
     if (row >= 0) row_token[row] = t;
   }
-  int rows[kMaxTopK];
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) rows[j] = __shfl(row, j);
+  // Copy the token row into each kept destination row (lane j holds slot j's row; the
+  // rows are read out one slot at a time as wave-uniform values). Whole chunks of
+  // 64 * U 16-byte vectors first, with all U loads in flight, then the remainder.
   const uint4* src = x + (size_t)t * row_vecs;
-  for (int base = 0; base < row_vecs; base += 64 * U) {
+  int base = 0;
+  for (; base + 64 * U <= row_vecs; base += 64 * U) {
     uint4 v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = base + u * 64 + lane;
-      if (c < row_vecs) v[u] = src[c];
+    for (int u = 0; u < U; ++u) v[u] = src[base + u * 64 + lane];
+    for (int j = 0; j < k; ++j) {
+      const int r = __builtin_amdgcn_readlane(row, j);
+      if (r < 0) continue;
+      uint4* dst = x_perm + (size_t)r * row_vecs + base + lane;
+#pragma unroll
+      for (int u = 0; u < U; ++u) dst[u * 64] = v[u];
     }
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-      if (j < k && rows[j] >= 0) {
-        uint4* dst = x_perm + (size_t)rows[j] * row_vecs;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int c = base + u * 64 + lane;
-          if (c < row_vecs) dst[c] = v[u];
-        }
-      }
+  }
+  for (int c = base + lane; c < row_vecs; c += 64) {
+    const uint4 v = src[c];
+    for (int j = 0; j < k; ++j) {
+      const int r = __builtin_amdgcn_readlane(row, j);
+      if (r >= 0) x_perm[(size_t)r * row_vecs + c] = v;
     }
   }
 }
@@ -185,9 +187,14 @@ hipError_t launch_permute(const void* x, int elem_bytes, const int32_t* topk_idx
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int row_vecs = (int)((size_t)H * elem_bytes / 16);
-  hipLaunchKernelGGL((permute_gather_kernel<8>), dim3((T + 3) / 4), dim3(256), 0, s,
-                     (const uint4*)x, topk_idx, slot_row, row_token, hist, offsets,
-                     (uint4*)x_perm, T, E, k, cap, row_vecs);
+  const dim3 grid((T + 3) / 4), block(256);
+#define MOE_GATHER(U_)                                                                      \
+  hipLaunchKernelGGL((permute_gather_kernel<U_>), grid, block, 0, s, (const uint4*)x, topk_idx, \
+                     slot_row, row_token, hist, offsets, (uint4*)x_perm, T, E, k, cap, row_vecs)
+  if (row_vecs >= 256) MOE_GATHER(4);   // 4 x 1 KB per chunk keeps the kernel spill-free
+  else if (row_vecs >= 128) MOE_GATHER(2);
+  else MOE_GATHER(1);
+#undef MOE_GATHER
   return hipGetLastError();
 }
 
