@@ -349,7 +349,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   }
 }
 
-static int device_cus() {
+int device_cus() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||

@@ -125,6 +125,11 @@ moe_status do_route(const moe_config* c, const void* x, const void* w_router, co
   const int renorm = c->renormalize != 0;
   if (x == nullptr)
     return hip_status(moe::launch_route_topk(logits, idx, w, flags, T, E, k, renorm, s));
+  if (c->dtype == MOE_DTYPE_BF16 && moe::route_lds_fits(H, E))
+    return hip_status(moe::launch_route_bf16_lds((const moe::bf16_t*)x,
+                                                 (const moe::bf16_t*)w_router, bias, logits,
+                                                 idx, w, flags, T, H, E, k, renorm,
+                                                 moe::device_cus(), s));
   if (c->dtype == MOE_DTYPE_BF16) {
     moe::bf16_t* wt = region<moe::bf16_t>(ws, L, R_WT);
     MOE_TRY(hip_status(moe::launch_router_transpose((const moe::bf16_t*)w_router, wt, H, E, s)));

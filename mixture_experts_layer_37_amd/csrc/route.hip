@@ -8,15 +8,21 @@
 // of its best experts, filled in ascending expert order with a strict comparison, so among
 // equal logits the lower expert index wins and the result is deterministic.
 //
-// bf16 path: the gate GEMM runs on MFMA (v_mfma_f32_16x16x32_bf16, fp32 accumulation).
-// x is streamed from HBM exactly once; the router weight is first transposed into the
-// workspace as WT[E_pad][H] so that both MFMA operands are 16-byte K-contiguous loads.
+// bf16 path: the gate GEMM runs on MFMA (v_mfma_f32_16x16x32_bf16, fp32 accumulation) and
+// x is streamed from HBM exactly once. For a small gate (E <= 16) route_stream_kernel
+// stages the token rows through LDS in coalesced pieces and keeps the router weight in
+// registers; a larger gate is first transposed into the workspace as WT[E_pad][H]
+// (route_mfma_kernel).
 #include <climits>
 
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
+
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void global_void;
 
 // Total order used for selection: -0.0 == +0.0, NaN below -inf, otherwise the float order.
 __device__ __forceinline__ int order_key(float f) {
@@ -267,6 +273,187 @@ hipError_t launch_route_bf16(const bf16_t* x, const bf16_t* wt, const float* bia
     case 128: return launch_route_tg<4, 8>(x, wt, bias, logits, idx, w, flags, T, H, E, k, renorm, s);
     default: return launch_route_tg<2, 16>(x, wt, bias, logits, idx, w, flags, T, H, E, k, renorm, s);
   }
+}
+
+// ---------------------------------------------------------------------------------------
+// Router for a small gate (E <= 16, H a multiple of 1024 up to 4096, E * H <= 32768). A block of 8 waves
+// owns 32 tokens; wave w owns the w-th eighth of H. Each wave
+//   - copies its slice of the router weight (contiguous in W[H, E]) into LDS and reads
+//     its MFMA operands from there into registers (8 consecutive k of expert lane & 15 per
+//     lane; lanes for experts >= E hold zeros), so W is never transposed in memory;
+//   - streams its slice of the 32 token rows through two private LDS buffers of
+//     32 rows x 128 k, filled by global->LDS DMA in fully coalesced 1 KB pieces (4 rows x
+//     256 bytes): token rows are read from HBM exactly once, in whole 128-byte lines;
+//   - runs v_mfma_f32_16x16x32_bf16 (fp32 accumulation) on fragments read back from LDS
+//     (16-byte chunk c of row r stored at c ^ (r & 15): conflict-free for 16 rows).
+// No barrier is needed until the end: each wave only reads what it loaded. The eight
+// partial [32 x 16] tiles are then added in a fixed order through LDS (deterministic
+// logits), and one lane per token runs the same top-k and weights as the other paths.
+constexpr int kRouteWaves = 8;
+constexpr int kRouteSubK = 128;                   // k per staged sub-chunk
+constexpr int kRouteBufElems = 32 * kRouteSubK;   // one wave's buffer: 32 rows x 128 k
+constexpr int kRouteMaxSteps = 16;                // 32-wide k-steps per wave (H <= 4096)
+// s_waitcnt immediates (gfx9: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8):
+// wait for all but the newest n vector-memory operations / for every LDS operation.
+constexpr int wait_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitLgkm0 = 0xC07F;
+
+bool route_lds_fits(int H, int E) {
+  // H / 8 a multiple of 128 and at most 512 wide; a wave's weight slice fits its buffer
+  return E <= 16 && H % (kRouteWaves * kRouteSubK) == 0 &&
+         H / kRouteWaves / 32 <= kRouteMaxSteps && (H / kRouteWaves) * E <= kRouteBufElems;
+}
+
+template <int KMAX>
+__global__ __launch_bounds__(512, 1) void route_stream_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, const float* __restrict__ bias,
+    float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    int32_t* __restrict__ flags, int T, int H, int E, int k, int renorm) {
+  constexpr int BT = 32, LDR = 17;
+  // Two buffer sets in two distinct LDS objects, so the compiler can tell a DMA into one
+  // from reads of the other.
+  __shared__ __attribute__((aligned(1024))) bf16_t xb0[kRouteWaves * kRouteBufElems];
+  __shared__ __attribute__((aligned(1024))) bf16_t xb1[kRouteWaves * kRouteBufElems];
+  __shared__ float red[kRouteWaves][BT * LDR];
+  __shared__ float lg[BT * LDR];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t0 = blockIdx.x * BT;
+  const int hs = H / kRouteWaves;        // this wave's slice of H
+  const int kbase = wave * hs;
+  const int nsteps = hs / 32;            // 32-wide k-steps in the slice
+  const int nsub = hs / kRouteSubK;      // staged sub-chunks (4 steps each)
+
+  // DMA of sub-chunk j of this wave's slice into its buffer: instruction i fills rows
+  // 4i .. 4i+3; lane l lands at position l & 15 of row 4i + l/16 and loads the row's chunk
+  // (l & 15) ^ (row & 15). Rows past T re-read row T-1 (never used).
+  const int drow = lane >> 4, dpos = lane & 15;
+  auto dma = [&](int j, bf16_t* set) {
+    bf16_t* dst = set + wave * kRouteBufElems;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * i + drow;
+      const int row = min(t0 + r, T - 1);
+      const bf16_t* src = x + (size_t)row * H + kbase + j * kRouteSubK + ((dpos ^ (r & 15)) << 3);
+      __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)(dst + i * 512), 16, 0, 0);
+    }
+  };
+  // The wave's slice of the router weight is contiguous in W[H, E] (hs * E elements, at
+  // most one buffer). It is DMA'd into the wave's second buffer ahead of the first x
+  // sub-chunk; once it has landed (all but the 8 newest DMA instructions done), the MFMA
+  // operands of every k-step (8 consecutive k of expert lane & 15; zeros for experts
+  // >= E) are read from LDS into registers, after which the buffer is free for x.
+  const int n = lane & 15;
+  const bool live = n < E;
+  bf16_t* wsl = xb1 + wave * kRouteBufElems;
+  const int wchunks = hs * E / 8;                 // 16-byte chunks of the slice
+  const int wdma = (wchunks + 63) / 64;           // 1 KB DMA instructions (<= 8)
+  const bf16_t* wsrc = w + (size_t)kbase * E;
+  for (int i = 0; i < wdma; ++i) {
+    const bf16_t* src = wsrc + (size_t)min(i * 64 + lane, wchunks - 1) * 8;
+    __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)(wsl + i * 512), 16, 0, 0);
+  }
+  dma(0, xb0);
+  __builtin_amdgcn_s_waitcnt(wait_vmcnt(8));   // the weight slice has landed
+  bf16x8 wf[kRouteMaxSteps];
+#pragma unroll
+  for (int st = 0; st < kRouteMaxSteps; ++st) {
+    v8i16 v = {};
+    if (st < nsteps && live) {
+      const bf16_t* p = wsl + (st * 32 + 8 * (lane >> 4)) * E + n;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = (short)p[i * E];
+    }
+    wf[st] = __builtin_bit_cast(bf16x8, v);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // the weight slice has been read out
+
+  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  auto compute = [&](int j, const bf16_t* set) {
+    const bf16_t* b = set + wave * kRouteBufElems;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = 4 * q + (lane >> 4);
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int r = 16 * g + (lane & 15);
+        const bf16x8 a = *(const bf16x8*)(b + r * kRouteSubK + ((c ^ (r & 15)) << 3));
+        // k-step j*4 + q of the slice; the weight operand array is indexed statically
+        bf16x8 wv = wf[0];
+#pragma unroll
+        for (int st = 1; st < kRouteMaxSteps; ++st)
+          if (st == j * 4 + q) wv = wf[st];
+        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wv, acc[g], 0, 0, 0);
+      }
+    }
+  };
+
+  // Wait for all but the newest DMA batch (8 instructions) or for everything.
+  auto wait_dma = [&](bool one_more_in_flight) {
+    if (one_more_in_flight) __builtin_amdgcn_s_waitcnt(wait_vmcnt(8));
+    else __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+  };
+  if (nsub > 1) dma(1, xb1);
+  for (int j = 0; j < nsub; j += 2) {
+    // sub-chunk j is in xb0; sub-chunk j + 1 (if any) is in flight into xb1
+    wait_dma(j + 1 < nsub);
+    compute(j, xb0);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // reads of xb0 done
+    if (j + 2 < nsub) dma(j + 2, xb0);
+    if (j + 1 < nsub) {
+      wait_dma(j + 2 < nsub);
+      compute(j + 1, xb1);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      if (j + 3 < nsub) dma(j + 3, xb1);
+    }
+  }
+
+  // MFMA 16x16 output: lane holds expert lane & 15 of tokens 4 (lane >> 4) + r.
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave][(g * 16 + 4 * (lane >> 4) + r) * LDR + n] = acc[g][r];
+  __syncthreads();
+  // Fixed-order sum of the eight partial tiles, plus the gate bias.
+  for (int i = tid; i < BT * E; i += blockDim.x) {
+    const int tt = i / E, e = i - tt * E;
+    float sum = red[0][tt * LDR + e];
+#pragma unroll
+    for (int v = 1; v < kRouteWaves; ++v) sum += red[v][tt * LDR + e];
+    sum += bias != nullptr ? bias[e] : 0.f;
+    lg[tt * LDR + e] = sum;
+    if (t0 + tt < T) logits[(size_t)(t0 + tt) * E + e] = sum;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    bool nf = false;
+    const int t = t0 + tid;
+    if (tid < BT && t < T)
+      nf = topk_token<KMAX>(lg + tid * LDR, E, k, renorm, topk_idx + (size_t)t * k,
+                            topk_w + (size_t)t * k);
+    const unsigned long long m = __ballot(nf);
+    const int ngroups = (T + kRouteFlagGroup - 1) / kRouteFlagGroup;
+    if (tid < 2 && blockIdx.x * 2 + tid < ngroups)
+      flags[blockIdx.x * 2 + tid] =
+          ((m >> (16 * tid)) & 0xffffull) ? 2 /* MOE_FLAG_NONFINITE_LOGIT */ : 0;
+  }
+}
+
+hipError_t launch_route_bf16_lds(const bf16_t* x, const bf16_t* w_router, const float* bias,
+                                 float* logits, int32_t* idx, float* w, int32_t* flags, int T,
+                                 int H, int E, int k, int renorm, int cus, hipStream_t s) {
+  (void)cus;
+  const dim3 grid((T + 31) / 32), block(64 * kRouteWaves);
+#define MOE_ROUTE_STREAM(KM)                                                                    \
+  hipLaunchKernelGGL((route_stream_kernel<KM>), grid, block, 0, s, x, w_router, bias, logits, idx, \
+                     w, flags, T, H, E, k, renorm)
+  if (k <= 1) MOE_ROUTE_STREAM(1);
+  else if (k <= 2) MOE_ROUTE_STREAM(2);
+  else if (k <= 4) MOE_ROUTE_STREAM(4);
+  else if (k <= 8) MOE_ROUTE_STREAM(8);
+  else MOE_ROUTE_STREAM(16);
+#undef MOE_ROUTE_STREAM
+  return hipGetLastError();
 }
 
 // fp32 gate GEMM on the vector ALUs: one thread per (token, expert), h in ascending order.

@@ -41,6 +41,13 @@ CASES = {
                                      experts=256, top_k=16, bias=("normal", 4.0)),
     "bf16_one_expert": C.SMALL.with_(name="bf16_one_expert", tokens=333, hidden=256, inter=256,
                                      experts=1, top_k=1, bias=None),
+    # the streaming router (E <= 16, H a multiple of 1024): ragged token blocks, E not a
+    # multiple of 8 (lanes for experts >= E carry zeros), both staging buffers in use
+    "bf16_stream_router": C.SMALL.with_(name="bf16_stream_router", tokens=1000, hidden=1024,
+                                        inter=256, experts=12, top_k=3),
+    "bf16_stream_router_e16": C.SMALL.with_(name="bf16_stream_router_e16", tokens=777,
+                                            hidden=2048, inter=256, experts=16, top_k=4,
+                                            bias=("normal", 1.0)),
     "fp32_swiglu_capacity": C.TINY.with_(name="fp32_swiglu_capacity", tokens=257, hidden=40,
                                          inter=24, experts=5, top_k=2, activation=C.SWIGLU,
                                          capacity_factor=0.6, bias=("zipf", 1.1)),
