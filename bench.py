@@ -95,7 +95,6 @@ def main():
     logits = torch.empty((T, E), dtype=torch.float32, device=dev)
     idx = torch.empty((T, k), dtype=torch.int32, device=dev)
     w = torch.empty((T, k), dtype=torch.float32, device=dev)
-    xp = torch.empty((T * k, H), dtype=edt, device=dev)
     counts = torch.empty(E, dtype=torch.int32, device=dev)
     offs = torch.empty(E + 1, dtype=torch.int32, device=dev)
     rt = torch.empty(T * k, dtype=torch.int32, device=dev)
@@ -107,12 +106,14 @@ def main():
     names = ["route", "permute", "gemm_up", "gemm_down", "combine"]
 
     def step(ev=None):
+        # the path moe_forward runs: the permute writes the row maps only and GEMM 1 reads
+        # the token rows in place through them
         if ev: ev[0].record(stream)
         L.moe_route(c, x, layer.w_router, layer.bias, logits, idx, w, ws, stream)
         if ev: ev[1].record(stream)
-        L.moe_permute(c, x, idx, xp, counts, offs, rt, sr, ws, stream)
+        L.moe_permute(c, x, idx, None, counts, offs, rt, sr, ws, stream)
         if ev: ev[2].record(stream)
-        L.moe_expert_up(c, xp, offs, layer.w_gate, layer.w_up, h, stream)
+        L.moe_expert_up_rows(c, x, rt, offs, layer.w_gate, layer.w_up, h, stream)
         if ev: ev[3].record(stream)
         L.moe_expert_down(c, h, offs, layer.w_down, y, stream)
         if ev: ev[4].record(stream)
@@ -154,9 +155,10 @@ def main():
     up_tflops = up_flops / (stage_ms["gemm_up"] * 1e-3) / 1e12
     ffn_tflops = ffn_flops / ((stage_ms["gemm_up"] + stage_ms["gemm_down"]) * 1e-3) / 1e12
     es = 2 if cfg.dtype == C.BF16 else 4
-    # algorithmic bytes of the bandwidth-bound steps
+    # algorithmic bytes of the bandwidth-bound steps (the permute moves index data only: its
+    # row gather is fused into GEMM 1)
     route_bytes = T * H * es + H * E * es + T * E * 4 + T * k * 8
-    permute_bytes = T * H * es + n_kept * H * es + T * k * 4 * 4
+    permute_bytes = T * k * 4 * 4
     combine_bytes = n_kept * H * es + T * H * es + T * k * 8
     traffic = measured_traffic()
     result = {
@@ -175,7 +177,7 @@ def main():
         "config": {"workload": cfg.description, "tokens": T, "hidden": H, "inter": I,
                    "experts": E, "top_k": k, "capacity_factor": cfg.capacity_factor,
                    "activation": cfg.activation, "kept_rows": n_kept},
-        "roofline": {"kernel": "grouped_gemm_bf16_kernel<SwiGLU> (moe_expert_up)",
+        "roofline": {"kernel": "grouped_gemm_bf16_kernel<SwiGLU> (moe_expert_up_rows)",
                      "bound": "mfma", "achieved": up_tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": up_tflops / PEAK_BF16_TFLOPS,
                      "traffic": traffic, "algorithmic_flops": up_flops},
@@ -183,15 +185,35 @@ def main():
         "layer_tflops": total_flops / (ms_per_step * 1e-3) / 1e12,
         "stages_us": {n: v * 1e3 for n, v in stage_ms.items()},
         "hbm_frac": {"route": route_bytes / (stage_ms["route"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                     "permute": permute_bytes / (stage_ms["permute"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                     "permute_row_maps": permute_bytes / (stage_ms["permute"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
                      "combine": combine_bytes / (stage_ms["combine"] * 1e-3) / 1e9 / PEAK_HBM_GBS},
     }
+    result["materialised_permute"] = materialised_permute(L, c, x, idx, counts, offs, rt, sr, ws,
+                                                          stream, T, H, k, n_kept, es)
 
     result["device_flags"] = L.moe_read_device_status(c, ws, 3, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, inp, out, logits, idx, args.cpu_sample_tokens,
                                               result)
     print(json.dumps(result), flush=True)
+
+
+def materialised_permute(L, c, x, idx, counts, offs, rt, sr, ws, stream, T, H, k, n_kept, es):
+    """moe_permute writing x_perm (the standalone gather, not on the timed path): mean time
+    over 10 calls and its HBM fraction for x read once + x_perm written + index arrays."""
+    import torch
+    xp = torch.empty((T * k, H), dtype=x.dtype, device=x.device)
+    L.moe_permute(c, x, idx, xp, counts, offs, rt, sr, ws, stream)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(10):
+        L.moe_permute(c, x, idx, xp, counts, offs, rt, sr, ws, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / 10
+    nbytes = T * H * es + n_kept * H * es + T * k * 4 * 4
+    return {"us": us, "hbm_frac": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
 
 
 def cpu_baseline(cfg, inp, out_dev, logits_dev, idx_dev, n_tok, result):

@@ -110,7 +110,8 @@ moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
  *   x              [T,H] dtype
  *   topk_idx       [T,k] int32 expert ids (invalid or repeated ids are dropped + flagged)
  *   x_perm         [T*k,H] dtype out: rows grouped by expert, token order inside an expert;
- *                  rows >= expert_offsets[E] are left untouched
+ *                  rows >= expert_offsets[E] are left untouched. May be NULL: then only the
+ *                  row maps below are written (x is not read), for moe_expert_up_rows
  *   expert_counts  [E] int32 out: assignments per expert before the capacity clamp
  *   expert_offsets [E+1] int32 out: first row of each expert after the clamp
  *   row_token      [T*k] int32 out: source token of each row (rows < expert_offsets[E])
@@ -130,6 +131,19 @@ moe_status moe_permute(const moe_config* cfg, const void* x, const int32_t* topk
 moe_status moe_expert_up(const moe_config* cfg, const void* x_perm,
                          const int32_t* expert_offsets, const void* w_gate, const void* w_up,
                          void* h, moe_stream_t stream);
+
+/* Grouped GEMM 1 with the permute gather fused into its operand loads: as moe_expert_up,
+ * but row r of the expert-major operand is read in place as token row x[row_token[r]]
+ * instead of from a materialised x_perm (lshu.cn/news/82007, section 1: the case for fusing
+ * the token permutation with the expert matmul; section 3, the fused up-projection).
+ *   x         [T,H] dtype, the token rows (not permuted)
+ *   row_token [T*k] int32, source token of each row, as written by moe_permute; entries
+ *             outside [0, T) are clamped into it (never read out of bounds)
+ *   expert_offsets, w_gate, w_up, h as for moe_expert_up.
+ * h is bit-identical to moe_expert_up on the x_perm that moe_permute would produce. */
+moe_status moe_expert_up_rows(const moe_config* cfg, const void* x, const int32_t* row_token,
+                              const int32_t* expert_offsets, const void* w_gate,
+                              const void* w_up, void* h, moe_stream_t stream);
 
 /* Grouped GEMM 2: y_perm = h Wd[e] for the rows of each expert (lshu.cn page, section 4,
  * npu_moe_matmul). h [rows,I], w_down [E,I,H], y_perm [T*k,H] out. */
@@ -151,8 +165,10 @@ moe_status moe_grouped_ffn(const moe_config* cfg, const void* x_perm,
 moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* slot_row,
                        const float* topk_w, void* out, moe_stream_t stream);
 
-/* The whole layer: moe_route -> moe_permute -> moe_grouped_ffn -> moe_combine, with every
- * intermediate in `ws` (readable with moe_workspace_view until the next call). */
+/* The whole layer: moe_route -> the row maps of moe_permute -> moe_expert_up_rows (the
+ * gather fused into GEMM 1, so x_perm is never materialised) -> moe_expert_down ->
+ * moe_combine, with every intermediate in `ws` (readable with moe_workspace_view until the
+ * next call). */
 moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_router,
                        const float* gate_bias, const void* w_gate, const void* w_up,
                        const void* w_down, void* out, void* ws, size_t ws_bytes,
@@ -167,7 +183,7 @@ enum {
   MOE_WS_OFFSETS = 4,     /* [E+1] int32 */
   MOE_WS_SLOT_ROW = 5,    /* [T,k] int32 */
   MOE_WS_ROW_TOKEN = 6,   /* [T*k] int32 */
-  MOE_WS_X_PERM = 7,      /* [T*k,H] dtype */
+  MOE_WS_X_PERM = 7,      /* not materialised by moe_forward: view -> MOE_ERR_INVALID_ARG */
   MOE_WS_H = 8,           /* [T*k,I] dtype */
   MOE_WS_Y_PERM = 9,      /* [T*k,H] dtype */
   MOE_WS_NUM_VIEWS = 10

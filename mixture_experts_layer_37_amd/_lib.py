@@ -25,7 +25,8 @@ MOE_FLAG_BAD_INDEX, MOE_FLAG_NONFINITE_LOGIT = 1, 2
  MOE_WS_ROW_TOKEN, MOE_WS_X_PERM, MOE_WS_H, MOE_WS_Y_PERM) = range(10)
 
 EXPORTS = ("moe_workspace_size", "moe_capacity", "moe_route", "moe_permute", "moe_expert_up",
-           "moe_expert_down", "moe_grouped_ffn", "moe_combine", "moe_forward",
+           "moe_expert_up_rows", "moe_expert_down", "moe_grouped_ffn", "moe_combine",
+           "moe_forward",
            "moe_workspace_view", "moe_read_device_status", "moe_status_string",
            "moe_last_hip_error")
 
@@ -64,6 +65,7 @@ def lib():
             "moe_route": [cfgp, vp, vp, vp, vp, vp, vp, vp, c_size_t, vp],
             "moe_permute": [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, c_size_t, vp],
             "moe_expert_up": [cfgp, vp, vp, vp, vp, vp, vp],
+            "moe_expert_up_rows": [cfgp, vp, vp, vp, vp, vp, vp, vp],
             "moe_expert_down": [cfgp, vp, vp, vp, vp, vp],
             "moe_grouped_ffn": [cfgp, vp, vp, vp, vp, vp, vp, vp, c_size_t, vp],
             "moe_combine": [cfgp, vp, vp, vp, vp, vp],
@@ -153,6 +155,12 @@ def moe_expert_up(cfg, x_perm, expert_offsets, w_gate, w_up, h, stream=None):
     _check("moe_expert_up", lib().moe_expert_up(
         ctypes.byref(_as_cfg(cfg)), _ptr(x_perm), _ptr(expert_offsets), _ptr(w_gate), _ptr(w_up),
         _ptr(h), _stream(stream)))
+
+
+def moe_expert_up_rows(cfg, x, row_token, expert_offsets, w_gate, w_up, h, stream=None):
+    _check("moe_expert_up_rows", lib().moe_expert_up_rows(
+        ctypes.byref(_as_cfg(cfg)), _ptr(x), _ptr(row_token), _ptr(expert_offsets), _ptr(w_gate),
+        _ptr(w_up), _ptr(h), _stream(stream)))
 
 
 def moe_expert_down(cfg, h, expert_offsets, w_down, y_perm, stream=None):

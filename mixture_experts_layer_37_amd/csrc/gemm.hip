@@ -9,6 +9,9 @@
 // The pages run one matmul per expert (gitcode.csdn.net MoE page, "核心代码解析": a loop
 // over experts); here every expert is one launch, as a persistent grid over a tile list
 // that is built on the device from the offsets, so no per-expert sizes reach the host.
+// GEMM 1 can also read its rows straight from the token matrix through the permutation's
+// row -> token map, which fuses the permute gather into its operand loads (the pages'
+// case for fusing permute with the matmul: lshu.cn/news/82007, section 1).
 //
 // gfx950 design (bf16):
 //   - block tile 256 x 256 x 64, 4 waves in 2 x 2, each wave 128 x 128 of output computed
@@ -122,11 +125,13 @@ constexpr int kWaitLgkm0 = 0xC07F;
 constexpr int kHalf = BK * 128;                  // elements of one B half [64 k][128 n]
 constexpr int kStage = BM * BK + 2 * kHalf;      // elements of one LDS stage (64 KB)
 
+// A rows: row r of the expert-major operand is A[r] (row_token == nullptr) or, with the
+// permute gather fused in, token row A[row_token[r]] (clamped into [0, a_rows)).
 template <int EPI>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
-    const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets,
-    const bf16_t* __restrict__ W0, const bf16_t* __restrict__ W1, bf16_t* __restrict__ C, int E,
-    int K, int N, int max_rows) {
+    const bf16_t* __restrict__ A, const int32_t* __restrict__ row_token, int a_rows,
+    const int32_t* __restrict__ offsets, const bf16_t* __restrict__ W0,
+    const bf16_t* __restrict__ W1, bf16_t* __restrict__ C, int E, int K, int N, int max_rows) {
   // Two stages in two distinct LDS objects: the compiler can then tell a DMA into one
   // stage from reads of the other and does not make those reads wait for the DMA.
   __shared__ __attribute__((aligned(1024))) bf16_t stage0[kStage];
@@ -202,7 +207,6 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     const int n_t = rem / mt_e, m_t = rem - n_t * mt_e;
     const int row0 = row_beg + m_t * BM;
     const int mrows = min(BM, m_e - m_t * BM);
-    const char* Ab = (const char*)(A + (size_t)row0 * K);
     // B halves: base pointers (uniform) of columns [0,128) and [128,256) of the tile
     const bf16_t* Bh0;
     const bf16_t* Bh1;
@@ -214,15 +218,18 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
       Bh1 = Bh0 + 128;
     }
 
-    // DMA source offsets (bytes, relative to Ab / Bh at k0 = 0) of this lane.
+    // DMA sources of this lane at k0 = 0 (A) / offsets relative to the B halves.
     // A: instruction i of wave w fills chunks [(w*8+i)*64, +64) of [256 m][8 chunks];
     // rows past the expert's last row re-read its last row (never written back).
-    uint32_t a_src[8];
+    const char* a_src[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r = wave * 64 + i * 8 + (lane >> 3);
       const int c = (lane & 7) ^ swz(r);
-      a_src[i] = (uint32_t)(min(r, mrows - 1) * K * 2 + c * 16);
+      const int rr = row0 + min(r, mrows - 1);
+      const size_t arow = row_token != nullptr ? (size_t)min(max(row_token[rr], 0), a_rows - 1)
+                                               : (size_t)rr;
+      a_src[i] = (const char*)(A + arow * K) + c * 16;
     }
     // B: instruction i of wave w fills units [(w*4 + i)*64, +64) of one half's
     // [64 k][16 units]: row k = (w*4 + i)*4 + lane/16.
@@ -239,7 +246,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
       const uint32_t kA = (uint32_t)(kt * BK * 2);
       const size_t kB = (size_t)kt * BK * N * 2;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) lds_dma16(Ab + (a_src[i] + kA), stg + (wave * 8 + i) * 512);
+      for (int i = 0; i < 8; ++i) lds_dma16(a_src[i] + kA, stg + (wave * 8 + i) * 512);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         lds_dma16((const char*)Bh0 + kB + b_src[i], stg + BM * BK + (wave * 4 + i) * 512);
@@ -358,9 +365,9 @@ int device_cus() {
   return cus;
 }
 
-hipError_t launch_gemm_bf16(int epi, const bf16_t* a, const int32_t* offsets, const bf16_t* w0,
-                            const bf16_t* w1, bf16_t* c, int E, int K, int N, int max_rows,
-                            hipStream_t s) {
+hipError_t launch_gemm_bf16(int epi, const bf16_t* a, const int32_t* row_token, int a_rows,
+                            const int32_t* offsets, const bf16_t* w0, const bf16_t* w1,
+                            bf16_t* c, int E, int K, int N, int max_rows, hipStream_t s) {
   const int outn = epi == EPI_SWIGLU ? 128 : 256;
   const long max_tiles = (long)((max_rows + BM - 1) / BM + E) * (N / outn);
   int grid = device_cus();
@@ -371,13 +378,13 @@ hipError_t launch_gemm_bf16(int epi, const bf16_t* a, const int32_t* offsets, co
   const dim3 g(grid), b(256);
   switch (epi) {
     case EPI_SWIGLU:
-      hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EPI_SWIGLU>), g, b, 0, s, a, offsets, w0, w1, c, E, K, N, max_rows);
+      hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EPI_SWIGLU>), g, b, 0, s, a, row_token, a_rows, offsets, w0, w1, c, E, K, N, max_rows);
       break;
     case EPI_GELU:
-      hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EPI_GELU>), g, b, 0, s, a, offsets, w0, w1, c, E, K, N, max_rows);
+      hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EPI_GELU>), g, b, 0, s, a, row_token, a_rows, offsets, w0, w1, c, E, K, N, max_rows);
       break;
     default:
-      hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EPI_NONE>), g, b, 0, s, a, offsets, w0, w1, c, E, K, N, max_rows);
+      hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EPI_NONE>), g, b, 0, s, a, row_token, a_rows, offsets, w0, w1, c, E, K, N, max_rows);
       break;
   }
   return hipGetLastError();
@@ -389,7 +396,8 @@ constexpr int FT = 16;
 
 template <int EPI>
 __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
-    const float* __restrict__ A, const int32_t* __restrict__ offsets, const float* __restrict__ W0,
+    const float* __restrict__ A, const int32_t* __restrict__ row_token, int a_rows,
+    const int32_t* __restrict__ offsets, const float* __restrict__ W0,
     const float* __restrict__ W1, float* __restrict__ C, int E, int K, int N, int max_rows) {
   __shared__ float As[FT][FT + 1], B0[FT][FT + 1], B1[FT][FT + 1];
   __shared__ int s_start[kMaxExperts + 1];
@@ -406,10 +414,14 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
   const int col = blockIdx.y * FT + tx;
   const float* We0 = W0 + (size_t)e * K * N;
   const float* We1 = (EPI == EPI_SWIGLU) ? W1 + (size_t)e * K * N : nullptr;
+  size_t arow = 0;
+  if (row < m_e)
+    arow = row_token != nullptr ? (size_t)min(max(row_token[row_beg + row], 0), a_rows - 1)
+                                : (size_t)(row_beg + row);
   float acc0 = 0.f, acc1 = 0.f;
   for (int k0 = 0; k0 < K; k0 += FT) {
     const int ka = k0 + tx, kb = k0 + ty;
-    As[ty][tx] = (row < m_e && ka < K) ? A[(size_t)(row_beg + row) * K + ka] : 0.f;
+    As[ty][tx] = (row < m_e && ka < K) ? A[arow * K + ka] : 0.f;
     B0[ty][tx] = (kb < K && col < N) ? We0[(size_t)kb * N + col] : 0.f;
     if (EPI == EPI_SWIGLU) B1[ty][tx] = (kb < K && col < N) ? We1[(size_t)kb * N + col] : 0.f;
     __syncthreads();
@@ -429,19 +441,19 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
   }
 }
 
-hipError_t launch_gemm_f32(int epi, const float* a, const int32_t* offsets, const float* w0,
-                           const float* w1, float* c, int E, int K, int N, int max_rows,
-                           hipStream_t s) {
+hipError_t launch_gemm_f32(int epi, const float* a, const int32_t* row_token, int a_rows,
+                           const int32_t* offsets, const float* w0, const float* w1, float* c,
+                           int E, int K, int N, int max_rows, hipStream_t s) {
   const dim3 g((max_rows + FT - 1) / FT + E, (N + FT - 1) / FT), b(256);
   switch (epi) {
     case EPI_SWIGLU:
-      hipLaunchKernelGGL((grouped_gemm_f32_kernel<EPI_SWIGLU>), g, b, 0, s, a, offsets, w0, w1, c, E, K, N, max_rows);
+      hipLaunchKernelGGL((grouped_gemm_f32_kernel<EPI_SWIGLU>), g, b, 0, s, a, row_token, a_rows, offsets, w0, w1, c, E, K, N, max_rows);
       break;
     case EPI_GELU:
-      hipLaunchKernelGGL((grouped_gemm_f32_kernel<EPI_GELU>), g, b, 0, s, a, offsets, w0, w1, c, E, K, N, max_rows);
+      hipLaunchKernelGGL((grouped_gemm_f32_kernel<EPI_GELU>), g, b, 0, s, a, row_token, a_rows, offsets, w0, w1, c, E, K, N, max_rows);
       break;
     default:
-      hipLaunchKernelGGL((grouped_gemm_f32_kernel<EPI_NONE>), g, b, 0, s, a, offsets, w0, w1, c, E, K, N, max_rows);
+      hipLaunchKernelGGL((grouped_gemm_f32_kernel<EPI_NONE>), g, b, 0, s, a, row_token, a_rows, offsets, w0, w1, c, E, K, N, max_rows);
       break;
   }
   return hipGetLastError();

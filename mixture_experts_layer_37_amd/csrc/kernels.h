@@ -35,12 +35,14 @@ hipError_t launch_permute(const void* x, int elem_bytes, const int32_t* topk_idx
 
 // ---- grouped expert GEMMs (gemm.hip)
 enum Epilogue { EPI_SWIGLU = 0, EPI_GELU = 1, EPI_NONE = 2 };
-hipError_t launch_gemm_bf16(int epi, const bf16_t* a, const int32_t* offsets, const bf16_t* w0,
-                            const bf16_t* w1, bf16_t* c, int E, int K, int N, int max_rows,
-                            hipStream_t s);
-hipError_t launch_gemm_f32(int epi, const float* a, const int32_t* offsets, const float* w0,
-                           const float* w1, float* c, int E, int K, int N, int max_rows,
-                           hipStream_t s);
+// A row r of the expert-major operand is a[r], or a[row_token[r]] when row_token is given
+// (token rows gathered in place; indexes clamped into [0, a_rows)).
+hipError_t launch_gemm_bf16(int epi, const bf16_t* a, const int32_t* row_token, int a_rows,
+                            const int32_t* offsets, const bf16_t* w0, const bf16_t* w1,
+                            bf16_t* c, int E, int K, int N, int max_rows, hipStream_t s);
+hipError_t launch_gemm_f32(int epi, const float* a, const int32_t* row_token, int a_rows,
+                           const int32_t* offsets, const float* w0, const float* w1, float* c,
+                           int E, int K, int N, int max_rows, hipStream_t s);
 
 // ---- combine (combine.hip)
 hipError_t launch_combine(int dtype_bf16, const void* y, const int32_t* slot_row,

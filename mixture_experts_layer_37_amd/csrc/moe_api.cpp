@@ -17,7 +17,7 @@ thread_local int g_last_hip_error = 0;
 
 enum Region {
   R_WT, R_LOGITS, R_TOPK_IDX, R_TOPK_W, R_ROUTE_FLAGS, R_HIST, R_PERM_FLAGS, R_COUNTS,
-  R_OFFSETS, R_SLOT_ROW, R_ROW_TOKEN, R_X_PERM, R_H, R_Y_PERM, R_NUM
+  R_OFFSETS, R_SLOT_ROW, R_ROW_TOKEN, R_H, R_Y_PERM, R_NUM
 };
 
 struct Layout {
@@ -36,7 +36,9 @@ Layout layout_of(const moe_config* c) {
   const size_t N = T * k;
   const size_t NB = (size_t)moe::permute_count_blocks(c->tokens);
   Layout L;
-  L.size[R_WT] = c->dtype == MOE_DTYPE_BF16 ? (size_t)moe::route_padded_experts(c->experts) * H * 2 : 0;
+  L.size[R_WT] = (c->dtype == MOE_DTYPE_BF16 && !moe::route_lds_fits(c->hidden, c->experts))
+                    ? (size_t)moe::route_padded_experts(c->experts) * H * 2
+                    : 0;
   L.size[R_LOGITS] = T * E * 4;
   L.size[R_TOPK_IDX] = N * 4;
   L.size[R_TOPK_W] = N * 4;
@@ -47,7 +49,6 @@ Layout layout_of(const moe_config* c) {
   L.size[R_OFFSETS] = (E + 1) * 4;
   L.size[R_SLOT_ROW] = N * 4;
   L.size[R_ROW_TOKEN] = N * 4;
-  L.size[R_X_PERM] = N * H * es;
   L.size[R_H] = N * I * es;
   L.size[R_Y_PERM] = N * H * es;
   size_t o = 0;
@@ -152,17 +153,21 @@ moe_status do_permute(const moe_config* c, const void* x, const int32_t* idx, vo
       c->experts, c->top_k, cap < c->tokens ? cap : c->tokens, s));
 }
 
-moe_status do_up(const moe_config* c, const void* x_perm, const int32_t* offsets,
-                 const void* w_gate, const void* w_up, void* h, hipStream_t s) {
+// GEMM 1. `a` is x_perm (row_token == nullptr) or the token matrix x read through
+// row_token (the permute gather fused into the operand loads).
+moe_status do_up(const moe_config* c, const void* a, const int32_t* row_token,
+                 const int32_t* offsets, const void* w_gate, const void* w_up, void* h,
+                 hipStream_t s) {
   const int swiglu = c->activation == MOE_ACT_SWIGLU;
   const int epi = swiglu ? moe::EPI_SWIGLU : moe::EPI_GELU;
   const int rows = c->tokens * c->top_k;
+  const int a_rows = row_token != nullptr ? c->tokens : rows;
   if (c->dtype == MOE_DTYPE_BF16)
     return hip_status(moe::launch_gemm_bf16(
-        epi, (const moe::bf16_t*)x_perm, offsets,
+        epi, (const moe::bf16_t*)a, row_token, a_rows, offsets,
         (const moe::bf16_t*)(swiglu ? w_gate : w_up), (const moe::bf16_t*)w_up,
         (moe::bf16_t*)h, c->experts, c->hidden, c->inter, rows, s));
-  return hip_status(moe::launch_gemm_f32(epi, (const float*)x_perm, offsets,
+  return hip_status(moe::launch_gemm_f32(epi, (const float*)a, row_token, a_rows, offsets,
                                          (const float*)(swiglu ? w_gate : w_up),
                                          (const float*)w_up, (float*)h, c->experts, c->hidden,
                                          c->inter, rows, s));
@@ -172,11 +177,11 @@ moe_status do_down(const moe_config* c, const void* h, const int32_t* offsets,
                    const void* w_down, void* y, hipStream_t s) {
   const int rows = c->tokens * c->top_k;
   if (c->dtype == MOE_DTYPE_BF16)
-    return hip_status(moe::launch_gemm_bf16(moe::EPI_NONE, (const moe::bf16_t*)h, offsets,
-                                            (const moe::bf16_t*)w_down, nullptr,
+    return hip_status(moe::launch_gemm_bf16(moe::EPI_NONE, (const moe::bf16_t*)h, nullptr, rows,
+                                            offsets, (const moe::bf16_t*)w_down, nullptr,
                                             (moe::bf16_t*)y, c->experts, c->inter, c->hidden,
                                             rows, s));
-  return hip_status(moe::launch_gemm_f32(moe::EPI_NONE, (const float*)h, offsets,
+  return hip_status(moe::launch_gemm_f32(moe::EPI_NONE, (const float*)h, nullptr, rows, offsets,
                                          (const float*)w_down, nullptr, (float*)y, c->experts,
                                          c->inter, c->hidden, rows, s));
 }
@@ -229,9 +234,11 @@ moe_status moe_permute(const moe_config* cfg, const void* x, const int32_t* topk
                        moe_stream_t stream) {
   MOE_TRY(check_cfg(cfg));
   if (cfg->tokens == 0) return MOE_OK;   // empty batch: nothing to read or write
-  MOE_TRY(need(x, 16));
+  if (x_perm != nullptr) {   // NULL: row maps only
+    MOE_TRY(need(x, 16));
+    MOE_TRY(need(x_perm, 16));
+  }
   MOE_TRY(need(topk_idx, 4));
-  MOE_TRY(need(x_perm, 16));
   MOE_TRY(need(expert_counts, 4));
   MOE_TRY(need(expert_offsets, 4));
   MOE_TRY(need(row_token, 4));
@@ -251,7 +258,21 @@ moe_status moe_expert_up(const moe_config* cfg, const void* x_perm,
   if (cfg->activation == MOE_ACT_SWIGLU) MOE_TRY(need(w_gate, 16));
   MOE_TRY(need(w_up, 16));
   MOE_TRY(need(h, 16));
-  return do_up(cfg, x_perm, expert_offsets, w_gate, w_up, h, (hipStream_t)stream);
+  return do_up(cfg, x_perm, nullptr, expert_offsets, w_gate, w_up, h, (hipStream_t)stream);
+}
+
+moe_status moe_expert_up_rows(const moe_config* cfg, const void* x, const int32_t* row_token,
+                              const int32_t* expert_offsets, const void* w_gate,
+                              const void* w_up, void* h, moe_stream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  if (cfg->tokens == 0) return MOE_OK;   // empty batch: nothing to read or write
+  MOE_TRY(need(x, 16));
+  MOE_TRY(need(row_token, 4));
+  MOE_TRY(need(expert_offsets, 4));
+  if (cfg->activation == MOE_ACT_SWIGLU) MOE_TRY(need(w_gate, 16));
+  MOE_TRY(need(w_up, 16));
+  MOE_TRY(need(h, 16));
+  return do_up(cfg, x, row_token, expert_offsets, w_gate, w_up, h, (hipStream_t)stream);
 }
 
 moe_status moe_expert_down(const moe_config* cfg, const void* h, const int32_t* expert_offsets,
@@ -281,7 +302,7 @@ moe_status moe_grouped_ffn(const moe_config* cfg, const void* x_perm,
   const Layout L = layout_of(cfg);
   void* h = region<void>(ws, L, R_H);
   const hipStream_t s = (hipStream_t)stream;
-  MOE_TRY(do_up(cfg, x_perm, expert_offsets, w_gate, w_up, h, s));
+  MOE_TRY(do_up(cfg, x_perm, nullptr, expert_offsets, w_gate, w_up, h, s));
   return do_down(cfg, h, expert_offsets, w_down, y_perm, s);
 }
 
@@ -319,12 +340,12 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
   int32_t* offsets = region<int32_t>(ws, L, R_OFFSETS);
   int32_t* slot_row = region<int32_t>(ws, L, R_SLOT_ROW);
   int32_t* row_token = region<int32_t>(ws, L, R_ROW_TOKEN);
-  void* x_perm = region<void>(ws, L, R_X_PERM);
   void* h = region<void>(ws, L, R_H);
   void* y = region<void>(ws, L, R_Y_PERM);
   MOE_TRY(do_route(cfg, x, w_router, gate_bias, logits, idx, w, ws, s));
-  MOE_TRY(do_permute(cfg, x, idx, x_perm, counts, offsets, row_token, slot_row, ws, s));
-  MOE_TRY(do_up(cfg, x_perm, offsets, w_gate, w_up, h, s));
+  // the permutation's row maps only: GEMM 1 gathers the token rows itself
+  MOE_TRY(do_permute(cfg, x, idx, nullptr, counts, offsets, row_token, slot_row, ws, s));
+  MOE_TRY(do_up(cfg, x, row_token, offsets, w_gate, w_up, h, s));
   MOE_TRY(do_down(cfg, h, offsets, w_down, y, s));
   return do_combine(cfg, y, slot_row, w, out, s);
 }
@@ -334,9 +355,9 @@ moe_status moe_workspace_view(const moe_config* cfg, void* ws, int32_t which, vo
   MOE_TRY(check_cfg(cfg));
   if (ws == nullptr || dev_ptr == nullptr) return MOE_ERR_INVALID_ARG;
   static const Region map[MOE_WS_NUM_VIEWS] = {R_LOGITS,   R_TOPK_IDX, R_TOPK_W,  R_COUNTS,
-                                               R_OFFSETS,  R_SLOT_ROW, R_ROW_TOKEN, R_X_PERM,
+                                               R_OFFSETS,  R_SLOT_ROW, R_ROW_TOKEN, R_NUM,
                                                R_H,        R_Y_PERM};
-  if (which < 0 || which >= MOE_WS_NUM_VIEWS) return MOE_ERR_INVALID_ARG;
+  if (which < 0 || which >= MOE_WS_NUM_VIEWS || map[which] == R_NUM) return MOE_ERR_INVALID_ARG;
   const Layout L = layout_of(cfg);
   *dev_ptr = static_cast<char*>(ws) + L.off[map[which]];
   if (bytes != nullptr) *bytes = L.size[map[which]];

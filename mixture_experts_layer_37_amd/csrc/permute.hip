@@ -3,7 +3,8 @@
 // 算子优化实战": a per-expert mask feeds SparseGather, and sparse data is kept CSR-style;
 // lshu.cn/news/82007, section 4: npu_moe_token_preprocess reorders the tokens).
 //
-// Three launches, no float and no global atomics:
+// Three launches, no float and no global atomics (without an x_perm destination the third
+// only computes the row maps, for a GEMM that gathers token rows itself):
 //   count  -- 1024 tokens per block. Per wave and expert a 64-bit lane mask (LDS OR);
 //             popcounts give the block's per-expert histogram and each assignment's rank
 //             inside the block in token order. Invalid or repeated ids are dropped, flagged.
@@ -173,6 +174,27 @@ __global__ __launch_bounds__(256) void permute_gather_kernel(
   }
 }
 
+// Index-only gather: the rows of each slot and the row -> token map, no row copy (for a
+// grouped GEMM that reads token rows in place). One thread per token.
+__global__ __launch_bounds__(256) void permute_rows_kernel(
+    const int32_t* __restrict__ idx, int32_t* __restrict__ slot_row,
+    int32_t* __restrict__ row_token, const int32_t* __restrict__ prefix,
+    const int32_t* __restrict__ offsets, int T, int E, int k, int cap) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  for (int j = 0; j < k; ++j) {
+    int row = -1;
+    const int r = slot_row[(size_t)t * k + j];
+    if (r >= 0) {
+      const int e = idx[(size_t)t * k + j];
+      const int pos = prefix[(size_t)(t / kCountBlockTokens) * E + e] + r;
+      if (pos < cap) row = offsets[e] + pos;
+    }
+    slot_row[(size_t)t * k + j] = row;
+    if (row >= 0) row_token[row] = t;
+  }
+}
+
 hipError_t launch_permute(const void* x, int elem_bytes, const int32_t* topk_idx, void* x_perm,
                           int32_t* counts, int32_t* offsets, int32_t* row_token,
                           int32_t* slot_row, int32_t* hist, int32_t* flags, int T, int H, int E,
@@ -186,6 +208,11 @@ hipError_t launch_permute(const void* x, int elem_bytes, const int32_t* topk_idx
                      cap);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (x_perm == nullptr) {
+    hipLaunchKernelGGL(permute_rows_kernel, dim3((T + 255) / 256), dim3(256), 0, s, topk_idx,
+                       slot_row, row_token, hist, offsets, T, E, k, cap);
+    return hipGetLastError();
+  }
   const int row_vecs = (int)((size_t)H * elem_bytes / 16);
   const dim3 grid((T + 3) / 4), block(256);
 #define MOE_GATHER(U_)                                                                      \

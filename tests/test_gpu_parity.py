@@ -220,3 +220,44 @@ def test_single_expert_gemm_matches_torch_matmul():
     torch.cuda.synchronize()
     rel = ((y.float() - ref).abs().max() / ref.abs().max()).item()
     assert rel < 1e-2, rel
+
+
+@pytest.mark.parametrize("name", ["bf16_capacity", "bf16_many_experts", "fp32_swiglu_capacity",
+                                  "bf16_gelu"])
+def test_expert_up_rows_equals_gather_then_expert_up(name):
+    """GEMM 1 reading token rows in place through row_token gives bit-identical h to GEMM 1 on
+    the x_perm that moe_permute materialises; the row-maps-only permute (x_perm = NULL) writes
+    the same maps as the materialising one."""
+    cfg = CASES[name]
+    inp = make_inputs(cfg, seed=4)
+    layer = MoELayer(cfg, inp)
+    c, T, k, E, H, I = layer.c, cfg.tokens, cfg.top_k, cfg.experts, cfg.hidden, cfg.inter
+    dev = "cuda"
+    x = to_device(cfg, inp["x"])
+    edt = x.dtype
+    ws = torch.empty_like(layer.ws)
+    lg = torch.empty((T, E), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    L.moe_route(c, x, layer.w_router, layer.bias, lg, idx, w, ws)
+    maps = []
+    for materialise in (True, False):
+        xp = torch.empty((T * k, H), dtype=edt, device=dev) if materialise else None
+        counts = torch.empty(E, dtype=torch.int32, device=dev)
+        offs = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        rt = torch.full((T * k,), -7, dtype=torch.int32, device=dev)
+        sr = torch.empty((T, k), dtype=torch.int32, device=dev)
+        L.moe_permute(c, x, idx, xp, counts, offs, rt, sr, ws)
+        maps.append((xp, counts, offs, rt, sr))
+    (xp, counts, offs, rt, sr), (_, counts2, offs2, rt2, sr2) = maps
+    torch.cuda.synchronize()
+    n = int(offs[-1].item())
+    assert torch.equal(counts, counts2) and torch.equal(offs, offs2) and torch.equal(sr, sr2)
+    assert torch.equal(rt[:n], rt2[:n])
+    h1 = torch.zeros((T * k, I), dtype=edt, device=dev)
+    h2 = torch.ones((T * k, I), dtype=edt, device=dev)
+    L.moe_expert_up(c, xp, offs, layer.w_gate, layer.w_up, h1)
+    L.moe_expert_up_rows(c, x, rt, offs, layer.w_gate, layer.w_up, h2)
+    torch.cuda.synchronize()
+    bits = torch.int16 if edt == torch.bfloat16 else torch.int32
+    assert torch.equal(h1[:n].view(bits), h2[:n].view(bits))
