@@ -36,7 +36,7 @@ def parse_args():
     ap.add_argument("--config", default="mixtral")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -54,7 +54,7 @@ def measured_traffic(per_launch_flops_unused=None):
         return None
     kv = {}
     for line in open(TRAFFIC_FILE):
-        m = re.match(r"^\s*([a-z_]+)\s*:\s*(\S+)", line)
+        m = re.match(r"^\s*([a-z0-9_]+)\s*:\s*(\S+)", line)
         if m:
             kv[m.group(1)] = m.group(2)
     if kv.get("gemm_source_sha256_16") != kernel_source_digest():
@@ -190,12 +190,62 @@ def main():
     }
     result["materialised_permute"] = materialised_permute(L, c, x, idx, counts, offs, rt, sr, ws,
                                                           stream, T, H, k, n_kept, es)
+    peaks = measured_peaks(stream)
+    result["measured_peaks"] = peaks
+    if peaks is not None:
+        result["roofline"]["peak_measured"] = peaks["mfma_bf16_tflops"]
+        result["roofline"]["frac_of_measured"] = up_tflops / peaks["mfma_bf16_tflops"]
+        result["hbm_frac_of_measured"] = {
+            n: v * PEAK_HBM_GBS / peaks["hbm_copy_gbs"] for n, v in result["hbm_frac"].items()}
+        result["materialised_permute"]["hbm_frac_of_measured"] = (
+            result["materialised_permute"]["hbm_frac"] * PEAK_HBM_GBS / peaks["hbm_copy_gbs"])
 
     result["device_flags"] = L.moe_read_device_status(c, ws, 3, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, inp, out, logits, idx, args.cpu_sample_tokens,
                                               result)
     print(json.dumps(result), flush=True)
+
+
+def measured_peaks(stream):
+    """What this device sustains, from the library's probes (libmoe_peaks.so): an MFMA-only
+    loop (bf16 v_mfma_f32_32x32x16, no memory traffic; 4 blocks of 4 waves per CU) and a
+    1 GiB device-to-device streaming copy (bytes read + written). None if not built."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "mixture_experts_layer_37_amd", "libmoe_peaks.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.moe_peak_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.moe_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                  ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, iters = 4 * cus, 4000
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    nbytes = 1 << 30
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    sh = stream.cuda_stream
+
+    def timed(fn, reps=3):
+        fn()
+        best = None
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+        return best
+
+    ms_mfma = timed(lambda: lib.moe_peak_mfma(sink.data_ptr(), blocks, iters, sh))
+    ms_copy = timed(lambda: lib.moe_peak_copy(src.data_ptr(), dst.data_ptr(), nbytes, sh))
+    return {"mfma_bf16_tflops": blocks * 4 * iters * 8 * 32768 / (ms_mfma * 1e-3) / 1e12,
+            "hbm_copy_gbs": 2 * nbytes / (ms_copy * 1e-3) / 1e9}
 
 
 def materialised_permute(L, c, x, idx, counts, offs, rt, sr, ws, stream, T, H, k, n_kept, es):
@@ -237,15 +287,19 @@ def cpu_baseline(cfg, inp, out_dev, logits_dev, idx_dev, n_tok, result):
     n_tok = min(n_tok, cfg.tokens)
     xs = as_float(cfg, inp["x"][:n_tok])
     wg = ExpertView(cfg, inp["w_gate"]) if cfg.activation == "swiglu" else None
-    t0 = time.perf_counter()
-    ref = O.forward(xs, as_float(cfg, inp["w_router"]), inp["bias"], wg,
-                    ExpertView(cfg, inp["w_up"]), ExpertView(cfg, inp["w_down"]),
-                    top_k=cfg.top_k, activation=cfg.activation,
-                    capacity_factor=cfg.capacity_factor, renormalize=cfg.renormalize)
-    dt = time.perf_counter() - t0
+    # repeat the whole sample until about 10 s of oracle time (at most 3 passes)
+    times = []
+    while len(times) < 3 and sum(times) < 10.0:
+        t0 = time.perf_counter()
+        ref = O.forward(xs, as_float(cfg, inp["w_router"]), inp["bias"], wg,
+                        ExpertView(cfg, inp["w_up"]), ExpertView(cfg, inp["w_down"]),
+                        top_k=cfg.top_k, activation=cfg.activation,
+                        capacity_factor=cfg.capacity_factor, renormalize=cfg.renormalize)
+        times.append(time.perf_counter() - t0)
+    dt = sum(times) / len(times)
     rep = {"value": n_tok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
            "sample": f"first {n_tok} of {cfg.tokens} tokens of the same layer, all experts; "
-                     f"{dt:.1f} s", "host_cpus": len(os.sched_getaffinity(0))}
+                     f"{len(times)} pass(es), {dt:.1f} s each", "host_cpus": len(os.sched_getaffinity(0))}
     if cfg.capacity_factor <= 0:      # a token prefix routes exactly as in the full batch
         got = from_device(out_dev[:n_tok])
         got = (bf16_bits_to_f32(got) if got.dtype == np.uint16 else got).astype(np.float64)

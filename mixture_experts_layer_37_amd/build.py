@@ -1,4 +1,5 @@
-"""Build libmoe.so (the HIP kernels and the C ABI of include/moe.h) for gfx950 with hipcc.
+"""Build libmoe.so (the HIP kernels and the C ABI of include/moe.h) and libmoe_peaks.so (the
+benchmark's achievable-peak probes) for gfx950 with hipcc.
 
 Run as ``python -m mixture_experts_layer_37_amd.build``; the library lands next to this file.
 """
@@ -15,7 +16,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
+PEAKS_LIB = os.path.join(PKG, "libmoe_peaks.so")     # benchmark-only probes
 SOURCES = ["route.hip", "permute.hip", "gemm.hip", "combine.hip", "moe_api.cpp"]
+PEAKS_SOURCES = ["peaks.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [
@@ -45,19 +48,25 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 5) -> str:
-    """Compile every source and link libmoe.so; always rebuilds."""
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max(1, jobs)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib, verbose):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, jobs: int = 6) -> str:
+    """Compile every source and link libmoe.so (and the benchmark's libmoe_peaks.so);
+    always rebuilds."""
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(max(1, jobs)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES + PEAKS_SOURCES))
+    _link(objs[:len(SOURCES)], LIB, verbose)
+    _link(objs[len(SOURCES):], PEAKS_LIB, verbose)
     return LIB
 
 

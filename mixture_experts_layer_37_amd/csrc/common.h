@@ -17,6 +17,13 @@ typedef uint16_t bf16_t;                  // raw bfloat16 bits
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte store with the nontemporal hint, for rows written once and not read back soon.
+__device__ __forceinline__ void st_stream(uint4* p, uint4 v) {
+  const u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, (u32x4*)p);
+}
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
