@@ -115,7 +115,7 @@ def main():
         if ev: ev[2].record(stream)
         L.moe_expert_up_rows(c, x, rt, offs, layer.w_gate, layer.w_up, h, stream)
         if ev: ev[3].record(stream)
-        L.moe_expert_down(c, h, offs, layer.w_down, y, stream)
+        L.moe_expert_down(c, h, offs, layer.w_down, y, ws, stream)
         if ev: ev[4].record(stream)
         L.moe_combine(c, y, sr, w, out, stream)
         if ev: ev[5].record(stream)

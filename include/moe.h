@@ -146,9 +146,15 @@ moe_status moe_expert_up_rows(const moe_config* cfg, const void* x, const int32_
                               const void* w_up, void* h, moe_stream_t stream);
 
 /* Grouped GEMM 2: y_perm = h Wd[e] for the rows of each expert (lshu.cn page, section 4,
- * npu_moe_matmul). h [rows,I], w_down [E,I,H], y_perm [T*k,H] out. */
+ * npu_moe_matmul). h [rows,I], w_down [E,I,H], y_perm [T*k,H] out.
+ * ws / ws_bytes: the layer's workspace (at least moe_workspace_size bytes), or NULL. With a
+ * workspace, bf16 layers run the tiles left over after the last whole round of the grid as
+ * K slices over all CUs (float32 partials in ws, added in a fixed order by a second kernel on
+ * the same stream), so y_perm stays deterministic; without one, every tile runs whole. The
+ * two differ only in float32 summation order. ws too small -> MOE_ERR_WORKSPACE. */
 moe_status moe_expert_down(const moe_config* cfg, const void* h, const int32_t* expert_offsets,
-                           const void* w_down, void* y_perm, moe_stream_t stream);
+                           const void* w_down, void* y_perm, void* ws, size_t ws_bytes,
+                           moe_stream_t stream);
 
 /* moe_expert_up followed by moe_expert_down, with h kept in the workspace. */
 moe_status moe_grouped_ffn(const moe_config* cfg, const void* x_perm,

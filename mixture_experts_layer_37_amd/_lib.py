@@ -66,7 +66,7 @@ def lib():
             "moe_permute": [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, c_size_t, vp],
             "moe_expert_up": [cfgp, vp, vp, vp, vp, vp, vp],
             "moe_expert_up_rows": [cfgp, vp, vp, vp, vp, vp, vp, vp],
-            "moe_expert_down": [cfgp, vp, vp, vp, vp, vp],
+            "moe_expert_down": [cfgp, vp, vp, vp, vp, vp, c_size_t, vp],
             "moe_grouped_ffn": [cfgp, vp, vp, vp, vp, vp, vp, vp, c_size_t, vp],
             "moe_combine": [cfgp, vp, vp, vp, vp, vp],
             "moe_forward": [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, c_size_t, vp],
@@ -120,7 +120,7 @@ def _check(fn, status):
 
 
 def _nbytes(ws):
-    return ws.numel() * ws.element_size()
+    return 0 if ws is None else ws.numel() * ws.element_size()
 
 
 # ------------------------------------------------------------------ host-only queries
@@ -163,10 +163,11 @@ def moe_expert_up_rows(cfg, x, row_token, expert_offsets, w_gate, w_up, h, strea
         _ptr(w_up), _ptr(h), _stream(stream)))
 
 
-def moe_expert_down(cfg, h, expert_offsets, w_down, y_perm, stream=None):
+def moe_expert_down(cfg, h, expert_offsets, w_down, y_perm, ws=None, stream=None):
+    """ws: the layer's workspace (enables the split-K tail on bf16 layers) or None."""
     _check("moe_expert_down", lib().moe_expert_down(
         ctypes.byref(_as_cfg(cfg)), _ptr(h), _ptr(expert_offsets), _ptr(w_down), _ptr(y_perm),
-        _stream(stream)))
+        _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def moe_grouped_ffn(cfg, x_perm, expert_offsets, w_gate, w_up, w_down, y_perm, ws, stream=None):

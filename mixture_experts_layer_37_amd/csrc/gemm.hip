@@ -35,7 +35,12 @@
 //     columns of one row, written straight to global memory as 8-byte stores;
 //   - persistent grid of one block per CU; tiles are ordered (expert, n-tile, m-tile) and
 //     each of the 8 XCDs walks its own contiguous range, so the blocks sharing an XCD's L2
-//     work on the same weight columns at the same time.
+//     work on the same weight columns at the same time;
+//   - split-K tail (GEMM 2, when the caller supplies a partial buffer): the tiles beyond the
+//     last whole round of the grid would leave most CUs idle for one full tile time, so each
+//     of them is cut into S slices of K (S a power of two, tail * S <= grid), every slice
+//     writes a float32 partial tile, and a small reduction kernel adds the S partials in
+//     slice order and writes the bf16 rows. The result is deterministic.
 #include <type_traits>
 
 #include "common.h"
@@ -91,6 +96,53 @@ __device__ __forceinline__ int find_expert(const int* s_start, int E, int tile) 
   return lo;
 }
 
+// Where a tile sits: its expert, first row, valid rows and n-tile.
+struct TileCoord {
+  int e, row0, mrows, n_t;
+};
+__device__ __forceinline__ TileCoord decode_tile(const int* s_start, const int* s_off, int E,
+                                                 int tile, int BMt) {
+  TileCoord t;
+  t.e = find_expert(s_start, E, tile);
+  const int row_beg = s_off[t.e];
+  const int m_e = s_off[t.e + 1] - row_beg;   // > 0: the expert owns this tile
+  const int mt_e = (m_e + BMt - 1) / BMt;
+  const int rem = tile - s_start[t.e];
+  t.n_t = rem / mt_e;
+  const int m_t = rem - t.n_t * mt_e;
+  t.row0 = row_beg + m_t * BMt;
+  t.mrows = min(BMt, m_e - m_t * BMt);
+  return t;
+}
+
+// Split-K plan of one launch: tiles [0, full) run whole, tiles [full, full + tail) run as
+// S slices of K each (S = 1: no split, full = total). Slices are whole pairs of k-steps, at
+// least 16 k-steps long, and tail * S fits both the grid and the partial buffer.
+struct SplitPlan {
+  int full, tail, S;
+};
+constexpr int kMaxSplit = 8;
+__device__ __forceinline__ SplitPlan split_plan(int total, int grid, int KT, bool enabled) {
+  SplitPlan p = {total, 0, 1};
+  if (!enabled) return p;
+  const int full = (total / grid) * grid, tail = total - full;
+  const int units = min(grid, kSplitMaxUnits);
+  int S = 1;
+  while (tail > 0 && S < kMaxSplit && tail * S * 2 <= units && KT >= 16 * S * 2) S *= 2;
+  if (S > 1) {
+    p.full = full;
+    p.tail = tail;
+    p.S = S;
+  }
+  return p;
+}
+// k-steps [kb, ke) of slice c of S (KT even).
+__device__ __forceinline__ void slice_range(int KT, int S, int c, int& kb, int& ke) {
+  const int pairs = KT / 2;
+  kb = 2 * (c * pairs / S);
+  ke = 2 * ((c + 1) * pairs / S);
+}
+
 __device__ __forceinline__ float silu_f(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
 }
@@ -131,7 +183,8 @@ template <int EPI>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ row_token, int a_rows,
     const int32_t* __restrict__ offsets, const bf16_t* __restrict__ W0,
-    const bf16_t* __restrict__ W1, bf16_t* __restrict__ C, int E, int K, int N, int max_rows) {
+    const bf16_t* __restrict__ W1, bf16_t* __restrict__ C, float* __restrict__ partial, int E,
+    int K, int N, int max_rows) {
   // Two stages in two distinct LDS objects: the compiler can then tell a DMA into one
   // stage from reads of the other and does not make those reads wait for the DMA.
   __shared__ __attribute__((aligned(1024))) bf16_t stage0[kStage];
@@ -148,8 +201,11 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
 
   const int xcd = blockIdx.x % kXcds, li = blockIdx.x / kXcds;
   const int nper = gridDim.x / kXcds;
-  const int per = (total + kXcds - 1) / kXcds;
   const int KT = K / BK;
+  const SplitPlan plan = split_plan(__builtin_amdgcn_readfirstlane(total), gridDim.x, KT,
+                                   EPI == EPI_NONE && partial != nullptr);
+  const int per = (plan.full + kXcds - 1) / kXcds;   // whole tiles per XCD
+  const int my_unit = xcd * nper + li;                // this block's split slice, if any
 
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, lhi = lane >> 5;
@@ -196,17 +252,16 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     }
   };
 
-  for (int it = li; it < per; it += nper) {
-    const int tile = xcd * per + it;
-    if (tile >= total) break;
-    const int e = find_expert(s_start, E, tile);
-    const int row_beg = s_off[e];
-    const int m_e = s_off[e + 1] - row_beg;   // > 0: the expert owns this tile
-    const int mt_e = (m_e + BM - 1) / BM;
-    const int rem = tile - s_start[e];
-    const int n_t = rem / mt_e, m_t = rem - n_t * mt_e;
-    const int row0 = row_beg + m_t * BM;
-    const int mrows = min(BM, m_e - m_t * BM);
+  // One work item: tile `tile`, k-steps [kb, ke). A slice item (GEMM 2's split-K tail)
+  // writes a float32 partial tile instead of bf16 rows. Each kind has its own call site, so
+  // each gets its own register allocation.
+  auto run_tile = [&](int tile, int kb, int ke, float* part, auto slice) {
+    constexpr bool kSlice = decltype(slice)::value;
+    const TileCoord tc = decode_tile(s_start, s_off, E, __builtin_amdgcn_readfirstlane(tile), BM);
+    const int e = __builtin_amdgcn_readfirstlane(tc.e);
+    const int n_t = __builtin_amdgcn_readfirstlane(tc.n_t);
+    const int row0 = __builtin_amdgcn_readfirstlane(tc.row0);
+    const int mrows = __builtin_amdgcn_readfirstlane(tc.mrows);
     // B halves: base pointers (uniform) of columns [0,128) and [128,256) of the tile
     const bf16_t* Bh0;
     const bf16_t* Bh1;
@@ -303,14 +358,15 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     using yes = std::true_type;
     using no = std::false_type;
 
-    // K / 64 is even (K is a multiple of 128), so the steps pair up as (stage0, stage1).
-    dma(0, stage0);
+    // ke - kb is even (K is a multiple of 128 and slices are whole pairs), so the steps
+    // pair up as (stage0, stage1).
+    dma(kb, stage0);
     __builtin_amdgcn_s_waitcnt(0);
-    dma(1, stage1);
+    dma(kb + 1, stage1);
     __syncthreads();
     load_frags(stage0, 0, f0);
-    int kt = 0;
-    for (; kt + 2 < KT; kt += 2) {
+    int kt = kb;
+    for (; kt + 2 < ke; kt += 2) {
       kstep(kt, stage0, stage1, yes{}, yes{});
       kstep(kt + 1, stage1, stage0, yes{}, yes{});
     }
@@ -320,6 +376,23 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
 
     // Epilogue. acc[i][j][4q+s]: row m = wm*128 + i*32 + l32,
     // column (within the wave's block j) = 8q + 4*lhi + s.
+    if constexpr (kSlice) {   // float32 partial tile [BM][256], valid rows only
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = wm * 128 + i * 32 + l32;
+        if (m >= mrows) continue;
+        float* prow = part + (size_t)m * 256;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int col = wn * 128 + j * 32 + 8 * q + 4 * lhi;
+            *(float4*)(prow + col) = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                                 acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+          }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = wm * 128 + i * 32 + l32;
@@ -353,6 +426,21 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
           }
       }
     }
+  };
+
+  // This XCD's whole tiles, then at most one split slice per block.
+  for (int it = li; it < per; it += nper) {
+    const int tile = xcd * per + it;
+    if (tile >= plan.full) break;
+    run_tile(tile, 0, KT, nullptr, std::false_type{});
+  }
+  if constexpr (EPI == EPI_NONE) {
+    if (my_unit < plan.tail * plan.S) {
+      int kb, ke;
+      slice_range(KT, plan.S, my_unit % plan.S, kb, ke);
+      run_tile(plan.full + my_unit / plan.S, kb, ke, partial + (size_t)my_unit * (BM * 256),
+               std::true_type{});
+    }
   }
 }
 
@@ -365,27 +453,73 @@ int device_cus() {
   return cus;
 }
 
+// Split-K tail reduction of GEMM 2: for each sliced tile, C rows = bf16(sum over slices, in
+// slice order, of the float32 partials). Re-derives the launch's tile list and split plan
+// from the same offsets and grid size. Block work item: 8 rows of one tile, 32 threads per
+// row, 8 columns per thread.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial,
+                                                            const int32_t* __restrict__ offsets,
+                                                            bf16_t* __restrict__ C, int E, int K,
+                                                            int N, int max_rows, int grid) {
+  __shared__ int s_start[kMaxExperts + 1];
+  __shared__ int s_off[kMaxExperts + 1];
+  __shared__ int s_wsum[4];
+  const int total = build_tile_starts<BM>(offsets, E, N / 256, max_rows, s_start, s_off, s_wsum);
+  const SplitPlan plan = split_plan(total, grid, K / BK, true);
+  const int tid = threadIdx.x;
+  for (int w = blockIdx.x; w < plan.tail * (BM / 8); w += gridDim.x) {
+    const int ti = w / (BM / 8);
+    const TileCoord tc = decode_tile(s_start, s_off, E, plan.full + ti, BM);
+    const int r = (w % (BM / 8)) * 8 + (tid >> 5);
+    if (r >= tc.mrows) continue;
+    const int c8 = (tid & 31) * 8;
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    for (int sl = 0; sl < plan.S; ++sl) {
+      const float* p = partial + ((size_t)(ti * plan.S + sl) * BM + r) * 256 + c8;
+      const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+      acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+      acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+    }
+    *(uint4*)(C + (size_t)(tc.row0 + r) * N + tc.n_t * 256 + c8) =
+        make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                   pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+  }
+}
+
 hipError_t launch_gemm_bf16(int epi, const bf16_t* a, const int32_t* row_token, int a_rows,
                             const int32_t* offsets, const bf16_t* w0, const bf16_t* w1,
-                            bf16_t* c, int E, int K, int N, int max_rows, hipStream_t s) {
+                            bf16_t* c, float* partial, int E, int K, int N, int max_rows,
+                            hipStream_t s) {
   const int outn = epi == EPI_SWIGLU ? 128 : 256;
+  const bool split = epi == EPI_NONE && partial != nullptr;
   const long max_tiles = (long)((max_rows + BM - 1) / BM + E) * (N / outn);
   int grid = device_cus();
   grid = (grid / kXcds) * kXcds;
   if (grid < kXcds) grid = kXcds;
+  // Without a split, no more blocks than tiles; with one, the whole grid (a short tile list
+  // is then cut into K slices over all CUs).
   const long need = ((max_tiles + kXcds - 1) / kXcds) * kXcds;
-  if (need < grid) grid = (int)need;
+  if (!split && need < grid) grid = (int)need;
+  if (!split) partial = nullptr;
   const dim3 g(grid), b(256);
   switch (epi) {
     case EPI_SWIGLU:
-      hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EPI_SWIGLU>), g, b, 0, s, a, row_token, a_rows, offsets, w0, w1, c, E, K, N, max_rows);
+      hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EPI_SWIGLU>), g, b, 0, s, a, row_token, a_rows, offsets, w0, w1, c, partial, E, K, N, max_rows);
       break;
     case EPI_GELU:
-      hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EPI_GELU>), g, b, 0, s, a, row_token, a_rows, offsets, w0, w1, c, E, K, N, max_rows);
+      hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EPI_GELU>), g, b, 0, s, a, row_token, a_rows, offsets, w0, w1, c, partial, E, K, N, max_rows);
       break;
     default:
-      hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EPI_NONE>), g, b, 0, s, a, row_token, a_rows, offsets, w0, w1, c, E, K, N, max_rows);
+      hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EPI_NONE>), g, b, 0, s, a, row_token, a_rows, offsets, w0, w1, c, partial, E, K, N, max_rows);
       break;
+  }
+  if (split) {
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(1024), dim3(256), 0, s, partial, offsets, c, E,
+                       K, N, max_rows, grid);
   }
   return hipGetLastError();
 }

@@ -37,9 +37,14 @@ hipError_t launch_permute(const void* x, int elem_bytes, const int32_t* topk_idx
 enum Epilogue { EPI_SWIGLU = 0, EPI_GELU = 1, EPI_NONE = 2 };
 // A row r of the expert-major operand is a[r], or a[row_token[r]] when row_token is given
 // (token rows gathered in place; indexes clamped into [0, a_rows)).
+// `partial` (EPI_NONE only; may be null): float32 scratch of kSplitPartialBytes for the
+// split-K tail; null runs every tile whole.
+constexpr int kSplitMaxUnits = 256;   // K slices of one launch, at most
+constexpr size_t kSplitPartialBytes = (size_t)kSplitMaxUnits * 256 * 256 * 4;
 hipError_t launch_gemm_bf16(int epi, const bf16_t* a, const int32_t* row_token, int a_rows,
                             const int32_t* offsets, const bf16_t* w0, const bf16_t* w1,
-                            bf16_t* c, int E, int K, int N, int max_rows, hipStream_t s);
+                            bf16_t* c, float* partial, int E, int K, int N, int max_rows,
+                            hipStream_t s);
 hipError_t launch_gemm_f32(int epi, const float* a, const int32_t* row_token, int a_rows,
                            const int32_t* offsets, const float* w0, const float* w1, float* c,
                            int E, int K, int N, int max_rows, hipStream_t s);

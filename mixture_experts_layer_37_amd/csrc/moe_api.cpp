@@ -17,7 +17,7 @@ thread_local int g_last_hip_error = 0;
 
 enum Region {
   R_WT, R_LOGITS, R_TOPK_IDX, R_TOPK_W, R_ROUTE_FLAGS, R_HIST, R_PERM_FLAGS, R_COUNTS,
-  R_OFFSETS, R_SLOT_ROW, R_ROW_TOKEN, R_H, R_Y_PERM, R_NUM
+  R_OFFSETS, R_SLOT_ROW, R_ROW_TOKEN, R_H, R_Y_PERM, R_SPLIT, R_NUM
 };
 
 struct Layout {
@@ -51,6 +51,8 @@ Layout layout_of(const moe_config* c) {
   L.size[R_ROW_TOKEN] = N * 4;
   L.size[R_H] = N * I * es;
   L.size[R_Y_PERM] = N * H * es;
+  // float32 partial tiles of GEMM 2's split-K tail (bf16 path)
+  L.size[R_SPLIT] = c->dtype == MOE_DTYPE_BF16 ? moe::kSplitPartialBytes : 0;
   size_t o = 0;
   for (int r = 0; r < R_NUM; ++r) {
     L.off[r] = o;
@@ -166,21 +168,22 @@ moe_status do_up(const moe_config* c, const void* a, const int32_t* row_token,
     return hip_status(moe::launch_gemm_bf16(
         epi, (const moe::bf16_t*)a, row_token, a_rows, offsets,
         (const moe::bf16_t*)(swiglu ? w_gate : w_up), (const moe::bf16_t*)w_up,
-        (moe::bf16_t*)h, c->experts, c->hidden, c->inter, rows, s));
+        (moe::bf16_t*)h, nullptr, c->experts, c->hidden, c->inter, rows, s));
   return hip_status(moe::launch_gemm_f32(epi, (const float*)a, row_token, a_rows, offsets,
                                          (const float*)(swiglu ? w_gate : w_up),
                                          (const float*)w_up, (float*)h, c->experts, c->hidden,
                                          c->inter, rows, s));
 }
 
+// GEMM 2. `partial` (bf16 only, may be null) is the split-K tail's scratch.
 moe_status do_down(const moe_config* c, const void* h, const int32_t* offsets,
-                   const void* w_down, void* y, hipStream_t s) {
+                   const void* w_down, void* y, float* partial, hipStream_t s) {
   const int rows = c->tokens * c->top_k;
   if (c->dtype == MOE_DTYPE_BF16)
     return hip_status(moe::launch_gemm_bf16(moe::EPI_NONE, (const moe::bf16_t*)h, nullptr, rows,
                                             offsets, (const moe::bf16_t*)w_down, nullptr,
-                                            (moe::bf16_t*)y, c->experts, c->inter, c->hidden,
-                                            rows, s));
+                                            (moe::bf16_t*)y, partial, c->experts, c->inter,
+                                            c->hidden, rows, s));
   return hip_status(moe::launch_gemm_f32(moe::EPI_NONE, (const float*)h, nullptr, rows, offsets,
                                          (const float*)w_down, nullptr, (float*)y, c->experts,
                                          c->inter, c->hidden, rows, s));
@@ -276,14 +279,20 @@ moe_status moe_expert_up_rows(const moe_config* cfg, const void* x, const int32_
 }
 
 moe_status moe_expert_down(const moe_config* cfg, const void* h, const int32_t* expert_offsets,
-                           const void* w_down, void* y_perm, moe_stream_t stream) {
+                           const void* w_down, void* y_perm, void* ws, size_t ws_bytes,
+                           moe_stream_t stream) {
   MOE_TRY(check_cfg(cfg));
   if (cfg->tokens == 0) return MOE_OK;   // empty batch: nothing to read or write
   MOE_TRY(need(h, 16));
   MOE_TRY(need(expert_offsets, 4));
   MOE_TRY(need(w_down, 16));
   MOE_TRY(need(y_perm, 16));
-  return do_down(cfg, h, expert_offsets, w_down, y_perm, (hipStream_t)stream);
+  float* partial = nullptr;
+  if (ws != nullptr) {
+    MOE_TRY(check_ws(cfg, ws, ws_bytes));
+    partial = region<float>(ws, layout_of(cfg), R_SPLIT);
+  }
+  return do_down(cfg, h, expert_offsets, w_down, y_perm, partial, (hipStream_t)stream);
 }
 
 moe_status moe_grouped_ffn(const moe_config* cfg, const void* x_perm,
@@ -303,7 +312,7 @@ moe_status moe_grouped_ffn(const moe_config* cfg, const void* x_perm,
   void* h = region<void>(ws, L, R_H);
   const hipStream_t s = (hipStream_t)stream;
   MOE_TRY(do_up(cfg, x_perm, nullptr, expert_offsets, w_gate, w_up, h, s));
-  return do_down(cfg, h, expert_offsets, w_down, y_perm, s);
+  return do_down(cfg, h, expert_offsets, w_down, y_perm, region<float>(ws, L, R_SPLIT), s);
 }
 
 moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* slot_row,
@@ -346,7 +355,7 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
   // the permutation's row maps only: GEMM 1 gathers the token rows itself
   MOE_TRY(do_permute(cfg, x, idx, nullptr, counts, offsets, row_token, slot_row, ws, s));
   MOE_TRY(do_up(cfg, x, row_token, offsets, w_gate, w_up, h, s));
-  MOE_TRY(do_down(cfg, h, offsets, w_down, y, s));
+  MOE_TRY(do_down(cfg, h, offsets, w_down, y, region<float>(ws, L, R_SPLIT), s));
   return do_combine(cfg, y, slot_row, w, out, s);
 }
 

@@ -133,7 +133,9 @@ def test_stage_argument_errors(lib):
     assert lib.moe_route(cp, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 16, None) == L.MOE_ERR_WORKSPACE
     assert lib.moe_permute(cp, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_expert_up(cp, FAKE, FAKE, None, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG
-    assert lib.moe_expert_down(cp, FAKE, None, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_down(cp, FAKE, None, FAKE, FAKE, None, 0, None) == L.MOE_ERR_INVALID_ARG
+    # a workspace is optional for GEMM 2, but one that is given must be large enough
+    assert lib.moe_expert_down(cp, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None) == L.MOE_ERR_WORKSPACE
     assert lib.moe_grouped_ffn(cp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == L.MOE_ERR_WORKSPACE
     assert lib.moe_combine(cp, FAKE, FAKE, None, FAKE, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_combine(ctypes.byref(cfg_of(top_k=0)), FAKE, FAKE, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG

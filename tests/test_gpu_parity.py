@@ -6,7 +6,7 @@ import torch
 import oracle as O
 from mixture_experts_layer_37_amd import _lib as L
 from mixture_experts_layer_37_amd import configs as C
-from mixture_experts_layer_37_amd.inputs import as_float, f32_to_bf16_bits, make_inputs
+from mixture_experts_layer_37_amd.inputs import ExpertView, as_float, f32_to_bf16_bits, make_inputs
 from mixture_experts_layer_37_amd.layer import MoELayer, from_device, to_device
 
 import parity as P
@@ -195,7 +195,7 @@ def test_stage_entry_points_compose_to_forward():
     h = torch.empty((T * k, I), dtype=torch.bfloat16, device=dev)
     y = torch.empty((T * k, H), dtype=torch.bfloat16, device=dev)
     L.moe_expert_up(c, xp, offs, layer.w_gate, layer.w_up, h)
-    L.moe_expert_down(c, h, offs, layer.w_down, y)
+    L.moe_expert_down(c, h, offs, layer.w_down, y, ws)
     y2 = torch.empty_like(y)
     L.moe_grouped_ffn(c, xp, offs, layer.w_gate, layer.w_up, layer.w_down, y2, ws)
     out = torch.empty_like(x)
@@ -261,3 +261,60 @@ def test_expert_up_rows_equals_gather_then_expert_up(name):
     torch.cuda.synchronize()
     bits = torch.int16 if edt == torch.bfloat16 else torch.int32
     assert torch.equal(h1[:n].view(bits), h2[:n].view(bits))
+
+
+# GEMM 2's split-K tail: shapes whose tile list leaves a partial round of the grid and whose
+# K is long enough to be sliced: two slices over an odd number of k-step pairs, four slices,
+# and whole rounds followed by a sliced tail.
+SPLIT_CASES = {
+    "split2_uneven": C.SMALL.with_(name="split2_uneven", tokens=1500, hidden=512, inter=2176,
+                                   bias=None),
+    "split4": C.SMALL.with_(name="split4", tokens=1500, hidden=512, inter=4096, bias=None),
+    "rounds_plus_tail": C.SMALL.with_(name="rounds_plus_tail", tokens=4000, hidden=2048,
+                                      inter=2048, bias=None),
+}
+
+
+def _expected_split(offsets, hidden, inter):
+    """(whole tiles, sliced tiles, slices) that the launch should use, for the coverage check."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    grid = max(8, cus // 8 * 8)
+    m = np.diff(offsets)
+    total = int(((m + 255) // 256).sum()) * (hidden // 256)
+    full, tail, kt, s = total // grid * grid, total % grid, inter // 64, 1
+    while tail > 0 and s < 8 and tail * s * 2 <= min(grid, 256) and kt >= 32 * s:
+        s *= 2
+    return (full, tail, s) if s > 1 else (total, 0, 1)
+
+
+@pytest.mark.parametrize("name", list(SPLIT_CASES))
+def test_down_split_tail(name):
+    """GEMM 2 with the workspace (split-K tail) and without (every tile whole), each against
+    the float64 product of the GPU's own h and W_down on every row; the two launches differ
+    only in float32 summation order, so they agree to within one bf16 ulp."""
+    cfg = SPLIT_CASES[name]
+    print(f"[case] {name} {cfg}", flush=True)
+    inp = make_inputs(cfg, seed=6)
+    layer = MoELayer(cfg, inp)
+    x = to_device(cfg, inp["x"])
+    layer.forward(x)
+    h, offs = layer.view(L.MOE_WS_H), layer.view(L.MOE_WS_OFFSETS)
+    y = layer.view(L.MOE_WS_Y_PERM).clone()
+    y2 = torch.empty_like(y)
+    L.moe_expert_down(layer.c, h, offs, layer.w_down, y2)
+    torch.cuda.synchronize()
+    o = offs.cpu().numpy().astype(np.int64)
+    full, tail, s = _expected_split(o, cfg.hidden, cfg.inter)
+    print(f"[split] {name}: whole tiles {full}, sliced tiles {tail} x {s}", flush=True)
+    assert s > 1, "the case no longer exercises the split"
+    n = int(o[-1])
+    hf, yf, y2f = P.decode(cfg, h[:n]), P.decode(cfg, y[:n]), P.decode(cfg, y2[:n])
+    wd = ExpertView(cfg, inp["w_down"])
+    ref = np.empty_like(yf)
+    for e in range(cfg.experts):
+        ref[o[e]:o[e + 1]] = hf[o[e]:o[e + 1]] @ wd[e].astype(np.float64)
+    _report(name, {"split": P.assert_layer_close(yf, ref, "split"),
+                   "whole": P.assert_layer_close(y2f, ref, "whole")})
+    mag = np.maximum(np.abs(yf), np.abs(y2f))
+    ulp = np.exp2(np.floor(np.log2(np.maximum(mag, 1e-30))) - 7)
+    assert (np.abs(yf - y2f) <= ulp + 1e-5 * np.abs(ref).max()).all()
