@@ -21,6 +21,10 @@ What is computed, and where the pages state it
 * Capacity: a capacity factor bounds each expert's load (hnwysp.cn/news/132341, section 3.2
   and section 4.2); imbalance overflows per-expert buffers (lshu.cn page, section 5.3).
 * Expert ids are int32 in [0, E) (lshu.cn page, section 5.2).
+* Threshold routing: compute every expert's gate score, keep only the experts whose score
+  exceeds a threshold delta (1/E by default), renormalise over the kept ones
+  (intelliparadigm.com page, section 3.2.1, the sparse gate; gitcode page, "路由算法": a
+  threshold router activates only the experts scoring above the threshold).
 
 Readings where the pages are silent or conflict (each is listed with its reason in the
 project's design notes):
@@ -31,8 +35,15 @@ project's design notes):
   R4 each expert keeps its assignments in ascending token order up to C; a dropped slot
      contributes zero, is not re-routed and the other weights are not renormalised.
   R5 SwiGLU is silu(x Wg) * (x Wu) then Wd; GELU is the exact erf form; no expert biases.
-  R6 a user-supplied expert id outside [0, E), or one repeated within a token's slots
-     (the later slot), is invalid: the slot is dropped and flagged.
+  R6 a user-supplied expert id outside [0, E) other than -1, or one repeated within a
+     token's slots (the later slot), is invalid: the slot is dropped and flagged. -1 marks
+     an empty slot (threshold routing): dropped, not flagged.
+  R14 threshold routing: the score is the softmax probability p (float64); an expert is
+     kept when p > delta strictly; delta <= 0 or absent means 1/E. The kept experts are
+     listed best first (the order of R1) in at most k slots (k caps the experts per token;
+     with k = E nothing is capped); the remaining slots hold -1 and weight 0. A token with
+     no expert above delta (all scores equal to 1/E, or a NaN or +inf logit) contributes
+     zero. Renormalisation (R2) is over the kept experts.
 
 Every function here is pinned by tests/test_oracle_*.py against hand-worked cases, closed
 forms, brute force and invariants that do not reuse this code.
@@ -106,6 +117,52 @@ def topk_weights(logits, idx, renormalize: bool = True) -> np.ndarray:
     return sel
 
 
+# ------------------------------------------------- steps 2-3, threshold routing (R14)
+def threshold_delta(experts: int, delta=None) -> float:
+    """The threshold: delta if given and > 0, else 1/E (intelliparadigm.com page, 3.2.1)."""
+    return 1.0 / experts if delta is None or delta <= 0 else float(delta)
+
+
+def threshold_select(logits, k: int, delta=None):
+    """Experts whose gate score p = softmax(L) exceeds delta, best first, at most k per
+    token; empty slots are -1 (reading R14). Returns (idx int32 [T, k], flags)."""
+    L = np.asarray(logits, dtype=np.float64)
+    T, E = L.shape
+    if not 1 <= k <= E:
+        raise ValueError("need 1 <= k <= E")
+    d = threshold_delta(E, delta)
+    order, flags = select_experts(L, E)                        # every expert, best first
+    p = np.take_along_axis(softmax(L), order.astype(np.int64), axis=1)
+    with np.errstate(invalid="ignore"):
+        keep = p > d                                           # NaN scores are never kept
+    idx = np.full((T, k), -1, dtype=np.int32)
+    for t in range(T):
+        kept = order[t][keep[t]][:k]
+        idx[t, :len(kept)] = kept
+    return idx, flags
+
+
+def threshold_weights(logits, idx, renormalize: bool = True) -> np.ndarray:
+    """Gate weights of the kept experts (0 in empty slots), float64 [T, k]; renormalised
+    over the kept experts when asked (intelliparadigm.com page, 3.2.1)."""
+    idx = np.asarray(idx, dtype=np.int64)
+    p = softmax(logits)
+    sel = np.where(idx >= 0, np.take_along_axis(p, np.maximum(idx, 0), axis=1), 0.0)
+    if renormalize:
+        s = sel.sum(axis=1, keepdims=True)
+        sel = np.divide(sel, s, out=np.zeros_like(sel), where=s > 0)
+    return sel
+
+
+def threshold_margin(logits, delta=None) -> np.ndarray:
+    """min over experts of |p - delta| / delta per token (how near a decision is)."""
+    L = np.asarray(logits, dtype=np.float64)
+    d = threshold_delta(L.shape[1], delta)
+    with np.errstate(invalid="ignore"):
+        m = np.abs(softmax(L) - d).min(axis=1) / d
+    return np.where(np.isnan(m), np.inf, m)
+
+
 # ------------------------------------------------------------ step 4: capacity rule
 def capacity(capacity_factor: float, tokens: int, top_k: int, experts: int) -> int:
     """C = ceil(cf * (T*k) / E) in IEEE double; no limit (C = T) when cf <= 0 (R3)."""
@@ -124,6 +181,12 @@ def valid_slots(idx, experts: int) -> np.ndarray:
     return ok
 
 
+def flagged_slots(idx, experts: int) -> np.ndarray:
+    """Invalid slots that raise the bad-index flag: every invalid slot except the empty
+    marker -1 (R6)."""
+    return ~valid_slots(idx, experts) & (np.asarray(idx) != -1)
+
+
 # ------------------------------------------------------------ steps 4-5: permutation
 def permute_indices(idx, experts: int, cap: int) -> dict:
     """Group assignments by expert, in token order, under the capacity rule (R4, R6).
@@ -137,7 +200,7 @@ def permute_indices(idx, experts: int, cap: int) -> dict:
     idx = np.asarray(idx, dtype=np.int64)
     T, k = idx.shape
     ok = valid_slots(idx, experts)
-    flags = FLAG_BAD_INDEX if not ok.all() else 0
+    flags = FLAG_BAD_INDEX if flagged_slots(idx, experts).any() else 0
     flat = np.where(ok, idx, experts).reshape(-1)            # invalid slots sort last
     order = np.argsort(flat, kind="stable")                  # expert-major, then (t, j)
     counts = np.bincount(flat[flat < experts], minlength=experts).astype(np.int64)
@@ -236,15 +299,25 @@ def combine(y, slot_row, weights, hidden: int, tokens=None) -> np.ndarray:
 # ---------------------------------------------------------------- whole layer
 def forward(x, w_router, bias, w_gate, w_up, w_down, *, top_k: int, activation: str,
             capacity_factor: float = 0.0, renormalize: bool = True, tokens=None,
-            logits=None) -> dict:
+            logits=None, routing: str = "topk", threshold=None) -> dict:
     """The whole layer. ``tokens`` restricts the expert FFN and combine to those tokens
-    (routing and the capacity rule always see every token). ``logits`` replaces step 1."""
+    (routing and the capacity rule always see every token). ``logits`` replaces step 1.
+    ``routing`` is "topk" or "threshold" (then ``top_k`` caps the experts per token and
+    ``threshold`` is delta, default 1/E)."""
     x = np.asarray(x)
     T, H = x.shape
     L = gate_logits(x, w_router, bias) if logits is None else np.asarray(logits, np.float64)
     E = L.shape[1]
-    idx, f1 = select_experts(L, top_k)
-    w = topk_weights(L, idx, renormalize)
+    if routing == "threshold":
+        idx, f1 = threshold_select(L, top_k, threshold)
+        w = threshold_weights(L, idx, renormalize)
+        margin = threshold_margin(L, threshold)
+    elif routing == "topk":
+        idx, f1 = select_experts(L, top_k)
+        w = topk_weights(L, idx, renormalize)
+        margin = selection_margin(L, top_k)
+    else:
+        raise ValueError(routing)
     cap = capacity(capacity_factor, T, top_k, E)
     perm = permute_indices(idx, E, cap)
     ts = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
@@ -257,5 +330,5 @@ def forward(x, w_router, bias, w_gate, w_up, w_down, *, top_k: int, activation: 
         y = np.zeros((int(perm["offsets"][-1]), H))
     out = combine(y, perm["slot_row"], w, H, tokens=ts)
     return dict(logits=L, topk_idx=idx, topk_w=w, capacity=cap, y=y, out=out, tokens=ts,
-                flags=f1 | perm["flags"], margin=selection_margin(L, top_k), **{
+                flags=f1 | perm["flags"], margin=margin, **{
                     k_: v for k_, v in perm.items() if k_ != "flags"})

@@ -303,3 +303,140 @@ def test_all_slots_dropped_gives_zero():
     assert r["capacity"] == 3
     np.testing.assert_array_equal(r["kept"], [3, 3])
     assert (r["out"][3:] == 0).all() and (r["out"][:3] != 0).all()
+
+
+# ------------------------------------------------------------------ threshold routing (R14)
+def test_hand_threshold_case():
+    g = GOLD["threshold"]
+    L = np.array(g["logits"])
+    idx, flags = O.threshold_select(L, 4)
+    assert flags == 0
+    np.testing.assert_array_equal(idx, g["default_delta_k4_idx"])
+    np.testing.assert_allclose(O.threshold_weights(L, idx), g["default_delta_k4_weights"],
+                               rtol=1e-15, atol=0)
+    idx1, _ = O.threshold_select(L, 1)
+    np.testing.assert_array_equal(idx1, g["default_delta_k1_idx"])
+    np.testing.assert_array_equal(O.threshold_weights(L, idx1), [[1.0], [1.0], [0.0], [1.0]])
+    idx2, _ = O.threshold_select(L, 4, delta=0.1)
+    np.testing.assert_array_equal(idx2, g["delta_0.1_k4_idx"])
+    w2 = O.threshold_weights(L, idx2)
+    e = math.e
+    want = [[e / (2 * e + 1), e / (2 * e + 1), 1 / (2 * e + 1), 0.0],
+            [logistic(1.0), logistic(-1.0), 0.0, 0.0], [0.25] * 4, [0.5, 0.5, 0.0, 0.0]]
+    np.testing.assert_allclose(w2, want, rtol=1e-15, atol=0)
+    # raw probabilities when not renormalised: row 1 keeps p0 = e^2 / (e^2 + e + 1 + 1/e)
+    raw = O.threshold_weights(L, idx, renormalize=False)
+    assert raw[1, 0] == pytest.approx(e * e / (e * e + e + 1 + 1 / e), rel=1e-15)
+
+
+@pytest.mark.parametrize("u", [0.3, -0.3])
+def test_threshold_two_level_closed_form(u):
+    # a experts at logit u, the rest at 0: p_u > 1/E exactly when u > 0, p_0 > 1/E exactly
+    # when u < 0, so the kept set is one of the two groups, with equal weights
+    E = 9
+    for a in range(1, E):
+        L = np.zeros((1, E))
+        hot = np.random.default_rng(a).choice(E, a, replace=False)
+        L[0, hot] = u
+        idx, _ = O.threshold_select(L, E)
+        want = np.sort(hot) if u > 0 else np.setdiff1d(np.arange(E), hot)
+        np.testing.assert_array_equal(idx[0, :len(want)], want)
+        assert (idx[0, len(want):] == -1).all()
+        np.testing.assert_allclose(O.threshold_weights(L, idx)[0, :len(want)], 1 / len(want),
+                                   rtol=1e-15)
+
+
+def _brute_threshold(row, k, delta):
+    """log-sum-exp form: keep e when l_e - lse > log(delta); order (-l, e); first k."""
+    m = max(row)
+    lse = m + math.log(math.fsum(math.exp(v - m) for v in row))
+    gap = [v - lse - math.log(delta) for v in row]
+    kept = sorted((e for e in range(len(row)) if gap[e] > 0), key=lambda e: (-row[e], e))
+    return kept[:k], min(abs(x) for x in gap)
+
+
+@pytest.mark.parametrize("E,k,delta", [(3, 3, None), (8, 8, None), (8, 2, None), (33, 5, 0.05),
+                                       (16, 16, 0.01)])
+def test_threshold_matches_brute_force(E, k, delta):
+    rng = np.random.default_rng(E * 100 + k)
+    L = rng.standard_normal((300, E)) * rng.uniform(0.2, 3.0, (300, 1))
+    L[::7, 1] = L[::7, 0]                     # ties
+    idx, _ = O.threshold_select(L, k, delta)
+    d = O.threshold_delta(E, delta)
+    checked = 0
+    for t in range(L.shape[0]):
+        want, gap = _brute_threshold(list(L[t]), k, d)
+        if gap < 1e-9:
+            continue
+        checked += 1
+        got = [int(e) for e in idx[t] if e >= 0]
+        assert got == want, t
+    assert checked > 250
+
+
+def test_threshold_tiny_delta_keeps_every_expert_as_topk():
+    rng = np.random.default_rng(12)
+    L = rng.standard_normal((50, 7))
+    idx, _ = O.threshold_select(L, 7, delta=1e-300)
+    ref, _ = O.select_experts(L, 7)
+    np.testing.assert_array_equal(idx, ref)
+    np.testing.assert_allclose(O.threshold_weights(L, idx), O.topk_weights(L, ref),
+                               rtol=1e-15, atol=0)
+
+
+def test_threshold_default_delta_keeps_between_one_and_E_minus_one():
+    rng = np.random.default_rng(13)
+    for E in (2, 5, 8, 64):
+        L = rng.standard_normal((400, E)) * 2.0
+        idx, _ = O.threshold_select(L, E)
+        n = (idx >= 0).sum(1)
+        assert n.min() >= 1 and n.max() <= E - 1
+        np.testing.assert_allclose(O.threshold_weights(L, idx).sum(1), 1.0, atol=1e-15)
+
+
+def test_threshold_nonfinite_rows():
+    L = np.array([[0.0, np.nan, 1.0], [np.inf, 0.0, 1.0], [-np.inf, 0.0, 2.0]])
+    idx, flags = O.threshold_select(L, 3)
+    assert flags & O.FLAG_NONFINITE_LOGIT
+    assert (idx[:2] == -1).all()                # NaN / +inf rows keep nothing
+    np.testing.assert_array_equal(idx[2], [2, -1, -1])   # -inf only scores zero
+    assert (O.threshold_weights(L, idx)[:2] == 0).all()
+
+
+@pytest.mark.parametrize("act", ["swiglu", "gelu"])
+def test_threshold_forward_extremes(act):
+    rng = np.random.default_rng(14)
+    T, H, I, E = 11, 4, 6, 5
+    x = rng.standard_normal((T, H))
+    wr = rng.standard_normal((H, E))
+    wg = rng.standard_normal((E, H, I)) if act == "swiglu" else None
+    wu = rng.standard_normal((E, H, I))
+    wd = rng.standard_normal((E, I, H))
+    # delta above every score: no expert anywhere, the layer outputs zeros
+    r0 = O.forward(x, wr, None, wg, wu, wd, top_k=E, activation=act, routing="threshold",
+                   threshold=1.5)
+    assert (r0["topk_idx"] == -1).all() and (r0["out"] == 0).all()
+    assert r0["flags"] == 0 and r0["offsets"][-1] == 0
+    # a vanishing delta with k = E keeps every expert: the dense mixture, as top-E routing
+    r1 = O.forward(x, wr, None, wg, wu, wd, top_k=E, activation=act, routing="threshold",
+                   threshold=1e-300)
+    want = np.zeros((T, H))
+    for t in range(T):
+        logit = [sum(x[t, h] * wr[h, e] for h in range(H)) for e in range(E)]
+        mx = max(logit)
+        z = [math.exp(v - mx) for v in logit]
+        for e in range(E):
+            want[t] += (z[e] / sum(z)) * _dense_ffn(x[t:t + 1], None if wg is None else wg[e],
+                                                    wu[e], wd[e], act)[0]
+    np.testing.assert_allclose(r1["out"], want, rtol=1e-10, atol=1e-10)
+
+
+def test_empty_slots_are_dropped_without_a_flag():
+    idx = np.array([[0, -1], [1, 0], [-1, -1]])
+    p = O.permute_indices(idx, 2, 10)
+    assert p["flags"] == 0
+    np.testing.assert_array_equal(p["counts"], [2, 1])
+    assert p["slot_row"][0, 1] == -1 and (p["slot_row"][2] == -1).all()
+    counts, offsets, slot_row, row_token = sequential_permute(idx, 2, 10)
+    np.testing.assert_array_equal(p["slot_row"], slot_row)
+    np.testing.assert_array_equal(p["row_token"], row_token)
