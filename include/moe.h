@@ -8,6 +8,7 @@
  *   logits = x @ W_router (+ gate_bias)             gate GEMM
  *   p      = softmax(logits)                          per token, over E experts
  *   idx, w = top-k of p, renormalised over the k      lower expert index wins ties
+ *            (or, threshold routing: the experts with p > delta, at most k of them)
  *   rows   = tokens grouped by expert, token order    capacity clamp, then gather
  *   h      = silu(x_e Wg[e]) * (x_e Wu[e])            grouped GEMM 1 (GELU: gelu(x_e Wu[e]))
  *   y      = h Wd[e]                                  grouped GEMM 2
@@ -63,6 +64,8 @@ enum { MOE_ACT_SWIGLU = 0, MOE_ACT_GELU = 1 };
 /* device status flags (moe_read_device_status) */
 enum { MOE_FLAG_BAD_INDEX = 1, MOE_FLAG_NONFINITE_LOGIT = 2 };
 enum { MOE_MAX_EXPERTS = 256, MOE_MAX_TOPK = 16 };
+/* routing rules (moe_config.routing) */
+enum { MOE_ROUTE_TOPK = 0, MOE_ROUTE_THRESHOLD = 1 };
 
 typedef struct moe_config {
   int32_t tokens;            /* T >= 0 */
@@ -79,6 +82,16 @@ typedef struct moe_config {
   double capacity_factor;    /* <= 0: no limit. Otherwise each expert keeps at most
                                 C = ceil(capacity_factor * (T*k) / E) assignments, lowest
                                 token index first (hnwysp.cn/news/132341, section 3.2) */
+  int32_t routing;           /* MOE_ROUTE_TOPK (0, the default): the k best experts.
+                                MOE_ROUTE_THRESHOLD: every expert whose softmax score p
+                                exceeds `threshold` (strictly, decided in float64), best
+                                first, at most top_k of them; unused slots get id -1 and
+                                weight 0, and a token with none above the threshold
+                                contributes zero (intelliparadigm.com page, section 3.2.1:
+                                keep the experts scoring above delta, default 1/E, then
+                                renormalise) */
+  int32_t reserved;          /* set to 0 */
+  double threshold;          /* delta of MOE_ROUTE_THRESHOLD; <= 0 means 1/E; not NaN */
 } moe_config;
 
 typedef void* moe_stream_t;  /* hipStream_t */
@@ -97,8 +110,10 @@ moe_status moe_capacity(const moe_config* cfg, int32_t* capacity);
  *   gate_bias [E] float32 or NULL, added to the logits before softmax and selection
  *   logits    [T,E] float32: output (input when x == NULL)
  *   topk_idx  [T,k] int32 out: experts in descending logit order, lower index first on ties
+ *             (threshold routing: the kept experts in that order, then -1)
  *   topk_w    [T,k] float32 out: softmax weights of those experts (renormalised if set);
- *             NaN for a token with a NaN logit
+ *             NaN for a token with a NaN logit (threshold routing: 0 in unused slots; a
+ *             token with a NaN or +inf logit keeps no expert)
  * Non-finite logits raise MOE_FLAG_NONFINITE_LOGIT; NaN ranks below -inf. */
 moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
                      const float* gate_bias, float* logits, int32_t* topk_idx, float* topk_w,
@@ -108,7 +123,8 @@ moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
  * SparseGather and the CSR storage of "MoE 算子核心原理"; lshu.cn page, section 4,
  * npu_moe_token_preprocess).
  *   x              [T,H] dtype
- *   topk_idx       [T,k] int32 expert ids (invalid or repeated ids are dropped + flagged)
+ *   topk_idx       [T,k] int32 expert ids; -1 is an empty slot (dropped, no flag); any
+ *                  other id outside [0,E), or a repeat within a token, is dropped + flagged
  *   x_perm         [T*k,H] dtype out: rows grouped by expert, token order inside an expert;
  *                  rows >= expert_offsets[E] are left untouched. May be NULL: then only the
  *                  row maps below are written (x is not read), for moe_expert_up_rows

@@ -21,6 +21,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_DTYPE_BF16, MOE_DTYPE_F32 = 0, 1
 MOE_ACT_SWIGLU, MOE_ACT_GELU = 0, 1
 MOE_FLAG_BAD_INDEX, MOE_FLAG_NONFINITE_LOGIT = 1, 2
+MOE_ROUTE_TOPK, MOE_ROUTE_THRESHOLD = 0, 1
 (MOE_WS_LOGITS, MOE_WS_TOPK_IDX, MOE_WS_TOPK_W, MOE_WS_COUNTS, MOE_WS_OFFSETS, MOE_WS_SLOT_ROW,
  MOE_WS_ROW_TOKEN, MOE_WS_X_PERM, MOE_WS_H, MOE_WS_Y_PERM) = range(10)
 
@@ -34,7 +35,8 @@ EXPORTS = ("moe_workspace_size", "moe_capacity", "moe_route", "moe_permute", "mo
 class CConfig(ctypes.Structure):
     _fields_ = [("tokens", c_int32), ("hidden", c_int32), ("inter", c_int32),
                 ("experts", c_int32), ("top_k", c_int32), ("activation", c_int32),
-                ("dtype", c_int32), ("renormalize", c_int32), ("capacity_factor", c_double)]
+                ("dtype", c_int32), ("renormalize", c_int32), ("capacity_factor", c_double),
+                ("routing", c_int32), ("reserved", c_int32), ("threshold", c_double)]
 
 
 class MoEError(RuntimeError):
@@ -91,7 +93,9 @@ def cconfig(cfg: MoEConfig, tokens: int | None = None) -> CConfig:
                    activation=MOE_ACT_GELU if cfg.activation == GELU else MOE_ACT_SWIGLU,
                    dtype=MOE_DTYPE_BF16 if cfg.dtype == BF16 else MOE_DTYPE_F32,
                    renormalize=1 if cfg.renormalize else 0,
-                   capacity_factor=float(cfg.capacity_factor))
+                   capacity_factor=float(cfg.capacity_factor),
+                   routing=MOE_ROUTE_THRESHOLD if cfg.routing == "threshold" else MOE_ROUTE_TOPK,
+                   threshold=float(cfg.threshold))
 
 
 def _as_cfg(cfg):

@@ -36,6 +36,10 @@ class MoEConfig:
     # gate-bias recipe: None, ("normal", variance) or ("zipf", s)
     bias: Optional[tuple] = None
     router_std: Optional[float] = None  # default 1/sqrt(hidden)
+    # "topk", or "threshold": experts with softmax score > threshold (<= 0: 1/E), at most
+    # top_k of them
+    routing: str = "topk"
+    threshold: float = 0.0
     description: str = field(default="", compare=False)
 
     def with_(self, **kw) -> "MoEConfig":
@@ -66,7 +70,14 @@ FINE = MoEConfig(
     description="32768 tokens (8 x 4096), H 2048, I 1408, 128 experts, top-8, SwiGLU, "
                 "gate bias N(0,1)")
 
-CONFIGS = {c.name: c for c in (TINY, SMALL, MIXTRAL, CAP32, FINE)}
+# Threshold routing on the Mixtral shape: every expert whose softmax score exceeds 1/E,
+# uncapped (top_k = E slots), renormalised (intelliparadigm.com page, section 3.2.1).
+MIXTRAL_THRESHOLD = MIXTRAL.with_(
+    name="mixtral_threshold", top_k=8, routing="threshold",
+    description="8192 tokens (8 x 1024), H 4096, I 14336, 8 experts, threshold routing "
+                "(score > 1/E, uncapped), SwiGLU")
+
+CONFIGS = {c.name: c for c in (TINY, SMALL, MIXTRAL, CAP32, FINE, MIXTRAL_THRESHOLD)}
 
 
 def get(name: str) -> MoEConfig:

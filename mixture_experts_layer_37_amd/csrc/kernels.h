@@ -9,22 +9,25 @@
 
 namespace moe {
 
-// ---- route (route.hip)
+// ---- route (route.hip). renorm: renormalised weights; thr: threshold routing with `delta`
 int route_padded_experts(int E);
 hipError_t launch_router_transpose(const bf16_t* w_router, bf16_t* wt, int H, int E,
                                    hipStream_t s);
 hipError_t launch_route_bf16(const bf16_t* x, const bf16_t* wt, const float* bias,
                              float* logits, int32_t* topk_idx, float* topk_w, int32_t* flags,
-                             int T, int H, int E, int k, int renorm, hipStream_t s);
+                             int T, int H, int E, int k, int renorm, int thr, double delta,
+                             hipStream_t s);
 bool route_lds_fits(int H, int E);
 hipError_t launch_route_bf16_lds(const bf16_t* x, const bf16_t* w_router, const float* bias,
                                  float* logits, int32_t* topk_idx, float* topk_w, int32_t* flags,
-                                 int T, int H, int E, int k, int renorm, int cus, hipStream_t s);
+                                 int T, int H, int E, int k, int renorm, int thr, double delta,
+                                 int cus, hipStream_t s);
 int device_cus();
 hipError_t launch_route_logits_f32(const float* x, const float* w_router, const float* bias,
                                    float* logits, int T, int H, int E, hipStream_t s);
 hipError_t launch_route_topk(const float* logits, int32_t* topk_idx, float* topk_w,
-                             int32_t* flags, int T, int E, int k, int renorm, hipStream_t s);
+                             int32_t* flags, int T, int E, int k, int renorm, int thr,
+                             double delta, hipStream_t s);
 
 // ---- permute (permute.hip)
 int permute_count_blocks(int T);

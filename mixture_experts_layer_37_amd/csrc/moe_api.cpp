@@ -4,12 +4,18 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <cstddef>
 #include <cmath>
 #include <cstring>
 #include <vector>
 
 #include "moe.h"
 #include "kernels.h"
+
+// The binding mirrors this layout (explicit reserved word, no implicit padding).
+static_assert(sizeof(moe_config) == 56 && offsetof(moe_config, routing) == 40 &&
+                  offsetof(moe_config, threshold) == 48,
+              "moe_config layout");
 
 namespace {
 
@@ -74,6 +80,9 @@ moe_status check_cfg(const moe_config* c) {
     return MOE_ERR_INVALID_ARG;
   if (c->top_k > c->experts) return MOE_ERR_INVALID_ARG;
   if (std::isnan(c->capacity_factor)) return MOE_ERR_INVALID_ARG;
+  if (c->routing != MOE_ROUTE_TOPK && c->routing != MOE_ROUTE_THRESHOLD)
+    return MOE_ERR_INVALID_ARG;
+  if (std::isnan(c->threshold)) return MOE_ERR_INVALID_ARG;
   if (c->dtype != MOE_DTYPE_BF16 && c->dtype != MOE_DTYPE_F32) return MOE_ERR_UNSUPPORTED;
   if (c->activation != MOE_ACT_SWIGLU && c->activation != MOE_ACT_GELU) return MOE_ERR_UNSUPPORTED;
   if (c->experts > MOE_MAX_EXPERTS || c->top_k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
@@ -126,22 +135,27 @@ moe_status do_route(const moe_config* c, const void* x, const void* w_router, co
   int32_t* flags = region<int32_t>(ws, L, R_ROUTE_FLAGS);
   const int T = c->tokens, H = c->hidden, E = c->experts, k = c->top_k;
   const int renorm = c->renormalize != 0;
+  // threshold routing: delta (<= 0 means 1/E), compared in float64
+  const int thr = c->routing == MOE_ROUTE_THRESHOLD;
+  const double delta = c->threshold > 0 ? c->threshold : 1.0 / (double)E;
   if (x == nullptr)
-    return hip_status(moe::launch_route_topk(logits, idx, w, flags, T, E, k, renorm, s));
+    return hip_status(
+        moe::launch_route_topk(logits, idx, w, flags, T, E, k, renorm, thr, delta, s));
   if (c->dtype == MOE_DTYPE_BF16 && moe::route_lds_fits(H, E))
     return hip_status(moe::launch_route_bf16_lds((const moe::bf16_t*)x,
                                                  (const moe::bf16_t*)w_router, bias, logits,
-                                                 idx, w, flags, T, H, E, k, renorm,
-                                                 moe::device_cus(), s));
+                                                 idx, w, flags, T, H, E, k, renorm, thr,
+                                                 delta, moe::device_cus(), s));
   if (c->dtype == MOE_DTYPE_BF16) {
     moe::bf16_t* wt = region<moe::bf16_t>(ws, L, R_WT);
     MOE_TRY(hip_status(moe::launch_router_transpose((const moe::bf16_t*)w_router, wt, H, E, s)));
     return hip_status(moe::launch_route_bf16((const moe::bf16_t*)x, wt, bias, logits, idx, w,
-                                             flags, T, H, E, k, renorm, s));
+                                             flags, T, H, E, k, renorm, thr, delta, s));
   }
   MOE_TRY(hip_status(moe::launch_route_logits_f32((const float*)x, (const float*)w_router, bias,
                                                   logits, T, H, E, s)));
-  return hip_status(moe::launch_route_topk(logits, idx, w, flags, T, E, k, renorm, s));
+  return hip_status(
+      moe::launch_route_topk(logits, idx, w, flags, T, E, k, renorm, thr, delta, s));
 }
 
 moe_status do_permute(const moe_config* c, const void* x, const int32_t* idx, void* x_perm,

@@ -7,7 +7,8 @@
 // only computes the row maps, for a GEMM that gathers token rows itself):
 //   count  -- 1024 tokens per block. Per wave and expert a 64-bit lane mask (LDS OR);
 //             popcounts give the block's per-expert histogram and each assignment's rank
-//             inside the block in token order. Invalid or repeated ids are dropped, flagged.
+//             inside the block in token order. Invalid or repeated ids are dropped, flagged
+//             (-1, an empty slot of threshold routing, is dropped silently).
 //   scan   -- one block: per expert, exclusive prefix over the count blocks (in place),
 //             pre-capacity counts, kept = min(count, C), and the kept offsets (a scan over E).
 //   gather -- one wave per token: row = offsets[e] + block prefix + in-block rank, kept iff
@@ -51,7 +52,7 @@ __global__ __launch_bounds__(1024) void permute_count_kernel(const int32_t* __re
         if (ok) {
           valid |= 1u << j;
           atomicOr(&masks[wave * E + e], 1ull << lane);
-        } else {
+        } else if (e != -1) {   // -1 marks an empty slot: dropped without a flag
           bad = true;
         }
       }

@@ -33,9 +33,13 @@ __device__ __forceinline__ int order_key(float f) {
 }
 
 // Top-k of one token's E logits (any address space) and its gate weights. Weights are
-// evaluated in float64 and rounded once to float32. Returns true if a logit is not finite.
+// evaluated in float64 and rounded once to float32. With `thr`, threshold routing
+// (intelliparadigm.com page, section 3.2.1): only the experts whose softmax score exceeds
+// `delta` are kept, best first, at most k; the other slots get id -1 and weight 0.
+// Returns true if a logit is not finite.
 template <int KMAX>
-__device__ bool topk_token(const float* L, int E, int k, int renorm, int32_t* idx_out,
+__device__ bool topk_token(const float* L, int E, int k, int renorm, int thr, double delta,
+                           int32_t* idx_out,
                            float* w_out) {
   int key[KMAX];
   int id[KMAX];
@@ -63,7 +67,27 @@ __device__ bool topk_token(const float* L, int E, int k, int renorm, int32_t* id
   const double top = (double)L[id[0]];
   double ev[KMAX];
   double s = 0.0;
-  if (renorm) {
+  int cnt = k;   // slots that hold an expert
+  if (thr) {
+    // threshold routing: p_j = exp(L_j - top) / sum over every expert, kept while
+    // p_j > delta (p falls along the sorted list, so the kept experts are a prefix)
+    double all = 0.0;
+    for (int e = 0; e < E; ++e) all += exp((double)L[e] - top);
+    cnt = 0;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (j < k) {
+        ev[j] = exp((double)L[id[j]] - top);
+        if (cnt == j && ev[j] / all > delta) cnt = j + 1;
+      }
+    if (renorm) {
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j)
+        if (j < cnt) s += ev[j];
+    } else {
+      s = all;
+    }
+  } else if (renorm) {
 #pragma unroll
     for (int j = 0; j < KMAX; ++j)
       if (j < k) { ev[j] = exp((double)L[id[j]] - top); s += ev[j]; }
@@ -75,9 +99,12 @@ __device__ bool topk_token(const float* L, int E, int k, int renorm, int32_t* id
   }
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
-    if (j < k) {
+    if (j < cnt) {
       idx_out[j] = id[j];
       w_out[j] = has_nan ? __builtin_nanf("") : (float)(ev[j] / s);
+    } else if (j < k) {
+      idx_out[j] = -1;
+      w_out[j] = 0.f;
     }
   }
   return nonfinite;
@@ -122,7 +149,7 @@ template <int TG, int NBE, int KMAX>
 __global__ __launch_bounds__(256) void route_mfma_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ wt, const float* __restrict__ bias,
     float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    int32_t* __restrict__ flags, int T, int H, int E, int k, int renorm) {
+    int32_t* __restrict__ flags, int T, int H, int E, int k, int renorm, int thr, double delta) {
   constexpr int BT = TG * 16, EP = NBE * 16, LDR = EP + 1;
   constexpr int U = (TG + NBE) >= 12 ? 1 : (12 / (TG + NBE) < 8 ? 12 / (TG + NBE) : 8);
   __shared__ float red[2][BT * LDR];
@@ -236,7 +263,8 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(
     bool nf = false;
     const int t = t0 + threadIdx.x;
     if (threadIdx.x < BT && t < T)
-      nf = topk_token<KMAX>(Ls + threadIdx.x * LDR, E, k, renorm, topk_idx + (size_t)t * k,
+      nf = topk_token<KMAX>(Ls + threadIdx.x * LDR, E, k, renorm, thr, delta,
+                            topk_idx + (size_t)t * k,
                             topk_w + (size_t)t * k);
     const unsigned long long m = __ballot(nf);
     const int ngroups = (T + kRouteFlagGroup - 1) / kRouteFlagGroup;
@@ -249,11 +277,12 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(
 template <int TG, int NBE>
 static hipError_t launch_route_tg(const bf16_t* x, const bf16_t* wt, const float* bias,
                                   float* logits, int32_t* idx, float* w, int32_t* flags, int T,
-                                  int H, int E, int k, int renorm, hipStream_t s) {
+                                  int H, int E, int k, int renorm, int thr, double delta,
+                                  hipStream_t s) {
   const dim3 grid((T + TG * 16 - 1) / (TG * 16)), block(256);
 #define MOE_ROUTE_LAUNCH(KM)                                                                  \
   hipLaunchKernelGGL((route_mfma_kernel<TG, NBE, KM>), grid, block, 0, s, x, wt, bias, logits, \
-                     idx, w, flags, T, H, E, k, renorm)
+                     idx, w, flags, T, H, E, k, renorm, thr, delta)
   if (k <= 1) MOE_ROUTE_LAUNCH(1);
   else if (k <= 2) MOE_ROUTE_LAUNCH(2);
   else if (k <= 4) MOE_ROUTE_LAUNCH(4);
@@ -265,14 +294,17 @@ static hipError_t launch_route_tg(const bf16_t* x, const bf16_t* wt, const float
 
 hipError_t launch_route_bf16(const bf16_t* x, const bf16_t* wt, const float* bias, float* logits,
                              int32_t* idx, float* w, int32_t* flags, int T, int H, int E, int k,
-                             int renorm, hipStream_t s) {
+                             int renorm, int thr, double delta, hipStream_t s) {
+#define MOE_ROUTE_TG(A, B) \
+  launch_route_tg<A, B>(x, wt, bias, logits, idx, w, flags, T, H, E, k, renorm, thr, delta, s)
   switch (route_padded_experts(E)) {
-    case 16: return launch_route_tg<1, 1>(x, wt, bias, logits, idx, w, flags, T, H, E, k, renorm, s);
-    case 32: return launch_route_tg<1, 2>(x, wt, bias, logits, idx, w, flags, T, H, E, k, renorm, s);
-    case 64: return launch_route_tg<2, 4>(x, wt, bias, logits, idx, w, flags, T, H, E, k, renorm, s);
-    case 128: return launch_route_tg<4, 8>(x, wt, bias, logits, idx, w, flags, T, H, E, k, renorm, s);
-    default: return launch_route_tg<2, 16>(x, wt, bias, logits, idx, w, flags, T, H, E, k, renorm, s);
+    case 16: return MOE_ROUTE_TG(1, 1);
+    case 32: return MOE_ROUTE_TG(1, 2);
+    case 64: return MOE_ROUTE_TG(2, 4);
+    case 128: return MOE_ROUTE_TG(4, 8);
+    default: return MOE_ROUTE_TG(2, 16);
   }
+#undef MOE_ROUTE_TG
 }
 
 // ---------------------------------------------------------------------------------------
@@ -308,7 +340,7 @@ template <int KMAX>
 __global__ __launch_bounds__(512, 1) void route_stream_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, const float* __restrict__ bias,
     float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    int32_t* __restrict__ flags, int T, int H, int E, int k, int renorm) {
+    int32_t* __restrict__ flags, int T, int H, int E, int k, int renorm, int thr, double delta) {
   constexpr int BT = 32, LDR = 17;
   // Two buffer sets in two distinct LDS objects, so the compiler can tell a DMA into one
   // from reads of the other.
@@ -429,7 +461,7 @@ __global__ __launch_bounds__(512, 1) void route_stream_kernel(
     bool nf = false;
     const int t = t0 + tid;
     if (tid < BT && t < T)
-      nf = topk_token<KMAX>(lg + tid * LDR, E, k, renorm, topk_idx + (size_t)t * k,
+      nf = topk_token<KMAX>(lg + tid * LDR, E, k, renorm, thr, delta, topk_idx + (size_t)t * k,
                             topk_w + (size_t)t * k);
     const unsigned long long m = __ballot(nf);
     const int ngroups = (T + kRouteFlagGroup - 1) / kRouteFlagGroup;
@@ -441,12 +473,13 @@ __global__ __launch_bounds__(512, 1) void route_stream_kernel(
 
 hipError_t launch_route_bf16_lds(const bf16_t* x, const bf16_t* w_router, const float* bias,
                                  float* logits, int32_t* idx, float* w, int32_t* flags, int T,
-                                 int H, int E, int k, int renorm, int cus, hipStream_t s) {
+                                 int H, int E, int k, int renorm, int thr, double delta,
+                                 int cus, hipStream_t s) {
   (void)cus;
   const dim3 grid((T + 31) / 32), block(64 * kRouteWaves);
 #define MOE_ROUTE_STREAM(KM)                                                                    \
   hipLaunchKernelGGL((route_stream_kernel<KM>), grid, block, 0, s, x, w_router, bias, logits, idx, \
-                     w, flags, T, H, E, k, renorm)
+                     w, flags, T, H, E, k, renorm, thr, delta)
   if (k <= 1) MOE_ROUTE_STREAM(1);
   else if (k <= 2) MOE_ROUTE_STREAM(2);
   else if (k <= 4) MOE_ROUTE_STREAM(4);
@@ -485,11 +518,12 @@ __global__ __launch_bounds__(64) void route_topk_kernel(const float* __restrict_
                                                         int32_t* __restrict__ idx,
                                                         float* __restrict__ w,
                                                         int32_t* __restrict__ flags, int T,
-                                                        int E, int k, int renorm) {
+                                                        int E, int k, int renorm, int thr,
+                                                        double delta) {
   const int t = blockIdx.x * 64 + threadIdx.x;
   bool nf = false;
   if (t < T)
-    nf = topk_token<KMAX>(logits + (size_t)t * E, E, k, renorm, idx + (size_t)t * k,
+    nf = topk_token<KMAX>(logits + (size_t)t * E, E, k, renorm, thr, delta, idx + (size_t)t * k,
                           w + (size_t)t * k);
   const unsigned long long m = __ballot(nf);
   const int ngroups = (T + kRouteFlagGroup - 1) / kRouteFlagGroup;
@@ -499,10 +533,11 @@ __global__ __launch_bounds__(64) void route_topk_kernel(const float* __restrict_
 }
 
 hipError_t launch_route_topk(const float* logits, int32_t* idx, float* w, int32_t* flags, int T,
-                             int E, int k, int renorm, hipStream_t s) {
+                             int E, int k, int renorm, int thr, double delta, hipStream_t s) {
   const dim3 grid((T + 63) / 64), block(64);
 #define MOE_TOPK_LAUNCH(KM) \
-  hipLaunchKernelGGL((route_topk_kernel<KM>), grid, block, 0, s, logits, idx, w, flags, T, E, k, renorm)
+  hipLaunchKernelGGL((route_topk_kernel<KM>), grid, block, 0, s, logits, idx, w, flags, T, E, k, \
+                     renorm, thr, delta)
   if (k <= 1) MOE_TOPK_LAUNCH(1);
   else if (k <= 2) MOE_TOPK_LAUNCH(2);
   else if (k <= 4) MOE_TOPK_LAUNCH(4);

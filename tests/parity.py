@@ -3,9 +3,13 @@ on the same inputs, compare. Tolerances are the ones the tests enforce:
 
   * routing from identical fp32 logits: expert ids, counts, drops, offsets, slot/row maps
     bit-exact; gate weights within 2e-6 relative (float64 softmax rounded once to fp32);
+    threshold routing: the same, except tokens with a score within 1e-12 (relative) of the
+    threshold, where the float64 score of either side may fall on either side (counted,
+    and their ids must still be a valid best-first list);
   * gate logits against the float64 oracle: |dL| <= 1e-5 * (1 + |L|);
   * layer output (and y_perm): max|err| <= 2e-2 * max|ref| and sum|err| / sum|ref| <= 5e-3,
-    after excluding tokens whose k-th/(k+1)-th logit margin is below 1e-4 (counted);
+    after excluding tokens whose k-th/(k+1)-th logit margin is below 1e-4 (threshold
+    routing: a score within 1e-3 relative of the threshold) (counted);
   * combine from the same y_perm and weights: within one bf16 ulp of the float64 result.
 """
 from __future__ import annotations
@@ -24,6 +28,8 @@ WEIGHT_RTOL = 2e-6
 LAYER_MAX_REL = 2e-2
 LAYER_MEAN_REL = 5e-3
 TIE_MARGIN = 1e-4
+THRESH_MARGIN = 1e-3        # end to end: |p - delta| / delta below this is a near tie
+THRESH_EXACT_MARGIN = 1e-12  # same logits: float64 scores of the two sides agree this far
 
 
 def decode(cfg: MoEConfig, t: torch.Tensor) -> np.ndarray:
@@ -55,16 +61,35 @@ def check_logits(gpu_L: np.ndarray, ref_L: np.ndarray):
     assert (d <= bound).all(), f"logit error {d.max():.3e} (worst ratio {(d / bound).max():.2f})"
 
 
-def check_route_from_logits(gpu_L, gpu_idx, gpu_w, k, renorm):
-    """Oracle selection and weights on the GPU's own fp32 logits: ids bit-exact."""
+def oracle_route(cfg, L64):
+    """The oracle's selection, weights and decision margins for ``cfg``'s routing rule."""
+    if cfg.routing == "threshold":
+        idx, _ = O.threshold_select(L64, cfg.top_k, cfg.threshold)
+        return (idx, O.threshold_weights(L64, idx, cfg.renormalize),
+                O.threshold_margin(L64, cfg.threshold))
+    idx, _ = O.select_experts(L64, cfg.top_k)
+    return idx, O.topk_weights(L64, idx, cfg.renormalize), O.selection_margin(L64, cfg.top_k)
+
+
+def check_route_from_logits(gpu_L, gpu_idx, gpu_w, cfg):
+    """Oracle selection and weights on the GPU's own fp32 logits: ids bit-exact (threshold
+    routing: on every token whose scores are not within THRESH_EXACT_MARGIN of delta).
+    Returns the number of tokens excluded that way."""
     L64 = np.asarray(gpu_L, dtype=np.float64)
-    idx, _ = O.select_experts(L64, k)
-    np.testing.assert_array_equal(gpu_idx, idx)
-    w = O.topk_weights(L64, idx, renorm)
+    idx, w, margin = oracle_route(cfg, L64)
+    use = np.ones(len(idx), dtype=bool)
+    if cfg.routing == "threshold":
+        use = margin >= THRESH_EXACT_MARGIN
+        for t in np.nonzero(~use)[0]:      # still a best-first list of distinct experts
+            got = [int(e) for e in gpu_idx[t] if e >= 0]
+            ref, _ = O.select_experts(L64[t:t + 1], L64.shape[1])
+            assert got == [int(e) for e in ref[0][:len(got)]], t
+    np.testing.assert_array_equal(gpu_idx[use], idx[use])
+    w, gw = w[use], gpu_w[use]
     nan = np.isnan(w)
-    np.testing.assert_array_equal(np.isnan(gpu_w), nan)
-    np.testing.assert_allclose(gpu_w[~nan], w[~nan], rtol=WEIGHT_RTOL, atol=0)
-    return idx, w
+    np.testing.assert_array_equal(np.isnan(gw), nan)
+    np.testing.assert_allclose(gw[~nan], w[~nan], rtol=WEIGHT_RTOL, atol=0)
+    return int((~use).sum())
 
 
 def check_permute(cfg, x_np, gpu_idx, cap, counts, offsets, slot_row, row_token, x_perm=None):
@@ -118,7 +143,7 @@ def full_check(cfg: MoEConfig, inputs: dict, tokens_sample: int | None = None, s
     # selection + weights from identical logits
     g_idx = layer.view(L.MOE_WS_TOPK_IDX).cpu().numpy()
     g_w = layer.view(L.MOE_WS_TOPK_W).cpu().numpy()
-    check_route_from_logits(gL, g_idx, g_w, k, cfg.renormalize)
+    rep["threshold_edge_tokens"] = check_route_from_logits(gL, g_idx, g_w, cfg)
     # permutation
     cap = O.capacity(cfg.capacity_factor, T, k, E)
     assert L.moe_capacity(layer.c) == cap
@@ -132,10 +157,8 @@ def full_check(cfg: MoEConfig, inputs: dict, tokens_sample: int | None = None, s
     assert layer.device_status() == 0
 
     # the oracle's own routing from its float64 logits
-    r_idx, _ = O.select_experts(refL, k)
-    r_w = O.topk_weights(refL, r_idx, cfg.renormalize)
+    r_idx, r_w, margin = oracle_route(cfg, refL)
     r_perm = O.permute_indices(r_idx, E, cap)
-    margin = O.selection_margin(refL, k)
 
     ts = np.arange(T) if tokens_sample is None else sample_tokens(T, tokens_sample, seed)
     # oracle FFN for every (token, expert) pair either side keeps
@@ -188,7 +211,7 @@ def full_check(cfg: MoEConfig, inputs: dict, tokens_sample: int | None = None, s
             if r >= 0:
                 y_ref[r] = y_pair[(int(t), int(r_idx[t, j]))]
     ref_out = O.combine(y_ref, r_perm["slot_row"], r_w, H, tokens=ts)
-    near = margin < TIE_MARGIN
+    near = margin < (THRESH_MARGIN if cfg.routing == "threshold" else TIE_MARGIN)
     same_route = (r_idx == g_idx).all(axis=1)
     assert (same_route | near).all(), "routing differs on a token without a near tie"
     same_keep = ((r_perm["slot_row"] >= 0) == (p["slot_row"] >= 0)).all(axis=1)

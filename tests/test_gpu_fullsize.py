@@ -11,7 +11,7 @@ import parity as P
 
 pytestmark = pytest.mark.gpu
 
-SAMPLE = {"tiny": None, "small": 48, "mixtral": 24, "cap32": 12, "fine": 16}
+SAMPLE = {"tiny": None, "small": 48, "mixtral": 24, "cap32": 12, "fine": 16, "mixtral_threshold": 24}
 
 
 @pytest.mark.parametrize("name", list(SAMPLE))

@@ -51,6 +51,21 @@ CASES = {
     "fp32_swiglu_capacity": C.TINY.with_(name="fp32_swiglu_capacity", tokens=257, hidden=40,
                                          inter=24, experts=5, top_k=2, activation=C.SWIGLU,
                                          capacity_factor=0.6, bias=("zipf", 1.1)),
+    # threshold routing (experts with softmax score > delta): delta = 1/E with no cap (the
+    # streaming router), a cap of 3 slots that binds, an explicit delta with capacity, the
+    # MFMA router with 64 experts, and the fp32 layer
+    "thr_uncapped": C.SMALL.with_(name="thr_uncapped", tokens=1200, hidden=1024, inter=384,
+                                  experts=8, top_k=8, routing="threshold", bias=None),
+    "thr_capped": C.SMALL.with_(name="thr_capped", tokens=900, hidden=512, inter=256,
+                                experts=12, top_k=3, routing="threshold",
+                                router_std=0.3 / 512 ** 0.5),
+    "thr_delta_capacity": C.SMALL.with_(name="thr_delta_capacity", tokens=1000, hidden=256,
+                                        inter=256, experts=16, top_k=6, routing="threshold",
+                                        threshold=0.08, capacity_factor=0.8, renormalize=False),
+    "thr_many_experts": C.FINE.with_(name="thr_many_experts", tokens=600, hidden=256,
+                                     inter=256, experts=64, top_k=16, routing="threshold"),
+    "thr_fp32": C.TINY.with_(name="thr_fp32", tokens=200, hidden=48, inter=32, experts=6,
+                             top_k=6, routing="threshold"),
 }
 
 
@@ -115,7 +130,7 @@ def test_topk_tie_suite(E, k):
     L_np[113, ::2] = np.nan
     cfg = C.SMALL.with_(tokens=T, hidden=256, inter=256, experts=E, top_k=k)
     idx, w, flags = _route_only(cfg, L_np)
-    P.check_route_from_logits(L_np, idx, w, k, True)
+    P.check_route_from_logits(L_np, idx, w, cfg)
     assert flags == L.MOE_FLAG_NONFINITE_LOGIT
     np.testing.assert_array_equal(idx[100:110], np.tile(np.arange(k), (10, 1)))
     idx2, w2, flags2 = _route_only(cfg, L_np[:100])
@@ -141,7 +156,7 @@ def test_route_entry_point_with_crafted_ties():
     L.moe_route(c, xd, wd, None, lg, idx, w, ws)
     gl = lg.cpu().numpy()
     np.testing.assert_array_equal(gl, wr[np.arange(T) % H])
-    P.check_route_from_logits(gl, idx.cpu().numpy(), w.cpu().numpy(), k, True)
+    P.check_route_from_logits(gl, idx.cpu().numpy(), w.cpu().numpy(), cfg)
 
 
 def test_permute_entry_point_flags_invalid_ids():
@@ -318,3 +333,53 @@ def test_down_split_tail(name):
     mag = np.maximum(np.abs(yf), np.abs(y2f))
     ulp = np.exp2(np.floor(np.log2(np.maximum(mag, 1e-30))) - 7)
     assert (np.abs(yf - y2f) <= ulp + 1e-5 * np.abs(ref).max()).all()
+
+
+def test_threshold_route_entry_point_edges():
+    """Threshold routing from given logits: rows whose scores sit exactly on delta = 1/E
+    (all equal: nothing kept), two-level rows (exactly one group kept), a cap that binds,
+    and non-finite rows (nothing kept, flagged); everything else on random logits."""
+    T, E, k = 400, 8, 8
+    cfg = C.SMALL.with_(tokens=T, hidden=256, inter=256, experts=E, top_k=k,
+                        routing="threshold")
+    rng = np.random.default_rng(21)
+    L_np = (rng.standard_normal((T, E)) * 1.5).astype(np.float32)
+    L_np[:10] = 0.25                                   # uniform: p = 1/E exactly
+    for i in range(10, 30):                            # a experts at u, the rest at 0
+        a, u = 1 + i % (E - 1), (0.5 if i % 2 else -0.5)
+        L_np[i] = 0.0
+        L_np[i, :a] = u
+    L_np[30, 2] = np.nan
+    L_np[31, 5] = np.inf
+    L_np[32, :4] = -np.inf
+    idx, w, flags = _route_only(cfg, L_np)
+    assert flags == L.MOE_FLAG_NONFINITE_LOGIT
+    assert P.check_route_from_logits(L_np, idx, w, cfg) == 10   # the uniform rows
+    assert (idx[:10] == -1).all() and (w[:10] == 0).all()
+    for i in range(10, 30):
+        a = 1 + i % (E - 1)
+        want = list(range(a)) if i % 2 else list(range(a, E))
+        assert [int(e) for e in idx[i] if e >= 0] == want
+    assert (idx[30:32] == -1).all()
+    # a cap of 2 slots keeps the two best of the experts above delta
+    cfg2 = cfg.with_(top_k=2)
+    idx2, w2, _ = _route_only(cfg2, L_np)
+    P.check_route_from_logits(L_np, idx2, w2, cfg2)
+    full = [[int(e) for e in r if e >= 0] for r in idx]
+    assert all([int(e) for e in r2 if e >= 0] == f[:2] for r2, f in zip(idx2, full))
+
+
+def test_threshold_rows_flow_through_permute_without_flags():
+    """-1 slots from threshold routing are empty, not invalid: no bad-index flag, and the
+    permutation of the GPU's ids matches the oracle's."""
+    cfg = CASES["thr_uncapped"]
+    inp = make_inputs(cfg, seed=3)
+    layer = MoELayer(cfg, inp)
+    layer.forward(to_device(cfg, inp["x"]))
+    torch.cuda.synchronize()
+    idx = layer.view(L.MOE_WS_TOPK_IDX).cpu().numpy()
+    assert (idx == -1).any() and layer.device_status() == 0
+    kept = (idx >= 0).sum(1)
+    print(f"[threshold] experts per token: mean {kept.mean():.2f}, min {kept.min()}, "
+          f"max {kept.max()}", flush=True)
+    assert kept.min() >= 1 and kept.max() <= cfg.experts - 1
