@@ -39,8 +39,43 @@ template <> struct Vec8<float> {
   }
 };
 
-// KMAX >= k slots, U vectors of 8 columns per lane per step (KMAX*U loads in flight).
-template <typename T, int KMAX, int U>
+// out row = sum over the first n of NR compacted slots (rows[j], ws[j]) of ws[j] * y[rows[j]],
+// float32, in slot order; U vectors of 8 columns per lane per step, so up to NR * U loads
+// are in flight per lane.
+template <typename T, int NR, int U>
+__device__ __forceinline__ void combine_rows(const T* __restrict__ y, const int* rows,
+                                             const float* ws, int n, T* __restrict__ o,
+                                             int nvec, int H, int lane) {
+  for (int base = 0; base < nvec; base += 64 * U) {
+    Vec8<T> v[NR][U];
+#pragma unroll
+    for (int j = 0; j < NR; ++j)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = base + u * 64 + lane;
+        if (j < n && c < nvec) v[j][u].load(y + (size_t)rows[j] * H + c * 8);
+      }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = base + u * 64 + lane;
+      if (c >= nvec) continue;
+      float acc[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll
+      for (int j = 0; j < NR; ++j)
+        if (j < n)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = fmaf(ws[j], v[j][u].get(i), acc[i]);
+      Vec8<T>::store(o + c * 8, acc);
+    }
+  }
+}
+
+// One wave per token. The token's kept slots (row >= 0) are first compacted to the front,
+// in slot order, so empty or dropped slots (threshold routing, capacity) cost no load
+// slots; the row loop is then sized by the number kept.
+template <typename T, int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y,
                                                       const int32_t* __restrict__ slot_row,
                                                       const float* __restrict__ topk_w,
@@ -56,50 +91,36 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y,
     w = topk_w[(size_t)t * k + lane];
     if (row >= nrows) row = -1;   // a row outside y_perm is never read
   }
+  unsigned long long kept = __ballot(row >= 0);
+  const int n = __popcll(kept);
   int rows[KMAX];
   float ws[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
-    rows[j] = __shfl(row, j);
-    ws[j] = __shfl(w, j);
+    const int src = kept ? __builtin_ctzll(kept) : 0;   // lane of the j-th kept slot
+    kept &= kept - 1;
+    rows[j] = __shfl(row, src);
+    ws[j] = __shfl(w, src);
   }
   const int nvec = H / 8;
   T* o = out + (size_t)t * H;
-  for (int base = 0; base < nvec; base += 64 * U) {
-    Vec8<T> v[KMAX][U];
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j)
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = base + u * 64 + lane;
-        if (j < k && rows[j] >= 0 && c < nvec) v[j][u].load(y + (size_t)rows[j] * H + c * 8);
-      }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = base + u * 64 + lane;
-      if (c >= nvec) continue;
-      float acc[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-#pragma unroll
-      for (int j = 0; j < KMAX; ++j)
-        if (j < k && rows[j] >= 0)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) acc[i] = fmaf(ws[j], v[j][u].get(i), acc[i]);
-      Vec8<T>::store(o + c * 8, acc);
-    }
-  }
+  if (n <= 2 || KMAX <= 2) combine_rows<T, (KMAX < 2 ? KMAX : 2), (KMAX < 2 ? 8 : 4)>(y, rows, ws, n, o, nvec, H, lane);
+  else if (n <= 4 || KMAX <= 4) combine_rows<T, (KMAX < 4 ? KMAX : 4), 2>(y, rows, ws, n, o, nvec, H, lane);
+  else combine_rows<T, KMAX, 1>(y, rows, ws, n, o, nvec, H, lane);
 }
 
 template <typename T>
 static hipError_t launch_combine_t(const T* y, const int32_t* slot_row, const float* w, T* out,
                                    int Tn, int H, int k, hipStream_t s) {
   const dim3 grid((Tn + 3) / 4), block(256);
-  if (k <= 1) hipLaunchKernelGGL((combine_kernel<T, 1, 8>), grid, block, 0, s, y, slot_row, w, out, Tn, H, k, Tn * k);
-  else if (k <= 2) hipLaunchKernelGGL((combine_kernel<T, 2, 4>), grid, block, 0, s, y, slot_row, w, out, Tn, H, k, Tn * k);
-  else if (k <= 4) hipLaunchKernelGGL((combine_kernel<T, 4, 2>), grid, block, 0, s, y, slot_row, w, out, Tn, H, k, Tn * k);
-  else if (k <= 8) hipLaunchKernelGGL((combine_kernel<T, 8, 1>), grid, block, 0, s, y, slot_row, w, out, Tn, H, k, Tn * k);
-  else hipLaunchKernelGGL((combine_kernel<T, 16, 1>), grid, block, 0, s, y, slot_row, w, out, Tn, H, k, Tn * k);
+#define MOE_COMBINE(KM) \
+  hipLaunchKernelGGL((combine_kernel<T, KM>), grid, block, 0, s, y, slot_row, w, out, Tn, H, k, Tn * k)
+  if (k <= 1) MOE_COMBINE(1);
+  else if (k <= 2) MOE_COMBINE(2);
+  else if (k <= 4) MOE_COMBINE(4);
+  else if (k <= 8) MOE_COMBINE(8);
+  else MOE_COMBINE(16);
+#undef MOE_COMBINE
   return hipGetLastError();
 }
 

@@ -94,7 +94,8 @@ def selection_margin(logits, k: int) -> np.ndarray:
     L = np.sort(np.asarray(logits, dtype=np.float64), axis=1)[:, ::-1]
     if k >= L.shape[1]:
         return np.full(L.shape[0], np.inf)
-    return L[:, k - 1] - L[:, k]
+    with np.errstate(invalid="ignore"):   # inf - inf on rows of infinities: NaN, no warning
+        return L[:, k - 1] - L[:, k]
 
 
 # ---------------------------------------------------------------- step 3: weights
