@@ -44,6 +44,10 @@ project's design notes):
      with k = E nothing is capped); the remaining slots hold -1 and weight 0. A token with
      no expert above delta (all scores equal to 1/E, or a NaN or +inf logit) contributes
      zero. Renormalisation (R2) is over the kept experts.
+  R15 backward: the gradient of sum(out * dout); the expert choice (top-k, threshold,
+     capacity) is piecewise constant in the logits and contributes no gradient; the gate
+     weights' dependence on the logits is differentiated exactly. No auxiliary
+     load-balancing loss: the pages give no formula for one.
 
 Every function here is pinned by tests/test_oracle_*.py against hand-worked cases, closed
 forms, brute force and invariants that do not reuse this code.
@@ -333,3 +337,104 @@ def forward(x, w_router, bias, w_gate, w_up, w_down, *, top_k: int, activation: 
     return dict(logits=L, topk_idx=idx, topk_w=w, capacity=cap, y=y, out=out, tokens=ts,
                 flags=f1 | perm["flags"], margin=margin, **{
                     k_: v for k_, v in perm.items() if k_ != "flags"})
+
+
+# ---------------------------------------------------------------- backward pass
+def silu_grad(z):
+    """d/dz of z * logistic(z) = s (1 + z (1 - s)), s = logistic(z)."""
+    s = 1.0 / (1.0 + np.exp(-z))
+    return s * (1.0 + z * (1.0 - s))
+
+
+def gelu_grad(z):
+    """d/dz of z * Phi(z) = Phi(z) + z * phi(z)."""
+    return 0.5 * (1.0 + _erf(z / math.sqrt(2.0))) + z * np.exp(-0.5 * z * z) / math.sqrt(2.0 * math.pi)
+
+
+def backward(x, w_router, bias, w_gate, w_up, w_down, dout, *, top_k: int, activation: str,
+             capacity_factor: float = 0.0, renormalize: bool = True, routing: str = "topk",
+             threshold=None) -> dict:
+    """Gradients of sum(out * dout) with respect to x, W_router, the gate bias and the expert
+    weights, in float64, for the layer of ``forward`` (reading R15: the expert choice is a
+    fixed function of the logits, so no gradient flows through the selection itself; the
+    weights' dependence on the logits is differentiated exactly).
+
+    The pages compute the backward only for the selected experts' parameters (gitcode
+    page, "MoE 算子核心原理": sparse computation runs forward and backward on the chosen
+    experts only); every step below is the chain rule of one forward step:
+      combine          dy_j = w_j dout,  dw_j = <dout, y_j>
+      down-projection  dh = dy Wd^T,     dWd += h^T dy
+      activation       SwiGLU: dg = dh u silu'(g), du = dh silu(g); GELU: da = dh gelu'(a)
+      up-projection    dWg += x^T dg, dWu += x^T du (da), dx += dg Wg^T + du Wu^T
+      weights          renormalised: dp_i = (dw_i - sum_j w_j dw_j) / sum_S p; raw: dp = dw
+      softmax          dL = p (dp - sum_e p_e dp_e)
+      gate GEMM        dW_router = x^T dL, dbias = sum_t dL, dx += dL W_router^T
+    Slots dropped by the capacity rule contribute dw = 0 but stay in the weights' sum."""
+    x = np.asarray(x, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    wr = np.asarray(w_router, dtype=np.float64)
+    T, H = x.shape
+    fwd = forward(x, wr, bias, w_gate, w_up, w_down, top_k=top_k, activation=activation,
+                  capacity_factor=capacity_factor, renormalize=renormalize, routing=routing,
+                  threshold=threshold)
+    L, idx, w = fwd["logits"], np.asarray(fwd["topk_idx"], np.int64), fwd["topk_w"]
+    slot_row, offsets, row_token = fwd["slot_row"], fwd["offsets"], fwd["row_token"]
+    E = L.shape[1]
+    dx = np.zeros_like(x)
+    dWg = None if w_gate is None else [None] * E
+    dWu, dWd = [None] * E, [None] * E
+    dw = np.zeros_like(w)
+    row_t = np.full(int(offsets[-1]), -1, dtype=np.int64)    # row -> (token, slot)
+    row_j = np.full(int(offsets[-1]), -1, dtype=np.int64)
+    t_k, j_k = np.nonzero(slot_row >= 0)
+    row_t[slot_row[t_k, j_k]] = t_k
+    row_j[slot_row[t_k, j_k]] = j_k
+    for e in range(E):
+        wu = np.asarray(w_up[e], dtype=np.float64)
+        wd = np.asarray(w_down[e], dtype=np.float64)
+        wg = None if w_gate is None else np.asarray(w_gate[e], dtype=np.float64)
+        rows = np.arange(offsets[e], offsets[e + 1])
+        toks = row_token[rows].astype(np.int64)
+        t_of, j_of = row_t[rows], row_j[rows]
+        xe = x[toks]
+        if activation == "swiglu":
+            g, u = xe @ wg, xe @ wu
+            h = silu(g) * u
+        else:
+            a = xe @ wu
+            h = gelu(a)
+        y = h @ wd
+        de = dout[toks]
+        dw[t_of, j_of] = (de * y).sum(axis=1)
+        dy = w[t_of, j_of][:, None] * de
+        dh = dy @ wd.T
+        dWd[e] = h.T @ dy
+        if activation == "swiglu":
+            dg = dh * u * silu_grad(g)
+            du = dh * silu(g)
+            dWg[e] = xe.T @ dg
+            dWu[e] = xe.T @ du
+            dxe = dg @ wg.T + du @ wu.T
+        else:
+            da = dh * gelu_grad(a)
+            dWu[e] = xe.T @ da
+            dxe = da @ wu.T
+        np.add.at(dx, toks, dxe)
+    # gate weights -> scores -> logits
+    p = softmax(L)
+    kept = idx >= 0
+    psel = np.where(kept, np.take_along_axis(p, np.maximum(idx, 0), axis=1), 0.0)
+    if renormalize:
+        s = psel.sum(axis=1, keepdims=True)
+        dps = np.divide(dw - (w * dw).sum(axis=1, keepdims=True), s,
+                        out=np.zeros_like(dw), where=s > 0)
+    else:
+        dps = dw
+    dp = np.zeros_like(p)
+    for j in range(idx.shape[1]):
+        m = kept[:, j]
+        dp[np.nonzero(m)[0], idx[m, j]] += dps[m, j]
+    dL = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    dx += dL @ wr.T
+    return dict(dx=dx, dw_router=x.T @ dL, dbias=dL.sum(axis=0), dw_gate=dWg, dw_up=dWu,
+                dw_down=dWd, dlogits=dL, dw=dw, forward=fwd)

@@ -440,3 +440,98 @@ def test_empty_slots_are_dropped_without_a_flag():
     counts, offsets, slot_row, row_token = sequential_permute(idx, 2, 10)
     np.testing.assert_array_equal(p["slot_row"], slot_row)
     np.testing.assert_array_equal(p["row_token"], row_token)
+
+
+# ------------------------------------------------------------------ backward (R15)
+def _layer(seed, T, H, I, E, act, bias=True):
+    rng = np.random.default_rng(seed)
+    return dict(x=rng.standard_normal((T, H)), w_router=rng.standard_normal((H, E)),
+                bias=rng.standard_normal(E) if bias else None,
+                w_gate=rng.standard_normal((E, H, I)) / math.sqrt(H) if act == "swiglu" else None,
+                w_up=rng.standard_normal((E, H, I)) / math.sqrt(H),
+                w_down=rng.standard_normal((E, I, H)) / math.sqrt(I)), rng
+
+
+def _loss(p, dout, **kw):
+    r = O.forward(p["x"], p["w_router"], p["bias"], p["w_gate"], p["w_up"], p["w_down"], **kw)
+    return float((r["out"] * dout).sum()), r
+
+
+BWD_CASES = [
+    dict(top_k=2, activation="swiglu"),
+    dict(top_k=3, activation="gelu", renormalize=False),
+    dict(top_k=2, activation="swiglu", capacity_factor=0.6),
+    dict(top_k=5, activation="swiglu", routing="threshold"),
+    dict(top_k=2, activation="swiglu", routing="threshold", threshold=0.3),
+]
+
+
+@pytest.mark.parametrize("kw", BWD_CASES, ids=lambda kw: "-".join(f"{k}{v}" for k, v in kw.items()))
+def test_backward_matches_central_differences(kw):
+    """Every gradient against the central difference of sum(out * dout) along a random
+    direction (eps = 1e-6, float64), on inputs whose routing decisions are at least 1e-3
+    away from flipping, so the selection is fixed over +-eps."""
+    T, H, I, E = 12, 5, 7, 5
+    p, rng = _layer(31, T, H, I, E, kw["activation"])
+    dout = rng.standard_normal((T, H))
+    L = O.gate_logits(p["x"], p["w_router"], p["bias"])
+    if kw.get("routing") == "threshold":
+        assert O.threshold_margin(L, kw.get("threshold")).min() > 1e-3
+    else:
+        assert O.selection_margin(L, kw["top_k"]).min() > 1e-3
+    g = O.backward(p["x"], p["w_router"], p["bias"], p["w_gate"], p["w_up"], p["w_down"], dout,
+                   **kw)
+    if kw.get("capacity_factor"):
+        assert (g["forward"]["slot_row"] < 0).any() and (g["forward"]["slot_row"] >= 0).any()
+    grads = dict(x=g["dx"], w_router=g["dw_router"], bias=g["dbias"],
+                 w_gate=None if g["dw_gate"] is None else np.stack(g["dw_gate"]),
+                 w_up=np.stack(g["dw_up"]), w_down=np.stack(g["dw_down"]))
+    eps = 1e-6
+    for name, grad in grads.items():
+        if grad is None:
+            continue
+        v = rng.standard_normal(p[name].shape)
+        plus = {**p, name: p[name] + eps * v}
+        minus = {**p, name: p[name] - eps * v}
+        fd = (_loss(plus, dout, **kw)[0] - _loss(minus, dout, **kw)[0]) / (2 * eps)
+        an = float((grad * v).sum())
+        assert an == pytest.approx(fd, rel=1e-6, abs=1e-8), name
+
+
+def test_backward_single_expert_is_dense_ffn_backward():
+    """E = 1, k = 1: the weight is 1 and the logits get no gradient; the expert gradients are
+    the textbook dense-FFN ones, written out separately."""
+    T, H, I = 9, 4, 6
+    p, rng = _layer(32, T, H, I, 1, "swiglu")
+    dout = rng.standard_normal((T, H))
+    g = O.backward(p["x"], p["w_router"], p["bias"], p["w_gate"], p["w_up"], p["w_down"], dout,
+                   top_k=1, activation="swiglu")
+    x, wg, wu, wd = p["x"], p["w_gate"][0], p["w_up"][0], p["w_down"][0]
+    a, b = x @ wg, x @ wu
+    sig = 1.0 / (1.0 + np.exp(-a))
+    h = a * sig * b
+    dh = dout @ wd.T
+    da = dh * b * (sig + a * sig * (1.0 - sig))
+    db = dh * a * sig
+    np.testing.assert_allclose(g["dw_down"][0], h.T @ dout, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(g["dw_gate"][0], x.T @ da, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(g["dw_up"][0], x.T @ db, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(g["dx"], da @ wg.T + db @ wu.T, rtol=1e-12, atol=1e-12)
+    assert np.abs(g["dw_router"]).max() == 0 and np.abs(g["dbias"]).max() == 0
+
+
+def test_backward_renormalised_logit_gradient_sums_to_zero():
+    """With renormalised weights the output depends on the selected logits only through
+    their differences: each token's logit gradient sums to zero and vanishes outside the
+    selected experts."""
+    T, H, I, E = 20, 4, 6, 6
+    p, rng = _layer(33, T, H, I, E, "swiglu")
+    dout = rng.standard_normal((T, H))
+    g = O.backward(p["x"], p["w_router"], p["bias"], p["w_gate"], p["w_up"], p["w_down"], dout,
+                   top_k=3, activation="swiglu")
+    dL = g["dlogits"]
+    np.testing.assert_allclose(dL.sum(axis=1), 0.0, atol=1e-12)
+    idx = g["forward"]["topk_idx"]
+    mask = np.zeros_like(dL, dtype=bool)
+    np.put_along_axis(mask, idx.astype(np.int64), True, axis=1)
+    assert np.abs(dL[~mask]).max() < 1e-15
