@@ -196,6 +196,28 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
                        const void* w_down, void* out, void* ws, size_t ws_bytes,
                        moe_stream_t stream);
 
+/* Backward pass of the layer: the gradients of sum(out * dout) with respect to x, the router
+ * weight, the gate bias and the expert weights (gitcode page, "MoE 算子核心原理": the
+ * backward runs on the selected experts only). The expert choice (top-k, threshold,
+ * capacity) carries no gradient; the gate weights' dependence on the logits is exact. There
+ * is no auxiliary load-balancing loss (the pages give no formula for one).
+ *   ws, ws_bytes   the workspace of a moe_forward call with the same cfg, x and weights,
+ *                  made on the same stream before this call: its routing, row maps and
+ *                  y_perm are reused (so is its gate bias, through the logits)
+ *   bws, bws_bytes backward scratch, at least moe_backward_workspace_size bytes
+ *   dout [T,H] bf16 in; dx [T,H] bf16 out; dw_router [H,E] float32 out; dgate_bias [E]
+ *   float32 out or NULL; dw_gate (SwiGLU only; NULL for GELU), dw_up [E,H,I] and dw_down
+ *   [E,I,H] bf16 out (float32 accumulation, rounded once)
+ * bf16 layers with I a multiple of 256 only (else MOE_ERR_UNSUPPORTED). Expert rows are
+ * regrouped in a padded row space (each expert's rows rounded up to a multiple of 128) and
+ * the up-projection is recomputed (its pre-activations are not kept by moe_forward). */
+moe_status moe_backward_workspace_size(const moe_config* cfg, size_t* bytes);
+moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_router,
+                        const void* w_gate, const void* w_up, const void* w_down,
+                        const void* dout, void* dx, float* dw_router, float* dgate_bias,
+                        void* dw_gate, void* dw_up, void* dw_down, void* ws, size_t ws_bytes,
+                        void* bws, size_t bws_bytes, moe_stream_t stream);
+
 /* Where moe_forward keeps an intermediate inside `ws` (device address and byte size). */
 enum {
   MOE_WS_LOGITS = 0,      /* [T,E] float32 */

@@ -27,7 +27,7 @@ MOE_ROUTE_TOPK, MOE_ROUTE_THRESHOLD = 0, 1
 
 EXPORTS = ("moe_workspace_size", "moe_capacity", "moe_route", "moe_permute", "moe_expert_up",
            "moe_expert_up_rows", "moe_expert_down", "moe_grouped_ffn", "moe_combine",
-           "moe_forward",
+           "moe_forward", "moe_backward_workspace_size", "moe_backward",
            "moe_workspace_view", "moe_read_device_status", "moe_status_string",
            "moe_last_hip_error")
 
@@ -72,6 +72,9 @@ def lib():
             "moe_grouped_ffn": [cfgp, vp, vp, vp, vp, vp, vp, vp, c_size_t, vp],
             "moe_combine": [cfgp, vp, vp, vp, vp, vp],
             "moe_forward": [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, c_size_t, vp],
+            "moe_backward_workspace_size": [cfgp, POINTER(c_size_t)],
+            "moe_backward": [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, c_size_t,
+                             vp, c_size_t, vp],
             "moe_workspace_view": [cfgp, vp, c_int32, POINTER(c_void_p), POINTER(c_size_t)],
             "moe_read_device_status": [cfgp, vp, c_int32, vp, POINTER(c_int32)],
         }
@@ -190,6 +193,23 @@ def moe_forward(cfg, x, w_router, gate_bias, w_gate, w_up, w_down, out, ws, stre
     _check("moe_forward", lib().moe_forward(
         ctypes.byref(_as_cfg(cfg)), _ptr(x), _ptr(w_router), _ptr(gate_bias), _ptr(w_gate),
         _ptr(w_up), _ptr(w_down), _ptr(out), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_backward_workspace_size(cfg) -> int:
+    n = c_size_t()
+    _check("moe_backward_workspace_size",
+           lib().moe_backward_workspace_size(ctypes.byref(_as_cfg(cfg)), ctypes.byref(n)))
+    return n.value
+
+
+def moe_backward(cfg, x, w_router, w_gate, w_up, w_down, dout, dx, dw_router, dgate_bias,
+                 dw_gate, dw_up, dw_down, ws, bws, stream=None):
+    """Gradients of the layer; ``ws`` is the workspace of the moe_forward call it follows."""
+    _check("moe_backward", lib().moe_backward(
+        ctypes.byref(_as_cfg(cfg)), _ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up),
+        _ptr(w_down), _ptr(dout), _ptr(dx), _ptr(dw_router), _ptr(dgate_bias), _ptr(dw_gate),
+        _ptr(dw_up), _ptr(dw_down), _ptr(ws), _nbytes(ws), _ptr(bws), _nbytes(bws),
+        _stream(stream)))
 
 
 def moe_workspace_view(cfg, ws, which: int):

@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 PEAKS_LIB = os.path.join(PKG, "libmoe_peaks.so")     # benchmark-only probes
-SOURCES = ["route.hip", "permute.hip", "gemm.hip", "combine.hip", "moe_api.cpp"]
+SOURCES = ["route.hip", "permute.hip", "gemm.hip", "combine.hip", "backward.hip", "moe_api.cpp"]
 PEAKS_SOURCES = ["peaks.hip"]
 ARCH = "gfx950"
 

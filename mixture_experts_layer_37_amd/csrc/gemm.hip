@@ -149,6 +149,21 @@ __device__ __forceinline__ float silu_f(float g) {
 __device__ __forceinline__ float gelu_f(float z) {
   return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
 }
+// d/dz of z Phi(z) = Phi(z) + z phi(z)
+__device__ __forceinline__ float gelu_grad_f(float z) {
+  return 0.5f * (1.0f + erff(z * 0.70710678118654752f)) +
+         z * 0.39894228040143268f * __expf(-0.5f * z * z);
+}
+// four floats <-> four packed bf16 (8 bytes)
+__device__ __forceinline__ uint2 pack4(const float* v) {
+  return make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+}
+__device__ __forceinline__ void unpack4(uint2 w, float* v) {
+  v[0] = bf16_to_f32(w.x & 0xffffu);
+  v[1] = bf16_to_f32(w.x >> 16);
+  v[2] = bf16_to_f32(w.y & 0xffffu);
+  v[3] = bf16_to_f32(w.y >> 16);
+}
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
@@ -183,8 +198,9 @@ template <int EPI>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ row_token, int a_rows,
     const int32_t* __restrict__ offsets, const bf16_t* __restrict__ W0,
-    const bf16_t* __restrict__ W1, bf16_t* __restrict__ C, float* __restrict__ partial, int E,
-    int K, int N, int max_rows) {
+    const bf16_t* __restrict__ W1, bf16_t* __restrict__ C, float* __restrict__ partial,
+    const bf16_t* __restrict__ aux, bf16_t* __restrict__ C2, int E, int K, int N,
+    int max_rows) {
   // Two stages in two distinct LDS objects: the compiler can then tell a DMA into one
   // stage from reads of the other and does not make those reads wait for the DMA.
   __shared__ __attribute__((aligned(1024))) bf16_t stage0[kStage];
@@ -195,7 +211,14 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  constexpr int OUTN = (EPI == EPI_SWIGLU) ? 128 : 256;   // output columns per tile
+  // Two-matrix tiles (gate and up columns of the same outputs) or one matrix of 256 columns.
+  constexpr bool kTwoMat = (EPI == EPI_SWIGLU || EPI == EPI_GU);
+  constexpr int OUTN = kTwoMat ? 128 : 256;   // output columns per tile
+  // Row strides of C and of the epilogue's second input (aux): the gate/up pair buffers
+  // [rows, 2N] hold the gate half in columns [0, N) and the up half in [N, 2N).
+  constexpr bool kPairOut = (EPI == EPI_GU || EPI == EPI_SWIGLU_BWD);
+  const size_t ldc = kPairOut ? 2 * (size_t)N : (size_t)N;
+  const size_t ldaux = (EPI == EPI_SWIGLU_BWD) ? 2 * (size_t)N : (size_t)N;
   const int NT = N / OUTN;
   const int total = build_tile_starts<BM>(offsets, E, NT, max_rows, s_start, s_off, s_wsum);
 
@@ -226,7 +249,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     int h, nb;
-    if (EPI == EPI_SWIGLU) { h = j >> 1; nb = wn * 64 + (j & 1) * 32; }
+    if (kTwoMat) { h = j >> 1; nb = wn * 64 + (j & 1) * 32; }
     else { h = wn; nb = j * 32; }
     const int krow0 = 8 * lhi + ((lane & 15) >> 2);
     const int c32 = (nb >> 4) + ((lane >> 4) & 1);
@@ -265,7 +288,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     // B halves: base pointers (uniform) of columns [0,128) and [128,256) of the tile
     const bf16_t* Bh0;
     const bf16_t* Bh1;
-    if (EPI == EPI_SWIGLU) {
+    if (kTwoMat) {
       Bh0 = W0 + (size_t)e * K * N + n_t * 128;
       Bh1 = W1 + (size_t)e * K * N + n_t * 128;
     } else {
@@ -397,32 +420,73 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     for (int i = 0; i < 4; ++i) {
       const int m = wm * 128 + i * 32 + l32;
       if (m >= mrows) continue;
-      bf16_t* crow = C + (size_t)(row0 + m) * N;
-      if (EPI == EPI_SWIGLU) {
+      bf16_t* crow = C + (size_t)(row0 + m) * ldc;
+      if constexpr (kTwoMat) {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            float hv[4];
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-              hv[s] = silu_f(acc[i][j][4 * q + s]) * acc[i][j + 2][4 * q + s];
             const int col = n_t * 128 + wn * 64 + j * 32 + 8 * q + 4 * lhi;
-            *(uint2*)(crow + col) = make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+            if constexpr (EPI == EPI_SWIGLU) {
+              float hv[4];
+#pragma unroll
+              for (int s = 0; s < 4; ++s)
+                hv[s] = silu_f(acc[i][j][4 * q + s]) * acc[i][j + 2][4 * q + s];
+              *(uint2*)(crow + col) = pack4(hv);
+            } else {   // EPI_GU: the gate and up pre-activations, and h into C2
+              float gv[4], uv[4], hv[4];
+#pragma unroll
+              for (int s = 0; s < 4; ++s) {
+                gv[s] = acc[i][j][4 * q + s];
+                uv[s] = acc[i][j + 2][4 * q + s];
+                hv[s] = silu_f(gv[s]) * uv[s];
+              }
+              *(uint2*)(crow + col) = pack4(gv);
+              *(uint2*)(crow + N + col) = pack4(uv);
+              *(uint2*)(C2 + (size_t)(row0 + m) * N + col) = pack4(hv);
+            }
           }
       } else {
+        const bf16_t* arow = aux + (size_t)(row0 + m) * ldaux;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
+            const int col = n_t * 256 + wn * 128 + j * 32 + 8 * q + 4 * lhi;
             float hv[4];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-              const float v = acc[i][j][4 * q + s];
-              hv[s] = (EPI == EPI_GELU) ? gelu_f(v) : v;
+            for (int s = 0; s < 4; ++s) hv[s] = acc[i][j][4 * q + s];
+            if constexpr (EPI == EPI_GELU) {
+#pragma unroll
+              for (int s = 0; s < 4; ++s) hv[s] = gelu_f(hv[s]);
+            } else if constexpr (EPI == EPI_AH) {   // a into C, gelu(a) into C2
+              float gv[4];
+#pragma unroll
+              for (int s = 0; s < 4; ++s) gv[s] = gelu_f(hv[s]);
+              *(uint2*)(C2 + (size_t)(row0 + m) * N + col) = pack4(gv);
+            } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+              // hv = dh; with g, u the saved pre-activations: dg = dh u silu'(g),
+              // du = dh silu(g)
+              float g[4], u[4], dg[4], du[4];
+              unpack4(*(const uint2*)(arow + col), g);
+              unpack4(*(const uint2*)(arow + N + col), u);
+#pragma unroll
+              for (int s = 0; s < 4; ++s) {
+                const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g[s]));
+                dg[s] = hv[s] * u[s] * (sg * (1.0f + g[s] * (1.0f - sg)));
+                du[s] = hv[s] * g[s] * sg;
+              }
+              *(uint2*)(crow + col) = pack4(dg);
+              *(uint2*)(crow + N + col) = pack4(du);
+              continue;
+            } else if constexpr (EPI == EPI_GELU_BWD) {
+              // hv = dh; with a the saved pre-activation: da = dh gelu'(a)
+              float a[4];
+              unpack4(*(const uint2*)(arow + col), a);
+#pragma unroll
+              for (int s = 0; s < 4; ++s) hv[s] *= gelu_grad_f(a[s]);
             }
-            const int col = n_t * 256 + wn * 128 + j * 32 + 8 * q + 4 * lhi;
-            *(uint2*)(crow + col) = make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+            *(uint2*)(crow + col) = pack4(hv);
           }
       }
     }
@@ -490,9 +554,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 
 hipError_t launch_gemm_bf16(int epi, const bf16_t* a, const int32_t* row_token, int a_rows,
                             const int32_t* offsets, const bf16_t* w0, const bf16_t* w1,
-                            bf16_t* c, float* partial, int E, int K, int N, int max_rows,
-                            hipStream_t s) {
-  const int outn = epi == EPI_SWIGLU ? 128 : 256;
+                            bf16_t* c, float* partial, const bf16_t* aux, bf16_t* c2, int E,
+                            int K, int N, int max_rows, hipStream_t s) {
+  const int outn = (epi == EPI_SWIGLU || epi == EPI_GU) ? 128 : 256;
   const bool split = epi == EPI_NONE && partial != nullptr;
   const long max_tiles = (long)((max_rows + BM - 1) / BM + E) * (N / outn);
   int grid = device_cus();
@@ -504,23 +568,196 @@ hipError_t launch_gemm_bf16(int epi, const bf16_t* a, const int32_t* row_token, 
   if (!split && need < grid) grid = (int)need;
   if (!split) partial = nullptr;
   const dim3 g(grid), b(256);
+#define MOE_GEMM(EP)                                                                          \
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EP>), g, b, 0, s, a, row_token, a_rows, offsets, \
+                     w0, w1, c, partial, aux, c2, E, K, N, max_rows)
   switch (epi) {
-    case EPI_SWIGLU:
-      hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EPI_SWIGLU>), g, b, 0, s, a, row_token, a_rows, offsets, w0, w1, c, partial, E, K, N, max_rows);
-      break;
-    case EPI_GELU:
-      hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EPI_GELU>), g, b, 0, s, a, row_token, a_rows, offsets, w0, w1, c, partial, E, K, N, max_rows);
-      break;
-    default:
-      hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EPI_NONE>), g, b, 0, s, a, row_token, a_rows, offsets, w0, w1, c, partial, E, K, N, max_rows);
-      break;
+    case EPI_SWIGLU: MOE_GEMM(EPI_SWIGLU); break;
+    case EPI_GELU: MOE_GEMM(EPI_GELU); break;
+    case EPI_GU: MOE_GEMM(EPI_GU); break;
+    case EPI_SWIGLU_BWD: MOE_GEMM(EPI_SWIGLU_BWD); break;
+    case EPI_GELU_BWD: MOE_GEMM(EPI_GELU_BWD); break;
+    case EPI_AH: MOE_GEMM(EPI_AH); break;
+    default: MOE_GEMM(EPI_NONE); break;
   }
+#undef MOE_GEMM
   if (split) {
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3(1024), dim3(256), 0, s, partial, offsets, c, E,
                        K, N, max_rows, grid);
   }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// Weight gradients, grouped over the reduction: for each expert e,
+//   C_e[M][N] = sum over the padded rows k of expert e of A[k][m] B[k][n]
+// (dW_down = h^T dy, dW_gate = x^T dg, dW_up = x^T du). A ([rows][lda]) and B ([rows][ldb])
+// are row-major with the reduction running over rows, so both go global -> LDS by DMA as
+// [64 k][2 x 128] tiles (the layout the forward kernel uses for weights) and reach the
+// MFMAs through transposing LDS reads. poff[e] .. poff[e+1] is expert e's padded row range,
+// a multiple of 128 rows (whole pairs of k-steps), possibly empty (then C_e = 0); pad rows
+// of B are zero. Same k-step pipeline as the forward kernel; tiles are ordered
+// (expert, m-tile, n-tile), so an XCD's blocks share A panels in L2.
+__global__ __launch_bounds__(256, 1) void grouped_wgrad_bf16_kernel(
+    const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ B, int ldb,
+    const int32_t* __restrict__ poff, bf16_t* __restrict__ C, int E, int M, int N) {
+  __shared__ __attribute__((aligned(1024))) bf16_t stage0[kStage];
+  __shared__ __attribute__((aligned(1024))) bf16_t stage1[kStage];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int MT = M / 256, NT = N / 256;
+  const int total = E * MT * NT;
+  const int xcd = blockIdx.x % kXcds, li = blockIdx.x / kXcds;
+  const int nper = gridDim.x / kXcds;
+  const int per = (total + kXcds - 1) / kXcds;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, lhi = lane >> 5;
+
+  // Transposing-read offsets (bytes within a stage): A in halves [0, 2) of the stage, B in
+  // halves [2, 4); fragment i / j covers 32 columns of the wave's 128.
+  const int krow0 = 8 * lhi + ((lane & 15) >> 2);
+  uint32_t a_rd[4], b_rd[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c32 = ((32 * i) >> 4) + ((lane >> 4) & 1);
+    const uint32_t in_half = (uint32_t)(krow0 * 256 + ((c32 ^ bswz(krow0)) << 5) + 8 * (lane & 3));
+    a_rd[i] = (uint32_t)(wm * kHalf * 2) + in_half;
+    b_rd[i] = (uint32_t)((BM * BK + wn * kHalf) * 2) + in_half;
+  }
+  auto tr_frag = [&](const char* p) {
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const lds_char*)p);
+    const v4i16 hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const lds_char*)(p + 4 * 256));
+    const v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  };
+  auto load_frags = [&](const bf16_t* stg, int kk, Frags& f) {
+    const char* st = (const char*)stg + kk * 16 * 256;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.a[i] = tr_frag(st + a_rd[i]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f.b[j] = tr_frag(st + b_rd[j]);
+  };
+  // DMA: instruction i of wave w fills rows k = (4w + i) * 4 .. + 3 of one [64][128] half;
+  // lane l loads 16-byte unit l & 15 of row 4(4w + i) + l / 16, stored swizzled.
+  uint32_t d_col[4];
+  int d_row[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int k = (wave * 4 + i) * 4 + (lane >> 4);
+    const int u = lane & 15;
+    d_row[i] = k;
+    d_col[i] = (uint32_t)((((u >> 1) ^ bswz(k)) << 4) + ((u & 1) << 3));
+  }
+
+  for (int it = li; it < per; it += nper) {
+    const int tile = xcd * per + it;
+    if (tile >= total) break;
+    const int e = tile / (MT * NT);
+    const int rem = tile - e * MT * NT;
+    const int m_t = rem / NT, n_t = rem - m_t * NT;
+    const int kbase = __builtin_amdgcn_readfirstlane(poff[e]);
+    const int KT = __builtin_amdgcn_readfirstlane((poff[e + 1] - poff[e]) / BK);
+    const bf16_t* Ab = A + m_t * 256;
+    const bf16_t* Bb = B + n_t * 256;
+    auto dma = [&](int kt, bf16_t* stg) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const size_t r = (size_t)(kbase + kt * BK + d_row[i]);
+        const bf16_t* a = Ab + r * lda + d_col[i];
+        const bf16_t* b = Bb + r * ldb + d_col[i];
+        lds_dma16(a, stg + (wave * 4 + i) * 512);
+        lds_dma16(a + 128, stg + kHalf + (wave * 4 + i) * 512);
+        lds_dma16(b, stg + BM * BK + (wave * 4 + i) * 512);
+        lds_dma16(b + 128, stg + BM * BK + kHalf + (wave * 4 + i) * 512);
+      }
+    };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    auto mfma16 = [&](const Frags& f) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+    };
+    // The forward kernel's k-slice phases: next slice's 16 LDS reads, then 16 MFMAs.
+    auto phase = [&](const bf16_t* stg, int kk_next, Frags& nxt, const Frags& cur) {
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      load_frags(stg, kk_next, nxt);
+      mfma16(cur);
+      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    Frags f0, f1;
+    auto kstep = [&](int kt, bf16_t* cur, bf16_t* nxt, auto refill, auto next) {
+      phase(cur, 1, f1, f0);
+      phase(cur, 2, f0, f1);
+      phase(cur, 3, f1, f0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (decltype(refill)::value) dma(kt + 2, cur);
+      if constexpr (decltype(next)::value) load_frags(nxt, 0, f0);
+      mfma16(f1);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    using yes = std::true_type;
+    using no = std::false_type;
+    if (KT > 0) {   // KT is even: the padded range is a multiple of 128 rows
+      dma(0, stage0);
+      __builtin_amdgcn_s_waitcnt(0);
+      dma(1, stage1);
+      __syncthreads();
+      load_frags(stage0, 0, f0);
+      int kt = 0;
+      for (; kt + 2 < KT; kt += 2) {
+        kstep(kt, stage0, stage1, yes{}, yes{});
+        kstep(kt + 1, stage1, stage0, yes{}, yes{});
+      }
+      kstep(kt, stage0, stage1, no{}, yes{});
+      kstep(kt + 1, stage1, stage0, no{}, no{});
+      __syncthreads();
+    }
+    // acc[i][j][4q+s]: row m = wm*128 + 32i + l32, column n = wn*128 + 32j + 8q + 4lhi + s
+    bf16_t* Ce = C + (size_t)e * M * N;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bf16_t* crow = Ce + (size_t)(m_t * 256 + wm * 128 + i * 32 + l32) * N + n_t * 256;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float v[4];
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2) v[s2] = acc[i][j][4 * q + s2];
+          *(uint2*)(crow + wn * 128 + j * 32 + 8 * q + 4 * lhi) = pack4(v);
+        }
+    }
+  }
+}
+
+hipError_t launch_wgrad_bf16(const bf16_t* a, int lda, const bf16_t* b, int ldb,
+                             const int32_t* poff, bf16_t* c, int E, int M, int N,
+                             hipStream_t s) {
+  int grid = device_cus();
+  grid = (grid / kXcds) * kXcds;
+  if (grid < kXcds) grid = kXcds;
+  const long need = (((long)E * (M / 256) * (N / 256) + kXcds - 1) / kXcds) * kXcds;
+  if (need < grid) grid = (int)need;
+  hipLaunchKernelGGL(grouped_wgrad_bf16_kernel, dim3(grid), dim3(256), 0, s, a, lda, b, ldb,
+                     poff, c, E, M, N);
   return hipGetLastError();
 }
 

@@ -37,7 +37,12 @@ hipError_t launch_permute(const void* x, int elem_bytes, const int32_t* topk_idx
                           int E, int k, int cap, hipStream_t s);
 
 // ---- grouped expert GEMMs (gemm.hip)
-enum Epilogue { EPI_SWIGLU = 0, EPI_GELU = 1, EPI_NONE = 2 };
+// Epilogues: SWIGLU h = silu(g) u; GELU h = gelu(a); NONE the product itself; GU the gate
+// and up pre-activations into a [rows, 2N] pair buffer and h into `c2`; AH a into c and
+// gelu(a) into `c2`; SWIGLU_BWD / GELU_BWD the activation's backward from the product dh and
+// the saved pre-activations in `aux` (SWIGLU_BWD writes the [dg | du] pair buffer).
+enum Epilogue { EPI_SWIGLU = 0, EPI_GELU = 1, EPI_NONE = 2, EPI_GU = 3, EPI_SWIGLU_BWD = 4,
+                EPI_GELU_BWD = 5, EPI_AH = 6 };
 // A row r of the expert-major operand is a[r], or a[row_token[r]] when row_token is given
 // (token rows gathered in place; indexes clamped into [0, a_rows)).
 // `partial` (EPI_NONE only; may be null): float32 scratch of kSplitPartialBytes for the
@@ -46,11 +51,38 @@ constexpr int kSplitMaxUnits = 256;   // K slices of one launch, at most
 constexpr size_t kSplitPartialBytes = (size_t)kSplitMaxUnits * 256 * 256 * 4;
 hipError_t launch_gemm_bf16(int epi, const bf16_t* a, const int32_t* row_token, int a_rows,
                             const int32_t* offsets, const bf16_t* w0, const bf16_t* w1,
-                            bf16_t* c, float* partial, int E, int K, int N, int max_rows,
-                            hipStream_t s);
+                            bf16_t* c, float* partial, const bf16_t* aux, bf16_t* c2, int E,
+                            int K, int N, int max_rows, hipStream_t s);
 hipError_t launch_gemm_f32(int epi, const float* a, const int32_t* row_token, int a_rows,
                            const int32_t* offsets, const float* w0, const float* w1, float* c,
                            int E, int K, int N, int max_rows, hipStream_t s);
+
+// Weight gradients C_e = A_e^T B_e over each expert's padded rows poff[e] .. poff[e+1]
+// (multiples of 128); A [rows][lda], B [rows][ldb] row-major; M, N multiples of 256.
+hipError_t launch_wgrad_bf16(const bf16_t* a, int lda, const bf16_t* b, int ldb,
+                             const int32_t* poff, bf16_t* c, int E, int M, int N,
+                             hipStream_t s);
+
+// ---- backward pass (backward.hip): padded row space, multiples of 128 rows per expert
+int bwd_padded_rows(int T, int k, int E);
+int bwd_wrouter_chunks(int T);
+hipError_t launch_bwd_prepare(const bf16_t* x, const int32_t* offsets, const int32_t* row_token,
+                              int32_t* poff, int32_t* prow_token, bf16_t* xP, int T, int H,
+                              int E, int k, hipStream_t s);
+hipError_t launch_bwd_combine(const bf16_t* dout, const bf16_t* y, const int32_t* slot_row,
+                              const int32_t* topk_idx, const float* topk_w,
+                              const int32_t* offsets, const int32_t* poff, bf16_t* dyP,
+                              float* dw, int T, int H, int E, int k, hipStream_t s);
+hipError_t launch_bwd_router(const float* logits, const int32_t* topk_idx, const float* dw,
+                             float* dL, int T, int E, int k, int renorm, hipStream_t s);
+hipError_t launch_bwd_dx(const bf16_t* dxP, const bf16_t* w_router, const float* dL,
+                         const int32_t* slot_row, const int32_t* topk_idx,
+                         const int32_t* offsets, const int32_t* poff, bf16_t* dx, int T, int H,
+                         int E, int k, hipStream_t s);
+hipError_t launch_bwd_wrouter(const bf16_t* x, const float* dL, float* part, float* bpart,
+                              float* dwr, float* dbias, int T, int H, int E, hipStream_t s);
+hipError_t launch_bwd_transpose(const bf16_t* in, bf16_t* out, int E, int R, int C,
+                                int out_rows, int row_off, hipStream_t s);
 
 // ---- combine (combine.hip)
 hipError_t launch_combine(int dtype_bf16, const void* y, const int32_t* slot_row,

@@ -72,6 +72,53 @@ template <typename P> P* region(void* ws, const Layout& L, Region r) {
   return reinterpret_cast<P*>(static_cast<char*>(ws) + L.off[r]);
 }
 
+// ---- backward workspace: the padded row space of the backward (multiples of 128 rows per
+// expert), the recomputed activations, the gradients on their way and transposed weights.
+enum BRegion {
+  B_POFF, B_PROW, B_XP, B_GU, B_H, B_DY, B_DGU, B_DXP, B_DL, B_DW, B_WDT, B_WGUT, B_SPLIT,
+  B_WRPART, B_BPART, B_NUM
+};
+
+struct BLayout {
+  size_t off[B_NUM];
+  size_t size[B_NUM];
+  size_t total;
+};
+
+BLayout blayout_of(const moe_config* c) {
+  BLayout L{};
+  const size_t T = (size_t)c->tokens, H = (size_t)c->hidden, I = (size_t)c->inter;
+  const size_t E = (size_t)c->experts, k = (size_t)c->top_k;
+  const size_t P = (size_t)moe::bwd_padded_rows(c->tokens, c->top_k, c->experts);
+  const size_t pair = c->activation == MOE_ACT_SWIGLU ? 2 : 1;   // [g | u] or a
+  L.size[B_POFF] = (E + 1) * 4;
+  L.size[B_PROW] = P * 4;
+  L.size[B_XP] = P * H * 2;
+  L.size[B_GU] = P * pair * I * 2;
+  L.size[B_H] = P * I * 2;
+  L.size[B_DY] = P * H * 2;
+  L.size[B_DGU] = P * pair * I * 2;
+  L.size[B_DXP] = P * H * 2;
+  L.size[B_DL] = T * E * 4;
+  L.size[B_DW] = T * k * 4;
+  L.size[B_WDT] = E * H * I * 2;
+  L.size[B_WGUT] = E * pair * I * H * 2;
+  L.size[B_SPLIT] = moe::kSplitPartialBytes;
+  L.size[B_WRPART] = (size_t)moe::bwd_wrouter_chunks(c->tokens) * H * E * 4;
+  L.size[B_BPART] = (size_t)moe::bwd_wrouter_chunks(c->tokens) * E * 4;
+  size_t o = 0;
+  for (int r = 0; r < B_NUM; ++r) {
+    L.off[r] = o;
+    o += (L.size[r] + kAlign - 1) / kAlign * kAlign;
+  }
+  L.total = o;
+  return L;
+}
+
+template <typename P> P* bregion(void* ws, const BLayout& L, BRegion r) {
+  return reinterpret_cast<P*>(static_cast<char*>(ws) + L.off[r]);
+}
+
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 moe_status check_cfg(const moe_config* c) {
@@ -182,7 +229,7 @@ moe_status do_up(const moe_config* c, const void* a, const int32_t* row_token,
     return hip_status(moe::launch_gemm_bf16(
         epi, (const moe::bf16_t*)a, row_token, a_rows, offsets,
         (const moe::bf16_t*)(swiglu ? w_gate : w_up), (const moe::bf16_t*)w_up,
-        (moe::bf16_t*)h, nullptr, c->experts, c->hidden, c->inter, rows, s));
+        (moe::bf16_t*)h, nullptr, nullptr, nullptr, c->experts, c->hidden, c->inter, rows, s));
   return hip_status(moe::launch_gemm_f32(epi, (const float*)a, row_token, a_rows, offsets,
                                          (const float*)(swiglu ? w_gate : w_up),
                                          (const float*)w_up, (float*)h, c->experts, c->hidden,
@@ -196,8 +243,8 @@ moe_status do_down(const moe_config* c, const void* h, const int32_t* offsets,
   if (c->dtype == MOE_DTYPE_BF16)
     return hip_status(moe::launch_gemm_bf16(moe::EPI_NONE, (const moe::bf16_t*)h, nullptr, rows,
                                             offsets, (const moe::bf16_t*)w_down, nullptr,
-                                            (moe::bf16_t*)y, partial, c->experts, c->inter,
-                                            c->hidden, rows, s));
+                                            (moe::bf16_t*)y, partial, nullptr, nullptr,
+                                            c->experts, c->inter, c->hidden, rows, s));
   return hip_status(moe::launch_gemm_f32(moe::EPI_NONE, (const float*)h, nullptr, rows, offsets,
                                          (const float*)w_down, nullptr, (float*)y, c->experts,
                                          c->inter, c->hidden, rows, s));
@@ -371,6 +418,123 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
   MOE_TRY(do_up(cfg, x, row_token, offsets, w_gate, w_up, h, s));
   MOE_TRY(do_down(cfg, h, offsets, w_down, y, region<float>(ws, L, R_SPLIT), s));
   return do_combine(cfg, y, slot_row, w, out, s);
+}
+
+// The backward's tiles: bf16 only, I a multiple of 256 (256-wide gradient tiles over I).
+moe_status check_backward_cfg(const moe_config* c) {
+  MOE_TRY(check_cfg(c));
+  if (c->dtype != MOE_DTYPE_BF16 || c->inter % 256 != 0) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status moe_backward_workspace_size(const moe_config* cfg, size_t* bytes) {
+  MOE_TRY(check_backward_cfg(cfg));
+  if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
+  *bytes = blayout_of(cfg).total;
+  return MOE_OK;
+}
+
+moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_router,
+                        const void* w_gate, const void* w_up, const void* w_down,
+                        const void* dout, void* dx, float* dw_router, float* dgate_bias,
+                        void* dw_gate, void* dw_up, void* dw_down, void* ws, size_t ws_bytes,
+                        void* bws, size_t bws_bytes, moe_stream_t stream) {
+  MOE_TRY(check_backward_cfg(cfg));
+  if (cfg->tokens == 0) return MOE_OK;   // empty batch: nothing to read or write
+  const bool swiglu = cfg->activation == MOE_ACT_SWIGLU;
+  MOE_TRY(need(x, 16));
+  MOE_TRY(need(w_router, 16));
+  if (swiglu) MOE_TRY(need(w_gate, 16));
+  MOE_TRY(need(w_up, 16));
+  MOE_TRY(need(w_down, 16));
+  MOE_TRY(need(dout, 16));
+  MOE_TRY(need(dx, 16));
+  MOE_TRY(need(dw_router, 4));
+  if (dgate_bias != nullptr) MOE_TRY(need(dgate_bias, 4));
+  if (swiglu) MOE_TRY(need(dw_gate, 16));
+  MOE_TRY(need(dw_up, 16));
+  MOE_TRY(need(dw_down, 16));
+  MOE_TRY(check_ws(cfg, ws, ws_bytes));
+  if (bws == nullptr || !aligned(bws, 16)) return MOE_ERR_INVALID_ARG;
+  if (bws_bytes < blayout_of(cfg).total) return MOE_ERR_WORKSPACE;
+  using moe::bf16_t;
+  const Layout L = layout_of(cfg);
+  const BLayout B = blayout_of(cfg);
+  const hipStream_t s = (hipStream_t)stream;
+  const int T = cfg->tokens, H = cfg->hidden, I = cfg->inter, E = cfg->experts,
+            k = cfg->top_k;
+  const int P = moe::bwd_padded_rows(T, k, E);
+  // the forward's intermediates
+  const float* logits = region<float>(ws, L, R_LOGITS);
+  const int32_t* idx = region<int32_t>(ws, L, R_TOPK_IDX);
+  const float* w = region<float>(ws, L, R_TOPK_W);
+  const int32_t* offsets = region<int32_t>(ws, L, R_OFFSETS);
+  const int32_t* slot_row = region<int32_t>(ws, L, R_SLOT_ROW);
+  const int32_t* row_token = region<int32_t>(ws, L, R_ROW_TOKEN);
+  const bf16_t* y = region<bf16_t>(ws, L, R_Y_PERM);
+  // the backward's own
+  int32_t* poff = bregion<int32_t>(bws, B, B_POFF);
+  int32_t* prow = bregion<int32_t>(bws, B, B_PROW);
+  bf16_t* xP = bregion<bf16_t>(bws, B, B_XP);
+  bf16_t* gu = bregion<bf16_t>(bws, B, B_GU);
+  bf16_t* hP = bregion<bf16_t>(bws, B, B_H);
+  bf16_t* dyP = bregion<bf16_t>(bws, B, B_DY);
+  bf16_t* dgu = bregion<bf16_t>(bws, B, B_DGU);
+  bf16_t* dxP = bregion<bf16_t>(bws, B, B_DXP);
+  float* dL = bregion<float>(bws, B, B_DL);
+  float* dwj = bregion<float>(bws, B, B_DW);
+  bf16_t* wdT = bregion<bf16_t>(bws, B, B_WDT);
+  bf16_t* wguT = bregion<bf16_t>(bws, B, B_WGUT);
+  float* split = bregion<float>(bws, B, B_SPLIT);
+  const bf16_t* wg = (const bf16_t*)w_gate;
+  const bf16_t* wu = (const bf16_t*)w_up;
+  const bf16_t* wd = (const bf16_t*)w_down;
+
+  // padded row maps and the token rows in padded expert-major order
+  MOE_TRY(hip_status(moe::launch_bwd_prepare((const bf16_t*)x, offsets, row_token, poff, prow,
+                                             xP, T, H, E, k, s)));
+  // transposed weights: Wd^T [E][H][I]; [Wg^T; Wu^T] [E][2I][H] (GELU: Wu^T [E][I][H])
+  MOE_TRY(hip_status(moe::launch_bwd_transpose(wd, wdT, E, I, H, H, 0, s)));
+  if (swiglu) {
+    MOE_TRY(hip_status(moe::launch_bwd_transpose(wg, wguT, E, H, I, 2 * I, 0, s)));
+    MOE_TRY(hip_status(moe::launch_bwd_transpose(wu, wguT, E, H, I, 2 * I, I, s)));
+  } else {
+    MOE_TRY(hip_status(moe::launch_bwd_transpose(wu, wguT, E, H, I, I, 0, s)));
+  }
+  // recompute the up-projection: [g | u] and h (GELU: a and h)
+  if (swiglu)
+    MOE_TRY(hip_status(moe::launch_gemm_bf16(moe::EPI_GU, xP, nullptr, P, poff, wg, wu, gu,
+                                             nullptr, nullptr, hP, E, H, I, P, s)));
+  else
+    MOE_TRY(hip_status(moe::launch_gemm_bf16(moe::EPI_AH, xP, nullptr, P, poff, wu, nullptr, gu,
+                                             nullptr, nullptr, hP, E, H, I, P, s)));
+  // combine backward: dy (padded, zero pads) and the gate-weight gradients
+  MOE_TRY(hip_status(moe::launch_bwd_combine((const bf16_t*)dout, y, slot_row, idx, w, offsets,
+                                             poff, dyP, dwj, T, H, E, k, s)));
+  MOE_TRY(hip_status(moe::launch_bwd_router(logits, idx, dwj, dL, T, E, k,
+                                            cfg->renormalize != 0, s)));
+  // dh = dy Wd^T with the activation's backward fused: [dg | du] (GELU: da)
+  MOE_TRY(hip_status(moe::launch_gemm_bf16(swiglu ? moe::EPI_SWIGLU_BWD : moe::EPI_GELU_BWD,
+                                           dyP, nullptr, P, poff, wdT, nullptr, dgu, nullptr,
+                                           gu, nullptr, E, H, I, P, s)));
+  // dx rows = [dg | du] [Wg^T; Wu^T] (GELU: da Wu^T)
+  MOE_TRY(hip_status(moe::launch_gemm_bf16(moe::EPI_NONE, dgu, nullptr, P, poff, wguT, nullptr,
+                                           dxP, split, nullptr, nullptr, E,
+                                           swiglu ? 2 * I : I, H, P, s)));
+  MOE_TRY(hip_status(moe::launch_bwd_dx(dxP, (const bf16_t*)w_router, dL, slot_row, idx,
+                                        offsets, poff, (bf16_t*)dx, T, H, E, k, s)));
+  MOE_TRY(hip_status(moe::launch_bwd_wrouter((const bf16_t*)x, dL, bregion<float>(bws, B, B_WRPART),
+                                             bregion<float>(bws, B, B_BPART), dw_router,
+                                             dgate_bias, T, H, E, s)));
+  // weight gradients over each expert's padded rows
+  MOE_TRY(hip_status(moe::launch_wgrad_bf16(hP, I, dyP, H, poff, (bf16_t*)dw_down, E, I, H, s)));
+  if (swiglu) {
+    MOE_TRY(hip_status(moe::launch_wgrad_bf16(xP, H, dgu, 2 * I, poff, (bf16_t*)dw_gate, E, H,
+                                              I, s)));
+    return hip_status(moe::launch_wgrad_bf16(xP, H, dgu + I, 2 * I, poff, (bf16_t*)dw_up, E, H,
+                                             I, s));
+  }
+  return hip_status(moe::launch_wgrad_bf16(xP, H, dgu, I, poff, (bf16_t*)dw_up, E, H, I, s));
 }
 
 moe_status moe_workspace_view(const moe_config* cfg, void* ws, int32_t which, void** dev_ptr,

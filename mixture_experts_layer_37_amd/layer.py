@@ -58,6 +58,22 @@ class MoELayer:
                       out, self.ws, stream)
         return out
 
+    def backward(self, x: torch.Tensor, dout: torch.Tensor, stream=None) -> dict:
+        """moe_backward after the last ``forward`` on ``x``: a dict of gradient tensors."""
+        cfg, dev = self.cfg, self.device
+        if not hasattr(self, "bws"):
+            self.bws = torch.empty(L.moe_backward_workspace_size(self.c), dtype=torch.uint8,
+                                   device=dev)
+        g = dict(dx=torch.empty_like(x),
+                 dw_router=torch.empty((cfg.hidden, cfg.experts), dtype=torch.float32, device=dev),
+                 dbias=torch.empty(cfg.experts, dtype=torch.float32, device=dev),
+                 dw_gate=torch.empty_like(self.w_gate) if self.w_gate is not None else None,
+                 dw_up=torch.empty_like(self.w_up), dw_down=torch.empty_like(self.w_down))
+        L.moe_backward(self.c, x, self.w_router, self.w_gate, self.w_up, self.w_down, dout,
+                       g["dx"], g["dw_router"], g["dbias"], g["dw_gate"], g["dw_up"],
+                       g["dw_down"], self.ws, self.bws, stream)
+        return g
+
     def view(self, which: int) -> torch.Tensor:
         """Tensor aliasing one intermediate of the last forward inside the workspace."""
         ptr, nbytes = L.moe_workspace_view(self.c, self.ws, which)

@@ -353,7 +353,7 @@ def gelu_grad(z):
 
 def backward(x, w_router, bias, w_gate, w_up, w_down, dout, *, top_k: int, activation: str,
              capacity_factor: float = 0.0, renormalize: bool = True, routing: str = "topk",
-             threshold=None) -> dict:
+             threshold=None, logits=None) -> dict:
     """Gradients of sum(out * dout) with respect to x, W_router, the gate bias and the expert
     weights, in float64, for the layer of ``forward`` (reading R15: the expert choice is a
     fixed function of the logits, so no gradient flows through the selection itself; the
@@ -369,14 +369,16 @@ def backward(x, w_router, bias, w_gate, w_up, w_down, dout, *, top_k: int, activ
       weights          renormalised: dp_i = (dw_i - sum_j w_j dw_j) / sum_S p; raw: dp = dw
       softmax          dL = p (dp - sum_e p_e dp_e)
       gate GEMM        dW_router = x^T dL, dbias = sum_t dL, dx += dL W_router^T
-    Slots dropped by the capacity rule contribute dw = 0 but stay in the weights' sum."""
+    Slots dropped by the capacity rule contribute dw = 0 but stay in the weights' sum.
+    ``logits`` replaces the gate GEMM's output (as in ``forward``); the gate GEMM's own
+    gradients still use ``x`` and ``w_router``."""
     x = np.asarray(x, dtype=np.float64)
     dout = np.asarray(dout, dtype=np.float64)
     wr = np.asarray(w_router, dtype=np.float64)
     T, H = x.shape
     fwd = forward(x, wr, bias, w_gate, w_up, w_down, top_k=top_k, activation=activation,
                   capacity_factor=capacity_factor, renormalize=renormalize, routing=routing,
-                  threshold=threshold)
+                  threshold=threshold, logits=logits)
     L, idx, w = fwd["logits"], np.asarray(fwd["topk_idx"], np.int64), fwd["topk_w"]
     slot_row, offsets, row_token = fwd["slot_row"], fwd["offsets"], fwd["row_token"]
     E = L.shape[1]
