@@ -37,6 +37,8 @@ def parse_args():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
+    ap.add_argument("--backward", action="store_true",
+                    help="time a training step instead: moe_forward then moe_backward")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -92,6 +94,8 @@ def main():
     c = layer.c
     ws = layer.ws
     edt = x.dtype
+    if args.backward:
+        return backward_bench(args, cfg, layer, x)
     logits = torch.empty((T, E), dtype=torch.float32, device=dev)
     idx = torch.empty((T, k), dtype=torch.int32, device=dev)
     w = torch.empty((T, k), dtype=torch.float32, device=dev)
@@ -207,6 +211,64 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, inp, out, logits, idx, args.cpu_sample_tokens,
                                               result)
+    print(json.dumps(result), flush=True)
+
+
+def backward_bench(args, cfg, layer, x):
+    """One training step of the layer: moe_forward, then moe_backward on a seeded dout.
+    Reports tokens/s of the whole step, the forward and backward times (HIP events on the
+    stream both run on), and the backward's GEMM rate: recomputed up-projection 4NHI, dh
+    2NHI, dx 4NHI and the three weight gradients 6NHI flops over the N kept rows (SwiGLU)."""
+    import numpy as np
+    import torch
+
+    from mixture_experts_layer_37_amd import _lib as L
+    from mixture_experts_layer_37_amd import configs as C
+    from mixture_experts_layer_37_amd.inputs import f32_to_bf16_bits
+    from mixture_experts_layer_37_amd.layer import to_device
+
+    T, H, I = cfg.tokens, cfg.hidden, cfg.inter
+    rng = np.random.default_rng(args.seed + 1)
+    dout = to_device(cfg, f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32)))
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        layer.forward(x, stream=stream)
+        if ev: ev[1].record(stream)
+        g = layer.backward(x, dout, stream=stream)
+        if ev: ev[2].record(stream)
+        return g
+
+    print(f"[bench] backward: warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    print(f"[bench] backward: timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    n_kept = int(layer.view(L.MOE_WS_OFFSETS)[-1].item())
+    per_row = 16 if cfg.activation == C.SWIGLU else 12
+    bwd_flops = per_row * n_kept * H * I
+    result = {
+        "metric": "MoE layer training step (forward + backward) tokens/s at 1 GPU",
+        "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded inputs and dout)",
+        "config": {"workload": cfg.description + "; forward + backward", "tokens": T,
+                   "hidden": H, "inter": I, "experts": cfg.experts, "top_k": cfg.top_k,
+                   "routing": cfg.routing, "kept_rows": n_kept},
+        "forward_ms": fwd_ms, "backward_ms": bwd_ms,
+        "backward_gemm_flops": bwd_flops,
+        "backward_tflops": bwd_flops / (bwd_ms * 1e-3) / 1e12,
+        "backward_frac_of_peak": bwd_flops / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+    }
     print(json.dumps(result), flush=True)
 
 

@@ -299,25 +299,6 @@ __global__ __launch_bounds__(256) void bwd_wrouter_sum_kernel(
   }
 }
 
-// out[e][c][r] = in[e][r][c] for a [R][C] bf16 matrix per expert; out rows have stride
-// `ldo` and start `row_off` rows into each expert's block of `out_rows` rows (so two
-// transposes can be stacked). 64 x 64 tiles through LDS.
-__global__ __launch_bounds__(256) void bwd_transpose_kernel(const bf16_t* __restrict__ in,
-                                                            bf16_t* __restrict__ out, int R,
-                                                            int C, int out_rows, int row_off) {
-  __shared__ bf16_t tile[64][65];
-  const int e = blockIdx.z;
-  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  const bf16_t* src = in + (size_t)e * R * C;
-  bf16_t* dst = out + (size_t)e * out_rows * R + (size_t)row_off * R;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4)
-    if (r0 + i < R && c0 + tx < C) tile[i][tx] = src[(size_t)(r0 + i) * C + c0 + tx];
-  __syncthreads();
-  for (int i = ty; i < 64; i += 4)
-    if (c0 + i < C && r0 + tx < R) dst[(size_t)(c0 + i) * R + r0 + tx] = tile[tx][i];
-}
-
 // ---------------------------------------------------------------------------------------
 int bwd_padded_rows(int T, int k, int E) { return T * k + E * (kPadRows - 1); }
 
@@ -391,11 +372,5 @@ hipError_t launch_bwd_wrouter(const bf16_t* x, const float* dL, float* part, flo
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_transpose(const bf16_t* in, bf16_t* out, int E, int R, int C,
-                                int out_rows, int row_off, hipStream_t s) {
-  hipLaunchKernelGGL(bwd_transpose_kernel, dim3((C + 63) / 64, (R + 63) / 64, E), dim3(256), 0,
-                     s, in, out, R, C, out_rows, row_off);
-  return hipGetLastError();
-}
 
 }  // namespace moe

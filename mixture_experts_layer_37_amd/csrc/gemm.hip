@@ -194,7 +194,7 @@ constexpr int kStage = BM * BK + 2 * kHalf;      // elements of one LDS stage (6
 
 // A rows: row r of the expert-major operand is A[r] (row_token == nullptr) or, with the
 // permute gather fused in, token row A[row_token[r]] (clamped into [0, a_rows)).
-template <int EPI>
+template <int EPI, bool BT>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ row_token, int a_rows,
     const int32_t* __restrict__ offsets, const bf16_t* __restrict__ W0,
@@ -213,6 +213,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // Two-matrix tiles (gate and up columns of the same outputs) or one matrix of 256 columns.
   constexpr bool kTwoMat = (EPI == EPI_SWIGLU || EPI == EPI_GU);
+  static_assert(!(BT && kTwoMat), "transposed weights: single-matrix epilogues only");
   constexpr int OUTN = kTwoMat ? 128 : 256;   // output columns per tile
   // Row strides of C and of the epilogue's second input (aux): the gate/up pair buffers
   // [rows, 2N] hold the gate half in columns [0, N) and the up half in [N, 2N).
@@ -245,6 +246,14 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   // B fragment (kk, j): 8 consecutive k of one weight column per lane from two
   // ds_read_b64_tr_b16 (rows krow0 + 16 kk and krow0 + 16 kk + 4). The swizzle depends on
   // k & 3 only, so kk is an immediate offset.
+  // With BT (weights given transposed, [N][K] with K contiguous) B sits in LDS like A,
+  // [256 n][64 k] swizzled, and its fragments are single ds_read_b128 as well.
+  uint32_t b_rd_bt[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int n = wn * 128 + l32;
+    b_rd_bt[kk] = (uint32_t)((BM * BK + n * BK) * 2 + (((kk * 2 + lhi) ^ swz(n)) << 4));
+  }
   uint32_t b_rd[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -264,14 +273,22 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
       const uint32_t off = a_rd[kk] ^ ((i & 1) << 6);
       f.a[i] = *(const bf16x8*)(st + off + i * 32 * BK * 2);
     }
+    if constexpr (BT) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const char* p = st + b_rd[j] + kk * 16 * 256;
-      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const lds_char*)p);
-      const v4i16 hi =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const lds_char*)(p + 4 * 256));
-      const v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      f.b[j] = __builtin_bit_cast(bf16x8, v);
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t off = b_rd_bt[kk] ^ ((j & 1) << 6);
+        f.b[j] = *(const bf16x8*)(st + off + j * 32 * BK * 2);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const char* p = st + b_rd[j] + kk * 16 * 256;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const lds_char*)p);
+        const v4i16 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const lds_char*)(p + 4 * 256));
+        const v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        f.b[j] = __builtin_bit_cast(bf16x8, v);
+      }
     }
   };
 
@@ -319,16 +336,36 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
       const int ncol = (((u >> 1) ^ bswz(k)) << 4) + ((u & 1) << 3);
       b_src[i] = (uint32_t)(k * N * 2 + ncol * 2);
     }
+    // BT: B^T rows n of this tile, K-contiguous, in one or two K parts (W0 for k < Ks,
+    // W1 for k >= Ks; each [E][N][Ks]); sources like A's, as byte offsets.
+    const int Ks = (BT && W1 != nullptr) ? K / 2 : K;
+    uint32_t bt_src[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = wave * 64 + i * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ swz(r);
+      bt_src[i] = (uint32_t)((n_t * 256 + r) * Ks * 2 + c * 16);
+    }
+    const char* Bt0 = (const char*)(W0 + (size_t)e * N * Ks);
+    const char* Bt1 = BT && W1 != nullptr ? (const char*)(W1 + (size_t)e * N * Ks) : Bt0;
 
     auto dma = [&](int kt, bf16_t* stg) {
       const uint32_t kA = (uint32_t)(kt * BK * 2);
       const size_t kB = (size_t)kt * BK * N * 2;
 #pragma unroll
       for (int i = 0; i < 8; ++i) lds_dma16(a_src[i] + kA, stg + (wave * 8 + i) * 512);
+      if constexpr (BT) {
+        const int k0 = kt * BK;
+        const char* bb = k0 < Ks ? Bt0 + k0 * 2 : Bt1 + (k0 - Ks) * 2;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        lds_dma16((const char*)Bh0 + kB + b_src[i], stg + BM * BK + (wave * 4 + i) * 512);
-        lds_dma16((const char*)Bh1 + kB + b_src[i], stg + BM * BK + kHalf + (wave * 4 + i) * 512);
+        for (int i = 0; i < 8; ++i) lds_dma16(bb + bt_src[i], stg + BM * BK + (wave * 8 + i) * 512);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          lds_dma16((const char*)Bh0 + kB + b_src[i], stg + BM * BK + (wave * 4 + i) * 512);
+          lds_dma16((const char*)Bh1 + kB + b_src[i],
+                    stg + BM * BK + kHalf + (wave * 4 + i) * 512);
+        }
       }
     };
 
@@ -568,9 +605,9 @@ hipError_t launch_gemm_bf16(int epi, const bf16_t* a, const int32_t* row_token, 
   if (!split && need < grid) grid = (int)need;
   if (!split) partial = nullptr;
   const dim3 g(grid), b(256);
-#define MOE_GEMM(EP)                                                                          \
-  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EP>), g, b, 0, s, a, row_token, a_rows, offsets, \
-                     w0, w1, c, partial, aux, c2, E, K, N, max_rows)
+#define MOE_GEMM(EP)                                                                        \
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EP, false>), g, b, 0, s, a, row_token, a_rows, \
+                     offsets, w0, w1, c, partial, aux, c2, E, K, N, max_rows)
   switch (epi) {
     case EPI_SWIGLU: MOE_GEMM(EPI_SWIGLU); break;
     case EPI_GELU: MOE_GEMM(EPI_GELU); break;
@@ -581,6 +618,38 @@ hipError_t launch_gemm_bf16(int epi, const bf16_t* a, const int32_t* row_token, 
     default: MOE_GEMM(EPI_NONE); break;
   }
 #undef MOE_GEMM
+  if (split) {
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(1024), dim3(256), 0, s, partial, offsets, c, E,
+                       K, N, max_rows, grid);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_bf16_bt(int epi, const bf16_t* a, const int32_t* offsets,
+                               const bf16_t* w0, const bf16_t* w1, bf16_t* c, float* partial,
+                               const bf16_t* aux, int E, int K, int N, int max_rows,
+                               hipStream_t s) {
+  const bool split = epi == EPI_NONE && partial != nullptr;
+  const long max_tiles = (long)((max_rows + BM - 1) / BM + E) * (N / 256);
+  int grid = device_cus();
+  grid = (grid / kXcds) * kXcds;
+  if (grid < kXcds) grid = kXcds;
+  const long need = ((max_tiles + kXcds - 1) / kXcds) * kXcds;
+  if (!split && need < grid) grid = (int)need;
+  if (!split) partial = nullptr;
+  const dim3 g(grid), b(256);
+#define MOE_GEMM_BT(EP)                                                                        \
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EP, true>), g, b, 0, s, a, nullptr, max_rows,    \
+                     offsets, w0, w1, c, partial, aux, nullptr, E, K, N, max_rows)
+  switch (epi) {
+    case EPI_SWIGLU_BWD: MOE_GEMM_BT(EPI_SWIGLU_BWD); break;
+    case EPI_GELU_BWD: MOE_GEMM_BT(EPI_GELU_BWD); break;
+    case EPI_NONE: MOE_GEMM_BT(EPI_NONE); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef MOE_GEMM_BT
   if (split) {
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;

@@ -57,6 +57,13 @@ hipError_t launch_gemm_f32(int epi, const float* a, const int32_t* row_token, in
                            const int32_t* offsets, const float* w0, const float* w1, float* c,
                            int E, int K, int N, int max_rows, hipStream_t s);
 
+// As launch_gemm_bf16 with the weights given transposed: w0 (and w1) [E][N][Ks] with K
+// contiguous; with w1, k < K/2 reads w0 and k >= K/2 reads w1 (Ks = K/2), else Ks = K.
+// Single-matrix epilogues (NONE with the split-K tail, SWIGLU_BWD, GELU_BWD); A plain rows.
+hipError_t launch_gemm_bf16_bt(int epi, const bf16_t* a, const int32_t* offsets,
+                               const bf16_t* w0, const bf16_t* w1, bf16_t* c, float* partial,
+                               const bf16_t* aux, int E, int K, int N, int max_rows,
+                               hipStream_t s);
 // Weight gradients C_e = A_e^T B_e over each expert's padded rows poff[e] .. poff[e+1]
 // (multiples of 128); A [rows][lda], B [rows][ldb] row-major; M, N multiples of 256.
 hipError_t launch_wgrad_bf16(const bf16_t* a, int lda, const bf16_t* b, int ldb,
@@ -81,8 +88,6 @@ hipError_t launch_bwd_dx(const bf16_t* dxP, const bf16_t* w_router, const float*
                          int E, int k, hipStream_t s);
 hipError_t launch_bwd_wrouter(const bf16_t* x, const float* dL, float* part, float* bpart,
                               float* dwr, float* dbias, int T, int H, int E, hipStream_t s);
-hipError_t launch_bwd_transpose(const bf16_t* in, bf16_t* out, int E, int R, int C,
-                                int out_rows, int row_off, hipStream_t s);
 
 // ---- combine (combine.hip)
 hipError_t launch_combine(int dtype_bf16, const void* y, const int32_t* slot_row,

@@ -73,10 +73,10 @@ template <typename P> P* region(void* ws, const Layout& L, Region r) {
 }
 
 // ---- backward workspace: the padded row space of the backward (multiples of 128 rows per
-// expert), the recomputed activations, the gradients on their way and transposed weights.
+// expert), the recomputed activations and the gradients on their way.
 enum BRegion {
-  B_POFF, B_PROW, B_XP, B_GU, B_H, B_DY, B_DGU, B_DXP, B_DL, B_DW, B_WDT, B_WGUT, B_SPLIT,
-  B_WRPART, B_BPART, B_NUM
+  B_POFF, B_PROW, B_XP, B_GU, B_H, B_DY, B_DGU, B_DXP, B_DL, B_DW, B_SPLIT, B_WRPART, B_BPART,
+  B_NUM
 };
 
 struct BLayout {
@@ -101,8 +101,6 @@ BLayout blayout_of(const moe_config* c) {
   L.size[B_DXP] = P * H * 2;
   L.size[B_DL] = T * E * 4;
   L.size[B_DW] = T * k * 4;
-  L.size[B_WDT] = E * H * I * 2;
-  L.size[B_WGUT] = E * pair * I * H * 2;
   L.size[B_SPLIT] = moe::kSplitPartialBytes;
   L.size[B_WRPART] = (size_t)moe::bwd_wrouter_chunks(c->tokens) * H * E * 4;
   L.size[B_BPART] = (size_t)moe::bwd_wrouter_chunks(c->tokens) * E * 4;
@@ -483,8 +481,6 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
   bf16_t* dxP = bregion<bf16_t>(bws, B, B_DXP);
   float* dL = bregion<float>(bws, B, B_DL);
   float* dwj = bregion<float>(bws, B, B_DW);
-  bf16_t* wdT = bregion<bf16_t>(bws, B, B_WDT);
-  bf16_t* wguT = bregion<bf16_t>(bws, B, B_WGUT);
   float* split = bregion<float>(bws, B, B_SPLIT);
   const bf16_t* wg = (const bf16_t*)w_gate;
   const bf16_t* wu = (const bf16_t*)w_up;
@@ -493,14 +489,6 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
   // padded row maps and the token rows in padded expert-major order
   MOE_TRY(hip_status(moe::launch_bwd_prepare((const bf16_t*)x, offsets, row_token, poff, prow,
                                              xP, T, H, E, k, s)));
-  // transposed weights: Wd^T [E][H][I]; [Wg^T; Wu^T] [E][2I][H] (GELU: Wu^T [E][I][H])
-  MOE_TRY(hip_status(moe::launch_bwd_transpose(wd, wdT, E, I, H, H, 0, s)));
-  if (swiglu) {
-    MOE_TRY(hip_status(moe::launch_bwd_transpose(wg, wguT, E, H, I, 2 * I, 0, s)));
-    MOE_TRY(hip_status(moe::launch_bwd_transpose(wu, wguT, E, H, I, 2 * I, I, s)));
-  } else {
-    MOE_TRY(hip_status(moe::launch_bwd_transpose(wu, wguT, E, H, I, I, 0, s)));
-  }
   // recompute the up-projection: [g | u] and h (GELU: a and h)
   if (swiglu)
     MOE_TRY(hip_status(moe::launch_gemm_bf16(moe::EPI_GU, xP, nullptr, P, poff, wg, wu, gu,
@@ -513,14 +501,16 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
                                              poff, dyP, dwj, T, H, E, k, s)));
   MOE_TRY(hip_status(moe::launch_bwd_router(logits, idx, dwj, dL, T, E, k,
                                             cfg->renormalize != 0, s)));
-  // dh = dy Wd^T with the activation's backward fused: [dg | du] (GELU: da)
-  MOE_TRY(hip_status(moe::launch_gemm_bf16(swiglu ? moe::EPI_SWIGLU_BWD : moe::EPI_GELU_BWD,
-                                           dyP, nullptr, P, poff, wdT, nullptr, dgu, nullptr,
-                                           gu, nullptr, E, H, I, P, s)));
-  // dx rows = [dg | du] [Wg^T; Wu^T] (GELU: da Wu^T)
-  MOE_TRY(hip_status(moe::launch_gemm_bf16(moe::EPI_NONE, dgu, nullptr, P, poff, wguT, nullptr,
-                                           dxP, split, nullptr, nullptr, E,
-                                           swiglu ? 2 * I : I, H, P, s)));
+  // dh = dy Wd^T with the activation's backward fused: [dg | du] (GELU: da). Wd[e] [I][H]
+  // is Wd^T with K contiguous, read as is (transposed-weight mode).
+  MOE_TRY(hip_status(moe::launch_gemm_bf16_bt(swiglu ? moe::EPI_SWIGLU_BWD : moe::EPI_GELU_BWD,
+                                              dyP, poff, wd, nullptr, dgu, nullptr, gu, E, H, I,
+                                              P, s)));
+  // dx rows = [dg | du] [Wg^T; Wu^T] (GELU: da Wu^T): one K = 2I product reading Wg[e] and
+  // Wu[e] ([H][I] each, K contiguous) as the two K halves of the transposed weight
+  MOE_TRY(hip_status(moe::launch_gemm_bf16_bt(moe::EPI_NONE, dgu, poff, swiglu ? wg : wu,
+                                              swiglu ? wu : nullptr, dxP, split, nullptr, E,
+                                              swiglu ? 2 * I : I, H, P, s)));
   MOE_TRY(hip_status(moe::launch_bwd_dx(dxP, (const bf16_t*)w_router, dL, slot_row, idx,
                                         offsets, poff, (bf16_t*)dx, T, H, E, k, s)));
   MOE_TRY(hip_status(moe::launch_bwd_wrouter((const bf16_t*)x, dL, bregion<float>(bws, B, B_WRPART),

@@ -35,6 +35,8 @@ CASES = {
                                  experts=64, top_k=8),
     "one_expert": C.SMALL.with_(name="bwd_one_expert", tokens=333, hidden=256, inter=256,
                                 experts=1, top_k=1, bias=None),
+    # the bench workload's layer shape (H 4096, I 14336, 8 experts, top-2) on 1024 tokens
+    "mixtral_shape": C.MIXTRAL.with_(name="bwd_mixtral_shape", tokens=1024),
 }
 
 
