@@ -215,10 +215,11 @@ def main():
 
 
 def backward_bench(args, cfg, layer, x):
-    """One training step of the layer: moe_forward, then moe_backward on a seeded dout.
-    Reports tokens/s of the whole step, the forward and backward times (HIP events on the
-    stream both run on), and the backward's GEMM rate: recomputed up-projection 4NHI, dh
-    2NHI, dx 4NHI and the three weight gradients 6NHI flops over the N kept rows (SwiGLU)."""
+    """One training step of the layer: moe_forward_train (the forward keeping GEMM 1's
+    pre-activations), then moe_backward on a seeded dout. Reports tokens/s of the whole step,
+    the forward and backward times (HIP events on the stream both run on), and the
+    backward's GEMM rate: dh 2NHI, dx 4NHI and the three weight gradients 6NHI flops over the
+    N kept rows (SwiGLU; GELU dh 2NHI, dx 2NHI, weight gradients 4NHI)."""
     import numpy as np
     import torch
 
@@ -234,7 +235,7 @@ def backward_bench(args, cfg, layer, x):
 
     def step(ev=None):
         if ev: ev[0].record(stream)
-        layer.forward(x, stream=stream)
+        layer.forward_train(x, stream=stream)   # keeps GEMM 1's pre-activations
         if ev: ev[1].record(stream)
         g = layer.backward(x, dout, stream=stream)
         if ev: ev[2].record(stream)
@@ -254,7 +255,7 @@ def backward_bench(args, cfg, layer, x):
     fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
     bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
     n_kept = int(layer.view(L.MOE_WS_OFFSETS)[-1].item())
-    per_row = 16 if cfg.activation == C.SWIGLU else 12
+    per_row = 12 if cfg.activation == C.SWIGLU else 8
     bwd_flops = per_row * n_kept * H * I
     result = {
         "metric": "MoE layer training step (forward + backward) tokens/s at 1 GPU",

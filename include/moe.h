@@ -201,10 +201,13 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
  * backward runs on the selected experts only). The expert choice (top-k, threshold,
  * capacity) carries no gradient; the gate weights' dependence on the logits is exact. There
  * is no auxiliary load-balancing loss (the pages give no formula for one).
- *   ws, ws_bytes   the workspace of a moe_forward call with the same cfg, x and weights,
- *                  made on the same stream before this call: its routing, row maps and
- *                  y_perm are reused (so is its gate bias, through the logits)
+ *   ws, ws_bytes   the workspace of a moe_forward (or moe_forward_train) call with the same
+ *                  cfg, x and weights, made on the same stream before this call: its
+ *                  routing, row maps and y_perm are reused (so is its gate bias, through the
+ *                  logits)
  *   bws, bws_bytes backward scratch, at least moe_backward_workspace_size bytes
+ *   saved          nonzero: that call was moe_forward_train with this bws, which kept the
+ *                  up-projection's pre-activations there; zero: they are recomputed here
  *   dout [T,H] bf16 in; dx [T,H] bf16 out; dw_router [H,E] float32 out; dgate_bias [E]
  *   float32 out or NULL; dw_gate (SwiGLU only; NULL for GELU), dw_up [E,H,I] and dw_down
  *   [E,I,H] bf16 out (float32 accumulation, rounded once)
@@ -216,7 +219,16 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
                         const void* w_gate, const void* w_up, const void* w_down,
                         const void* dout, void* dx, float* dw_router, float* dgate_bias,
                         void* dw_gate, void* dw_up, void* dw_down, void* ws, size_t ws_bytes,
-                        void* bws, size_t bws_bytes, moe_stream_t stream);
+                        void* bws, size_t bws_bytes, int32_t saved, moe_stream_t stream);
+
+/* moe_forward for training: the same output, and GEMM 1 also keeps its pre-activations
+ * ([g | u] per kept row; GELU: a) in `bws` for a following moe_backward(..., saved = 1), which
+ * then skips recomputing the up-projection. Same arguments as moe_forward plus the backward
+ * scratch; bf16 layers with I a multiple of 256 (else MOE_ERR_UNSUPPORTED). */
+moe_status moe_forward_train(const moe_config* cfg, const void* x, const void* w_router,
+                             const float* gate_bias, const void* w_gate, const void* w_up,
+                             const void* w_down, void* out, void* ws, size_t ws_bytes,
+                             void* bws, size_t bws_bytes, moe_stream_t stream);
 
 /* Where moe_forward keeps an intermediate inside `ws` (device address and byte size). */
 enum {

@@ -27,7 +27,7 @@ MOE_ROUTE_TOPK, MOE_ROUTE_THRESHOLD = 0, 1
 
 EXPORTS = ("moe_workspace_size", "moe_capacity", "moe_route", "moe_permute", "moe_expert_up",
            "moe_expert_up_rows", "moe_expert_down", "moe_grouped_ffn", "moe_combine",
-           "moe_forward", "moe_backward_workspace_size", "moe_backward",
+           "moe_forward", "moe_forward_train", "moe_backward_workspace_size", "moe_backward",
            "moe_workspace_view", "moe_read_device_status", "moe_status_string",
            "moe_last_hip_error")
 
@@ -74,7 +74,9 @@ def lib():
             "moe_forward": [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, c_size_t, vp],
             "moe_backward_workspace_size": [cfgp, POINTER(c_size_t)],
             "moe_backward": [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, c_size_t,
-                             vp, c_size_t, vp],
+                             vp, c_size_t, c_int32, vp],
+            "moe_forward_train": [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, c_size_t, vp, c_size_t,
+                                  vp],
             "moe_workspace_view": [cfgp, vp, c_int32, POINTER(c_void_p), POINTER(c_size_t)],
             "moe_read_device_status": [cfgp, vp, c_int32, vp, POINTER(c_int32)],
         }
@@ -203,12 +205,21 @@ def moe_backward_workspace_size(cfg) -> int:
 
 
 def moe_backward(cfg, x, w_router, w_gate, w_up, w_down, dout, dx, dw_router, dgate_bias,
-                 dw_gate, dw_up, dw_down, ws, bws, stream=None):
-    """Gradients of the layer; ``ws`` is the workspace of the moe_forward call it follows."""
+                 dw_gate, dw_up, dw_down, ws, bws, saved=False, stream=None):
+    """Gradients of the layer; ``ws`` is the workspace of the moe_forward call it follows
+    (``saved``: that call was moe_forward_train with this ``bws``)."""
     _check("moe_backward", lib().moe_backward(
         ctypes.byref(_as_cfg(cfg)), _ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up),
         _ptr(w_down), _ptr(dout), _ptr(dx), _ptr(dw_router), _ptr(dgate_bias), _ptr(dw_gate),
         _ptr(dw_up), _ptr(dw_down), _ptr(ws), _nbytes(ws), _ptr(bws), _nbytes(bws),
+        1 if saved else 0, _stream(stream)))
+
+
+def moe_forward_train(cfg, x, w_router, gate_bias, w_gate, w_up, w_down, out, ws, bws,
+                      stream=None):
+    _check("moe_forward_train", lib().moe_forward_train(
+        ctypes.byref(_as_cfg(cfg)), _ptr(x), _ptr(w_router), _ptr(gate_bias), _ptr(w_gate),
+        _ptr(w_up), _ptr(w_down), _ptr(out), _ptr(ws), _nbytes(ws), _ptr(bws), _nbytes(bws),
         _stream(stream)))
 
 

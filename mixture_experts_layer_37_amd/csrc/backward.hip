@@ -58,6 +58,22 @@ __global__ __launch_bounds__(256) void bwd_pad_rows_kernel(
   for (int c = lane; c < row_vecs; c += 64) d[c] = s[c];
 }
 
+// One wave per padded row r < poff[E]: dst[r] = src[the compact row of r] (pad rows repeat
+// the expert's last kept row).
+__global__ __launch_bounds__(256) void bwd_pad_copy_kernel(
+    const uint4* __restrict__ src, uint4* __restrict__ dst, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ poff, int E, int nrows, int prows_max, int row_vecs) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + wave;
+  if (r >= prows_max || r >= poff[E]) return;
+  const int e = find_padded_expert(poff, E, r);
+  const int m = offsets[e + 1] - offsets[e];
+  const int c = min(max(offsets[e] + min(r - poff[e], m - 1), 0), nrows - 1);
+  const uint4* s = src + (size_t)c * row_vecs;
+  uint4* d = dst + (size_t)r * row_vecs;
+  for (int i = lane; i < row_vecs; i += 64) d[i] = s[i];
+}
+
 // Combine backward, one wave per token: for each kept slot j (row r of expert e),
 // dyP[padded r] = w_j dout[t] (bf16) and dw[t,j] = <dout[t], y[r]> (float32, lane partial
 // sums in column order, then a fixed butterfly); dw = 0 for slots not kept.
@@ -312,6 +328,15 @@ hipError_t launch_bwd_prepare(const bf16_t* x, const int32_t* offsets, const int
   hipLaunchKernelGGL(bwd_pad_rows_kernel, dim3((prows + 3) / 4), dim3(256), 0, s,
                      (const uint4*)x, offsets, poff, row_token, prow_token, (uint4*)xP, E, T,
                      T * k, prows, H / 8);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_pad_copy(const bf16_t* src, bf16_t* dst, const int32_t* offsets,
+                               const int32_t* poff, int T, int k, int E, int row_vecs,
+                               hipStream_t s) {
+  const int prows = bwd_padded_rows(T, k, E);
+  hipLaunchKernelGGL(bwd_pad_copy_kernel, dim3((prows + 3) / 4), dim3(256), 0, s,
+                     (const uint4*)src, (uint4*)dst, offsets, poff, E, T * k, prows, row_vecs);
   return hipGetLastError();
 }
 

@@ -199,8 +199,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ row_token, int a_rows,
     const int32_t* __restrict__ offsets, const bf16_t* __restrict__ W0,
     const bf16_t* __restrict__ W1, bf16_t* __restrict__ C, float* __restrict__ partial,
-    const bf16_t* __restrict__ aux, bf16_t* __restrict__ C2, int E, int K, int N,
-    int max_rows) {
+    const bf16_t* __restrict__ aux, const int32_t* __restrict__ aux_off,
+    bf16_t* __restrict__ C2, int E, int K, int N, int max_rows) {
   // Two stages in two distinct LDS objects: the compiler can then tell a DMA into one
   // stage from reads of the other and does not make those reads wait for the DMA.
   __shared__ __attribute__((aligned(1024))) bf16_t stage0[kStage];
@@ -484,7 +484,15 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
             }
           }
       } else {
-        const bf16_t* arow = aux + (size_t)(row0 + m) * ldaux;
+        // aux rows: the C rows themselves, or (aux_off given) the compact rows of a layout
+        // without padding: row r of expert e maps to r - offsets[e] + aux_off[e], and pad
+        // rows to the expert's last row (their dh is zero)
+        size_t ar = (size_t)(row0 + m);
+        if (aux_off != nullptr) {
+          const int lo = aux_off[e], hi = aux_off[e + 1];
+          ar = (size_t)max(min(row0 + m - s_off[e] + lo, hi - 1), lo);
+        }
+        const bf16_t* arow = aux + ar * ldaux;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -522,6 +530,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
               unpack4(*(const uint2*)(arow + col), a);
 #pragma unroll
               for (int s = 0; s < 4; ++s) hv[s] *= gelu_grad_f(a[s]);
+
             }
             *(uint2*)(crow + col) = pack4(hv);
           }
@@ -607,7 +616,7 @@ hipError_t launch_gemm_bf16(int epi, const bf16_t* a, const int32_t* row_token, 
   const dim3 g(grid), b(256);
 #define MOE_GEMM(EP)                                                                        \
   hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EP, false>), g, b, 0, s, a, row_token, a_rows, \
-                     offsets, w0, w1, c, partial, aux, c2, E, K, N, max_rows)
+                     offsets, w0, w1, c, partial, aux, nullptr, c2, E, K, N, max_rows)
   switch (epi) {
     case EPI_SWIGLU: MOE_GEMM(EPI_SWIGLU); break;
     case EPI_GELU: MOE_GEMM(EPI_GELU); break;
@@ -629,8 +638,8 @@ hipError_t launch_gemm_bf16(int epi, const bf16_t* a, const int32_t* row_token, 
 
 hipError_t launch_gemm_bf16_bt(int epi, const bf16_t* a, const int32_t* offsets,
                                const bf16_t* w0, const bf16_t* w1, bf16_t* c, float* partial,
-                               const bf16_t* aux, int E, int K, int N, int max_rows,
-                               hipStream_t s) {
+                               const bf16_t* aux, const int32_t* aux_off, int E, int K, int N,
+                               int max_rows, hipStream_t s) {
   const bool split = epi == EPI_NONE && partial != nullptr;
   const long max_tiles = (long)((max_rows + BM - 1) / BM + E) * (N / 256);
   int grid = device_cus();
@@ -642,7 +651,7 @@ hipError_t launch_gemm_bf16_bt(int epi, const bf16_t* a, const int32_t* offsets,
   const dim3 g(grid), b(256);
 #define MOE_GEMM_BT(EP)                                                                        \
   hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EP, true>), g, b, 0, s, a, nullptr, max_rows,    \
-                     offsets, w0, w1, c, partial, aux, nullptr, E, K, N, max_rows)
+                     offsets, w0, w1, c, partial, aux, aux_off, nullptr, E, K, N, max_rows)
   switch (epi) {
     case EPI_SWIGLU_BWD: MOE_GEMM_BT(EPI_SWIGLU_BWD); break;
     case EPI_GELU_BWD: MOE_GEMM_BT(EPI_GELU_BWD); break;

@@ -60,10 +60,12 @@ hipError_t launch_gemm_f32(int epi, const float* a, const int32_t* row_token, in
 // As launch_gemm_bf16 with the weights given transposed: w0 (and w1) [E][N][Ks] with K
 // contiguous; with w1, k < K/2 reads w0 and k >= K/2 reads w1 (Ks = K/2), else Ks = K.
 // Single-matrix epilogues (NONE with the split-K tail, SWIGLU_BWD, GELU_BWD); A plain rows.
+// aux_off (may be null): the aux rows are compact, row r of expert e at
+// r - offsets[e] + aux_off[e] (pad rows: the expert's last row).
 hipError_t launch_gemm_bf16_bt(int epi, const bf16_t* a, const int32_t* offsets,
                                const bf16_t* w0, const bf16_t* w1, bf16_t* c, float* partial,
-                               const bf16_t* aux, int E, int K, int N, int max_rows,
-                               hipStream_t s);
+                               const bf16_t* aux, const int32_t* aux_off, int E, int K, int N,
+                               int max_rows, hipStream_t s);
 // Weight gradients C_e = A_e^T B_e over each expert's padded rows poff[e] .. poff[e+1]
 // (multiples of 128); A [rows][lda], B [rows][ldb] row-major; M, N multiples of 256.
 hipError_t launch_wgrad_bf16(const bf16_t* a, int lda, const bf16_t* b, int ldb,
@@ -76,6 +78,11 @@ int bwd_wrouter_chunks(int T);
 hipError_t launch_bwd_prepare(const bf16_t* x, const int32_t* offsets, const int32_t* row_token,
                               int32_t* poff, int32_t* prow_token, bf16_t* xP, int T, int H,
                               int E, int k, hipStream_t s);
+// dst[r] = src[compact row of padded row r] for r < poff[E] (rows of `row_vecs` 16-byte
+// vectors; pad rows repeat the expert's last kept row).
+hipError_t launch_bwd_pad_copy(const bf16_t* src, bf16_t* dst, const int32_t* offsets,
+                               const int32_t* poff, int T, int k, int E, int row_vecs,
+                               hipStream_t s);
 hipError_t launch_bwd_combine(const bf16_t* dout, const bf16_t* y, const int32_t* slot_row,
                               const int32_t* topk_idx, const float* topk_w,
                               const int32_t* offsets, const int32_t* poff, bf16_t* dyP,

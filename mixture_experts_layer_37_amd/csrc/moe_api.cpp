@@ -169,6 +169,13 @@ moe_status check_ws(const moe_config* c, void* ws, size_t ws_bytes) {
   return MOE_OK;
 }
 
+// The backward's tiles: bf16 only, I a multiple of 256 (256-wide gradient tiles over I).
+moe_status check_backward_cfg(const moe_config* c) {
+  MOE_TRY(check_cfg(c));
+  if (c->dtype != MOE_DTYPE_BF16 || c->inter % 256 != 0) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
 moe_status need(const void* p, size_t align) {
   return (p != nullptr && aligned(p, align)) ? MOE_OK : MOE_ERR_INVALID_ARG;
 }
@@ -418,11 +425,50 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
   return do_combine(cfg, y, slot_row, w, out, s);
 }
 
-// The backward's tiles: bf16 only, I a multiple of 256 (256-wide gradient tiles over I).
-moe_status check_backward_cfg(const moe_config* c) {
-  MOE_TRY(check_cfg(c));
-  if (c->dtype != MOE_DTYPE_BF16 || c->inter % 256 != 0) return MOE_ERR_UNSUPPORTED;
-  return MOE_OK;
+moe_status moe_forward_train(const moe_config* cfg, const void* x, const void* w_router,
+                             const float* gate_bias, const void* w_gate, const void* w_up,
+                             const void* w_down, void* out, void* ws, size_t ws_bytes,
+                             void* bws, size_t bws_bytes, moe_stream_t stream) {
+  MOE_TRY(check_backward_cfg(cfg));
+  if (cfg->tokens == 0) return MOE_OK;   // empty batch: nothing to read or write
+  MOE_TRY(need(x, 16));
+  MOE_TRY(need(w_router, 2));
+  if (gate_bias != nullptr) MOE_TRY(need(gate_bias, 4));
+  if (cfg->activation == MOE_ACT_SWIGLU) MOE_TRY(need(w_gate, 16));
+  MOE_TRY(need(w_up, 16));
+  MOE_TRY(need(w_down, 16));
+  MOE_TRY(need(out, 16));
+  MOE_TRY(check_ws(cfg, ws, ws_bytes));
+  if (bws == nullptr || !aligned(bws, 16)) return MOE_ERR_INVALID_ARG;
+  if (bws_bytes < blayout_of(cfg).total) return MOE_ERR_WORKSPACE;
+  const Layout L = layout_of(cfg);
+  const BLayout B = blayout_of(cfg);
+  const hipStream_t s = (hipStream_t)stream;
+  float* logits = region<float>(ws, L, R_LOGITS);
+  int32_t* idx = region<int32_t>(ws, L, R_TOPK_IDX);
+  float* w = region<float>(ws, L, R_TOPK_W);
+  int32_t* counts = region<int32_t>(ws, L, R_COUNTS);
+  int32_t* offsets = region<int32_t>(ws, L, R_OFFSETS);
+  int32_t* slot_row = region<int32_t>(ws, L, R_SLOT_ROW);
+  int32_t* row_token = region<int32_t>(ws, L, R_ROW_TOKEN);
+  moe::bf16_t* h = region<moe::bf16_t>(ws, L, R_H);
+  void* y = region<void>(ws, L, R_Y_PERM);
+  moe::bf16_t* gu = bregion<moe::bf16_t>(bws, B, B_GU);
+  const int T = cfg->tokens, H = cfg->hidden, I = cfg->inter, E = cfg->experts;
+  const int rows = T * cfg->top_k;
+  MOE_TRY(do_route(cfg, x, w_router, gate_bias, logits, idx, w, ws, s));
+  MOE_TRY(do_permute(cfg, x, idx, nullptr, counts, offsets, row_token, slot_row, ws, s));
+  // GEMM 1 keeping the pre-activations for the backward: [g | u] (GELU: a) into bws, h as usual
+  if (cfg->activation == MOE_ACT_SWIGLU)
+    MOE_TRY(hip_status(moe::launch_gemm_bf16(
+        moe::EPI_GU, (const moe::bf16_t*)x, row_token, T, offsets, (const moe::bf16_t*)w_gate,
+        (const moe::bf16_t*)w_up, gu, nullptr, nullptr, h, E, H, I, rows, s)));
+  else
+    MOE_TRY(hip_status(moe::launch_gemm_bf16(
+        moe::EPI_AH, (const moe::bf16_t*)x, row_token, T, offsets, (const moe::bf16_t*)w_up,
+        nullptr, gu, nullptr, nullptr, h, E, H, I, rows, s)));
+  MOE_TRY(do_down(cfg, h, offsets, w_down, y, region<float>(ws, L, R_SPLIT), s));
+  return do_combine(cfg, y, slot_row, w, out, s);
 }
 
 moe_status moe_backward_workspace_size(const moe_config* cfg, size_t* bytes) {
@@ -436,7 +482,7 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
                         const void* w_gate, const void* w_up, const void* w_down,
                         const void* dout, void* dx, float* dw_router, float* dgate_bias,
                         void* dw_gate, void* dw_up, void* dw_down, void* ws, size_t ws_bytes,
-                        void* bws, size_t bws_bytes, moe_stream_t stream) {
+                        void* bws, size_t bws_bytes, int32_t saved, moe_stream_t stream) {
   MOE_TRY(check_backward_cfg(cfg));
   if (cfg->tokens == 0) return MOE_OK;   // empty batch: nothing to read or write
   const bool swiglu = cfg->activation == MOE_ACT_SWIGLU;
@@ -489,13 +535,19 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
   // padded row maps and the token rows in padded expert-major order
   MOE_TRY(hip_status(moe::launch_bwd_prepare((const bf16_t*)x, offsets, row_token, poff, prow,
                                              xP, T, H, E, k, s)));
-  // recompute the up-projection: [g | u] and h (GELU: a and h)
-  if (swiglu)
-    MOE_TRY(hip_status(moe::launch_gemm_bf16(moe::EPI_GU, xP, nullptr, P, poff, wg, wu, gu,
-                                             nullptr, nullptr, hP, E, H, I, P, s)));
-  else
-    MOE_TRY(hip_status(moe::launch_gemm_bf16(moe::EPI_AH, xP, nullptr, P, poff, wu, nullptr, gu,
-                                             nullptr, nullptr, hP, E, H, I, P, s)));
+  // the up-projection's pre-activations: kept by moe_forward_train (compact rows, in bws), or
+  // recomputed here in the padded row space together with h (GELU: a and h)
+  if (saved) {   // h of the forward (ws), moved into the padded rows for dW_down
+    MOE_TRY(hip_status(moe::launch_bwd_pad_copy(region<bf16_t>(ws, L, R_H), hP, offsets, poff, T,
+                                                k, E, I / 8, s)));
+  } else {
+    if (swiglu)
+      MOE_TRY(hip_status(moe::launch_gemm_bf16(moe::EPI_GU, xP, nullptr, P, poff, wg, wu, gu,
+                                               nullptr, nullptr, hP, E, H, I, P, s)));
+    else
+      MOE_TRY(hip_status(moe::launch_gemm_bf16(moe::EPI_AH, xP, nullptr, P, poff, wu, nullptr,
+                                               gu, nullptr, nullptr, hP, E, H, I, P, s)));
+  }
   // combine backward: dy (padded, zero pads) and the gate-weight gradients
   MOE_TRY(hip_status(moe::launch_bwd_combine((const bf16_t*)dout, y, slot_row, idx, w, offsets,
                                              poff, dyP, dwj, T, H, E, k, s)));
@@ -503,14 +555,15 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
                                             cfg->renormalize != 0, s)));
   // dh = dy Wd^T with the activation's backward fused: [dg | du] (GELU: da). Wd[e] [I][H]
   // is Wd^T with K contiguous, read as is (transposed-weight mode).
+  // (saved pre-activations are read through the compact row map)
   MOE_TRY(hip_status(moe::launch_gemm_bf16_bt(swiglu ? moe::EPI_SWIGLU_BWD : moe::EPI_GELU_BWD,
-                                              dyP, poff, wd, nullptr, dgu, nullptr, gu, E, H, I,
-                                              P, s)));
+                                              dyP, poff, wd, nullptr, dgu, nullptr, gu,
+                                              saved ? offsets : nullptr, E, H, I, P, s)));
   // dx rows = [dg | du] [Wg^T; Wu^T] (GELU: da Wu^T): one K = 2I product reading Wg[e] and
   // Wu[e] ([H][I] each, K contiguous) as the two K halves of the transposed weight
   MOE_TRY(hip_status(moe::launch_gemm_bf16_bt(moe::EPI_NONE, dgu, poff, swiglu ? wg : wu,
-                                              swiglu ? wu : nullptr, dxP, split, nullptr, E,
-                                              swiglu ? 2 * I : I, H, P, s)));
+                                              swiglu ? wu : nullptr, dxP, split, nullptr,
+                                              nullptr, E, swiglu ? 2 * I : I, H, P, s)));
   MOE_TRY(hip_status(moe::launch_bwd_dx(dxP, (const bf16_t*)w_router, dL, slot_row, idx,
                                         offsets, poff, (bf16_t*)dx, T, H, E, k, s)));
   MOE_TRY(hip_status(moe::launch_bwd_wrouter((const bf16_t*)x, dL, bregion<float>(bws, B, B_WRPART),

@@ -52,18 +52,34 @@ class MoELayer:
         self.ws = torch.empty(L.moe_workspace_size(self.c), dtype=torch.uint8, device=device)
 
     def forward(self, x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        self._saved = False
         if out is None:
             out = torch.empty_like(x)
         L.moe_forward(self.c, x, self.w_router, self.bias, self.w_gate, self.w_up, self.w_down,
                       out, self.ws, stream)
         return out
 
-    def backward(self, x: torch.Tensor, dout: torch.Tensor, stream=None) -> dict:
-        """moe_backward after the last ``forward`` on ``x``: a dict of gradient tensors."""
-        cfg, dev = self.cfg, self.device
+    def _bws(self):
         if not hasattr(self, "bws"):
             self.bws = torch.empty(L.moe_backward_workspace_size(self.c), dtype=torch.uint8,
-                                   device=dev)
+                                   device=self.device)
+        return self.bws
+
+    def forward_train(self, x: torch.Tensor, out: torch.Tensor | None = None,
+                      stream=None) -> torch.Tensor:
+        """moe_forward_train: the forward, keeping GEMM 1's pre-activations for ``backward``."""
+        if out is None:
+            out = torch.empty_like(x)
+        L.moe_forward_train(self.c, x, self.w_router, self.bias, self.w_gate, self.w_up,
+                            self.w_down, out, self.ws, self._bws(), stream)
+        self._saved = True
+        return out
+
+    def backward(self, x: torch.Tensor, dout: torch.Tensor, stream=None) -> dict:
+        """moe_backward after the last ``forward`` / ``forward_train`` on ``x``: a dict of
+        gradient tensors."""
+        cfg, dev = self.cfg, self.device
+        self._bws()
         g = dict(dx=torch.empty_like(x),
                  dw_router=torch.empty((cfg.hidden, cfg.experts), dtype=torch.float32, device=dev),
                  dbias=torch.empty(cfg.experts, dtype=torch.float32, device=dev),
@@ -71,7 +87,8 @@ class MoELayer:
                  dw_up=torch.empty_like(self.w_up), dw_down=torch.empty_like(self.w_down))
         L.moe_backward(self.c, x, self.w_router, self.w_gate, self.w_up, self.w_down, dout,
                        g["dx"], g["dw_router"], g["dbias"], g["dw_gate"], g["dw_up"],
-                       g["dw_down"], self.ws, self.bws, stream)
+                       g["dw_down"], self.ws, self.bws, getattr(self, "_saved", False), stream)
+        self._saved = False
         return g
 
     def view(self, which: int) -> torch.Tensor:

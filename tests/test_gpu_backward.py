@@ -103,3 +103,24 @@ def test_backward_is_deterministic():
         outs.append({k: v.clone() for k, v in g.items() if v is not None})
     for k in outs[0]:
         assert torch.equal(outs[0][k].view(torch.uint8), outs[1][k].view(torch.uint8)), k
+
+
+@pytest.mark.parametrize("name", ["swiglu", "gelu_raw", "capacity", "threshold"])
+def test_saved_preactivations_match_recompute(name):
+    """moe_forward_train gives moe_forward's output bit for bit, and the backward that uses
+    its kept pre-activations gives the recomputing backward's gradients bit for bit (same
+    products, same order)."""
+    cfg = CASES[name]
+    inp = make_inputs(cfg, seed=10)
+    layer = MoELayer(cfg, inp)
+    x = to_device(cfg, inp["x"])
+    dout = to_device(cfg, f32_to_bf16_bits(
+        np.random.default_rng(6).standard_normal((cfg.tokens, cfg.hidden)).astype(np.float32)))
+    out_a = layer.forward(x).clone()
+    ga = {k: v.clone() for k, v in layer.backward(x, dout).items() if v is not None}
+    out_b = layer.forward_train(x).clone()
+    gb = {k: v.clone() for k, v in layer.backward(x, dout).items() if v is not None}
+    torch.cuda.synchronize()
+    assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16))
+    for k in ga:
+        assert torch.equal(ga[k].view(torch.uint8), gb[k].view(torch.uint8)), k
