@@ -37,6 +37,13 @@ CASES = {
                                 experts=1, top_k=1, bias=None),
     # the bench workload's layer shape (H 4096, I 14336, 8 experts, top-2) on 1024 tokens
     "mixtral_shape": C.MIXTRAL.with_(name="bwd_mixtral_shape", tokens=1024),
+    # the largest gate the library takes (256 experts, top-16); one token; experts left
+    # without rows (their weight gradients must be exactly zero)
+    "max_experts": C.FINE.with_(name="bwd_max_experts", tokens=300, hidden=256, inter=256,
+                                experts=256, top_k=16, bias=("normal", 4.0)),
+    "single_token": C.MIXTRAL.with_(name="bwd_single_token", tokens=1, hidden=256, inter=256),
+    "empty_experts": C.SMALL.with_(name="bwd_empty_experts", tokens=20, hidden=256, inter=256,
+                                   experts=16, top_k=1, bias=None),
 }
 
 
@@ -80,11 +87,16 @@ def test_backward_matches_oracle(name):
            "dw_router": _close(g["dw_router"].cpu().numpy().astype(np.float64), ref["dw_router"],
                                "dw_router"),
            "dbias": _close(g["dbias"].cpu().numpy().astype(np.float64), ref["dbias"], "dbias")}
+    offs = layer.view(L.MOE_WS_OFFSETS).cpu().numpy()
+    empty = np.nonzero(np.diff(offs) == 0)[0]
     for key in ("dw_gate", "dw_up", "dw_down"):
         if g[key] is None:
             continue
         want = np.stack(ref[key])
-        rep[key] = _close(P.decode(cfg, g[key]).reshape(want.shape), want, key)
+        got = P.decode(cfg, g[key]).reshape(want.shape)
+        rep[key] = _close(got, want, key)
+        assert (got[empty] == 0).all(), f"{key}: experts without rows must get zero gradients"
+    rep["experts_without_rows"] = int(len(empty))
     print(f"[backward] {name}: {rep}", flush=True)
 
 
