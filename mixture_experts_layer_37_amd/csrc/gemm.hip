@@ -677,7 +677,8 @@ hipError_t launch_gemm_bf16_bt(int epi, const bf16_t* a, const int32_t* offsets,
 // MFMAs through transposing LDS reads. poff[e] .. poff[e+1] is expert e's padded row range,
 // a multiple of 128 rows (whole pairs of k-steps), possibly empty (then C_e = 0); pad rows
 // of B are zero. Same k-step pipeline as the forward kernel; tiles are ordered
-// (expert, m-tile, n-tile), so an XCD's blocks share A panels in L2.
+// (expert, m-tile, n-tile), so an XCD's blocks share A panels in L2, and the XCDs split the
+// order by cost rather than by tile count.
 __global__ __launch_bounds__(256, 1) void grouped_wgrad_bf16_kernel(
     const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ B, int ldb,
     const int32_t* __restrict__ poff, bf16_t* __restrict__ C, int E, int M, int N) {
@@ -690,8 +691,34 @@ __global__ __launch_bounds__(256, 1) void grouped_wgrad_bf16_kernel(
   const int total = E * MT * NT;
   const int xcd = blockIdx.x % kXcds, li = blockIdx.x / kXcds;
   const int nper = gridDim.x / kXcds;
-  const int per = (total + kXcds - 1) / kXcds;
   const int wm = wave >> 1, wn = wave & 1;
+  // Experts differ in rows, so tiles differ in cost (k-steps). Each XCD takes a contiguous
+  // range of the (expert, m-tile, n-tile) order holding an eighth of the total cost; an
+  // expert without rows costs one step per tile (its tiles still write zeros).
+  __shared__ int s_cost[kMaxExperts + 1];   // cost before expert e's first tile
+  if (tid == 0) {
+    int acc = 0;
+    for (int e = 0; e < E; ++e) {
+      s_cost[e] = acc;
+      acc += max((poff[e + 1] - poff[e]) / BK, 1) * MT * NT;
+    }
+    s_cost[E] = acc;
+  }
+  __syncthreads();
+  auto first_tile_at = [&](long c) {   // first tile whose cost start is >= c
+    if (c >= s_cost[E]) return total;
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_cost[mid] <= c) lo = mid; else hi = mid - 1;
+    }
+    const int kt = max((poff[lo + 1] - poff[lo]) / BK, 1);
+    const long idx = (c - s_cost[lo] + kt - 1) / kt;
+    return lo * MT * NT + (int)min(idx, (long)MT * NT);
+  };
+  const int t_begin = __builtin_amdgcn_readfirstlane(first_tile_at((long)xcd * s_cost[E] / kXcds));
+  const int t_end =
+      __builtin_amdgcn_readfirstlane(first_tile_at((long)(xcd + 1) * s_cost[E] / kXcds));
   const int l32 = lane & 31, lhi = lane >> 5;
 
   // Transposing-read offsets (bytes within a stage): A in halves [0, 2) of the stage, B in
@@ -731,9 +758,7 @@ __global__ __launch_bounds__(256, 1) void grouped_wgrad_bf16_kernel(
     d_col[i] = (uint32_t)((((u >> 1) ^ bswz(k)) << 4) + ((u & 1) << 3));
   }
 
-  for (int it = li; it < per; it += nper) {
-    const int tile = xcd * per + it;
-    if (tile >= total) break;
+  for (int tile = t_begin + li; tile < t_end; tile += nper) {
     const int e = tile / (MT * NT);
     const int rem = tile - e * MT * NT;
     const int m_t = rem / NT, n_t = rem - m_t * NT;
