@@ -34,8 +34,12 @@
 //   - operands are issued as (W, x) so each lane's accumulators hold 4 consecutive output
 //     columns of one row, written straight to global memory as 8-byte stores;
 //   - persistent grid of one block per CU; tiles are ordered (expert, n-tile, m-tile) and
-//     each of the 8 XCDs walks its own contiguous range, so the blocks sharing an XCD's L2
-//     work on the same weight columns at the same time;
+//     run round by round: each round of the grid is a contiguous stretch of the list, cut
+//     into 8 contiguous pieces, one per XCD. The blocks sharing an XCD's L2 then work on the
+//     same weight columns and token rows at the same time, and the XCDs of one round read
+//     the rows of the same one or two experts, so a row fetched from HBM by one XCD is found
+//     in the Infinity Cache by the others (instead of each XCD streaming its own expert's
+//     rows, several times over, from HBM);
 //   - split-K tail (GEMM 2, when the caller supplies a partial buffer): the tiles beyond the
 //     last whole round of the grid would leave most CUs idle for one full tile time, so each
 //     of them is cut into S slices of K (S a power of two, tail * S <= grid), every slice
@@ -228,7 +232,6 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   const int KT = K / BK;
   const SplitPlan plan = split_plan(__builtin_amdgcn_readfirstlane(total), gridDim.x, KT,
                                    EPI == EPI_NONE && partial != nullptr);
-  const int per = (plan.full + kXcds - 1) / kXcds;   // whole tiles per XCD
   const int my_unit = xcd * nper + li;                // this block's split slice, if any
 
   const int wm = wave >> 1, wn = wave & 1;
@@ -538,9 +541,11 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     }
   };
 
-  // This XCD's whole tiles, then at most one split slice per block.
-  for (int it = li; it < per; it += nper) {
-    const int tile = xcd * per + it;
+  // Whole tiles round by round, then at most one split slice per block. Round r covers
+  // tiles [r G, (r + 1) G) of the list; XCD x takes the x-th eighth of it, one tile per
+  // block.
+  for (int base = 0; base < plan.full; base += gridDim.x) {
+    const int tile = base + xcd * nper + li;
     if (tile >= plan.full) break;
     run_tile(tile, 0, KT, nullptr, std::false_type{});
   }
@@ -677,8 +682,8 @@ hipError_t launch_gemm_bf16_bt(int epi, const bf16_t* a, const int32_t* offsets,
 // MFMAs through transposing LDS reads. poff[e] .. poff[e+1] is expert e's padded row range,
 // a multiple of 128 rows (whole pairs of k-steps), possibly empty (then C_e = 0); pad rows
 // of B are zero. Same k-step pipeline as the forward kernel; tiles are ordered
-// (expert, m-tile, n-tile), so an XCD's blocks share A panels in L2, and the XCDs split the
-// order by cost rather than by tile count.
+// (expert, m-tile, n-tile), so an XCD's blocks share A panels in L2, and the XCDs of one
+// round of the grid read the same expert's rows (shared through the Infinity Cache).
 __global__ __launch_bounds__(256, 1) void grouped_wgrad_bf16_kernel(
     const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ B, int ldb,
     const int32_t* __restrict__ poff, bf16_t* __restrict__ C, int E, int M, int N) {
@@ -692,33 +697,6 @@ __global__ __launch_bounds__(256, 1) void grouped_wgrad_bf16_kernel(
   const int xcd = blockIdx.x % kXcds, li = blockIdx.x / kXcds;
   const int nper = gridDim.x / kXcds;
   const int wm = wave >> 1, wn = wave & 1;
-  // Experts differ in rows, so tiles differ in cost (k-steps). Each XCD takes a contiguous
-  // range of the (expert, m-tile, n-tile) order holding an eighth of the total cost; an
-  // expert without rows costs one step per tile (its tiles still write zeros).
-  __shared__ int s_cost[kMaxExperts + 1];   // cost before expert e's first tile
-  if (tid == 0) {
-    int acc = 0;
-    for (int e = 0; e < E; ++e) {
-      s_cost[e] = acc;
-      acc += max((poff[e + 1] - poff[e]) / BK, 1) * MT * NT;
-    }
-    s_cost[E] = acc;
-  }
-  __syncthreads();
-  auto first_tile_at = [&](long c) {   // first tile whose cost start is >= c
-    if (c >= s_cost[E]) return total;
-    int lo = 0, hi = E - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_cost[mid] <= c) lo = mid; else hi = mid - 1;
-    }
-    const int kt = max((poff[lo + 1] - poff[lo]) / BK, 1);
-    const long idx = (c - s_cost[lo] + kt - 1) / kt;
-    return lo * MT * NT + (int)min(idx, (long)MT * NT);
-  };
-  const int t_begin = __builtin_amdgcn_readfirstlane(first_tile_at((long)xcd * s_cost[E] / kXcds));
-  const int t_end =
-      __builtin_amdgcn_readfirstlane(first_tile_at((long)(xcd + 1) * s_cost[E] / kXcds));
   const int l32 = lane & 31, lhi = lane >> 5;
 
   // Transposing-read offsets (bytes within a stage): A in halves [0, 2) of the stage, B in
@@ -758,7 +736,11 @@ __global__ __launch_bounds__(256, 1) void grouped_wgrad_bf16_kernel(
     d_col[i] = (uint32_t)((((u >> 1) ^ bswz(k)) << 4) + ((u & 1) << 3));
   }
 
-  for (int tile = t_begin + li; tile < t_end; tile += nper) {
+  // Round by round as in the forward kernel: round r is tiles [r G, (r + 1) G), XCD x takes
+  // its x-th eighth. Each block meets every expert's tiles in turn, so experts that differ
+  // in rows (cost) leave the blocks' totals nearly equal.
+  for (int base = 0, tile = xcd * nper + li; tile < total;
+       base += gridDim.x, tile = base + xcd * nper + li) {
     const int e = tile / (MT * NT);
     const int rem = tile - e * MT * NT;
     const int m_t = rem / NT, n_t = rem - m_t * NT;
