@@ -3,9 +3,12 @@
 
 A step is one pass of the whole path -- route, permute, grouped GEMM 1 (gate/up + SwiGLU),
 grouped GEMM 2 (down), combine -- over one batch of seeded synthetic inputs already in
-HBM, through the library's C ABI on torch's current stream. HIP events recorded on that
-stream between the stages give per-stage times; the dominant kernel (GEMM 1) is reported
-against the bf16 dense MFMA peak. The CPU oracle is timed on a bounded token sample.
+HBM, through the library's C ABI on torch's current stream. The expert weights are resident
+in the library's packed layout (moe_pack_expert_weight, run once when the layer is loaded,
+outside the timed region, as an inference engine stores its weights); the same steps on
+the plain row-major weights are timed beside them. HIP events recorded on the stream
+between the stages give per-stage times; the dominant kernel (GEMM 1) is reported against
+the bf16 dense MFMA peak. The CPU oracle is timed on a bounded token sample.
 
 Prints ONE JSON line.
 """
@@ -31,14 +34,16 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_up_mixtral_traffic.txt")
 def parse_args():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="mixtral")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     ap.add_argument("--backward", action="store_true",
                     help="time a training step instead: moe_forward then moe_backward")
+    ap.add_argument("--weights", choices=("packed", "plain"), default="packed",
+                    help="expert weight layout of the timed forward (bf16)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -85,6 +90,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     cfg = C.get(args.config)
+    if cfg.dtype == C.BF16 and not args.backward:
+        cfg = cfg.with_(weights=args.weights)
     T, H, I, E, k = cfg.tokens, cfg.hidden, cfg.inter, cfg.experts, cfg.top_k
     print(f"[bench] {cfg.name}: generating inputs", file=sys.stderr, flush=True)
     inp = make_inputs(cfg, seed=args.seed, threads=16)
@@ -109,19 +116,22 @@ def main():
     stream = torch.cuda.current_stream()
     names = ["route", "permute", "gemm_up", "gemm_down", "combine"]
 
-    def step(ev=None):
+    def step(ev=None, plain=False):
         # the path moe_forward runs: the permute writes the row maps only and GEMM 1 reads
         # the token rows in place through them
+        cw = layer.c_plain if plain else c
+        wg, wu, wd = ((layer.w_gate, layer.w_up, layer.w_down) if plain
+                      else (layer.fw_gate, layer.fw_up, layer.fw_down))
         if ev: ev[0].record(stream)
-        L.moe_route(c, x, layer.w_router, layer.bias, logits, idx, w, ws, stream)
+        L.moe_route(cw, x, layer.w_router, layer.bias, logits, idx, w, ws, stream)
         if ev: ev[1].record(stream)
-        L.moe_permute(c, x, idx, None, counts, offs, rt, sr, ws, stream)
+        L.moe_permute(cw, x, idx, None, counts, offs, rt, sr, ws, stream)
         if ev: ev[2].record(stream)
-        L.moe_expert_up_rows(c, x, rt, offs, layer.w_gate, layer.w_up, h, stream)
+        L.moe_expert_up_rows(cw, x, rt, offs, wg, wu, h, stream)
         if ev: ev[3].record(stream)
-        L.moe_expert_down(c, h, offs, layer.w_down, y, ws, stream)
+        L.moe_expert_down(cw, h, offs, wd, y, ws, stream)
         if ev: ev[4].record(stream)
-        L.moe_combine(c, y, sr, w, out, stream)
+        L.moe_combine(cw, y, sr, w, out, stream)
         if ev: ev[5].record(stream)
 
     if args.calib_copy_mib > 0:
@@ -150,6 +160,24 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     stage_ms = {n: float(np.mean([events[s][i].elapsed_time(events[s][i + 1])
                                   for s in range(args.steps)])) for i, n in enumerate(names)}
+    plain = None
+    if cfg.weights == "packed":
+        # context: the same steps on the plain row-major weights (bit-identical output)
+        n_plain = max(2, args.steps // 2)
+        for _ in range(2):
+            step(plain=True)
+        pev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_plain)]
+        torch.cuda.synchronize()
+        p0 = time.perf_counter()
+        for s in range(n_plain):
+            step(pev[s], plain=True)
+        torch.cuda.synchronize()
+        plain = {"ms_per_step": (time.perf_counter() - p0) * 1e3 / n_plain, "steps": n_plain,
+                 "stages_us": {n: 1e3 * float(np.mean([pev[s][i].elapsed_time(pev[s][i + 1])
+                                                       for s in range(n_plain)]))
+                               for i, n in enumerate(names)}}
+        step()   # leave the packed step's results in place for the checks below
+        torch.cuda.synchronize()
 
     n_kept = int(offs[-1].item())
     up_flops = (4 if cfg.activation == C.SWIGLU else 2) * n_kept * H * I
@@ -164,8 +192,10 @@ def main():
     route_bytes = T * H * es + H * E * es + T * E * 4 + T * k * 8
     permute_bytes = T * k * 4 * 4
     combine_bytes = n_kept * H * es + T * H * es + T * k * 8
-    # the committed counter summary covers GEMM 1 of the Mixtral top-2 workload only
-    traffic = measured_traffic() if cfg.name == "mixtral" else None
+    # the committed counter summary covers GEMM 1 (packed weights) of the Mixtral top-2
+    # workload only
+    traffic = (measured_traffic() if cfg.name == "mixtral" and cfg.weights == "packed"
+               else None)
     result = {
         "metric": METRIC,
         "value": T / (ms_per_step * 1e-3),
@@ -183,8 +213,12 @@ def main():
                    "experts": E, "top_k": k, "capacity_factor": cfg.capacity_factor,
                    "activation": cfg.activation, "routing": cfg.routing,
                    "threshold": (cfg.threshold if cfg.threshold > 0 else 1.0 / E)
-                   if cfg.routing == "threshold" else None, "kept_rows": n_kept},
-        "roofline": {"kernel": "grouped_gemm_bf16_kernel<SwiGLU> (moe_expert_up_rows)",
+                   if cfg.routing == "threshold" else None, "kept_rows": n_kept,
+                   "weights": ("packed once at load (moe_pack_expert_weight)"
+                               if cfg.weights == "packed" else "plain row-major")},
+        "roofline": {"kernel": ("grouped_gemm_packed_kernel<SwiGLU> (moe_expert_up_rows)"
+                                if cfg.weights == "packed" else
+                                "grouped_gemm_bf16_kernel<SwiGLU> (moe_expert_up_rows)"),
                      "bound": "mfma", "achieved": up_tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": up_tflops / PEAK_BF16_TFLOPS,
                      "traffic": traffic, "algorithmic_flops": up_flops},
@@ -195,6 +229,8 @@ def main():
                      "permute_row_maps": permute_bytes / (stage_ms["permute"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
                      "combine": combine_bytes / (stage_ms["combine"] * 1e-3) / 1e9 / PEAK_HBM_GBS},
     }
+    if plain is not None:
+        result["plain_weights"] = plain
     result["materialised_permute"] = materialised_permute(L, c, x, idx, counts, offs, rt, sr, ws,
                                                           stream, T, H, k, n_kept, es)
     peaks = measured_peaks(stream)

@@ -66,6 +66,9 @@ enum { MOE_FLAG_BAD_INDEX = 1, MOE_FLAG_NONFINITE_LOGIT = 2 };
 enum { MOE_MAX_EXPERTS = 256, MOE_MAX_TOPK = 16 };
 /* routing rules (moe_config.routing) */
 enum { MOE_ROUTE_TOPK = 0, MOE_ROUTE_THRESHOLD = 1 };
+/* expert weight layouts (moe_config.weight_layout) and weights (moe_pack_expert_weight) */
+enum { MOE_WEIGHTS_PLAIN = 0, MOE_WEIGHTS_PACKED = 1 };
+enum { MOE_WEIGHT_GATE = 0, MOE_WEIGHT_UP = 1, MOE_WEIGHT_DOWN = 2 };
 
 typedef struct moe_config {
   int32_t tokens;            /* T >= 0 */
@@ -90,7 +93,14 @@ typedef struct moe_config {
                                 contributes zero (intelliparadigm.com page, section 3.2.1:
                                 keep the experts scoring above delta, default 1/E, then
                                 renormalise) */
-  int32_t reserved;          /* set to 0 */
+  int32_t weight_layout;     /* MOE_WEIGHTS_PLAIN (0, the default): w_gate, w_up, w_down
+                                in the row-major layouts below. MOE_WEIGHTS_PACKED (bf16
+                                only): the same tensors as written by
+                                moe_pack_expert_weight, for the forward entry points
+                                (moe_expert_up, moe_expert_up_rows, moe_expert_down,
+                                moe_grouped_ffn, moe_forward); the backward and
+                                moe_forward_train need plain weights
+                                (MOE_ERR_UNSUPPORTED). Other values: MOE_ERR_INVALID_ARG */
   double threshold;          /* delta of MOE_ROUTE_THRESHOLD; <= 0 means 1/E; not NaN */
 } moe_config;
 
@@ -177,6 +187,19 @@ moe_status moe_grouped_ffn(const moe_config* cfg, const void* x_perm,
                            const int32_t* expert_offsets, const void* w_gate, const void* w_up,
                            const void* w_down, void* y_perm, void* ws, size_t ws_bytes,
                            moe_stream_t stream);
+
+/* Repack one expert weight tensor for MOE_WEIGHTS_PACKED (bf16 only; once, when weights
+ * are loaded: inference weights are constant). which = MOE_WEIGHT_GATE or MOE_WEIGHT_UP
+ * (w [E,H,I]; gate: SwiGLU only) or MOE_WEIGHT_DOWN (w [E,I,H]); for w [E,K,N], `packed`
+ * (same byte size, must not overlap w) receives, for each expert e, 32-column block nb and
+ * 16-row slice ks, a 1 KB block whose 16-byte chunk l (0..63) holds
+ *   w[e][16 ks + 8 (l >> 5) + q][32 nb + (l & 31)],  q = 0..7,
+ * blocks ordered [e][nb][ks]: chunk l is lane l's operand of one 32x32x16 bf16 MFMA, so the
+ * packed GEMMs load weights straight into registers. The packed GEMMs give bit-identical
+ * results to the plain ones (the summation order is unchanged). Asynchronous on `stream`;
+ * a bad `which` or overlapping buffers -> MOE_ERR_INVALID_ARG. */
+moe_status moe_pack_expert_weight(const moe_config* cfg, int32_t which, const void* w,
+                                  void* packed, moe_stream_t stream);
 
 /* Weighted combine back to token order (lshu.cn page, section 4,
  * npu_moe_token_postprocess; the pages aggregate with an atomic scatter-add, this library

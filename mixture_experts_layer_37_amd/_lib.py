@@ -22,11 +22,14 @@ MOE_DTYPE_BF16, MOE_DTYPE_F32 = 0, 1
 MOE_ACT_SWIGLU, MOE_ACT_GELU = 0, 1
 MOE_FLAG_BAD_INDEX, MOE_FLAG_NONFINITE_LOGIT = 1, 2
 MOE_ROUTE_TOPK, MOE_ROUTE_THRESHOLD = 0, 1
+MOE_WEIGHTS_PLAIN, MOE_WEIGHTS_PACKED = 0, 1
+MOE_WEIGHT_GATE, MOE_WEIGHT_UP, MOE_WEIGHT_DOWN = 0, 1, 2
 (MOE_WS_LOGITS, MOE_WS_TOPK_IDX, MOE_WS_TOPK_W, MOE_WS_COUNTS, MOE_WS_OFFSETS, MOE_WS_SLOT_ROW,
  MOE_WS_ROW_TOKEN, MOE_WS_X_PERM, MOE_WS_H, MOE_WS_Y_PERM) = range(10)
 
 EXPORTS = ("moe_workspace_size", "moe_capacity", "moe_route", "moe_permute", "moe_expert_up",
-           "moe_expert_up_rows", "moe_expert_down", "moe_grouped_ffn", "moe_combine",
+           "moe_expert_up_rows", "moe_expert_down", "moe_grouped_ffn",
+           "moe_pack_expert_weight", "moe_combine",
            "moe_forward", "moe_forward_train", "moe_backward_workspace_size", "moe_backward",
            "moe_workspace_view", "moe_read_device_status", "moe_status_string",
            "moe_last_hip_error")
@@ -36,7 +39,7 @@ class CConfig(ctypes.Structure):
     _fields_ = [("tokens", c_int32), ("hidden", c_int32), ("inter", c_int32),
                 ("experts", c_int32), ("top_k", c_int32), ("activation", c_int32),
                 ("dtype", c_int32), ("renormalize", c_int32), ("capacity_factor", c_double),
-                ("routing", c_int32), ("reserved", c_int32), ("threshold", c_double)]
+                ("routing", c_int32), ("weight_layout", c_int32), ("threshold", c_double)]
 
 
 class MoEError(RuntimeError):
@@ -70,6 +73,7 @@ def lib():
             "moe_expert_up_rows": [cfgp, vp, vp, vp, vp, vp, vp, vp],
             "moe_expert_down": [cfgp, vp, vp, vp, vp, vp, c_size_t, vp],
             "moe_grouped_ffn": [cfgp, vp, vp, vp, vp, vp, vp, vp, c_size_t, vp],
+            "moe_pack_expert_weight": [cfgp, c_int32, vp, vp, vp],
             "moe_combine": [cfgp, vp, vp, vp, vp, vp],
             "moe_forward": [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, c_size_t, vp],
             "moe_backward_workspace_size": [cfgp, POINTER(c_size_t)],
@@ -100,6 +104,8 @@ def cconfig(cfg: MoEConfig, tokens: int | None = None) -> CConfig:
                    renormalize=1 if cfg.renormalize else 0,
                    capacity_factor=float(cfg.capacity_factor),
                    routing=MOE_ROUTE_THRESHOLD if cfg.routing == "threshold" else MOE_ROUTE_TOPK,
+                   weight_layout=(MOE_WEIGHTS_PACKED if cfg.weights == "packed"
+                                  else MOE_WEIGHTS_PLAIN),
                    threshold=float(cfg.threshold))
 
 
@@ -183,6 +189,11 @@ def moe_grouped_ffn(cfg, x_perm, expert_offsets, w_gate, w_up, w_down, y_perm, w
     _check("moe_grouped_ffn", lib().moe_grouped_ffn(
         ctypes.byref(_as_cfg(cfg)), _ptr(x_perm), _ptr(expert_offsets), _ptr(w_gate), _ptr(w_up),
         _ptr(w_down), _ptr(y_perm), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_pack_expert_weight(cfg, which: int, w, packed, stream=None):
+    _check("moe_pack_expert_weight", lib().moe_pack_expert_weight(
+        ctypes.byref(_as_cfg(cfg)), which, _ptr(w), _ptr(packed), _stream(stream)))
 
 
 def moe_combine(cfg, y_perm, slot_row, topk_w, out, stream=None):

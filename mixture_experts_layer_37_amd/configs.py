@@ -40,6 +40,9 @@ class MoEConfig:
     # top_k of them
     routing: str = "topk"
     threshold: float = 0.0
+    # expert weight layout handed to the library: "plain" (row-major) or "packed" (repacked
+    # once into MFMA operand order by moe_pack_expert_weight; bf16 forward only)
+    weights: str = "plain"
     description: str = field(default="", compare=False)
 
     def with_(self, **kw) -> "MoEConfig":

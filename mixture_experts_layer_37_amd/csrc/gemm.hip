@@ -45,6 +45,7 @@
 //     of them is cut into S slices of K (S a power of two, tail * S <= grid), every slice
 //     writes a float32 partial tile, and a small reduction kernel adds the S partials in
 //     slice order and writes the bf16 rows. The result is deterministic.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -664,6 +665,345 @@ hipError_t launch_gemm_bf16_bt(int epi, const bf16_t* a, const int32_t* offsets,
     default: return hipErrorInvalidValue;
   }
 #undef MOE_GEMM_BT
+  if (split) {
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(1024), dim3(256), 0, s, partial, offsets, c, E,
+                       K, N, max_rows, grid);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// Packed weights. Inference weights are constant, so they can be stored once in the order
+// the MFMAs consume them: a bf16 matrix W[E][K][N] packed by pack_weight_kernel holds, for
+// expert e, 32-column block nb and 16-row k slice ks, one 1 KB block
+//   P[e][nb][ks][l][q] = W[e][16 ks + 8 (l >> 5) + q][32 nb + (l & 31)],  l < 64, q < 8,
+// which is exactly lane l's operand of v_mfma_f32_32x32x16_bf16 for those 32 columns and
+// 16 k. The packed GEMM then loads each wave's weight fragments straight into registers,
+// one coalesced 16-byte load per lane and block, and only the token rows go through LDS:
+// per k-step a block moves 32 KB into LDS and reads 64 KB of fragments out of it, against
+// 64 KB and 128 KB when both operands are staged. Sums run in the same order as in
+// grouped_gemm_bf16_kernel, so the results are bit-identical to it.
+__global__ __launch_bounds__(256) void pack_weight_kernel(const bf16_t* __restrict__ W,
+                                                          bf16_t* __restrict__ P, int E, int K,
+                                                          int N) {
+  const int NB = N / 32, KS = K / 16;
+  const size_t total = (size_t)E * NB * KS * 64;   // 16-byte chunks of P
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const int l = (int)(i & 63);
+    size_t t = i >> 6;
+    const int ks = (int)(t % KS);
+    t /= KS;
+    const int nb = (int)(t % NB);
+    const int e = (int)(t / NB);
+    const bf16_t* src = W + ((size_t)e * K + ks * 16 + 8 * (l >> 5)) * N + nb * 32 + (l & 31);
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      w[q] = (uint32_t)src[(size_t)(2 * q) * N] | ((uint32_t)src[(size_t)(2 * q + 1) * N] << 16);
+    *(uint4*)(P + i * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_char*)p;
+}
+// The packed kernel's k-loop issues its loads as asm, so the compiler tracks none of them
+// and adds no waits of its own (mixing LDS DMA and register loads, it would wait for all of
+// them in every k-step); the loop waits with explicit counts instead.
+// 16 bytes per lane global -> LDS at lds + 16 l. m0 is written right before the load that
+// reads it, with the one wait state an LDS DMA needs after an SALU write of m0.
+__device__ __forceinline__ void dma16_asm(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ bf16x8 load16_asm(const bf16_t* p) {
+  bf16x8 v;
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+// Wait until at most N of this wave's loads are in flight. The four fragments pass through
+// the wait, so no instruction that reads them can be scheduled above it.
+template <int N>
+__device__ __forceinline__ void wait_loads(bf16x8* b) {
+  asm volatile("s_waitcnt vmcnt(%4)" : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]) : "n"(N));
+}
+// s_waitcnt immediate: vmcnt(n) and lgkmcnt(0)
+constexpr int wait_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+
+// Grouped GEMM on packed weights: SWIGLU (P0 gate, P1 up), GELU and NONE (P0), with the
+// tile list, round-by-round order, fused gather and split-K tail of
+// grouped_gemm_bf16_kernel. Wave (wm, wn) computes rows wm*128 .. +127 and the four
+// 32-column blocks j: SwiGLU gate (j < 2) / up (j >= 2) columns wn*64 + 32 (j & 1), else
+// columns wn*128 + 32 j.
+template <int EPI>
+__global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
+    const bf16_t* __restrict__ A, const int32_t* __restrict__ row_token, int a_rows,
+    const int32_t* __restrict__ offsets, const bf16_t* __restrict__ P0,
+    const bf16_t* __restrict__ P1, bf16_t* __restrict__ C, float* __restrict__ partial, int E,
+    int K, int N, int max_rows) {
+  static_assert(EPI == EPI_SWIGLU || EPI == EPI_GELU || EPI == EPI_NONE, "packed epilogues");
+  __shared__ __attribute__((aligned(1024))) bf16_t sa0[BM * BK];
+  __shared__ __attribute__((aligned(1024))) bf16_t sa1[BM * BK];
+  __shared__ int s_start[kMaxExperts + 1];
+  __shared__ int s_off[kMaxExperts + 1];
+  __shared__ int s_wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  constexpr bool kTwoMat = EPI == EPI_SWIGLU;
+  constexpr int OUTN = kTwoMat ? 128 : 256;
+  const int NT = N / OUTN, NB = N / 32, KS = K / 16;
+  const int total = build_tile_starts<BM>(offsets, E, NT, max_rows, s_start, s_off, s_wsum);
+  const int xcd = blockIdx.x % kXcds, li = blockIdx.x / kXcds;
+  const int nper = gridDim.x / kXcds;
+  const int KT = K / BK;
+  const SplitPlan plan = split_plan(__builtin_amdgcn_readfirstlane(total), gridDim.x, KT,
+                                   EPI == EPI_NONE && partial != nullptr);
+  const int my_unit = xcd * nper + li;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, lhi = lane >> 5;
+  uint32_t a_rd[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int m = wm * 128 + l32;
+    a_rd[kk] = (uint32_t)(m * BK * 2 + (((kk * 2 + lhi) ^ swz(m)) << 4));
+  }
+  struct FragA {
+    bf16x8 a[4];
+  };
+  auto load_a = [&](const bf16_t* stg, int kk, FragA& f) {
+    const char* st = (const char*)stg;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t off = a_rd[kk] ^ ((i & 1) << 6);
+      f.a[i] = *(const bf16x8*)(st + off + i * 32 * BK * 2);
+    }
+  };
+
+  auto run_tile = [&](int tile, int kb, int ke, float* part, auto slice) {
+    constexpr bool kSlice = decltype(slice)::value;
+    const TileCoord tc = decode_tile(s_start, s_off, E, __builtin_amdgcn_readfirstlane(tile), BM);
+    const int e = __builtin_amdgcn_readfirstlane(tc.e);
+    const int n_t = __builtin_amdgcn_readfirstlane(tc.n_t);
+    const int row0 = __builtin_amdgcn_readfirstlane(tc.row0);
+    const int mrows = __builtin_amdgcn_readfirstlane(tc.mrows);
+    // A: as grouped_gemm_bf16_kernel (rows past the expert's end re-read its last row)
+    const char* a_src[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = wave * 64 + i * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ swz(r);
+      const int rr = row0 + min(r, mrows - 1);
+      const size_t arow = row_token != nullptr ? (size_t)min(max(row_token[rr], 0), a_rows - 1)
+                                               : (size_t)rr;
+      a_src[i] = (const char*)(A + arow * K) + c * 16;
+    }
+    // B fragment j of k slice s: this lane's 16 bytes of block (nb_j, s)
+    const bf16_t* bsrc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16_t* P;
+      int nb;
+      if (kTwoMat) { P = j < 2 ? P0 : P1; nb = n_t * 4 + wn * 2 + (j & 1); }
+      else { P = P0; nb = n_t * 8 + wn * 4 + j; }
+      bsrc[j] = P + ((size_t)e * NB + nb) * KS * 512 + lane * 8;
+    }
+    // ring of eight k slices of B fragments (slot = slice & 7 within a pair of k-steps)
+    bf16x8 bv[8][4];
+    auto load_b = [&](int s, int slot) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bv[slot][j] = load16_asm(bsrc[j] + (size_t)s * 512);
+    };
+    auto dma_a = [&](int kt, bf16_t* stg) {
+      const uint32_t kA = (uint32_t)(kt * BK * 2);
+      const uint32_t dst = lds_offset(stg) + wave * 8 * 1024;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dma16_asm(a_src[i] + kA, dst + i * 1024);
+    };
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    auto mfma16 = [&](const FragA& f, int slot) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[slot][j], f.a[i], acc[i][j], 0,
+                                                              0, 0);
+    };
+    FragA f0, f1;
+    // One k slice: wait for its B fragments, issue the next slice's A reads and (ahead by
+    // one k-step) the B loads of slice s + 4, then the 16 MFMAs.
+    auto phase = [&](const bf16_t* stg, int kk_next, FragA& nxt, const FragA& cur, int slot,
+                     int s_ahead, bool ahead, auto wait) {
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      wait_loads<decltype(wait)::value>(bv[slot]);
+      load_a(stg, kk_next, nxt);
+      if (ahead) load_b(s_ahead, (slot + 4) & 7);
+      mfma16(cur, slot);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // the A reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // then the MFMAs
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // k-step kt on stage `cur` (its B in slots sb .. sb+3). Loads issue in this order:
+    //   step kt-1: ..., A(kt+1) [8], B(4kt+3) [4]
+    //   step kt:   B(4kt+4) [4], B(4kt+5), B(4kt+6) | wait A(kt+1) | A(kt+2), B(4kt+7)
+    // (A(kt+2) only if kt+2 < ke, B(4kt+4 ..) only if kt+1 < ke), so each wait below is
+    // the number of loads issued after the one it needs.
+    auto kstep = [&](int kt, bf16_t* cur, bf16_t* nxt, int sb, auto refill, auto next) {
+      constexpr int n1 = decltype(next)::value ? 1 : 0;
+      using W0 = std::integral_constant<int, 12 + 8 * n1>;
+      using W1 = std::integral_constant<int, 8 + 12 * n1>;
+      using W2 = std::integral_constant<int, 4 + 16 * n1>;
+      phase(cur, 1, f1, f0, sb + 0, 4 * kt + 4, n1, W0{});
+      phase(cur, 2, f0, f1, sb + 1, 4 * kt + 5, n1, W1{});
+      phase(cur, 3, f1, f0, sb + 2, 4 * kt + 6, n1, W2{});
+      // A(kt+1) has landed once at most B(4kt+3) .. B(4kt+6) are in flight
+      if constexpr (n1) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(16));
+      else __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      wait_loads<12 * n1>(bv[(sb + 3) & 7]);
+      if constexpr (decltype(refill)::value) dma_a(kt + 2, cur);
+      if constexpr (n1) {
+        load_a(nxt, 0, f0);
+        load_b(4 * kt + 7, (sb + 7) & 7);
+      }
+      mfma16(f1, sb + 3);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    using yes = std::true_type;
+    using no = std::false_type;
+    // prologue: A(kb) landed, then B(4kb) .. B(4kb+2), A(kb+1), B(4kb+3) in flight
+    dma_a(kb, sa0);
+    __builtin_amdgcn_s_waitcnt(0);
+    load_b(4 * kb + 0, 0);
+    load_b(4 * kb + 1, 1);
+    load_b(4 * kb + 2, 2);
+    dma_a(kb + 1, sa1);
+    load_b(4 * kb + 3, 3);
+    __syncthreads();
+    load_a(sa0, 0, f0);
+    int kt = kb;   // ke - kb is even
+    for (; kt + 2 < ke; kt += 2) {
+      kstep(kt, sa0, sa1, 0, yes{}, yes{});
+      kstep(kt + 1, sa1, sa0, 4, yes{}, yes{});
+    }
+    kstep(kt, sa0, sa1, 0, no{}, yes{});
+    kstep(kt + 1, sa1, sa0, 4, no{}, no{});
+    __syncthreads();   // every wave is done with both stages before the next tile's DMA
+
+    // Epilogue. acc[i][j][4q+s]: row m = wm*128 + i*32 + l32, column (within the wave's
+    // block j) = 8q + 4*lhi + s.
+    if constexpr (kSlice) {   // float32 partial tile [BM][256], valid rows only
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = wm * 128 + i * 32 + l32;
+        if (m >= mrows) continue;
+        float* prow = part + (size_t)m * 256;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int col = wn * 128 + j * 32 + 8 * q + 4 * lhi;
+            *(float4*)(prow + col) = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                                 acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+          }
+      }
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = wm * 128 + i * 32 + l32;
+      if (m >= mrows) continue;
+      bf16_t* crow = C + (size_t)(row0 + m) * N;
+      if constexpr (kTwoMat) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int col = n_t * 128 + wn * 64 + j * 32 + 8 * q + 4 * lhi;
+            float hv[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+              hv[s] = silu_f(acc[i][j][4 * q + s]) * acc[i][j + 2][4 * q + s];
+            *(uint2*)(crow + col) = pack4(hv);
+          }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int col = n_t * 256 + wn * 128 + j * 32 + 8 * q + 4 * lhi;
+            float hv[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+              hv[s] = EPI == EPI_GELU ? gelu_f(acc[i][j][4 * q + s]) : acc[i][j][4 * q + s];
+            *(uint2*)(crow + col) = pack4(hv);
+          }
+      }
+    }
+  };
+
+  for (int base = 0; base < plan.full; base += gridDim.x) {
+    const int tile = base + xcd * nper + li;
+    if (tile >= plan.full) break;
+    run_tile(tile, 0, KT, nullptr, std::false_type{});
+  }
+  if constexpr (EPI == EPI_NONE) {
+    if (my_unit < plan.tail * plan.S) {
+      int kb, ke;
+      slice_range(KT, plan.S, my_unit % plan.S, kb, ke);
+      run_tile(plan.full + my_unit / plan.S, kb, ke, partial + (size_t)my_unit * (BM * 256),
+               std::true_type{});
+    }
+  }
+}
+
+hipError_t launch_pack_weight_bf16(const bf16_t* w, bf16_t* packed, int E, int K, int N,
+                                   hipStream_t s) {
+  const size_t chunks = (size_t)E * (N / 32) * (K / 16) * 64;
+  const unsigned blocks = (unsigned)std::min<size_t>((chunks + 255) / 256, 16384);
+  hipLaunchKernelGGL(pack_weight_kernel, dim3(blocks), dim3(256), 0, s, w, packed, E, K, N);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_bf16_packed(int epi, const bf16_t* a, const int32_t* row_token,
+                                   int a_rows, const int32_t* offsets, const bf16_t* p0,
+                                   const bf16_t* p1, bf16_t* c, float* partial, int E, int K,
+                                   int N, int max_rows, hipStream_t s) {
+  const int outn = epi == EPI_SWIGLU ? 128 : 256;
+  const bool split = epi == EPI_NONE && partial != nullptr;
+  const long max_tiles = (long)((max_rows + BM - 1) / BM + E) * (N / outn);
+  int grid = device_cus();
+  grid = (grid / kXcds) * kXcds;
+  if (grid < kXcds) grid = kXcds;
+  const long need = ((max_tiles + kXcds - 1) / kXcds) * kXcds;
+  if (!split && need < grid) grid = (int)need;
+  if (!split) partial = nullptr;
+  const dim3 g(grid), b(256);
+  switch (epi) {
+    case EPI_SWIGLU:
+      hipLaunchKernelGGL((grouped_gemm_packed_kernel<EPI_SWIGLU>), g, b, 0, s, a, row_token,
+                         a_rows, offsets, p0, p1, c, partial, E, K, N, max_rows);
+      break;
+    case EPI_GELU:
+      hipLaunchKernelGGL((grouped_gemm_packed_kernel<EPI_GELU>), g, b, 0, s, a, row_token,
+                         a_rows, offsets, p0, p1, c, partial, E, K, N, max_rows);
+      break;
+    case EPI_NONE:
+      hipLaunchKernelGGL((grouped_gemm_packed_kernel<EPI_NONE>), g, b, 0, s, a, row_token,
+                         a_rows, offsets, p0, p1, c, partial, E, K, N, max_rows);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   if (split) {
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;

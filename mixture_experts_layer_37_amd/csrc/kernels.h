@@ -66,6 +66,16 @@ hipError_t launch_gemm_bf16_bt(int epi, const bf16_t* a, const int32_t* offsets,
                                const bf16_t* w0, const bf16_t* w1, bf16_t* c, float* partial,
                                const bf16_t* aux, const int32_t* aux_off, int E, int K, int N,
                                int max_rows, hipStream_t s);
+// Packed weights: W [E][K][N] -> P of the same size, P[e][N/32][K/16][64][8] with lane l's
+// 8 values of block (nb, ks) = W[e][16 ks + 8 (l >> 5) + 0..7][32 nb + (l & 31)].
+hipError_t launch_pack_weight_bf16(const bf16_t* w, bf16_t* packed, int E, int K, int N,
+                                   hipStream_t s);
+// As launch_gemm_bf16 with packed weights (SWIGLU: p0 gate, p1 up; GELU, NONE: p0), for the
+// forward epilogues only; bit-identical results.
+hipError_t launch_gemm_bf16_packed(int epi, const bf16_t* a, const int32_t* row_token,
+                                   int a_rows, const int32_t* offsets, const bf16_t* p0,
+                                   const bf16_t* p1, bf16_t* c, float* partial, int E, int K,
+                                   int N, int max_rows, hipStream_t s);
 // Weight gradients C_e = A_e^T B_e over each expert's padded rows poff[e] .. poff[e+1]
 // (multiples of 128); A [rows][lda], B [rows][ldb] row-major; M, N multiples of 256.
 hipError_t launch_wgrad_bf16(const bf16_t* a, int lda, const bf16_t* b, int ldb,

@@ -12,8 +12,9 @@
 #include "moe.h"
 #include "kernels.h"
 
-// The binding mirrors this layout (explicit reserved word, no implicit padding).
+// The binding mirrors this layout (explicit 32-bit fields, no implicit padding).
 static_assert(sizeof(moe_config) == 56 && offsetof(moe_config, routing) == 40 &&
+                  offsetof(moe_config, weight_layout) == 44 &&
                   offsetof(moe_config, threshold) == 48,
               "moe_config layout");
 
@@ -128,7 +129,11 @@ moe_status check_cfg(const moe_config* c) {
   if (c->routing != MOE_ROUTE_TOPK && c->routing != MOE_ROUTE_THRESHOLD)
     return MOE_ERR_INVALID_ARG;
   if (std::isnan(c->threshold)) return MOE_ERR_INVALID_ARG;
+  if (c->weight_layout != MOE_WEIGHTS_PLAIN && c->weight_layout != MOE_WEIGHTS_PACKED)
+    return MOE_ERR_INVALID_ARG;
   if (c->dtype != MOE_DTYPE_BF16 && c->dtype != MOE_DTYPE_F32) return MOE_ERR_UNSUPPORTED;
+  if (c->weight_layout == MOE_WEIGHTS_PACKED && c->dtype != MOE_DTYPE_BF16)
+    return MOE_ERR_UNSUPPORTED;
   if (c->activation != MOE_ACT_SWIGLU && c->activation != MOE_ACT_GELU) return MOE_ERR_UNSUPPORTED;
   if (c->experts > MOE_MAX_EXPERTS || c->top_k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
   if (c->dtype == MOE_DTYPE_BF16) {
@@ -169,10 +174,12 @@ moe_status check_ws(const moe_config* c, void* ws, size_t ws_bytes) {
   return MOE_OK;
 }
 
-// The backward's tiles: bf16 only, I a multiple of 256 (256-wide gradient tiles over I).
+// The backward's tiles: bf16 only, I a multiple of 256 (256-wide gradient tiles over I),
+// plain weights (its products read them transposed in place).
 moe_status check_backward_cfg(const moe_config* c) {
   MOE_TRY(check_cfg(c));
   if (c->dtype != MOE_DTYPE_BF16 || c->inter % 256 != 0) return MOE_ERR_UNSUPPORTED;
+  if (c->weight_layout != MOE_WEIGHTS_PLAIN) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -230,6 +237,11 @@ moe_status do_up(const moe_config* c, const void* a, const int32_t* row_token,
   const int epi = swiglu ? moe::EPI_SWIGLU : moe::EPI_GELU;
   const int rows = c->tokens * c->top_k;
   const int a_rows = row_token != nullptr ? c->tokens : rows;
+  if (c->weight_layout == MOE_WEIGHTS_PACKED)
+    return hip_status(moe::launch_gemm_bf16_packed(
+        epi, (const moe::bf16_t*)a, row_token, a_rows, offsets,
+        (const moe::bf16_t*)(swiglu ? w_gate : w_up), (const moe::bf16_t*)w_up,
+        (moe::bf16_t*)h, nullptr, c->experts, c->hidden, c->inter, rows, s));
   if (c->dtype == MOE_DTYPE_BF16)
     return hip_status(moe::launch_gemm_bf16(
         epi, (const moe::bf16_t*)a, row_token, a_rows, offsets,
@@ -245,6 +257,11 @@ moe_status do_up(const moe_config* c, const void* a, const int32_t* row_token,
 moe_status do_down(const moe_config* c, const void* h, const int32_t* offsets,
                    const void* w_down, void* y, float* partial, hipStream_t s) {
   const int rows = c->tokens * c->top_k;
+  if (c->weight_layout == MOE_WEIGHTS_PACKED)
+    return hip_status(moe::launch_gemm_bf16_packed(
+        moe::EPI_NONE, (const moe::bf16_t*)h, nullptr, rows, offsets,
+        (const moe::bf16_t*)w_down, nullptr, (moe::bf16_t*)y, partial, c->experts, c->inter,
+        c->hidden, rows, s));
   if (c->dtype == MOE_DTYPE_BF16)
     return hip_status(moe::launch_gemm_bf16(moe::EPI_NONE, (const moe::bf16_t*)h, nullptr, rows,
                                             offsets, (const moe::bf16_t*)w_down, nullptr,
@@ -379,6 +396,31 @@ moe_status moe_grouped_ffn(const moe_config* cfg, const void* x_perm,
   const hipStream_t s = (hipStream_t)stream;
   MOE_TRY(do_up(cfg, x_perm, nullptr, expert_offsets, w_gate, w_up, h, s));
   return do_down(cfg, h, expert_offsets, w_down, y_perm, region<float>(ws, L, R_SPLIT), s);
+}
+
+moe_status moe_pack_expert_weight(const moe_config* cfg, int32_t which, const void* w,
+                                  void* packed, moe_stream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  if (cfg->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+  int K, N;
+  if (which == MOE_WEIGHT_GATE || which == MOE_WEIGHT_UP) {
+    K = cfg->hidden;
+    N = cfg->inter;
+  } else if (which == MOE_WEIGHT_DOWN) {
+    K = cfg->inter;
+    N = cfg->hidden;
+  } else {
+    return MOE_ERR_INVALID_ARG;
+  }
+  if (which == MOE_WEIGHT_GATE && cfg->activation != MOE_ACT_SWIGLU) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(need(w, 16));
+  MOE_TRY(need(packed, 16));
+  const size_t bytes = (size_t)cfg->experts * K * N * 2;
+  const char* wb = (const char*)w;
+  const char* pb = (const char*)packed;
+  if (pb < wb + bytes && wb < pb + bytes) return MOE_ERR_INVALID_ARG;   // must not overlap
+  return hip_status(moe::launch_pack_weight_bf16((const moe::bf16_t*)w, (moe::bf16_t*)packed,
+                                                 cfg->experts, K, N, (hipStream_t)stream));
 }
 
 moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* slot_row,

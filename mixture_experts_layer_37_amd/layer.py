@@ -36,32 +36,55 @@ def from_device(t: torch.Tensor) -> np.ndarray:
     return t.numpy()
 
 
+def pack_weights(c, w_gate, w_up, w_down, stream=None):
+    """Packed copies of the expert weights (moe_pack_expert_weight; w_gate may be None)."""
+    out = []
+    for which, w in ((L.MOE_WEIGHT_GATE, w_gate), (L.MOE_WEIGHT_UP, w_up),
+                     (L.MOE_WEIGHT_DOWN, w_down)):
+        if w is None:
+            out.append(None)
+            continue
+        p = torch.empty_like(w)
+        L.moe_pack_expert_weight(c, which, w, p, stream)
+        out.append(p)
+    return tuple(out)
+
+
 class MoELayer:
-    """Holds device weights and one workspace; ``forward`` calls moe_forward."""
+    """Holds device weights and one workspace; ``forward`` calls moe_forward.
+
+    With ``cfg.weights == "packed"`` the expert weights are also repacked once
+    (moe_pack_expert_weight) and the forward runs on the packed copies (``fw_*``); the
+    training forward and the backward use the plain ones (``w_*``)."""
 
     def __init__(self, cfg: MoEConfig, inputs: dict, device="cuda", tokens: int | None = None):
         self.cfg = cfg
         self.tokens = cfg.tokens if tokens is None else tokens
         self.c = L.cconfig(cfg, self.tokens)
+        self.c_plain = L.cconfig(cfg.with_(weights="plain"), self.tokens)
         self.device = device
         self.w_router = to_device(cfg, inputs["w_router"], device)
         self.bias = to_device(cfg, inputs.get("bias"), device)
         self.w_gate = to_device(cfg, inputs.get("w_gate"), device) if cfg.activation == SWIGLU else None
         self.w_up = to_device(cfg, inputs["w_up"], device)
         self.w_down = to_device(cfg, inputs["w_down"], device)
+        self.fw_gate, self.fw_up, self.fw_down = self.w_gate, self.w_up, self.w_down
+        if cfg.weights == "packed":
+            self.fw_gate, self.fw_up, self.fw_down = pack_weights(self.c, self.w_gate, self.w_up,
+                                                                  self.w_down)
         self.ws = torch.empty(L.moe_workspace_size(self.c), dtype=torch.uint8, device=device)
 
     def forward(self, x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
         self._saved = False
         if out is None:
             out = torch.empty_like(x)
-        L.moe_forward(self.c, x, self.w_router, self.bias, self.w_gate, self.w_up, self.w_down,
-                      out, self.ws, stream)
+        L.moe_forward(self.c, x, self.w_router, self.bias, self.fw_gate, self.fw_up,
+                      self.fw_down, out, self.ws, stream)
         return out
 
     def _bws(self):
         if not hasattr(self, "bws"):
-            self.bws = torch.empty(L.moe_backward_workspace_size(self.c), dtype=torch.uint8,
+            self.bws = torch.empty(L.moe_backward_workspace_size(self.c_plain), dtype=torch.uint8,
                                    device=self.device)
         return self.bws
 
@@ -70,7 +93,7 @@ class MoELayer:
         """moe_forward_train: the forward, keeping GEMM 1's pre-activations for ``backward``."""
         if out is None:
             out = torch.empty_like(x)
-        L.moe_forward_train(self.c, x, self.w_router, self.bias, self.w_gate, self.w_up,
+        L.moe_forward_train(self.c_plain, x, self.w_router, self.bias, self.w_gate, self.w_up,
                             self.w_down, out, self.ws, self._bws(), stream)
         self._saved = True
         return out
@@ -85,7 +108,7 @@ class MoELayer:
                  dbias=torch.empty(cfg.experts, dtype=torch.float32, device=dev),
                  dw_gate=torch.empty_like(self.w_gate) if self.w_gate is not None else None,
                  dw_up=torch.empty_like(self.w_up), dw_down=torch.empty_like(self.w_down))
-        L.moe_backward(self.c, x, self.w_router, self.w_gate, self.w_up, self.w_down, dout,
+        L.moe_backward(self.c_plain, x, self.w_router, self.w_gate, self.w_up, self.w_down, dout,
                        g["dx"], g["dw_router"], g["dbias"], g["dw_gate"], g["dw_up"],
                        g["dw_down"], self.ws, self.bws, getattr(self, "_saved", False), stream)
         self._saved = False

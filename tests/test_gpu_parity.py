@@ -278,6 +278,45 @@ def test_expert_up_rows_equals_gather_then_expert_up(name):
     assert torch.equal(h1[:n].view(bits), h2[:n].view(bits))
 
 
+# Expert row counts around the 256-row m-tile and the 128-row half tile that takes an
+# expert's last 1 .. 128 rows: none, one, 127, exactly 128, 129 (a whole ragged tile), 255,
+# 256, 257 (a whole tile and a one-row half tile), 384 (a whole tile and a full half tile),
+# 600 (two whole tiles and 88 rows), 700 (two whole tiles and a whole tile of 188 rows).
+RAGGED_ROWS = [0, 1, 127, 128, 129, 255, 256, 257, 384, 600, 700]
+
+
+@pytest.mark.parametrize("activation", [C.SWIGLU, C.GELU])
+def test_expert_up_ragged_rows(activation):
+    """GEMM 1 on x_perm with crafted expert offsets: every row of h against the float64
+    activation of the products of the same bf16 inputs."""
+    E, T = len(RAGGED_ROWS), sum(RAGGED_ROWS)
+    cfg = C.SMALL.with_(name=f"ragged_{activation}", tokens=T, hidden=512, inter=512,
+                        experts=E, top_k=1, activation=activation, bias=None)
+    print(f"[case] ragged rows {activation} {RAGGED_ROWS}", flush=True)
+    inp = make_inputs(cfg, seed=8)
+    layer = MoELayer(cfg, inp)
+    x = to_device(cfg, inp["x"])
+    o = np.concatenate([[0], np.cumsum(RAGGED_ROWS)]).astype(np.int32)
+    offs = torch.from_numpy(o).to("cuda")
+    h = torch.full((T, cfg.inter), 0x7FC0, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    L.moe_expert_up(layer.c, x, offs, layer.w_gate, layer.w_up, h)
+    torch.cuda.synchronize()
+    hf = P.decode(cfg, h)
+    xf = as_float(cfg, inp["x"]).astype(np.float64)
+    wu = ExpertView(cfg, inp["w_up"])
+    wg = ExpertView(cfg, inp["w_gate"]) if activation == C.SWIGLU else None
+    ref = np.empty_like(hf)
+    for e in range(E):
+        xr = xf[o[e]:o[e + 1]]
+        u = xr @ wu[e].astype(np.float64)
+        ref[o[e]:o[e + 1]] = (O.silu(xr @ wg[e].astype(np.float64)) * u
+                              if activation == C.SWIGLU else O.gelu(u))
+    _report(f"ragged_{activation}", P.assert_layer_close(hf, ref, "h"))
+    for e in range(E):   # every expert's rows, checked on their own
+        if o[e + 1] > o[e]:
+            P.assert_layer_close(hf[o[e]:o[e + 1]], ref[o[e]:o[e + 1]], f"h of expert {e}")
+
+
 # GEMM 2's split-K tail: shapes whose tile list leaves a partial round of the grid and whose
 # K is long enough to be sliced: two slices over an odd number of k-step pairs, four slices,
 # and whole rounds followed by a sliced tail.
