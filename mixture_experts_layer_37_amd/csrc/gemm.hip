@@ -812,15 +812,21 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
     }
     // ring of eight k slices of B fragments (slot = slice & 7 within a pair of k-steps)
     bf16x8 bv[8][4];
+    // Loads each unit issues per wave; the wait counts below are derived from these, so
+    // they stay exact if either changes. An inexact count is not only a wrong result: a
+    // wait that passes early lets the compiler reuse a register that a load still in
+    // flight will overwrite.
+    constexpr int kLB = 4;   // B loads per k slice (one per fragment j)
+    constexpr int kLA = 8;   // A DMA loads per k-step
     auto load_b = [&](int s, int slot) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bv[slot][j] = load16_asm(bsrc[j] + (size_t)s * 512);
+      for (int j = 0; j < kLB; ++j) bv[slot][j] = load16_asm(bsrc[j] + (size_t)s * 512);
     };
     auto dma_a = [&](int kt, bf16_t* stg) {
       const uint32_t kA = (uint32_t)(kt * BK * 2);
-      const uint32_t dst = lds_offset(stg) + wave * 8 * 1024;
+      const uint32_t dst = lds_offset(stg) + wave * kLA * 1024;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) dma16_asm(a_src[i] + kA, dst + i * 1024);
+      for (int i = 0; i < kLA; ++i) dma16_asm(a_src[i] + kA, dst + i * 1024);
     };
     f32x16 acc[4][4];
 #pragma unroll
@@ -851,25 +857,32 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
       __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // then the MFMAs
       __builtin_amdgcn_sched_barrier(0);
     };
-    // k-step kt on stage `cur` (its B in slots sb .. sb+3). Loads issue in this order:
-    //   step kt-1: ..., A(kt+1) [8], B(4kt+3) [4]
-    //   step kt:   B(4kt+4) [4], B(4kt+5), B(4kt+6) | wait A(kt+1) | A(kt+2), B(4kt+7)
-    // (A(kt+2) only if kt+2 < ke, B(4kt+4 ..) only if kt+1 < ke), so each wait below is
-    // the number of loads issued after the one it needs.
+    // k-step kt on stage `cur` (its B in slots sb .. sb+3). Loads issue in this order
+    // (vector memory loads complete in issue order, the LDS DMA ones included):
+    //   prologue:  A(kb), wait all | B(4kb), B(4kb+1), B(4kb+2), A(kb+1), B(4kb+3)
+    //   step kt-1: ..., A(kt+1), B(4kt+3)
+    //   step kt:   B(4kt+4), B(4kt+5), B(4kt+6) | wait A(kt+1) | A(kt+2), B(4kt+7)
+    // A(kt+2) only if kt+2 < ke, B(4kt+4 ..) only if kt+1 < ke (n1), and A(kt+1) was issued
+    // exactly when n1 holds. Each wait is the number of loads issued after the one it needs.
     auto kstep = [&](int kt, bf16_t* cur, bf16_t* nxt, int sb, auto refill, auto next) {
       constexpr int n1 = decltype(next)::value ? 1 : 0;
-      using W0 = std::integral_constant<int, 12 + 8 * n1>;
-      using W1 = std::integral_constant<int, 8 + 12 * n1>;
-      using W2 = std::integral_constant<int, 4 + 16 * n1>;
+      // B(4kt): then B(4kt+1), B(4kt+2), A(kt+1), B(4kt+3)
+      using W0 = std::integral_constant<int, 3 * kLB + n1 * kLA>;
+      // B(4kt+1): then B(4kt+2), A(kt+1), B(4kt+3), B(4kt+4)
+      using W1 = std::integral_constant<int, 2 * kLB + n1 * (kLA + kLB)>;
+      // B(4kt+2): then A(kt+1), B(4kt+3), B(4kt+4), B(4kt+5)
+      using W2 = std::integral_constant<int, kLB + n1 * (kLA + 2 * kLB)>;
+      static_assert(W0::value < 64 && W1::value < 64 && W2::value < 64, "vmcnt is 6 bits");
       phase(cur, 1, f1, f0, sb + 0, 4 * kt + 4, n1, W0{});
       phase(cur, 2, f0, f1, sb + 1, 4 * kt + 5, n1, W1{});
       phase(cur, 3, f1, f0, sb + 2, 4 * kt + 6, n1, W2{});
-      // A(kt+1) has landed once at most B(4kt+3) .. B(4kt+6) are in flight
-      if constexpr (n1) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(16));
+      // A(kt+1): then B(4kt+3) .. B(4kt+6)
+      if constexpr (n1) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(4 * kLB));
       else __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
-      wait_loads<12 * n1>(bv[(sb + 3) & 7]);
+      // B(4kt+3): then B(4kt+4) .. B(4kt+6)
+      wait_loads<3 * kLB * n1>(bv[(sb + 3) & 7]);
       if constexpr (decltype(refill)::value) dma_a(kt + 2, cur);
       if constexpr (n1) {
         load_a(nxt, 0, f0);
