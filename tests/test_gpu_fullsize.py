@@ -28,3 +28,28 @@ def test_full_size_workload(name):
         assert rep["dropped"] > 0
     del layer
     torch.cuda.empty_cache()
+
+
+def test_full_size_packed_forward_is_bit_identical():
+    """The Mixtral workload on packed weights, in the bench's launch configuration: the
+    output equals the plain-weight forward bit for bit (the plain one is checked against the
+    oracle above)."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from mixture_experts_layer_37_amd.layer import MoELayer, to_device
+    cfg = C.get("mixtral")
+    print("[fullsize] mixtral packed vs plain: generating inputs", flush=True)
+    inputs = make_inputs(cfg, seed=0, threads=16)
+    x = to_device(cfg, inputs["x"])
+    plain = MoELayer(cfg, inputs)
+    a = plain.forward(x).clone()
+    del plain
+    torch.cuda.empty_cache()
+    packed = MoELayer(cfg.with_(weights="packed"), inputs)
+    b = packed.forward(x)
+    torch.cuda.synchronize()
+    same = torch.equal(a.view(torch.int16), b.view(torch.int16))
+    print(f"[fullsize] mixtral packed vs plain: bit-identical {same}", flush=True)
+    assert same
+    del packed
+    torch.cuda.empty_cache()
