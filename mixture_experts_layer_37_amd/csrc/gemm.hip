@@ -1027,22 +1027,27 @@ hipError_t launch_gemm_bf16_packed(int epi, const bf16_t* a, const int32_t* row_
 }
 
 // ---------------------------------------------------------------------------------------
-// Weight gradients, grouped over the reduction: for each expert e,
-//   C_e[M][N] = sum over the padded rows k of expert e of A[k][m] B[k][n]
-// (dW_down = h^T dy, dW_gate = x^T dg, dW_up = x^T du). A ([rows][lda]) and B ([rows][ldb])
-// are row-major with the reduction running over rows, so both go global -> LDS by DMA as
-// [64 k][2 x 128] tiles (the layout the forward kernel uses for weights) and reach the
-// MFMAs through transposing LDS reads. poff[e] .. poff[e+1] is expert e's padded row range,
-// a multiple of 128 rows (whole pairs of k-steps), possibly empty (then C_e = 0); pad rows
-// of B are zero. Same k-step pipeline as the forward kernel; tiles are ordered
-// (expert, m-tile, n-tile), so an XCD's blocks share A panels in L2, and the XCDs of one
-// round of the grid read the same expert's rows (shared through the Infinity Cache).
-__global__ __launch_bounds__(256, 1) void grouped_wgrad_bf16_kernel(
-    const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ B, int ldb,
+// Weight gradients with the second operand packed: for each expert e,
+//   C_e[M][N] = sum over the padded rows k of expert e of A[k][m] B[k][n],
+// with B given packed over the whole padded row space (pack_weight_kernel's layout with
+// K = the packed rows, E = 1): block (nb, ks) holds B[16 ks + 8 (l >> 5) + q][32 nb + (l & 31)]
+// in chunk l. B reduces over rows exactly as a weight reduces over k, so its fragments load
+// straight into registers as in grouped_gemm_packed_kernel. A ([rows][lda], reduced over
+// rows) goes global -> LDS by DMA as two [64 k][128 m] halves per k-step (the layout the
+// plain forward kernel uses for weights) and reaches the MFMAs through transposing LDS
+// reads. poff[e] .. poff[e+1] is expert e's padded row range, a multiple of 128 rows (whole
+// pairs of k-steps), possibly empty (then C_e = 0); pad rows are zero. Tiles are ordered
+// (expert, m-tile, n-tile) and run round by round: an XCD's blocks share A panels in L2,
+// the XCDs of one round read the same expert's rows, and every block meets every expert in
+// turn, which balances experts of different row counts. The k-loop, its load order and its
+// wait counts are those of grouped_gemm_packed_kernel.
+// TOUT: C is stored transposed, C_e^T [N][M] (dW_gate / dW_up computed as dg^T x).
+template <bool TOUT>
+__global__ __launch_bounds__(256, 1) void grouped_wgrad_packed_kernel(
+    const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ PB, int ksb,
     const int32_t* __restrict__ poff, bf16_t* __restrict__ C, int E, int M, int N) {
-  __shared__ __attribute__((aligned(1024))) bf16_t stage0[kStage];
-  __shared__ __attribute__((aligned(1024))) bf16_t stage1[kStage];
-
+  __shared__ __attribute__((aligned(1024))) bf16_t sa0[BM * BK];
+  __shared__ __attribute__((aligned(1024))) bf16_t sa1[BM * BK];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int MT = M / 256, NT = N / 256;
@@ -1051,34 +1056,32 @@ __global__ __launch_bounds__(256, 1) void grouped_wgrad_bf16_kernel(
   const int nper = gridDim.x / kXcds;
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, lhi = lane >> 5;
-
-  // Transposing-read offsets (bytes within a stage): A in halves [0, 2) of the stage, B in
-  // halves [2, 4); fragment i / j covers 32 columns of the wave's 128.
+  // A in the stage as two [64 k][128 m] halves; fragment i covers 32 of the wave's 128 m
   const int krow0 = 8 * lhi + ((lane & 15) >> 2);
-  uint32_t a_rd[4], b_rd[4];
+  uint32_t a_rd[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c32 = ((32 * i) >> 4) + ((lane >> 4) & 1);
-    const uint32_t in_half = (uint32_t)(krow0 * 256 + ((c32 ^ bswz(krow0)) << 5) + 8 * (lane & 3));
-    a_rd[i] = (uint32_t)(wm * kHalf * 2) + in_half;
-    b_rd[i] = (uint32_t)((BM * BK + wn * kHalf) * 2) + in_half;
+    a_rd[i] = (uint32_t)(wm * kHalf * 2) +
+              (uint32_t)(krow0 * 256 + ((c32 ^ bswz(krow0)) << 5) + 8 * (lane & 3));
   }
-  auto tr_frag = [&](const char* p) {
-    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const lds_char*)p);
-    const v4i16 hi =
-        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const lds_char*)(p + 4 * 256));
-    const v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(bf16x8, v);
+  struct FragA {
+    bf16x8 a[4];
   };
-  auto load_frags = [&](const bf16_t* stg, int kk, Frags& f) {
+  auto load_a = [&](const bf16_t* stg, int kk, FragA& f) {
     const char* st = (const char*)stg + kk * 16 * 256;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f.a[i] = tr_frag(st + a_rd[i]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) f.b[j] = tr_frag(st + b_rd[j]);
+    for (int i = 0; i < 4; ++i) {
+      const char* p = st + a_rd[i];
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const lds_char*)p);
+      const v4i16 hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const lds_char*)(p + 4 * 256));
+      const v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      f.a[i] = __builtin_bit_cast(bf16x8, v);
+    }
   };
-  // DMA: instruction i of wave w fills rows k = (4w + i) * 4 .. + 3 of one [64][128] half;
-  // lane l loads 16-byte unit l & 15 of row 4(4w + i) + l / 16, stored swizzled.
+  // DMA of A: instruction i of wave w fills rows k = (4w + i) * 4 .. + 3 of each half; lane
+  // l loads 16-byte unit l & 15 of row 4(4w + i) + l / 16, stored swizzled
   uint32_t d_col[4];
   int d_row[4];
 #pragma unroll
@@ -1089,9 +1092,6 @@ __global__ __launch_bounds__(256, 1) void grouped_wgrad_bf16_kernel(
     d_col[i] = (uint32_t)((((u >> 1) ^ bswz(k)) << 4) + ((u & 1) << 3));
   }
 
-  // Round by round as in the forward kernel: round r is tiles [r G, (r + 1) G), XCD x takes
-  // its x-th eighth. Each block meets every expert's tiles in turn, so experts that differ
-  // in rows (cost) leave the blocks' totals nearly equal.
   for (int base = 0, tile = xcd * nper + li; tile < total;
        base += gridDim.x, tile = base + xcd * nper + li) {
     const int e = tile / (MT * NT);
@@ -1100,20 +1100,30 @@ __global__ __launch_bounds__(256, 1) void grouped_wgrad_bf16_kernel(
     const int kbase = __builtin_amdgcn_readfirstlane(poff[e]);
     const int KT = __builtin_amdgcn_readfirstlane((poff[e + 1] - poff[e]) / BK);
     const bf16_t* Ab = A + m_t * 256;
-    const bf16_t* Bb = B + n_t * 256;
-    auto dma = [&](int kt, bf16_t* stg) {
+    const char* a_src[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const size_t r = (size_t)(kbase + kt * BK + d_row[i]);
-        const bf16_t* a = Ab + r * lda + d_col[i];
-        const bf16_t* b = Bb + r * ldb + d_col[i];
-        lds_dma16(a, stg + (wave * 4 + i) * 512);
-        lds_dma16(a + 128, stg + kHalf + (wave * 4 + i) * 512);
-        lds_dma16(b, stg + BM * BK + (wave * 4 + i) * 512);
-        lds_dma16(b + 128, stg + BM * BK + kHalf + (wave * 4 + i) * 512);
+    for (int i = 0; i < 4; ++i)
+      a_src[i] = (const char*)(Ab + (size_t)(kbase + d_row[i]) * lda + d_col[i]);
+    const bf16_t* bsrc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      bsrc[j] = PB + ((size_t)(n_t * 8 + wn * 4 + j) * ksb + kbase / 16) * 512 + lane * 8;
+    bf16x8 bv[8][4];
+    constexpr int kLB = 4;   // B loads per k slice
+    constexpr int kLA = 8;   // A DMA loads per k-step (4 rows x 2 halves)
+    auto load_b = [&](int s, int slot) {
+#pragma unroll
+      for (int j = 0; j < kLB; ++j) bv[slot][j] = load16_asm(bsrc[j] + (size_t)s * 512);
+    };
+    auto dma_a = [&](int kt, bf16_t* stg) {
+      const size_t kA = (size_t)kt * BK * lda * 2;
+      const uint32_t dst = lds_offset(stg) + wave * 4 * 1024;
+#pragma unroll
+      for (int i = 0; i < kLA / 2; ++i) {
+        dma16_asm(a_src[i] + kA, dst + i * 1024);
+        dma16_asm(a_src[i] + kA + 256, dst + kHalf * 2 + i * 1024);
       }
     };
-
     f32x16 acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -1121,81 +1131,111 @@ __global__ __launch_bounds__(256, 1) void grouped_wgrad_bf16_kernel(
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-    auto mfma16 = [&](const Frags& f) {
+    auto mfma16 = [&](const FragA& f, int slot) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[slot][j], f.a[i], acc[i][j], 0,
+                                                              0, 0);
     };
-    // The forward kernel's k-slice phases: next slice's 16 LDS reads, then 16 MFMAs.
-    auto phase = [&](const bf16_t* stg, int kk_next, Frags& nxt, const Frags& cur) {
+    FragA f0, f1;
+    auto phase = [&](const bf16_t* stg, int kk_next, FragA& nxt, const FragA& cur, int slot,
+                     int s_ahead, bool ahead, auto wait) {
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-      load_frags(stg, kk_next, nxt);
-      mfma16(cur);
-      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+      wait_loads<decltype(wait)::value>(bv[slot]);
+      load_a(stg, kk_next, nxt);
+      if (ahead) load_b(s_ahead, (slot + 4) & 7);
+      mfma16(cur, slot);
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // the A reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // then the MFMAs
       __builtin_amdgcn_sched_barrier(0);
     };
-    Frags f0, f1;
-    auto kstep = [&](int kt, bf16_t* cur, bf16_t* nxt, auto refill, auto next) {
-      phase(cur, 1, f1, f0);
-      phase(cur, 2, f0, f1);
-      phase(cur, 3, f1, f0);
-      __builtin_amdgcn_s_waitcnt(0);
+    // issue order and wait counts: as grouped_gemm_packed_kernel
+    auto kstep = [&](int kt, bf16_t* cur, bf16_t* nxt, int sb, auto refill, auto next) {
+      constexpr int n1 = decltype(next)::value ? 1 : 0;
+      using W0 = std::integral_constant<int, 3 * kLB + n1 * kLA>;
+      using W1 = std::integral_constant<int, 2 * kLB + n1 * (kLA + kLB)>;
+      using W2 = std::integral_constant<int, kLB + n1 * (kLA + 2 * kLB)>;
+      static_assert(W0::value < 64 && W1::value < 64 && W2::value < 64, "vmcnt is 6 bits");
+      phase(cur, 1, f1, f0, sb + 0, 4 * kt + 4, n1, W0{});
+      phase(cur, 2, f0, f1, sb + 1, 4 * kt + 5, n1, W1{});
+      phase(cur, 3, f1, f0, sb + 2, 4 * kt + 6, n1, W2{});
+      if constexpr (n1) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(4 * kLB));
+      else __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (decltype(refill)::value) dma(kt + 2, cur);
-      if constexpr (decltype(next)::value) load_frags(nxt, 0, f0);
-      mfma16(f1);
+      wait_loads<3 * kLB * n1>(bv[(sb + 3) & 7]);
+      if constexpr (decltype(refill)::value) dma_a(kt + 2, cur);
+      if constexpr (n1) {
+        load_a(nxt, 0, f0);
+        load_b(4 * kt + 7, (sb + 7) & 7);
+      }
+      mfma16(f1, sb + 3);
       __builtin_amdgcn_sched_barrier(0);
     };
     using yes = std::true_type;
     using no = std::false_type;
     if (KT > 0) {   // KT is even: the padded range is a multiple of 128 rows
-      dma(0, stage0);
+      dma_a(0, sa0);
       __builtin_amdgcn_s_waitcnt(0);
-      dma(1, stage1);
+      load_b(0, 0);
+      load_b(1, 1);
+      load_b(2, 2);
+      dma_a(1, sa1);
+      load_b(3, 3);
       __syncthreads();
-      load_frags(stage0, 0, f0);
+      load_a(sa0, 0, f0);
       int kt = 0;
       for (; kt + 2 < KT; kt += 2) {
-        kstep(kt, stage0, stage1, yes{}, yes{});
-        kstep(kt + 1, stage1, stage0, yes{}, yes{});
+        kstep(kt, sa0, sa1, 0, yes{}, yes{});
+        kstep(kt + 1, sa1, sa0, 4, yes{}, yes{});
       }
-      kstep(kt, stage0, stage1, no{}, yes{});
-      kstep(kt + 1, stage1, stage0, no{}, no{});
+      kstep(kt, sa0, sa1, 0, no{}, yes{});
+      kstep(kt + 1, sa1, sa0, 4, no{}, no{});
       __syncthreads();
     }
     // acc[i][j][4q+s]: row m = wm*128 + 32i + l32, column n = wn*128 + 32j + 8q + 4lhi + s
     bf16_t* Ce = C + (size_t)e * M * N;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      bf16_t* crow = Ce + (size_t)(m_t * 256 + wm * 128 + i * 32 + l32) * N + n_t * 256;
+      const int m = m_t * 256 + wm * 128 + i * 32 + l32;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
+          const int n = n_t * 256 + wn * 128 + j * 32 + 8 * q + 4 * lhi;
           float v[4];
 #pragma unroll
           for (int s2 = 0; s2 < 4; ++s2) v[s2] = acc[i][j][4 * q + s2];
-          *(uint2*)(crow + wn * 128 + j * 32 + 8 * q + 4 * lhi) = pack4(v);
+          if constexpr (TOUT) {
+            // C^T[n][m]: for each of the four columns, lanes with consecutive m write
+            // consecutive bytes of one row
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2)
+              Ce[(size_t)(n + s2) * M + m] = (bf16_t)f32_to_bf16(v[s2]);
+          } else {
+            *(uint2*)(Ce + (size_t)m * N + n) = pack4(v);
+          }
         }
     }
   }
 }
 
-hipError_t launch_wgrad_bf16(const bf16_t* a, int lda, const bf16_t* b, int ldb,
-                             const int32_t* poff, bf16_t* c, int E, int M, int N,
-                             hipStream_t s) {
+hipError_t launch_wgrad_bf16_packed(const bf16_t* a, int lda, const bf16_t* pb, int kpack,
+                                    const int32_t* poff, bf16_t* c, int E, int M, int N,
+                                    int trans_out, hipStream_t s) {
   int grid = device_cus();
   grid = (grid / kXcds) * kXcds;
   if (grid < kXcds) grid = kXcds;
   const long need = (((long)E * (M / 256) * (N / 256) + kXcds - 1) / kXcds) * kXcds;
   if (need < grid) grid = (int)need;
-  hipLaunchKernelGGL(grouped_wgrad_bf16_kernel, dim3(grid), dim3(256), 0, s, a, lda, b, ldb,
-                     poff, c, E, M, N);
+  if (trans_out)
+    hipLaunchKernelGGL((grouped_wgrad_packed_kernel<true>), dim3(grid), dim3(256), 0, s, a, lda,
+                       pb, kpack / 16, poff, c, E, M, N);
+  else
+    hipLaunchKernelGGL((grouped_wgrad_packed_kernel<false>), dim3(grid), dim3(256), 0, s, a, lda,
+                       pb, kpack / 16, poff, c, E, M, N);
   return hipGetLastError();
 }
 

@@ -77,10 +77,12 @@ hipError_t launch_gemm_bf16_packed(int epi, const bf16_t* a, const int32_t* row_
                                    const bf16_t* p1, bf16_t* c, float* partial, int E, int K,
                                    int N, int max_rows, hipStream_t s);
 // Weight gradients C_e = A_e^T B_e over each expert's padded rows poff[e] .. poff[e+1]
-// (multiples of 128); A [rows][lda], B [rows][ldb] row-major; M, N multiples of 256.
-hipError_t launch_wgrad_bf16(const bf16_t* a, int lda, const bf16_t* b, int ldb,
-                             const int32_t* poff, bf16_t* c, int E, int M, int N,
-                             hipStream_t s);
+// (multiples of 128): A [rows][lda] row-major, B packed over the whole padded row space
+// (pack_weight_kernel's layout, E = 1, K = kpack rows, a multiple of 16 covering poff[E]);
+// M, N multiples of 256; trans_out stores C^T ([E][N][M]).
+hipError_t launch_wgrad_bf16_packed(const bf16_t* a, int lda, const bf16_t* pb, int kpack,
+                                    const int32_t* poff, bf16_t* c, int E, int M, int N,
+                                    int trans_out, hipStream_t s);
 
 // ---- backward pass (backward.hip): padded row space, multiples of 128 rows per expert
 int bwd_padded_rows(int T, int k, int E);

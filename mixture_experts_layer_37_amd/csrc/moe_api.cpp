@@ -77,7 +77,7 @@ template <typename P> P* region(void* ws, const Layout& L, Region r) {
 // expert), the recomputed activations and the gradients on their way.
 enum BRegion {
   B_POFF, B_PROW, B_XP, B_GU, B_H, B_DY, B_DGU, B_DXP, B_DL, B_DW, B_SPLIT, B_WRPART, B_BPART,
-  B_NUM
+  B_XPK, B_DYPK, B_NUM
 };
 
 struct BLayout {
@@ -105,6 +105,9 @@ BLayout blayout_of(const moe_config* c) {
   L.size[B_SPLIT] = moe::kSplitPartialBytes;
   L.size[B_WRPART] = (size_t)moe::bwd_wrouter_chunks(c->tokens) * H * E * 4;
   L.size[B_BPART] = (size_t)moe::bwd_wrouter_chunks(c->tokens) * E * 4;
+  // x rows and dy in the packed operand layout, for the weight gradients' register operand
+  L.size[B_XPK] = (P / 16) * 16 * H * 2;
+  L.size[B_DYPK] = (P / 16) * 16 * H * 2;
   size_t o = 0;
   for (int r = 0; r < B_NUM; ++r) {
     L.off[r] = o;
@@ -611,15 +614,25 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
   MOE_TRY(hip_status(moe::launch_bwd_wrouter((const bf16_t*)x, dL, bregion<float>(bws, B, B_WRPART),
                                              bregion<float>(bws, B, B_BPART), dw_router,
                                              dgate_bias, T, H, E, s)));
-  // weight gradients over each expert's padded rows
-  MOE_TRY(hip_status(moe::launch_wgrad_bf16(hP, I, dyP, H, poff, (bf16_t*)dw_down, E, I, H, s)));
+  // weight gradients over each expert's padded rows. dy and the x rows reduce over rows as
+  // a weight reduces over k, so they are packed once (the rows up to a multiple of 16 that
+  // covers every expert's range) and loaded straight into registers; h and [dg | du] go
+  // through LDS. dW_gate and dW_up are computed as dg^T x and du^T x and stored transposed.
+  const int kpack = P / 16 * 16;
+  bf16_t* xPk = bregion<bf16_t>(bws, B, B_XPK);
+  bf16_t* dyPk = bregion<bf16_t>(bws, B, B_DYPK);
+  MOE_TRY(hip_status(moe::launch_pack_weight_bf16(dyP, dyPk, 1, kpack, H, s)));
+  MOE_TRY(hip_status(moe::launch_pack_weight_bf16(xP, xPk, 1, kpack, H, s)));
+  MOE_TRY(hip_status(moe::launch_wgrad_bf16_packed(hP, I, dyPk, kpack, poff, (bf16_t*)dw_down,
+                                                   E, I, H, 0, s)));
   if (swiglu) {
-    MOE_TRY(hip_status(moe::launch_wgrad_bf16(xP, H, dgu, 2 * I, poff, (bf16_t*)dw_gate, E, H,
-                                              I, s)));
-    return hip_status(moe::launch_wgrad_bf16(xP, H, dgu + I, 2 * I, poff, (bf16_t*)dw_up, E, H,
-                                             I, s));
+    MOE_TRY(hip_status(moe::launch_wgrad_bf16_packed(dgu, 2 * I, xPk, kpack, poff,
+                                                     (bf16_t*)dw_gate, E, I, H, 1, s)));
+    return hip_status(moe::launch_wgrad_bf16_packed(dgu + I, 2 * I, xPk, kpack, poff,
+                                                    (bf16_t*)dw_up, E, I, H, 1, s));
   }
-  return hip_status(moe::launch_wgrad_bf16(xP, H, dgu, I, poff, (bf16_t*)dw_up, E, H, I, s));
+  return hip_status(moe::launch_wgrad_bf16_packed(dgu, I, xPk, kpack, poff, (bf16_t*)dw_up, E, I,
+                                                  H, 1, s));
 }
 
 moe_status moe_workspace_view(const moe_config* cfg, void* ws, int32_t which, void** dev_ptr,
