@@ -30,15 +30,17 @@ def test_full_size_workload(name):
     torch.cuda.empty_cache()
 
 
-def test_full_size_packed_forward_is_bit_identical():
-    """The Mixtral workload on packed weights, in the bench's launch configuration: the
-    output equals the plain-weight forward bit for bit (the plain one is checked against the
-    oracle above)."""
+@pytest.mark.parametrize("name", ["mixtral", "cap32", "fine"])
+def test_full_size_packed_forward_is_bit_identical(name):
+    """Full-size workloads on packed weights, in the bench's launch configuration: the output
+    equals the plain-weight forward bit for bit (the plain one is checked against the oracle
+    above). cap32 has 32 experts and a binding capacity, fine 128 experts and an odd number
+    of n-tiles in GEMM 1 (I = 1408)."""
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     from mixture_experts_layer_37_amd.layer import MoELayer, to_device
-    cfg = C.get("mixtral")
-    print("[fullsize] mixtral packed vs plain: generating inputs", flush=True)
+    cfg = C.get(name)
+    print(f"[fullsize] {name} packed vs plain: generating inputs", flush=True)
     inputs = make_inputs(cfg, seed=0, threads=16)
     x = to_device(cfg, inputs["x"])
     plain = MoELayer(cfg, inputs)
@@ -49,7 +51,7 @@ def test_full_size_packed_forward_is_bit_identical():
     b = packed.forward(x)
     torch.cuda.synchronize()
     same = torch.equal(a.view(torch.int16), b.view(torch.int16))
-    print(f"[fullsize] mixtral packed vs plain: bit-identical {same}", flush=True)
+    print(f"[fullsize] {name} packed vs plain: bit-identical {same}", flush=True)
     assert same
     del packed
     torch.cuda.empty_cache()
