@@ -719,9 +719,12 @@ __device__ __forceinline__ void dma16_asm(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :: "v"(src), "s"(lds) : "memory", "m0");
 }
-__device__ __forceinline__ bf16x8 load16_asm(const bf16_t* p) {
+// 16 bytes per lane global -> registers, from p + OFF bytes (OFF in the instruction's
+// immediate field, so the slices of one k-step share one address computation).
+template <int OFF>
+__device__ __forceinline__ bf16x8 load16_asm_at(const bf16_t* p) {
   bf16x8 v;
-  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+  asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "=v"(v) : "v"(p), "n"(OFF) : "memory");
   return v;
 }
 // Wait until at most N of this wave's loads are in flight. The four fragments pass through
@@ -818,9 +821,12 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
     // flight will overwrite.
     constexpr int kLB = 4;   // B loads per k slice (one per fragment j)
     constexpr int kLA = 8;   // A DMA loads per k-step
-    auto load_b = [&](int s, int slot) {
+    // B slice kk (0..3) of the k-step whose first slice is at base[j] (slices are 1 KB
+    // apart: one address per k-step, the slice in the immediate offset)
+    auto load_b = [&](const bf16_t* const* base, auto kk, int slot) {
 #pragma unroll
-      for (int j = 0; j < kLB; ++j) bv[slot][j] = load16_asm(bsrc[j] + (size_t)s * 512);
+      for (int j = 0; j < kLB; ++j)
+        bv[slot][j] = load16_asm_at<decltype(kk)::value * 1024>(base[j]);
     };
     auto dma_a = [&](int kt, bf16_t* stg) {
       const uint32_t kA = (uint32_t)(kt * BK * 2);
@@ -847,11 +853,11 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
     // One k slice: wait for its B fragments, issue the next slice's A reads and (ahead by
     // one k-step) the B loads of slice s + 4, then the 16 MFMAs.
     auto phase = [&](const bf16_t* stg, int kk_next, FragA& nxt, const FragA& cur, int slot,
-                     int s_ahead, bool ahead, auto wait) {
+                     const bf16_t* const* nbase, auto kk, bool ahead, auto wait) {
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
       wait_loads<decltype(wait)::value>(bv[slot]);
       load_a(stg, kk_next, nxt);
-      if (ahead) load_b(s_ahead, (slot + 4) & 7);
+      if (ahead) load_b(nbase, kk, (slot + 4) & 7);
       mfma16(cur, slot);
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // the A reads
       __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // then the MFMAs
@@ -873,9 +879,16 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
       // B(4kt+2): then A(kt+1), B(4kt+3), B(4kt+4), B(4kt+5)
       using W2 = std::integral_constant<int, kLB + n1 * (kLA + 2 * kLB)>;
       static_assert(W0::value < 64 && W1::value < 64 && W2::value < 64, "vmcnt is 6 bits");
-      phase(cur, 1, f1, f0, sb + 0, 4 * kt + 4, n1, W0{});
-      phase(cur, 2, f0, f1, sb + 1, 4 * kt + 5, n1, W1{});
-      phase(cur, 3, f1, f0, sb + 2, 4 * kt + 6, n1, W2{});
+      using S0 = std::integral_constant<int, 0>;
+      using S1 = std::integral_constant<int, 1>;
+      using S2 = std::integral_constant<int, 2>;
+      using S3 = std::integral_constant<int, 3>;
+      const bf16_t* nbase[kLB];   // slice 4(kt+1) of each fragment: B(4kt+4) .. B(4kt+7)
+#pragma unroll
+      for (int j = 0; j < kLB; ++j) nbase[j] = bsrc[j] + (size_t)(kt + 1) * 2048;
+      phase(cur, 1, f1, f0, sb + 0, nbase, S0{}, n1, W0{});
+      phase(cur, 2, f0, f1, sb + 1, nbase, S1{}, n1, W1{});
+      phase(cur, 3, f1, f0, sb + 2, nbase, S2{}, n1, W2{});
       // A(kt+1): then B(4kt+3) .. B(4kt+6)
       if constexpr (n1) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(4 * kLB));
       else __builtin_amdgcn_s_waitcnt(0);
@@ -886,7 +899,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
       if constexpr (decltype(refill)::value) dma_a(kt + 2, cur);
       if constexpr (n1) {
         load_a(nxt, 0, f0);
-        load_b(4 * kt + 7, (sb + 7) & 7);
+        load_b(nbase, S3{}, (sb + 7) & 7);
       }
       mfma16(f1, sb + 3);
       __builtin_amdgcn_sched_barrier(0);
@@ -896,11 +909,16 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
     // prologue: A(kb) landed, then B(4kb) .. B(4kb+2), A(kb+1), B(4kb+3) in flight
     dma_a(kb, sa0);
     __builtin_amdgcn_s_waitcnt(0);
-    load_b(4 * kb + 0, 0);
-    load_b(4 * kb + 1, 1);
-    load_b(4 * kb + 2, 2);
-    dma_a(kb + 1, sa1);
-    load_b(4 * kb + 3, 3);
+    {
+      const bf16_t* pbase[kLB];   // slice 4kb of each fragment
+#pragma unroll
+      for (int j = 0; j < kLB; ++j) pbase[j] = bsrc[j] + (size_t)kb * 2048;
+      load_b(pbase, std::integral_constant<int, 0>{}, 0);
+      load_b(pbase, std::integral_constant<int, 1>{}, 1);
+      load_b(pbase, std::integral_constant<int, 2>{}, 2);
+      dma_a(kb + 1, sa1);
+      load_b(pbase, std::integral_constant<int, 3>{}, 3);
+    }
     __syncthreads();
     load_a(sa0, 0, f0);
     int kt = kb;   // ke - kb is even
@@ -1111,9 +1129,12 @@ __global__ __launch_bounds__(256, 1) void grouped_wgrad_packed_kernel(
     bf16x8 bv[8][4];
     constexpr int kLB = 4;   // B loads per k slice
     constexpr int kLA = 8;   // A DMA loads per k-step (4 rows x 2 halves)
-    auto load_b = [&](int s, int slot) {
+    // B slice kk (0..3) of the k-step whose first slice is at base[j] (slices are 1 KB
+    // apart: one address per k-step, the slice in the immediate offset)
+    auto load_b = [&](const bf16_t* const* base, auto kk, int slot) {
 #pragma unroll
-      for (int j = 0; j < kLB; ++j) bv[slot][j] = load16_asm(bsrc[j] + (size_t)s * 512);
+      for (int j = 0; j < kLB; ++j)
+        bv[slot][j] = load16_asm_at<decltype(kk)::value * 1024>(base[j]);
     };
     auto dma_a = [&](int kt, bf16_t* stg) {
       const size_t kA = (size_t)kt * BK * lda * 2;
@@ -1141,11 +1162,11 @@ __global__ __launch_bounds__(256, 1) void grouped_wgrad_packed_kernel(
     };
     FragA f0, f1;
     auto phase = [&](const bf16_t* stg, int kk_next, FragA& nxt, const FragA& cur, int slot,
-                     int s_ahead, bool ahead, auto wait) {
+                     const bf16_t* const* nbase, auto kk, bool ahead, auto wait) {
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
       wait_loads<decltype(wait)::value>(bv[slot]);
       load_a(stg, kk_next, nxt);
-      if (ahead) load_b(s_ahead, (slot + 4) & 7);
+      if (ahead) load_b(nbase, kk, (slot + 4) & 7);
       mfma16(cur, slot);
       __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // the A reads
       __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // then the MFMAs
@@ -1158,9 +1179,16 @@ __global__ __launch_bounds__(256, 1) void grouped_wgrad_packed_kernel(
       using W1 = std::integral_constant<int, 2 * kLB + n1 * (kLA + kLB)>;
       using W2 = std::integral_constant<int, kLB + n1 * (kLA + 2 * kLB)>;
       static_assert(W0::value < 64 && W1::value < 64 && W2::value < 64, "vmcnt is 6 bits");
-      phase(cur, 1, f1, f0, sb + 0, 4 * kt + 4, n1, W0{});
-      phase(cur, 2, f0, f1, sb + 1, 4 * kt + 5, n1, W1{});
-      phase(cur, 3, f1, f0, sb + 2, 4 * kt + 6, n1, W2{});
+      using S0 = std::integral_constant<int, 0>;
+      using S1 = std::integral_constant<int, 1>;
+      using S2 = std::integral_constant<int, 2>;
+      using S3 = std::integral_constant<int, 3>;
+      const bf16_t* nbase[kLB];   // slice 4(kt+1) of each fragment: B(4kt+4) .. B(4kt+7)
+#pragma unroll
+      for (int j = 0; j < kLB; ++j) nbase[j] = bsrc[j] + (size_t)(kt + 1) * 2048;
+      phase(cur, 1, f1, f0, sb + 0, nbase, S0{}, n1, W0{});
+      phase(cur, 2, f0, f1, sb + 1, nbase, S1{}, n1, W1{});
+      phase(cur, 3, f1, f0, sb + 2, nbase, S2{}, n1, W2{});
       if constexpr (n1) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(4 * kLB));
       else __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
@@ -1169,7 +1197,7 @@ __global__ __launch_bounds__(256, 1) void grouped_wgrad_packed_kernel(
       if constexpr (decltype(refill)::value) dma_a(kt + 2, cur);
       if constexpr (n1) {
         load_a(nxt, 0, f0);
-        load_b(4 * kt + 7, (sb + 7) & 7);
+        load_b(nbase, S3{}, (sb + 7) & 7);
       }
       mfma16(f1, sb + 3);
       __builtin_amdgcn_sched_barrier(0);
@@ -1179,11 +1207,11 @@ __global__ __launch_bounds__(256, 1) void grouped_wgrad_packed_kernel(
     if (KT > 0) {   // KT is even: the padded range is a multiple of 128 rows
       dma_a(0, sa0);
       __builtin_amdgcn_s_waitcnt(0);
-      load_b(0, 0);
-      load_b(1, 1);
-      load_b(2, 2);
+      load_b(bsrc, std::integral_constant<int, 0>{}, 0);
+      load_b(bsrc, std::integral_constant<int, 1>{}, 1);
+      load_b(bsrc, std::integral_constant<int, 2>{}, 2);
       dma_a(1, sa1);
-      load_b(3, 3);
+      load_b(bsrc, std::integral_constant<int, 3>{}, 3);
       __syncthreads();
       load_a(sa0, 0, f0);
       int kt = 0;
