@@ -49,10 +49,10 @@ def parse_args():
     return ap.parse_args()
 
 
-def kernel_source_digest() -> str:
+def kernel_source_digest(path: str | None = None) -> str:
     """Digest of the GEMM source with comments and whitespace removed, so that an edit of
     comments alone keeps the committed counter summary valid."""
-    p = os.path.join(ROOT, "mixture_experts_layer_37_amd", "csrc", "gemm.hip")
+    p = path or os.path.join(ROOT, "mixture_experts_layer_37_amd", "csrc", "gemm.hip")
     text = re.sub(r"//[^\n]*", "", open(p, encoding="utf-8").read())
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return hashlib.sha256("".join(text.split()).encode()).hexdigest()[:16]
