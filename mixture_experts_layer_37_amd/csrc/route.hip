@@ -111,200 +111,378 @@ __device__ bool topk_token(const float* L, int E, int k, int renorm, int thr, do
 }
 
 int route_padded_experts(int E) {
-  return E <= 16 ? 16 : E <= 32 ? 32 : E <= 64 ? 64 : E <= 128 ? 128 : 256;
+  return E <= 32 ? 32 : E <= 64 ? 64 : E <= 128 ? 128 : 256;
 }
 
-// WT[e][h] = W[h][e] for e < E, 0 for E <= e < E_pad. One thread per (e, 8 consecutive h).
-__global__ __launch_bounds__(256) void router_transpose_kernel(const bf16_t* __restrict__ w,
-                                                               bf16_t* __restrict__ wt, int H,
-                                                               int E, int EP) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  const int e = i % EP, hc = i / EP;
-  if (hc * 8 >= H) return;
+// Router weights W[H][E] -> MFMA B operands in load order: WP[nb][s][l] (16 bytes per lane) =
+// W[32 s + 8 (l >> 4) + i][16 nb + (l & 15)], i = 0..7, zero for experts >= E. One k-step's
+// operand of 16 experts is then one contiguous 1 KB block. One thread per 16-byte chunk.
+__global__ __launch_bounds__(256) void router_pack_kernel(const bf16_t* __restrict__ w,
+                                                          bf16_t* __restrict__ wp, int H, int E,
+                                                          int EP) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const int S = H / 32;
+  if (i >= (long)(EP / 16) * S * 64) return;
+  const int l = (int)(i & 63);
+  const long bs = i >> 6;
+  const int s = (int)(bs % S), nb = (int)(bs / S);
+  const int e = nb * 16 + (l & 15);
+  const int k0 = s * 32 + 8 * (l >> 4);
   uint32_t d[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     uint32_t lo = 0, hi = 0;
     if (e < E) {
-      lo = w[(size_t)(hc * 8 + 2 * q) * E + e];
-      hi = w[(size_t)(hc * 8 + 2 * q + 1) * E + e];
+      lo = w[(size_t)(k0 + 2 * q) * E + e];
+      hi = w[(size_t)(k0 + 2 * q + 1) * E + e];
     }
     d[q] = lo | (hi << 16);
   }
-  *(uint4*)(wt + (size_t)e * H + hc * 8) = make_uint4(d[0], d[1], d[2], d[3]);
+  *(uint4*)(wp + i * 8) = make_uint4(d[0], d[1], d[2], d[3]);
 }
 
 hipError_t launch_router_transpose(const bf16_t* w, bf16_t* wt, int H, int E, hipStream_t s) {
   const int EP = route_padded_experts(E);
-  const long n = (long)EP * (H / 8);
+  const long n = (long)(EP / 16) * (H / 32) * 64;
   const int blocks = (int)((n + 255) / 256);
-  hipLaunchKernelGGL(router_transpose_kernel, dim3(blocks), dim3(256), 0, s, w, wt, H, E, EP);
+  hipLaunchKernelGGL(router_pack_kernel, dim3(blocks), dim3(256), 0, s, w, wt, H, E, EP);
   return hipGetLastError();
 }
 
-// Gate GEMM on MFMA + top-k. A block of 4 waves owns BT = 16*TG tokens; wave w sums over
-// its quarter of H, the four partial [BT x 16*NBE] tiles are added in a fixed order through
-// LDS, then threads 0..BT-1 each select the experts of one token.
-template <int TG, int NBE, int KMAX>
-__global__ __launch_bounds__(256) void route_mfma_kernel(
-    const bf16_t* __restrict__ x, const bf16_t* __restrict__ wt, const float* __restrict__ bias,
+// DPP lane moves inside rows of 16 lanes (quad_perm and mirror controls).
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2, 3, 0, 1]
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+  const unsigned long long u = __double_as_longlong(v);
+  const int lo = dpp_i<CTRL>((int)(u & 0xffffffffu)), hi = dpp_i<CTRL>((int)(u >> 32));
+  return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
+}
+// (key, id) pair order of the selection: larger key first, then the lower expert id.
+__device__ __forceinline__ bool pair_before(int ka, int ia, int kb, int ib) {
+  return ka > kb || (ka == kb && ia < ib);
+}
+// Best pair over the 4 lanes of a quad, identical in all of them.
+template <int CTRL>
+__device__ __forceinline__ void quad_best_step(int& key, int& id) {
+  const int ok = dpp_i<CTRL>(key), oi = dpp_i<CTRL>(id);
+  if (pair_before(ok, oi, key, id)) { key = ok; id = oi; }
+}
+
+// Gate GEMM on MFMA + top-k for gates the streaming router does not take (E up to 256, any
+// H that is a multiple of 256). A block of 8 waves owns BT tokens; wave (tw, ew, kw) computes
+// TGW token groups of 16 x NBW expert blocks of 16 over its share (1 / KW) of each piece of
+// H. Token rows are shared by all waves through LDS: a piece is BT rows x 128 PW k, loaded
+// as 16-byte register loads that each cover four whole 256-byte row pieces (fully
+// coalesced), D pieces in flight, written to one of two LDS buffers (16-byte chunk c of row r
+// at c ^ (r & 15): conflict-free) and read back as v_mfma_f32_16x16x32_bf16 operands (fp32
+// accumulation). The router weight comes in packed form (router_pack_kernel), one 1 KB load
+// per k-step and expert block, straight into registers, from L2 after the first blocks.
+// The KW partial sums of a logit are added in a fixed order through LDS (deterministic).
+// Selection: 4 lanes per token, each holding every 4th expert; k rounds each take the best
+// remaining (key, id) pair of the quad -- so the lower index wins ties, as in topk_token --
+// and the weights follow topk_token's formulas in float64, the sums spread over the quad in
+// a fixed order.
+template <int BT, int TW, int EW, int KW, int NBW, int PW, int D>
+__global__ __launch_bounds__(512, 1) void route_wide_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ wp, const float* __restrict__ bias,
     float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     int32_t* __restrict__ flags, int T, int H, int E, int k, int renorm, int thr, double delta) {
-  constexpr int BT = TG * 16, EP = NBE * 16, LDR = EP + 1;
-  constexpr int U = (TG + NBE) >= 12 ? 1 : (12 / (TG + NBE) < 8 ? 12 / (TG + NBE) : 8);
-  __shared__ float red[2][BT * LDR];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  static_assert(TW * EW * KW == 8, "eight waves");
+  static_assert(D % 2 == 0, "weight register sets alternate with the pieces");
+  constexpr int TGW = BT / (16 * TW);   // token groups per wave
+  constexpr int EP = EW * NBW * 16;     // padded experts
+  constexpr int SUB = BT * 128;         // elements of one [BT][128] sub-piece
+  constexpr int PIECE = SUB * PW;
+  constexpr int XL = BT * PW / 32;      // 1 KB x loads per wave per piece
+  constexpr int QS = 4 * PW;            // k-steps per piece
+  constexpr int QW = QS / KW;           // k-steps per wave per piece
+  constexpr int LDL = EP + 1;           // logit tile row stride (floats)
+  constexpr int G = 4, EPL = EP / G;    // lanes per token in the selection, experts per lane
+  static_assert(TGW >= 1 && XL >= 1 && QW >= 1 && BT <= 128, "block shape");
+  __shared__ __attribute__((aligned(1024))) bf16_t xs[2 * PIECE];
+  __shared__ float lt[BT * LDL];
+  __shared__ int nfs[BT];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kw = wave % KW, ew = (wave / KW) % EW, tw = wave / (KW * EW);
   const int t0 = blockIdx.x * BT;
-  const int nchunk = H / 32;
-  const int c0 = wave * nchunk / 4, c1 = (wave + 1) * nchunk / 4;
+  const int S = H / 32;
+  const int NP = H / (128 * PW);
 
-  f32x4 acc[TG][NBE];
+  // x loads of this wave: load i covers rows 4 rg .. 4 rg + 3 of sub-piece sp
+  const bf16_t* xsrc[XL];
+  int xdst[XL];
 #pragma unroll
-  for (int g = 0; g < TG; ++g)
-#pragma unroll
-    for (int n = 0; n < NBE; ++n) acc[g][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const bf16_t* xr[TG];
-#pragma unroll
-  for (int g = 0; g < TG; ++g) {
-    int row = t0 + g * 16 + (lane & 15);
-    row = row < T ? row : T - 1;
-    xr[g] = x + (size_t)row * H + (lane >> 4) * 8;
+  for (int i = 0; i < XL; ++i) {
+    const int gi = wave * XL + i, sp = gi / (BT / 4), rg = gi % (BT / 4);
+    const int r = 4 * rg + (lane >> 4), c = lane & 15;
+    xsrc[i] = x + (size_t)min(t0 + r, T - 1) * H + sp * 128 + c * 8;
+    xdst[i] = sp * SUB + r * 128 + ((c ^ (r & 15)) << 3);
   }
-  const bf16_t* wr[NBE];
+  // packed weight operands of this wave: expert block ew * NBW + j, k-step p * QS + kw * QW + q
+  const bf16_t* wsrc[NBW];
 #pragma unroll
-  for (int n = 0; n < NBE; ++n) wr[n] = wt + (size_t)(n * 16 + (lane & 15)) * H + (lane >> 4) * 8;
+  for (int j = 0; j < NBW; ++j)
+    wsrc[j] = wp + ((size_t)(ew * NBW + j) * S + kw * QW) * 512 + lane * 8;
 
-  int c = c0;
-  for (; c + U <= c1; c += U) {
-    bf16x8 a[U][TG], b[U][NBE];
+  bf16x8 xr[D][XL];
+  bf16x8 wr[D][QW][NBW];
+  auto load_x = [&](int p, bf16x8* v) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-#pragma unroll
-      for (int g = 0; g < TG; ++g) a[u][g] = *(const bf16x8*)(xr[g] + (c + u) * 32);
-#pragma unroll
-      for (int n = 0; n < NBE; ++n) b[u][n] = *(const bf16x8*)(wr[n] + (c + u) * 32);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int g = 0; g < TG; ++g)
-#pragma unroll
-        for (int n = 0; n < NBE; ++n)
-          acc[g][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][g], b[u][n], acc[g][n], 0, 0, 0);
-  }
-  for (; c < c1; ++c) {
-    bf16x8 a[TG], b[NBE];
-#pragma unroll
-    for (int g = 0; g < TG; ++g) a[g] = *(const bf16x8*)(xr[g] + c * 32);
-#pragma unroll
-    for (int n = 0; n < NBE; ++n) b[n] = *(const bf16x8*)(wr[n] + c * 32);
-#pragma unroll
-    for (int g = 0; g < TG; ++g)
-#pragma unroll
-      for (int n = 0; n < NBE; ++n)
-        acc[g][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[g], b[n], acc[g][n], 0, 0, 0);
-  }
-
-  // Fixed-order reduction of the four K-quarters: (w0 + w2) + (w1 + w3).
-  // MFMA 16x16 output: lane holds column (expert) lane&15, rows 4*(lane>>4) + r.
-  auto tile_at = [&](float* buf, int g, int n, int r) -> float& {
-    return buf[(g * 16 + (lane >> 4) * 4 + r) * LDR + n * 16 + (lane & 15)];
+    for (int i = 0; i < XL; ++i) v[i] = *(const bf16x8*)(xsrc[i] + (size_t)p * 128 * PW);
   };
-  if (wave >= 2) {
+  auto load_w = [&](int p, bf16x8 (*v)[NBW]) {
 #pragma unroll
-    for (int g = 0; g < TG; ++g)
+    for (int q = 0; q < QW; ++q)
 #pragma unroll
-      for (int n = 0; n < NBE; ++n)
+      for (int j = 0; j < NBW; ++j) v[q][j] = *(const bf16x8*)(wsrc[j] + ((size_t)p * QS + q) * 512);
+  };
+
+  f32x4 acc[TGW][NBW];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) tile_at(red[wave - 2], g, n, r) = acc[g][n][r];
+  for (int g = 0; g < TGW; ++g)
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) acc[g][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // A wave's vector loads complete in issue order, so piece p's token rows and weights are
+  // both issued D pieces ahead (a ring of D register sets): waiting for them never waits for
+  // a later piece. Issue order: pieces 0 .. D - 1 (kept by the scheduling barriers), then in
+  // step p the rows of piece p + D right after their registers are written to LDS and its
+  // weights after the MFMAs that read the set. D divides NP, so the loop body has no branch
+  // and every wait is an exact count; prefetches past the last piece re-read it.
+#pragma unroll
+  for (int u = 0; u < D; ++u) {
+    load_x(min(u, NP - 1), xr[u]);
+    load_w(min(u, NP - 1), wr[u]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int p0 = 0; p0 < NP; p0 += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      const int p = p0 + u;
+      bf16_t* buf = xs + (p & 1) * PIECE;
+#pragma unroll
+      for (int i = 0; i < XL; ++i) *(bf16x8*)(buf + xdst[i]) = xr[u][i];
+      load_x(min(p + D, NP - 1), xr[u]);
+      // this piece is in LDS for every wave; every wave is done with the buffer's previous
+      // piece (its reads fed MFMAs issued before this point). No wait on the loads in flight.
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+      for (int q = 0; q < QW; ++q) {
+        const int qq = kw * QW + q;
+        const int sp = qq >> 2, c = 4 * (qq & 3) + (lane >> 4);
+        bf16x8 a[TGW];
+#pragma unroll
+        for (int g = 0; g < TGW; ++g) {
+          const int r = (tw * TGW + g) * 16 + (lane & 15);
+          a[g] = *(const bf16x8*)(buf + sp * SUB + r * 128 + ((c ^ (r & 15)) << 3));
+        }
+#pragma unroll
+        for (int g = 0; g < TGW; ++g)
+#pragma unroll
+          for (int j = 0; j < NBW; ++j)
+            acc[g][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[g], wr[u][q][j], acc[g][j],
+                                                                0, 0, 0);
+      }
+      load_w(min(p + D, NP - 1), wr[u]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // Logit tile [BT][EP]: MFMA 16x16 output, lane holds expert lane & 15 of tokens
+  // 4 (lane >> 4) + r. The KW k-shares are added in the order ((kw 0 + kw 1) + kw 2) + ..,
+  // then the gate bias.
+  auto tile = [&](int g, int j, int r) -> float& {
+    return lt[((tw * TGW + g) * 16 + 4 * (lane >> 4) + r) * LDL + (ew * NBW + j) * 16 +
+              (lane & 15)];
+  };
+#pragma unroll
+  for (int kk = 1; kk < KW; ++kk) {
+    if (kw == kk) {
+#pragma unroll
+      for (int g = 0; g < TGW; ++g)
+#pragma unroll
+        for (int j = 0; j < NBW; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) tile(g, j, r) = acc[g][j][r];
+    }
+    __syncthreads();
+    if (kw == 0) {
+#pragma unroll
+      for (int g = 0; g < TGW; ++g)
+#pragma unroll
+        for (int j = 0; j < NBW; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[g][j][r] += tile(g, j, r);
+    }
+    __syncthreads();
+  }
+  if (kw == 0) {
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+      const int e = (ew * NBW + j) * 16 + (lane & 15);
+      const float b = (bias != nullptr && e < E) ? bias[e] : 0.f;
+#pragma unroll
+      for (int g = 0; g < TGW; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tile(g, j, r) = acc[g][j][r] + b;
+    }
   }
   __syncthreads();
-  if (wave < 2) {
-#pragma unroll
-    for (int g = 0; g < TG; ++g)
-#pragma unroll
-      for (int n = 0; n < NBE; ++n)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[g][n][r] += tile_at(red[wave], g, n, r);
+  for (int i = tid; i < BT * E; i += blockDim.x) {
+    const int tt = i / E, e = i - tt * E;
+    if (t0 + tt < T) logits[(size_t)(t0 + tt) * E + e] = lt[tt * LDL + e];
   }
-  __syncthreads();
-  if (wave == 1) {
+
+  // Selection and weights: quad (tid >> 2) owns token tt; lane gl holds experts gl + 4 i.
+  const int tt = tid >> 2, gl = tid & 3;
+  const int t = t0 + tt;
+  if (tt < BT) {
+    const float* row = lt + tt * LDL;
+    int key[EPL];
+    int nan_l = 0, nf_l = 0;
 #pragma unroll
-    for (int g = 0; g < TG; ++g)
+    for (int i = 0; i < EPL; ++i) {
+      const int e = gl + G * i;
+      key[i] = INT_MIN;   // below every real key (NaN maps to INT_MIN + 1)
+      if (e < E) {
+        const float v = row[e];
+        key[i] = order_key(v);
+        nan_l |= (v != v);
+        nf_l |= !__builtin_isfinite(v);
+      }
+    }
+    nan_l |= dpp_i<kDppXor1>(nan_l);
+    nan_l |= dpp_i<kDppXor2>(nan_l);
+    nf_l |= dpp_i<kDppXor1>(nf_l);
+    nf_l |= dpp_i<kDppXor2>(nf_l);
+    // k rounds; lane gl keeps the ids of slots gl, gl + 4, ... (k <= 16)
+    int sid[4] = {-1, -1, -1, -1};
+    int id0 = 0;
+    for (int j = 0; j < k; ++j) {
+      int bk = INT_MIN, bi = INT_MAX;
 #pragma unroll
-      for (int n = 0; n < NBE; ++n)
+      for (int i = 0; i < EPL; ++i)
+        if (key[i] > bk) { bk = key[i]; bi = gl + G * i; }   // ascending ids: lowest id wins
+      quad_best_step<kDppXor1>(bk, bi);
+      quad_best_step<kDppXor2>(bk, bi);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) tile_at(red[0], g, n, r) = acc[g][n][r];
-  }
-  __syncthreads();
-  if (wave == 0) {
+      for (int i = 0; i < EPL; ++i)
+        if (gl + G * i == bi) key[i] = INT_MIN;
+      if (j == 0) id0 = bi;
 #pragma unroll
-    for (int g = 0; g < TG; ++g)
+      for (int s = 0; s < 4; ++s)
+        if (j == gl + G * s) sid[s] = bi;
+    }
+    const double top = (double)row[id0];
+    // ev of this lane's slots; sums over the quad in a fixed order
+    double ev[4];
 #pragma unroll
-      for (int n = 0; n < NBE; ++n) {
-        const int e = n * 16 + (lane & 15);
-        const float b = (bias != nullptr && e < E) ? bias[e] : 0.f;
+    for (int s = 0; s < 4; ++s) ev[s] = sid[s] >= 0 ? exp((double)row[sid[s]] - top) : 0.0;
+    auto quad_sum = [&](double v) {
+      v += dpp_d<kDppXor1>(v);
+      return v + dpp_d<kDppXor2>(v);
+    };
+    double all = 0.0;
+    if (thr || !renorm) {
+      double a = 0.0;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float& slot = tile_at(red[0], g, n, r);
-          slot = (acc[g][n][r] + slot) + b;
+      for (int i = 0; i < EPL; ++i) {
+        const int e = gl + G * i;
+        if (e < E) a += exp((double)row[e] - top);
+      }
+      all = quad_sum(a);
+    }
+    int cnt = k;
+    if (thr) {
+      // leading slots whose softmax score exceeds delta
+      int pass = 0;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        if (sid[s] >= 0 && ev[s] / all > delta) pass |= 1 << (gl + G * s);
+      pass |= dpp_i<kDppXor1>(pass);
+      pass |= dpp_i<kDppXor2>(pass);
+      cnt = min(k, __builtin_ctz(~pass));
+    }
+    double ssum;
+    if (renorm) {
+      double a = 0.0;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        if (gl + G * s < cnt) a += ev[s];
+      ssum = quad_sum(a);
+    } else {
+      ssum = all;
+    }
+    if (t < T) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int j = gl + G * s;
+        if (j < cnt) {
+          topk_idx[(size_t)t * k + j] = sid[s];
+          topk_w[(size_t)t * k + j] = nan_l ? __builtin_nanf("") : (float)(ev[s] / ssum);
+        } else if (j < k) {
+          topk_idx[(size_t)t * k + j] = -1;
+          topk_w[(size_t)t * k + j] = 0.f;
         }
       }
+    }
+    if (gl == 0) nfs[tt] = (t < T) ? nf_l : 0;
   }
   __syncthreads();
-
-  const float* Ls = red[0];
-  for (int i = threadIdx.x; i < BT * E; i += blockDim.x) {
-    const int t = i / E, e = i - t * E;
-    if (t0 + t < T) logits[(size_t)(t0 + t) * E + e] = Ls[t * LDR + e];
-  }
-  if (threadIdx.x < 64) {
-    bool nf = false;
-    const int t = t0 + threadIdx.x;
-    if (threadIdx.x < BT && t < T)
-      nf = topk_token<KMAX>(Ls + threadIdx.x * LDR, E, k, renorm, thr, delta,
-                            topk_idx + (size_t)t * k,
-                            topk_w + (size_t)t * k);
-    const unsigned long long m = __ballot(nf);
-    const int ngroups = (T + kRouteFlagGroup - 1) / kRouteFlagGroup;
-    if (threadIdx.x < TG && blockIdx.x * TG + threadIdx.x < ngroups)
-      flags[blockIdx.x * TG + threadIdx.x] =
-          ((m >> (16 * threadIdx.x)) & 0xffffull) ? 2 /* MOE_FLAG_NONFINITE_LOGIT */ : 0;
+  const int ngroups = (T + kRouteFlagGroup - 1) / kRouteFlagGroup;
+  constexpr int FG = BT / kRouteFlagGroup;
+  if (tid < FG && (t0 / kRouteFlagGroup) + tid < ngroups) {
+    int any = 0;
+    for (int i = 0; i < kRouteFlagGroup; ++i) any |= nfs[tid * kRouteFlagGroup + i];
+    flags[t0 / kRouteFlagGroup + tid] = any ? 2 /* MOE_FLAG_NONFINITE_LOGIT */ : 0;
   }
 }
 
-template <int TG, int NBE>
-static hipError_t launch_route_tg(const bf16_t* x, const bf16_t* wt, const float* bias,
-                                  float* logits, int32_t* idx, float* w, int32_t* flags, int T,
-                                  int H, int E, int k, int renorm, int thr, double delta,
-                                  hipStream_t s) {
-  const dim3 grid((T + TG * 16 - 1) / (TG * 16)), block(256);
-#define MOE_ROUTE_LAUNCH(KM)                                                                  \
-  hipLaunchKernelGGL((route_mfma_kernel<TG, NBE, KM>), grid, block, 0, s, x, wt, bias, logits, \
-                     idx, w, flags, T, H, E, k, renorm, thr, delta)
-  if (k <= 1) MOE_ROUTE_LAUNCH(1);
-  else if (k <= 2) MOE_ROUTE_LAUNCH(2);
-  else if (k <= 4) MOE_ROUTE_LAUNCH(4);
-  else if (k <= 8) MOE_ROUTE_LAUNCH(8);
-  else MOE_ROUTE_LAUNCH(16);
-#undef MOE_ROUTE_LAUNCH
+template <int BT, int TW, int EW, int KW, int NBW, int PW>
+static hipError_t launch_route_wide(const bf16_t* x, const bf16_t* wp, const float* bias,
+                                    float* logits, int32_t* idx, float* w, int32_t* flags, int T,
+                                    int H, int E, int k, int renorm, int thr, double delta,
+                                    hipStream_t s) {
+  const int NP = H / (128 * PW);   // pieces (even); the ring depth divides it
+  const dim3 grid((T + BT - 1) / BT), block(512);
+#define MOE_ROUTE_WIDE_D(DD)                                                                  \
+  hipLaunchKernelGGL((route_wide_kernel<BT, TW, EW, KW, NBW, PW, DD>), grid, block, 0, s, x, wp, \
+                     bias, logits, idx, w, flags, T, H, E, k, renorm, thr, delta)
+  if (NP % 4 == 0) MOE_ROUTE_WIDE_D(4);
+  else MOE_ROUTE_WIDE_D(2);
+#undef MOE_ROUTE_WIDE_D
   return hipGetLastError();
 }
 
 hipError_t launch_route_bf16(const bf16_t* x, const bf16_t* wt, const float* bias, float* logits,
                              int32_t* idx, float* w, int32_t* flags, int T, int H, int E, int k,
                              int renorm, int thr, double delta, hipStream_t s) {
-#define MOE_ROUTE_TG(A, B) \
-  launch_route_tg<A, B>(x, wt, bias, logits, idx, w, flags, T, H, E, k, renorm, thr, delta, s)
+  if (H % 256 != 0 || k > 16 || k > E) return hipErrorInvalidValue;
+#define MOE_ROUTE_WIDE(...) \
+  launch_route_wide<__VA_ARGS__>(x, wt, bias, logits, idx, w, flags, T, H, E, k, renorm, thr, delta, s)
+  // widest piece (PW x 128 k) that leaves an even number of pieces; H / 128 is even
+  const int h128 = H / 128;
+  const int pw = h128 % 8 == 0 ? 4 : h128 % 4 == 0 ? 2 : 1;
   switch (route_padded_experts(E)) {
-    case 16: return MOE_ROUTE_TG(1, 1);
-    case 32: return MOE_ROUTE_TG(1, 2);
-    case 64: return MOE_ROUTE_TG(2, 4);
-    case 128: return MOE_ROUTE_TG(4, 8);
-    default: return MOE_ROUTE_TG(2, 16);
+    // BT, TW, EW, KW, NBW, PW
+    case 32:
+      if (pw == 4) return MOE_ROUTE_WIDE(32, 1, 2, 4, 1, 4);
+      if (pw == 2) return MOE_ROUTE_WIDE(32, 1, 2, 4, 1, 2);
+      return MOE_ROUTE_WIDE(32, 1, 2, 4, 1, 1);
+    case 64:
+      if (pw >= 2) return MOE_ROUTE_WIDE(64, 1, 4, 2, 1, 2);
+      return MOE_ROUTE_WIDE(64, 1, 4, 2, 1, 1);
+    case 128: return MOE_ROUTE_WIDE(128, 1, 8, 1, 1, 1);
+    default: return MOE_ROUTE_WIDE(64, 1, 8, 1, 2, 1);
   }
-#undef MOE_ROUTE_TG
+#undef MOE_ROUTE_WIDE
 }
 
 // ---------------------------------------------------------------------------------------
