@@ -138,6 +138,52 @@ def test_topk_tie_suite(E, k):
     np.testing.assert_array_equal(idx2, idx[:100])
 
 
+@pytest.mark.parametrize("E,k,H,routing,renorm", [
+    (8, 2, 1024, "topk", True),        # streaming router (small gate)
+    (32, 4, 256, "topk", True),        # general router, 32-expert layout
+    (64, 8, 512, "topk", False),       # 64-expert layout, raw softmax weights
+    (128, 8, 1024, "topk", True),      # 128-expert layout
+    (256, 16, 256, "topk", True),      # 256-expert layout
+    (128, 8, 512, "threshold", True),  # threshold routing through the general router
+])
+def test_router_gemm_ties_and_nonfinite_logits(E, k, H, routing, renorm):
+    """Tied, infinite and NaN logits made by the gate GEMM itself: one-hot token rows of value
+    1 copy router rows of small integers (exact ties), rows of value +inf / -inf give +-inf
+    (NaN where the router entry is 0), an all-NaN row gives NaN logits; the rest are random.
+    Selection from the exported logits is bit-exact to the oracle's rank rule (NaN lowest,
+    lower index first), the weights agree, and the non-finite flag is raised."""
+    T = 300
+    cfg = C.SMALL.with_(tokens=T, hidden=H, inter=256, experts=E, top_k=k, bias=None,
+                        routing=routing, renormalize=renorm)
+    print(f"[case] router E={E} k={k} H={H} {routing} renorm={renorm}", flush=True)
+    rng = np.random.default_rng(E + 7 * k + H)
+    x = np.zeros((T, H), dtype=np.float32)
+    hot = np.arange(T) % H
+    x[np.arange(150), hot[:150]] = 1.0
+    x[np.arange(150, 200), hot[150:200]] = np.inf
+    x[np.arange(200, 210), hot[200:210]] = -np.inf
+    x[210] = np.nan
+    x[211:] = rng.standard_normal((T - 211, H)).astype(np.float32)
+    wr = rng.integers(-2, 3, (H, E)).astype(np.float32)
+    c = L.cconfig(cfg)
+    ws = torch.empty(L.moe_workspace_size(c), dtype=torch.uint8, device="cuda")
+    xd = to_device(cfg, f32_to_bf16_bits(x))
+    wd = to_device(cfg, f32_to_bf16_bits(wr))
+    lg = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    L.moe_route(c, xd, wd, None, lg, idx, w, ws)
+    flags = L.moe_read_device_status(c, ws, 1)
+    gl = lg.cpu().numpy()
+    np.testing.assert_array_equal(gl[:150], wr[hot[:150]])
+    with np.errstate(invalid="ignore"):
+        np.testing.assert_array_equal(gl[150:200], np.inf * wr[hot[150:200]])
+        np.testing.assert_array_equal(gl[200:210], -np.inf * wr[hot[200:210]])
+    assert np.isnan(gl[210]).all()
+    P.check_route_from_logits(gl, idx.cpu().numpy(), w.cpu().numpy(), cfg)
+    assert flags == L.MOE_FLAG_NONFINITE_LOGIT
+
+
 def test_route_entry_point_with_crafted_ties():
     """Logits made exactly equal through the gate GEMM itself: one-hot x rows pick router rows."""
     T, E, k, H = 200, 16, 4, 256
