@@ -247,6 +247,15 @@ def main():
         result["materialised_permute"]["hbm_frac_of_measured"] = (
             result["materialised_permute"]["hbm_frac"] * PEAK_HBM_GBS / peaks["hbm_copy_gbs"])
 
+    rd = one_pass_read_us(stream, x, T * H * es, step)
+    if rd is not None:
+        # the router against a plain one-pass read of the same token matrix, each timed
+        # right after a full step (the same cache state): 1.0 = as fast as reading x
+        result["route_vs_one_pass_read"] = {
+            "read_us": rd, "route_us": stage_ms["route"] * 1e3,
+            "read_gbs": T * H * es / (rd * 1e-6) / 1e9,
+            "frac": rd / (stage_ms["route"] * 1e3)}
+
     result["device_flags"] = L.moe_read_device_status(c, ws, 3, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, inp, out, logits, idx, args.cpu_sample_tokens,
@@ -352,6 +361,37 @@ def measured_peaks(stream):
     ms_copy = timed(lambda: lib.moe_peak_copy(src.data_ptr(), dst.data_ptr(), nbytes, sh))
     return {"mfma_bf16_tflops": blocks * 4 * iters * 8 * 32768 / (ms_mfma * 1e-3) / 1e12,
             "hbm_copy_gbs": 2 * nbytes / (ms_copy * 1e-3) / 1e9}
+
+
+def one_pass_read_us(stream, buf, nbytes, step, reps=7):
+    """Median time of one plain streaming read of `nbytes` of `buf` (libmoe_peaks.so's
+    moe_peak_read, 2 blocks of 256 threads per CU), each rep right after a full forward step
+    so that caches hold what they hold when the router runs. None if the probes are not
+    built."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "mixture_experts_layer_37_amd", "libmoe_peaks.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.moe_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                  ctypes.c_int, ctypes.c_void_p]
+    blocks = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+    times = []
+    for _ in range(reps):
+        step()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        rc = lib.moe_peak_read(buf.data_ptr(), nbytes, sink.data_ptr(), blocks,
+                               stream.cuda_stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if rc != 0:
+            return None
+        times.append(e0.elapsed_time(e1) * 1e3)
+    return float(sorted(times)[len(times) // 2])
 
 
 def materialised_permute(L, c, x, idx, counts, offs, rt, sr, ws, stream, T, H, k, n_kept, es):

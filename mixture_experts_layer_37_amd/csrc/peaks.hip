@@ -55,6 +55,27 @@ __global__ __launch_bounds__(256) void peak_copy_kernel(const u32x4* __restrict_
   }
 }
 
+// One pass over `n16` 16-byte chunks, grid-stride, eight loads in flight per thread; the
+// XOR of what each thread read goes to `sink` so that no load is dropped.
+__global__ __launch_bounds__(256) void peak_read_kernel(const u32x4* __restrict__ src,
+                                                        size_t n16, unsigned* __restrict__ sink) {
+  constexpr int U = 8;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  const size_t stride = (size_t)gridDim.x * blockDim.x * U;
+  for (size_t base = (size_t)blockIdx.x * blockDim.x * U + threadIdx.x; base < n16;
+       base += stride) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t i = base + (size_t)u * blockDim.x;
+      v[u] = i < n16 ? src[i] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u];
+  }
+  sink[blockIdx.x * blockDim.x + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -74,6 +95,17 @@ int moe_peak_copy(const void* src, void* dst, size_t bytes, void* stream) {
     return 1;
   hipLaunchKernelGGL(peak_copy_kernel, dim3(2048), dim3(256), 0, (hipStream_t)stream,
                      (const u32x4*)src, (u32x4*)dst, bytes / 32768);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+// Read `bytes` (a multiple of 16) of src once: `blocks` blocks of 256 threads; `sink` holds
+// blocks * 256 words.
+int moe_peak_read(const void* src, size_t bytes, unsigned* sink, int blocks, void* stream) {
+  if (src == nullptr || sink == nullptr || blocks < 1 || bytes % 16 != 0 ||
+      (uintptr_t)src % 16)
+    return 1;
+  hipLaunchKernelGGL(peak_read_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                     (const u32x4*)src, bytes / 16, sink);
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 
