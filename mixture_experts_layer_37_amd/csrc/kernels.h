@@ -11,8 +11,9 @@ namespace moe {
 
 // ---- route (route.hip). renorm: renormalised weights; thr: threshold routing with `delta`
 int route_padded_experts(int E);
-hipError_t launch_router_transpose(const bf16_t* w_router, bf16_t* wt, int H, int E,
-                                   hipStream_t s);
+// w_router [H][E] -> wt: MFMA operands [E_pad / 16][H / 32][64][8] (E_pad =
+// route_padded_experts(E)), zeros past E; the general router (launch_route_bf16) reads wt
+hipError_t launch_router_pack(const bf16_t* w_router, bf16_t* wt, int H, int E, hipStream_t s);
 hipError_t launch_route_bf16(const bf16_t* x, const bf16_t* wt, const float* bias,
                              float* logits, int32_t* topk_idx, float* topk_w, int32_t* flags,
                              int T, int H, int E, int k, int renorm, int thr, double delta,

@@ -210,7 +210,7 @@ moe_status do_route(const moe_config* c, const void* x, const void* w_router, co
                                                  delta, moe::device_cus(), s));
   if (c->dtype == MOE_DTYPE_BF16) {
     moe::bf16_t* wt = region<moe::bf16_t>(ws, L, R_WT);
-    MOE_TRY(hip_status(moe::launch_router_transpose((const moe::bf16_t*)w_router, wt, H, E, s)));
+    MOE_TRY(hip_status(moe::launch_router_pack((const moe::bf16_t*)w_router, wt, H, E, s)));
     return hip_status(moe::launch_route_bf16((const moe::bf16_t*)x, wt, bias, logits, idx, w,
                                              flags, T, H, E, k, renorm, thr, delta, s));
   }

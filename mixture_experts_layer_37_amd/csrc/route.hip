@@ -11,8 +11,9 @@
 // bf16 path: the gate GEMM runs on MFMA (v_mfma_f32_16x16x32_bf16, fp32 accumulation) and
 // x is streamed from HBM exactly once. For a small gate (E <= 16) route_stream_kernel
 // stages the token rows through LDS in coalesced pieces and keeps the router weight in
-// registers; a larger gate is first transposed into the workspace as WT[E_pad][H]
-// (route_mfma_kernel).
+// registers; a larger gate is first packed into the workspace as MFMA operands
+// (router_pack_kernel) and route_wide_kernel shares each piece of token rows among eight
+// waves through LDS.
 #include <climits>
 
 #include "common.h"
@@ -141,7 +142,7 @@ __global__ __launch_bounds__(256) void router_pack_kernel(const bf16_t* __restri
   *(uint4*)(wp + i * 8) = make_uint4(d[0], d[1], d[2], d[3]);
 }
 
-hipError_t launch_router_transpose(const bf16_t* w, bf16_t* wt, int H, int E, hipStream_t s) {
+hipError_t launch_router_pack(const bf16_t* w, bf16_t* wt, int H, int E, hipStream_t s) {
   const int EP = route_padded_experts(E);
   const long n = (long)(EP / 16) * (H / 32) * 64;
   const int blocks = (int)((n + 255) / 256);
