@@ -949,6 +949,50 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
       }
       return;
     }
+    if constexpr (!kTwoMat) {
+      // The 256 x 256 output tile leaves through LDS (the two A stages, free after the
+      // barrier above), 64 rows at a time: the fragments' 8-byte pieces scatter over 32 rows
+      // per store instruction, which made the stores of the previous tile, waited for in the
+      // next prologue, a tenth of GEMM 2's time at short K. Read back in row order, every
+      // store instruction writes two whole 512-byte rows. 16-byte chunk c of LDS row r sits
+      // at c ^ (r & 31). LDS-only barriers: the global stores are never waited for here.
+      constexpr int kRowB = 512;
+      // Tile coordinates and lane index pass through empty asm, so no address below is
+      // computed (and held in registers) across the k-loop.
+      int e_row0 = row0, e_nt = n_t, e_mrows = mrows, e_lane = lane, e_tid = tid;
+      asm volatile("" : "+s"(e_row0), "+s"(e_nt), "+s"(e_mrows));
+      asm volatile("" : "+v"(e_lane), "+v"(e_tid));
+      bf16_t* const ctile = C + (size_t)e_row0 * N + e_nt * 256;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        char* buf = (char*)((i & 1) ? sa1 : sa0);
+        const int lr = wm * 32 + (e_lane & 31);   // row of this lane's outputs in the block
+        const int lh = e_lane >> 5;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float hv[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+              hv[s] = EPI == EPI_GELU ? gelu_f(acc[i][j][4 * q + s]) : acc[i][j][4 * q + s];
+            const int chunk = wn * 16 + j * 4 + q;   // columns 8 chunk .. 8 chunk + 7
+            *(uint2*)(buf + lr * kRowB + ((chunk ^ (lr & 31)) << 4) + lh * 8) = pack4(hv);
+          }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int g = r * 256 + e_tid;     // 16-byte chunk of the 64 x 512-byte block
+          const int row = g >> 5, chunk = g & 31;
+          const int m = (row < 32 ? 0 : 128) + i * 32 + (row & 31);
+          const uint4 v = *(const uint4*)(buf + row * kRowB + ((chunk ^ (row & 31)) << 4));
+          if (m < e_mrows) *(uint4*)(ctile + (size_t)m * N + chunk * 8) = v;
+        }
+      }
+      // every wave is done reading the stages before the next tile's DMA refills them
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = wm * 128 + i * 32 + l32;
