@@ -184,6 +184,39 @@ def test_router_gemm_ties_and_nonfinite_logits(E, k, H, routing, renorm):
     assert flags == L.MOE_FLAG_NONFINITE_LOGIT
 
 
+@pytest.mark.parametrize("T,H,E,k", [
+    (333, 768, 40, 3),     # 64-expert layout, 6 pieces of 128 k: two-deep ring
+    (129, 1280, 20, 5),    # 32-expert layout, 10 pieces of 128 k: one k-step per k-share
+    (200, 2560, 17, 4),    # 32-expert layout, 10 pieces of 256 k
+    (64, 768, 100, 7),     # 128-expert layout, one block of 128 tokens, half past the end
+    (97, 1536, 200, 9),    # 256-expert layout, 12 pieces: four-deep ring
+])
+def test_general_router_shapes(T, H, E, k):
+    """The general router at hidden sizes whose piece counts take the two-deep ring or
+    narrower pieces, expert counts between the layouts' multiples of 16, and token counts
+    that end inside a block: logits against the fp64 gate GEMM, routing bit-exact from the
+    exported logits, no flags."""
+    cfg = C.SMALL.with_(tokens=T, hidden=H, inter=256, experts=E, top_k=k,
+                        bias=("normal", 0.5))
+    print(f"[case] general router T={T} H={H} E={E} k={k}", flush=True)
+    inp = make_inputs(cfg, seed=T + E)
+    c = L.cconfig(cfg)
+    ws = torch.empty(L.moe_workspace_size(c), dtype=torch.uint8, device="cuda")
+    xd = to_device(cfg, inp["x"])
+    wd = to_device(cfg, inp["w_router"])
+    bd = torch.from_numpy(np.asarray(inp["bias"], dtype=np.float32)).cuda()
+    lg = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    L.moe_route(c, xd, wd, bd, lg, idx, w, ws)
+    flags = L.moe_read_device_status(c, ws, 1)
+    gl = lg.cpu().numpy()
+    ref = O.gate_logits(as_float(cfg, inp["x"]), as_float(cfg, inp["w_router"]), inp["bias"])
+    assert np.all(np.abs(gl - ref) <= P.LOGIT_RTOL * (1.0 + np.abs(ref)))
+    P.check_route_from_logits(gl, idx.cpu().numpy(), w.cpu().numpy(), cfg)
+    assert flags == 0
+
+
 def test_route_entry_point_with_crafted_ties():
     """Logits made exactly equal through the gate GEMM itself: one-hot x rows pick router rows."""
     T, E, k, H = 200, 16, 4, 256
