@@ -32,7 +32,9 @@
 //     receives column L, rows 0..3. Both swizzles keep reads conflict-free for 32 and 64
 //     banks;
 //   - operands are issued as (W, x) so each lane's accumulators hold 4 consecutive output
-//     columns of one row, written straight to global memory as 8-byte stores;
+//     columns of one row, written straight to global memory as 8-byte stores (the packed
+//     kernel's single-matrix epilogues instead pass the tile through LDS and store whole
+//     512-byte rows);
 //   - persistent grid of one block per CU; tiles are ordered (expert, n-tile, m-tile) and
 //     run round by round: each round of the grid is a contiguous stretch of the list, cut
 //     into 8 contiguous pieces, one per XCD. The blocks sharing an XCD's L2 then work on the
