@@ -179,10 +179,11 @@ __device__ __forceinline__ void quad_best_step(int& key, int& id) {
 // TGW token groups of 16 x NBW expert blocks of 16 over its share (1 / KW) of each piece of
 // H. Token rows are shared by all waves through LDS: a piece is BT rows x 128 PW k, loaded
 // as 16-byte register loads that each cover four whole 256-byte row pieces (fully
-// coalesced), D pieces in flight, written to one of two LDS buffers (16-byte chunk c of row r
-// at c ^ (r & 15): conflict-free) and read back as v_mfma_f32_16x16x32_bf16 operands (fp32
-// accumulation). The router weight comes in packed form (router_pack_kernel), one 1 KB load
-// per k-step and expert block, straight into registers, from L2 after the first blocks.
+// coalesced), written to one of two LDS buffers (16-byte chunk c of row r at c ^ (r & 15):
+// conflict-free) and read back as v_mfma_f32_16x16x32_bf16 operands (fp32 accumulation).
+// The router weight comes in packed form (router_pack_kernel), one 1 KB load per k-step and
+// expert block, straight into registers, from L2 after the first blocks. A piece's rows and
+// weights are issued together, D pieces (2 or 4, dividing the piece count) ahead.
 // The KW partial sums of a logit are added in a fixed order through LDS (deterministic).
 // Selection: 4 lanes per token, each holding every 4th expert; k rounds each take the best
 // remaining (key, id) pair of the quad -- so the lower index wins ties, as in topk_token --
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(512, 1) void route_wide_kernel(
     float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     int32_t* __restrict__ flags, int T, int H, int E, int k, int renorm, int thr, double delta) {
   static_assert(TW * EW * KW == 8, "eight waves");
-  static_assert(D % 2 == 0, "weight register sets alternate with the pieces");
+  static_assert(D == 2 || D == 4, "ring depths the launcher picks");
   constexpr int TGW = BT / (16 * TW);   // token groups per wave
   constexpr int EP = EW * NBW * 16;     // padded experts
   constexpr int SUB = BT * 128;         // elements of one [BT][128] sub-piece
