@@ -46,8 +46,16 @@ project's design notes):
      zero. Renormalisation (R2) is over the kept experts.
   R15 backward: the gradient of sum(out * dout); the expert choice (top-k, threshold,
      capacity) is piecewise constant in the logits and contributes no gradient; the gate
-     weights' dependence on the logits is differentiated exactly. No auxiliary
-     load-balancing loss: the pages give no formula for one.
+     weights' dependence on the logits is differentiated exactly.
+  R16 auxiliary load-balancing loss. The pages describe an extra loss term that penalises
+     uneven expert load and pushes the router to spread tokens evenly (mhpn.cn/news/871594,
+     the routing chapter), scaled by MindSpeed's moe-aux-loss-coeff (0.01, at most 0.1:
+     lshu.cn/news/82007, section 5.3), but give no formula. Read as the published
+     switch-style form coeff * E * sum_e f_e P_e: f_e is the fraction of the routed
+     assignments (the valid selected slots, before any capacity drop; T*k under top-k)
+     that chose expert e, P_e the mean over the T tokens of expert e's softmax probability.
+     The counts are piecewise constant in the logits (no gradient, as R15); the gradient
+     flows through P. Off (coefficient 0) unless asked for.
 
 Every function here is pinned by tests/test_oracle_*.py against hand-worked cases, closed
 forms, brute force and invariants that do not reuse this code.
@@ -351,9 +359,31 @@ def gelu_grad(z):
     return 0.5 * (1.0 + _erf(z / math.sqrt(2.0))) + z * np.exp(-0.5 * z * z) / math.sqrt(2.0 * math.pi)
 
 
+def aux_loss(logits, idx, coeff: float) -> dict:
+    """Auxiliary load-balancing loss of reading R16 and its gradient with respect to the
+    logits, float64: loss = coeff * E * sum_e f_e P_e with f_e = count_e / sum(count) over
+    the valid selected slots of ``idx`` (ids in [0, E); -1 and invalid ids do not count) and
+    P_e = mean_t softmax(logits)[t, e]. With the counts fixed, dloss/dP_e = coeff E f_e and
+    P_e = (1/T) sum_t p[t, e], so dloss/dlogits[t, :] = p[t] (g - <p[t], g>) with
+    g = coeff E f / T (the softmax Jacobian)."""
+    L = np.asarray(logits, dtype=np.float64)
+    T, E = L.shape
+    ids = np.asarray(idx, dtype=np.int64).ravel()
+    ids = ids[(ids >= 0) & (ids < E)]
+    counts = np.bincount(ids, minlength=E).astype(np.float64)
+    n = counts.sum()
+    f = counts / n if n > 0 else np.zeros(E)
+    p = softmax(L)
+    P = p.sum(axis=0) / T if T > 0 else np.zeros(E)
+    loss = float(coeff) * E * float((f * P).sum())
+    g = float(coeff) * E * f / T if T > 0 else np.zeros(E)
+    dlogits = p * (g[None, :] - (p * g[None, :]).sum(axis=1, keepdims=True))
+    return dict(loss=loss, f=f, P=P, counts=counts, dlogits=dlogits)
+
+
 def backward(x, w_router, bias, w_gate, w_up, w_down, dout, *, top_k: int, activation: str,
              capacity_factor: float = 0.0, renormalize: bool = True, routing: str = "topk",
-             threshold=None, logits=None) -> dict:
+             threshold=None, logits=None, aux_loss_coeff: float = 0.0) -> dict:
     """Gradients of sum(out * dout) with respect to x, W_router, the gate bias and the expert
     weights, in float64, for the layer of ``forward`` (reading R15: the expert choice is a
     fixed function of the logits, so no gradient flows through the selection itself; the
@@ -371,7 +401,9 @@ def backward(x, w_router, bias, w_gate, w_up, w_down, dout, *, top_k: int, activ
       gate GEMM        dW_router = x^T dL, dbias = sum_t dL, dx += dL W_router^T
     Slots dropped by the capacity rule contribute dw = 0 but stay in the weights' sum.
     ``logits`` replaces the gate GEMM's output (as in ``forward``); the gate GEMM's own
-    gradients still use ``x`` and ``w_router``."""
+    gradients still use ``x`` and ``w_router``. With ``aux_loss_coeff`` > 0 the objective is
+    sum(out * dout) + aux_loss(logits, topk_idx, aux_loss_coeff) (reading R16): its logit
+    gradient is added to dL before the gate GEMM's gradients, and its value is returned."""
     x = np.asarray(x, dtype=np.float64)
     dout = np.asarray(dout, dtype=np.float64)
     wr = np.asarray(w_router, dtype=np.float64)
@@ -437,6 +469,11 @@ def backward(x, w_router, bias, w_gate, w_up, w_down, dout, *, top_k: int, activ
         m = kept[:, j]
         dp[np.nonzero(m)[0], idx[m, j]] += dps[m, j]
     dL = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    aux = None
+    if aux_loss_coeff > 0:
+        aux = aux_loss(L, idx, aux_loss_coeff)
+        dL = dL + aux["dlogits"]
     dx += dL @ wr.T
     return dict(dx=dx, dw_router=x.T @ dL, dbias=dL.sum(axis=0), dw_gate=dWg, dw_up=dWu,
-                dw_down=dWd, dlogits=dL, dw=dw, forward=fwd)
+                dw_down=dWd, dlogits=dL, dw=dw, forward=fwd,
+                aux_loss=None if aux is None else aux["loss"])

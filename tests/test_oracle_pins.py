@@ -535,3 +535,101 @@ def test_backward_renormalised_logit_gradient_sums_to_zero():
     mask = np.zeros_like(dL, dtype=bool)
     np.put_along_axis(mask, idx.astype(np.int64), True, axis=1)
     assert np.abs(dL[~mask]).max() < 1e-15
+
+
+# ------------------------------------------------- auxiliary load-balancing loss (R16)
+def test_aux_loss_balanced_closed_forms():
+    """Where every expert's mean probability is 1/E the loss is the coefficient itself:
+    (a) all logits equal: p = 1/E everywhere, ties send every token to experts 0..k-1, so
+    f = 1/k on those and the loss is coeff * E * k * (1/k)(1/E); (b) E tokens, token t
+    one-hot at expert t (k = 1): f = 1/E and, by symmetry, P = 1/E."""
+    for E, k, c in ((8, 2, 0.01), (5, 5, 0.1), (3, 1, 1.0)):
+        L = np.zeros((7, E))
+        idx, _ = O.select_experts(L, k)
+        r = O.aux_loss(L, idx, c)
+        assert r["loss"] == pytest.approx(c, rel=1e-14)
+        np.testing.assert_allclose(r["P"], 1.0 / E, rtol=1e-15)
+        # p = 1/E and g = c E f / T: experts 0..k-1 get (1/E)(c E / (k T) - c / T), the rest
+        # -c / (E T) (zero when k = E)
+        T = L.shape[0]
+        np.testing.assert_allclose(r["dlogits"][:, :k], c / T * (1.0 / k - 1.0 / E), rtol=1e-13,
+                                   atol=1e-18)
+        np.testing.assert_allclose(r["dlogits"][:, k:], -c / (E * T), rtol=1e-13)
+    E, a, c = 6, 2.5, 0.05
+    L = a * np.eye(E)
+    idx, _ = O.select_experts(L, 1)
+    np.testing.assert_array_equal(idx[:, 0], np.arange(E))
+    r = O.aux_loss(L, idx, c)
+    np.testing.assert_allclose(r["P"], 1.0 / E, rtol=1e-14)
+    assert r["loss"] == pytest.approx(c, rel=1e-14)
+
+
+def test_aux_loss_collapsed_routing_closed_form():
+    """Every token on expert 0 (k = 1) with the same logits [z, 0, .., 0]: f = (1, 0, ..),
+    P_0 = e^z / (e^z + E - 1), so the loss is coeff * E * P_0; the gradient on logit j of
+    each token is p_j (g_j - p_0 g_0) with only g_0 = coeff * E / T nonzero."""
+    T, E, z, c = 9, 4, 1.7, 0.02
+    L = np.zeros((T, E))
+    L[:, 0] = z
+    idx, _ = O.select_experts(L, 1)
+    r = O.aux_loss(L, idx, c)
+    p0 = math.exp(z) / (math.exp(z) + E - 1)
+    pj = 1.0 / (math.exp(z) + E - 1)
+    assert r["loss"] == pytest.approx(c * E * p0, rel=1e-14)
+    g0 = c * E / T
+    np.testing.assert_allclose(r["dlogits"][:, 0], p0 * (g0 - p0 * g0), rtol=1e-13)
+    np.testing.assert_allclose(r["dlogits"][:, 1:], pj * (0.0 - p0 * g0), rtol=1e-13)
+
+
+def test_aux_loss_gradient_matches_central_differences():
+    """Gradient of the loss with the routing held fixed against central differences along
+    random directions; each token's gradient sums to zero (softmax). Invalid ids and -1
+    slots do not count."""
+    rng = np.random.default_rng(41)
+    T, E, k, c = 11, 7, 3, 0.03
+    L = rng.standard_normal((T, E))
+    idx, _ = O.select_experts(L, k)
+    idx = idx.copy()
+    idx[0, 2] = -1
+    idx[1, 1] = E + 3
+    r = O.aux_loss(L, idx, c)
+    assert r["counts"].sum() == T * k - 2
+    np.testing.assert_allclose(r["dlogits"].sum(axis=1), 0.0, atol=1e-16)
+    eps = 1e-6
+    for _ in range(3):
+        v = rng.standard_normal(L.shape)
+        fd = (O.aux_loss(L + eps * v, idx, c)["loss"] - O.aux_loss(L - eps * v, idx, c)["loss"]) / (2 * eps)
+        assert float((r["dlogits"] * v).sum()) == pytest.approx(fd, rel=1e-7, abs=1e-12)
+
+
+@pytest.mark.parametrize("kw", [dict(top_k=2, activation="swiglu"),
+                                dict(top_k=2, activation="swiglu", capacity_factor=0.6),
+                                dict(top_k=3, activation="gelu", renormalize=False)],
+                         ids=["topk", "capacity", "gelu-raw"])
+def test_backward_with_aux_loss_matches_central_differences(kw):
+    """The objective sum(out * dout) + aux_loss(logits, ids): the gradients with respect to
+    x, W_router and the gate bias against central differences (routing fixed over +-eps);
+    the expert-weight gradients do not change."""
+    T, H, I, E, c = 12, 5, 7, 5, 0.05
+    p, rng = _layer(31, T, H, I, E, kw["activation"])
+    dout = rng.standard_normal((T, H))
+    L = O.gate_logits(p["x"], p["w_router"], p["bias"])
+    assert O.selection_margin(L, kw["top_k"]).min() > 1e-3
+    idx, _ = O.select_experts(L, kw["top_k"])
+
+    def objective(q):
+        val, r = _loss(q, dout, **kw)
+        return val + O.aux_loss(r["logits"], r["topk_idx"], c)["loss"]
+
+    g0 = O.backward(p["x"], p["w_router"], p["bias"], p["w_gate"], p["w_up"], p["w_down"], dout,
+                    **kw)
+    g = O.backward(p["x"], p["w_router"], p["bias"], p["w_gate"], p["w_up"], p["w_down"], dout,
+                   aux_loss_coeff=c, **kw)
+    assert g["aux_loss"] == pytest.approx(O.aux_loss(L, idx, c)["loss"], rel=1e-14)
+    np.testing.assert_allclose(np.stack(g["dw_up"]), np.stack(g0["dw_up"]), rtol=0, atol=0)
+    eps = 1e-6
+    for name, grad in dict(x=g["dx"], w_router=g["dw_router"], bias=g["dbias"]).items():
+        v = rng.standard_normal(p[name].shape)
+        fd = (objective({**p, name: p[name] + eps * v}) -
+              objective({**p, name: p[name] - eps * v})) / (2 * eps)
+        assert float((grad * v).sum()) == pytest.approx(fd, rel=1e-6, abs=1e-8), name
