@@ -102,6 +102,16 @@ typedef struct moe_config {
                                 moe_forward_train need plain weights
                                 (MOE_ERR_UNSUPPORTED). Other values: MOE_ERR_INVALID_ARG */
   double threshold;          /* delta of MOE_ROUTE_THRESHOLD; <= 0 means 1/E; not NaN */
+  double aux_loss_coeff;     /* >= 0, not NaN. > 0: moe_backward also differentiates the
+                                auxiliary load-balancing loss coeff * E * sum_e f_e P_e (f_e:
+                                fraction of the routed assignments, before capacity, that
+                                chose expert e; P_e: mean softmax probability of e over the
+                                tokens) and leaves its value in the MOE_WS_AUX_LOSS view. The
+                                pages add such a loss term to balance the experts' load
+                                (mhpn.cn/news/871594, routing chapter), with MindSpeed's
+                                moe-aux-loss-coeff 0.01, at most 0.1 (lshu.cn/news/82007,
+                                section 5.3), but give no formula; this is the switch-style
+                                one. 0 (the default): off */
 } moe_config;
 
 typedef void* moe_stream_t;  /* hipStream_t */
@@ -222,8 +232,11 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
 /* Backward pass of the layer: the gradients of sum(out * dout) with respect to x, the router
  * weight, the gate bias and the expert weights (gitcode page, "MoE 算子核心原理": the
  * backward runs on the selected experts only). The expert choice (top-k, threshold,
- * capacity) carries no gradient; the gate weights' dependence on the logits is exact. There
- * is no auxiliary load-balancing loss (the pages give no formula for one).
+ * capacity) carries no gradient; the gate weights' dependence on the logits is exact. With
+ * cfg->aux_loss_coeff > 0 the auxiliary load-balancing loss is added to that objective: its
+ * logit gradient p (g - <p, g>), g_e = coeff * E * f_e / T, joins the router's before dx,
+ * dw_router and dgate_bias are formed, and its value (float64) is written to the
+ * MOE_WS_AUX_LOSS view of `ws`.
  *   ws, ws_bytes   the workspace of a moe_forward (or moe_forward_train) call with the same
  *                  cfg, x and weights, made on the same stream before this call: its
  *                  routing, row maps and y_perm are reused (so is its gate bias, through the
@@ -265,7 +278,9 @@ enum {
   MOE_WS_X_PERM = 7,      /* not materialised by moe_forward: view -> MOE_ERR_INVALID_ARG */
   MOE_WS_H = 8,           /* [T*k,I] dtype */
   MOE_WS_Y_PERM = 9,      /* [T*k,H] dtype */
-  MOE_WS_NUM_VIEWS = 10
+  MOE_WS_AUX_LOSS = 10,   /* [1] float64: the auxiliary load-balancing loss, written by a
+                             moe_backward with aux_loss_coeff > 0 */
+  MOE_WS_NUM_VIEWS = 11
 };
 moe_status moe_workspace_view(const moe_config* cfg, void* ws, int32_t which, void** dev_ptr,
                               size_t* bytes);

@@ -25,7 +25,7 @@ MOE_ROUTE_TOPK, MOE_ROUTE_THRESHOLD = 0, 1
 MOE_WEIGHTS_PLAIN, MOE_WEIGHTS_PACKED = 0, 1
 MOE_WEIGHT_GATE, MOE_WEIGHT_UP, MOE_WEIGHT_DOWN = 0, 1, 2
 (MOE_WS_LOGITS, MOE_WS_TOPK_IDX, MOE_WS_TOPK_W, MOE_WS_COUNTS, MOE_WS_OFFSETS, MOE_WS_SLOT_ROW,
- MOE_WS_ROW_TOKEN, MOE_WS_X_PERM, MOE_WS_H, MOE_WS_Y_PERM) = range(10)
+ MOE_WS_ROW_TOKEN, MOE_WS_X_PERM, MOE_WS_H, MOE_WS_Y_PERM, MOE_WS_AUX_LOSS) = range(11)
 
 EXPORTS = ("moe_workspace_size", "moe_capacity", "moe_route", "moe_permute", "moe_expert_up",
            "moe_expert_up_rows", "moe_expert_down", "moe_grouped_ffn",
@@ -39,7 +39,8 @@ class CConfig(ctypes.Structure):
     _fields_ = [("tokens", c_int32), ("hidden", c_int32), ("inter", c_int32),
                 ("experts", c_int32), ("top_k", c_int32), ("activation", c_int32),
                 ("dtype", c_int32), ("renormalize", c_int32), ("capacity_factor", c_double),
-                ("routing", c_int32), ("weight_layout", c_int32), ("threshold", c_double)]
+                ("routing", c_int32), ("weight_layout", c_int32), ("threshold", c_double),
+                ("aux_loss_coeff", c_double)]
 
 
 class MoEError(RuntimeError):
@@ -106,7 +107,8 @@ def cconfig(cfg: MoEConfig, tokens: int | None = None) -> CConfig:
                    routing=MOE_ROUTE_THRESHOLD if cfg.routing == "threshold" else MOE_ROUTE_TOPK,
                    weight_layout=(MOE_WEIGHTS_PACKED if cfg.weights == "packed"
                                   else MOE_WEIGHTS_PLAIN),
-                   threshold=float(cfg.threshold))
+                   threshold=float(cfg.threshold),
+                   aux_loss_coeff=float(cfg.aux_loss_coeff))
 
 
 def _as_cfg(cfg):

@@ -43,6 +43,8 @@ class MoEConfig:
     # expert weight layout handed to the library: "plain" (row-major) or "packed" (repacked
     # once into MFMA operand order by moe_pack_expert_weight; bf16 forward only)
     weights: str = "plain"
+    # auxiliary load-balancing loss coefficient of the backward (0: off)
+    aux_loss_coeff: float = 0.0
     description: str = field(default="", compare=False)
 
     def with_(self, **kw) -> "MoEConfig":

@@ -147,10 +147,13 @@ __global__ __launch_bounds__(256) void bwd_zero_pads_kernel(const int32_t* __res
 // (id >= 0, capacity-dropped ones included, with dw = 0); renormalised weights:
 // dps_j = (dw_j - sum_i w_i dw_i) / sum_S p, raw: dps_j = dw_j; then
 // dL_e = p_e (dp_e - sum_i p_i dp_i) with dp_e = sum of dps_j over slots with id e.
+// With the auxiliary load-balancing loss (aux_g != nullptr) every expert's dp_e also gets
+// g_e = coeff E f_e / T, the loss's derivative with respect to p[t, e].
 template <int KMAX>
 __global__ __launch_bounds__(256) void bwd_router_kernel(
     const float* __restrict__ logits, const int32_t* __restrict__ topk_idx,
-    const float* __restrict__ dw, float* __restrict__ dL, int T, int E, int k, int renorm) {
+    const float* __restrict__ dw, const double* __restrict__ aux_g, float* __restrict__ dL,
+    int T, int E, int k, int renorm) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= T) return;
   const float* L = logits + (size_t)t * E;
@@ -186,14 +189,94 @@ __global__ __launch_bounds__(256) void bwd_router_kernel(
 #pragma unroll
   for (int j = 0; j < KMAX; ++j)
     if (id[j] >= 0) dot += ps[j] * dws[j];
+  if (aux_g != nullptr)
+    for (int e = 0; e < E; ++e) dot += exp((double)L[e] - mx) / sum * aux_g[e];
   for (int e = 0; e < E; ++e) {
-    double dp = 0.0;
+    double dp = aux_g != nullptr ? aux_g[e] : 0.0;
 #pragma unroll
     for (int j = 0; j < KMAX; ++j)
       if (id[j] == e) dp += dws[j];
     const double p = exp((double)L[e] - mx) / sum;
     dL[(size_t)t * E + e] = (float)(p * (dp - dot));
   }
+}
+
+// Auxiliary load-balancing loss coeff * E * sum_e f_e P_e (the switch-style form; the
+// mhpn.cn page's routing chapter adds a loss term that balances the experts' load, the
+// lshu.cn page, section 5.3, scales it by moe-aux-loss-coeff), in two deterministic stages.
+// Stage 1: block b sums the float64 softmax probabilities of its kAuxTokens tokens per
+// expert, in token order.
+constexpr int kAuxTokens = 256;
+int bwd_aux_blocks(int T) { return (T + kAuxTokens - 1) / kAuxTokens; }
+
+__global__ __launch_bounds__(256) void bwd_aux_partial_kernel(const float* __restrict__ logits,
+                                                              double* __restrict__ part, int T,
+                                                              int E) {
+  __shared__ double smx[kAuxTokens], ssum[kAuxTokens];
+  const int t0 = blockIdx.x * kAuxTokens, tid = threadIdx.x;
+  const int n = min(kAuxTokens, T - t0);
+  if (tid < n) {   // this token's max and partition sum
+    const float* L = logits + (size_t)(t0 + tid) * E;
+    double mx = -__builtin_inf();
+    for (int e = 0; e < E; ++e) mx = fmax(mx, (double)L[e]);
+    double sum = 0.0;
+    for (int e = 0; e < E; ++e) sum += exp((double)L[e] - mx);
+    smx[tid] = mx;
+    ssum[tid] = sum;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += blockDim.x) {
+    double acc = 0.0;
+    for (int i = 0; i < n; ++i)
+      acc += exp((double)logits[(size_t)(t0 + i) * E + e] - smx[i]) / ssum[i];
+    part[(size_t)blockIdx.x * E + e] = acc;
+  }
+}
+
+// Stage 2 (one block): P_e = sum of the block partials in block order / T; f_e = counts[e] /
+// sum(counts) (pre-capacity counts of the valid selections); g_e = coeff E f_e / T for the
+// router backward; loss = coeff E sum_e f_e P_e, summed in expert order.
+__global__ __launch_bounds__(256) void bwd_aux_finish_kernel(const double* __restrict__ part,
+                                                             int nblocks,
+                                                             const int32_t* __restrict__ counts,
+                                                             int T, int E, double coeff,
+                                                             double* __restrict__ g,
+                                                             double* __restrict__ loss) {
+  __shared__ double sfp[kMaxExperts];
+  __shared__ double sn;
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    double n = 0.0;
+    for (int e = 0; e < E; ++e) n += (double)max(counts[e], 0);
+    sn = n;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += blockDim.x) {
+    double P = 0.0;
+    for (int b = 0; b < nblocks; ++b) P += part[(size_t)b * E + e];
+    P /= (double)T;
+    const double f = sn > 0.0 ? (double)max(counts[e], 0) / sn : 0.0;
+    g[e] = coeff * (double)E * f / (double)T;
+    sfp[e] = f * P;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double acc = 0.0;
+    for (int e = 0; e < E; ++e) acc += sfp[e];
+    *loss = coeff * (double)E * acc;
+  }
+}
+
+hipError_t launch_bwd_aux_loss(const float* logits, const int32_t* counts, double* part,
+                               double* g, double* loss, int T, int E, double coeff,
+                               hipStream_t s) {
+  const int nb = bwd_aux_blocks(T);
+  hipLaunchKernelGGL(bwd_aux_partial_kernel, dim3(nb), dim3(256), 0, s, logits, part, T, E);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(bwd_aux_finish_kernel, dim3(1), dim3(256), 0, s, part, nb, counts, T, E,
+                     coeff, g, loss);
+  return hipGetLastError();
 }
 
 // dx[t] = sum_e dL[t,e] W_router[:, e] + sum over kept slots (slot order) of dxP[padded row],
@@ -361,10 +444,12 @@ hipError_t launch_bwd_combine(const bf16_t* dout, const bf16_t* y, const int32_t
 }
 
 hipError_t launch_bwd_router(const float* logits, const int32_t* topk_idx, const float* dw,
-                             float* dL, int T, int E, int k, int renorm, hipStream_t s) {
+                             const double* aux_g, float* dL, int T, int E, int k, int renorm,
+                             hipStream_t s) {
   const dim3 grid((T + 255) / 256), block(256);
 #define MOE_BR(KM) \
-  hipLaunchKernelGGL((bwd_router_kernel<KM>), grid, block, 0, s, logits, topk_idx, dw, dL, T, E, k, renorm)
+  hipLaunchKernelGGL((bwd_router_kernel<KM>), grid, block, 0, s, logits, topk_idx, dw, aux_g, \
+                     dL, T, E, k, renorm)
   if (k <= 2) MOE_BR(2);
   else if (k <= 4) MOE_BR(4);
   else if (k <= 8) MOE_BR(8);

@@ -100,8 +100,16 @@ hipError_t launch_bwd_combine(const bf16_t* dout, const bf16_t* y, const int32_t
                               const int32_t* topk_idx, const float* topk_w,
                               const int32_t* offsets, const int32_t* poff, bf16_t* dyP,
                               float* dw, int T, int H, int E, int k, hipStream_t s);
+// aux_g: per-expert derivative of the auxiliary loss with respect to p (or nullptr: none)
 hipError_t launch_bwd_router(const float* logits, const int32_t* topk_idx, const float* dw,
-                             float* dL, int T, int E, int k, int renorm, hipStream_t s);
+                             const double* aux_g, float* dL, int T, int E, int k, int renorm,
+                             hipStream_t s);
+// Auxiliary load-balancing loss: part [bwd_aux_blocks(T) * E] float64 scratch; g [E] and
+// loss [1] float64 out
+int bwd_aux_blocks(int T);
+hipError_t launch_bwd_aux_loss(const float* logits, const int32_t* counts, double* part,
+                               double* g, double* loss, int T, int E, double coeff,
+                               hipStream_t s);
 hipError_t launch_bwd_dx(const bf16_t* dxP, const bf16_t* w_router, const float* dL,
                          const int32_t* slot_row, const int32_t* topk_idx,
                          const int32_t* offsets, const int32_t* poff, bf16_t* dx, int T, int H,

@@ -13,9 +13,10 @@
 #include "kernels.h"
 
 // The binding mirrors this layout (explicit 32-bit fields, no implicit padding).
-static_assert(sizeof(moe_config) == 56 && offsetof(moe_config, routing) == 40 &&
+static_assert(sizeof(moe_config) == 64 && offsetof(moe_config, routing) == 40 &&
                   offsetof(moe_config, weight_layout) == 44 &&
-                  offsetof(moe_config, threshold) == 48,
+                  offsetof(moe_config, threshold) == 48 &&
+                  offsetof(moe_config, aux_loss_coeff) == 56,
               "moe_config layout");
 
 namespace {
@@ -24,7 +25,7 @@ thread_local int g_last_hip_error = 0;
 
 enum Region {
   R_WT, R_LOGITS, R_TOPK_IDX, R_TOPK_W, R_ROUTE_FLAGS, R_HIST, R_PERM_FLAGS, R_COUNTS,
-  R_OFFSETS, R_SLOT_ROW, R_ROW_TOKEN, R_H, R_Y_PERM, R_SPLIT, R_NUM
+  R_OFFSETS, R_SLOT_ROW, R_ROW_TOKEN, R_H, R_Y_PERM, R_SPLIT, R_AUX_LOSS, R_NUM
 };
 
 struct Layout {
@@ -60,6 +61,7 @@ Layout layout_of(const moe_config* c) {
   L.size[R_Y_PERM] = N * H * es;
   // float32 partial tiles of GEMM 2's split-K tail (bf16 path)
   L.size[R_SPLIT] = c->dtype == MOE_DTYPE_BF16 ? moe::kSplitPartialBytes : 0;
+  L.size[R_AUX_LOSS] = 8;   // float64
   size_t o = 0;
   for (int r = 0; r < R_NUM; ++r) {
     L.off[r] = o;
@@ -77,7 +79,7 @@ template <typename P> P* region(void* ws, const Layout& L, Region r) {
 // expert), the recomputed activations and the gradients on their way.
 enum BRegion {
   B_POFF, B_PROW, B_XP, B_GU, B_H, B_DY, B_DGU, B_DXP, B_DL, B_DW, B_SPLIT, B_WRPART, B_BPART,
-  B_XPK, B_DYPK, B_NUM
+  B_XPK, B_DYPK, B_AUXP, B_AUXG, B_NUM
 };
 
 struct BLayout {
@@ -108,6 +110,9 @@ BLayout blayout_of(const moe_config* c) {
   // x rows and dy in the packed operand layout, for the weight gradients' register operand
   L.size[B_XPK] = (P / 16) * 16 * H * 2;
   L.size[B_DYPK] = (P / 16) * 16 * H * 2;
+  // auxiliary load-balancing loss: per-block probability sums and per-expert gradients
+  L.size[B_AUXP] = c->aux_loss_coeff > 0 ? (size_t)moe::bwd_aux_blocks(c->tokens) * E * 8 : 0;
+  L.size[B_AUXG] = c->aux_loss_coeff > 0 ? E * 8 : 0;
   size_t o = 0;
   for (int r = 0; r < B_NUM; ++r) {
     L.off[r] = o;
@@ -132,6 +137,7 @@ moe_status check_cfg(const moe_config* c) {
   if (c->routing != MOE_ROUTE_TOPK && c->routing != MOE_ROUTE_THRESHOLD)
     return MOE_ERR_INVALID_ARG;
   if (std::isnan(c->threshold)) return MOE_ERR_INVALID_ARG;
+  if (!(c->aux_loss_coeff >= 0.0) || std::isinf(c->aux_loss_coeff)) return MOE_ERR_INVALID_ARG;
   if (c->weight_layout != MOE_WEIGHTS_PLAIN && c->weight_layout != MOE_WEIGHTS_PACKED)
     return MOE_ERR_INVALID_ARG;
   if (c->dtype != MOE_DTYPE_BF16 && c->dtype != MOE_DTYPE_F32) return MOE_ERR_UNSUPPORTED;
@@ -596,7 +602,17 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
   // combine backward: dy (padded, zero pads) and the gate-weight gradients
   MOE_TRY(hip_status(moe::launch_bwd_combine((const bf16_t*)dout, y, slot_row, idx, w, offsets,
                                              poff, dyP, dwj, T, H, E, k, s)));
-  MOE_TRY(hip_status(moe::launch_bwd_router(logits, idx, dwj, dL, T, E, k,
+  // the auxiliary load-balancing loss (its value into ws, its per-expert p-derivative for
+  // the router backward), from the forward's logits and pre-capacity counts
+  double* aux_g = nullptr;
+  if (cfg->aux_loss_coeff > 0) {
+    aux_g = bregion<double>(bws, B, B_AUXG);
+    MOE_TRY(hip_status(moe::launch_bwd_aux_loss(logits, region<int32_t>(ws, L, R_COUNTS),
+                                                bregion<double>(bws, B, B_AUXP), aux_g,
+                                                region<double>(ws, L, R_AUX_LOSS), T, E,
+                                                cfg->aux_loss_coeff, s)));
+  }
+  MOE_TRY(hip_status(moe::launch_bwd_router(logits, idx, dwj, aux_g, dL, T, E, k,
                                             cfg->renormalize != 0, s)));
   // dh = dy Wd^T with the activation's backward fused: [dg | du] (GELU: da). Wd[e] [I][H]
   // is Wd^T with K contiguous, read as is (transposed-weight mode).
@@ -641,7 +657,7 @@ moe_status moe_workspace_view(const moe_config* cfg, void* ws, int32_t which, vo
   if (ws == nullptr || dev_ptr == nullptr) return MOE_ERR_INVALID_ARG;
   static const Region map[MOE_WS_NUM_VIEWS] = {R_LOGITS,   R_TOPK_IDX, R_TOPK_W,  R_COUNTS,
                                                R_OFFSETS,  R_SLOT_ROW, R_ROW_TOKEN, R_NUM,
-                                               R_H,        R_Y_PERM};
+                                               R_H,        R_Y_PERM,   R_AUX_LOSS};
   if (which < 0 || which >= MOE_WS_NUM_VIEWS || map[which] == R_NUM) return MOE_ERR_INVALID_ARG;
   const Layout L = layout_of(cfg);
   *dev_ptr = static_cast<char*>(ws) + L.off[map[which]];

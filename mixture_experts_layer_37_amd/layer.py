@@ -11,7 +11,7 @@ from .configs import BF16, SWIGLU, MoEConfig
 _VIEW_DTYPES = {
     L.MOE_WS_LOGITS: torch.float32, L.MOE_WS_TOPK_IDX: torch.int32, L.MOE_WS_TOPK_W: torch.float32,
     L.MOE_WS_COUNTS: torch.int32, L.MOE_WS_OFFSETS: torch.int32, L.MOE_WS_SLOT_ROW: torch.int32,
-    L.MOE_WS_ROW_TOKEN: torch.int32,
+    L.MOE_WS_ROW_TOKEN: torch.int32, L.MOE_WS_AUX_LOSS: torch.float64,
 }
 
 
@@ -112,6 +112,8 @@ class MoELayer:
                        g["dx"], g["dw_router"], g["dbias"], g["dw_gate"], g["dw_up"],
                        g["dw_down"], self.ws, self.bws, getattr(self, "_saved", False), stream)
         self._saved = False
+        if cfg.aux_loss_coeff > 0:   # the auxiliary load-balancing loss, float64 [1]
+            g["aux_loss"] = self.view(L.MOE_WS_AUX_LOSS)
         return g
 
     def view(self, which: int) -> torch.Tensor:

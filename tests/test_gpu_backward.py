@@ -44,6 +44,9 @@ CASES = {
     "single_token": C.MIXTRAL.with_(name="bwd_single_token", tokens=1, hidden=256, inter=256),
     "empty_experts": C.SMALL.with_(name="bwd_empty_experts", tokens=20, hidden=256, inter=256,
                                    experts=16, top_k=1, bias=None),
+    # with the auxiliary load-balancing loss at MindSpeed's largest advised coefficient
+    "aux_loss": C.SMALL.with_(name="bwd_aux_loss", tokens=700, hidden=512, inter=512,
+                              experts=8, top_k=2, aux_loss_coeff=0.1),
 }
 
 
@@ -82,7 +85,9 @@ def test_backward_matches_oracle(name):
                      as_float(cfg, dout_np).astype(np.float64), top_k=cfg.top_k,
                      activation=cfg.activation, capacity_factor=cfg.capacity_factor,
                      renormalize=cfg.renormalize, routing=cfg.routing,
-                     threshold=cfg.threshold, logits=gl)
+                     threshold=cfg.threshold, logits=gl, aux_loss_coeff=cfg.aux_loss_coeff)
+    if cfg.aux_loss_coeff > 0:
+        assert float(g["aux_loss"].item()) == pytest.approx(ref["aux_loss"], rel=1e-9)
     rep = {"dx": _close(P.decode(cfg, g["dx"]), ref["dx"], "dx"),
            "dw_router": _close(g["dw_router"].cpu().numpy().astype(np.float64), ref["dw_router"],
                                "dw_router"),
@@ -136,3 +141,52 @@ def test_saved_preactivations_match_recompute(name):
     assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16))
     for k in ga:
         assert torch.equal(ga[k].view(torch.uint8), gb[k].view(torch.uint8)), k
+
+
+AUX_CASES = {
+    "topk": C.SMALL.with_(name="aux_topk", tokens=700, hidden=512, inter=256, experts=8,
+                          top_k=2, aux_loss_coeff=0.1),
+    "capacity": C.SMALL.with_(name="aux_capacity", tokens=900, hidden=256, inter=256,
+                              experts=16, top_k=2, capacity_factor=0.7, aux_loss_coeff=0.01),
+    "threshold_raw": C.SMALL.with_(name="aux_threshold_raw", tokens=600, hidden=512, inter=256,
+                                   experts=8, top_k=8, routing="threshold", renormalize=False,
+                                   bias=None, aux_loss_coeff=0.05),
+    "many_experts": C.FINE.with_(name="aux_many_experts", tokens=513, hidden=256, inter=256,
+                                 experts=64, top_k=8, aux_loss_coeff=0.02),
+}
+
+
+@pytest.mark.parametrize("name", list(AUX_CASES))
+def test_aux_loss_alone(name):
+    """dout = 0 leaves the auxiliary load-balancing loss as the only objective: its value
+    against the oracle's (both in float64 from the same float32 logits and counts), the
+    router-side gradients (dx, dW_router, dbias) against the oracle's at float32 accuracy,
+    and expert-weight gradients exactly zero."""
+    cfg = AUX_CASES[name]
+    print(f"[case] aux {name} {cfg}", flush=True)
+    inp = make_inputs(cfg, seed=12)
+    layer = MoELayer(cfg, inp)
+    x = to_device(cfg, inp["x"])
+    layer.forward(x)
+    dout = torch.zeros_like(x)
+    g = layer.backward(x, dout)
+    torch.cuda.synchronize()
+    gl = layer.view(L.MOE_WS_LOGITS).cpu().numpy().astype(np.float64)
+    wg = ExpertView(cfg, inp["w_gate"]) if cfg.activation == C.SWIGLU else None
+    ref = O.backward(as_float(cfg, inp["x"]), as_float(cfg, inp["w_router"]), inp["bias"], wg,
+                     ExpertView(cfg, inp["w_up"]), ExpertView(cfg, inp["w_down"]),
+                     np.zeros((cfg.tokens, cfg.hidden)), top_k=cfg.top_k,
+                     activation=cfg.activation, capacity_factor=cfg.capacity_factor,
+                     renormalize=cfg.renormalize, routing=cfg.routing,
+                     threshold=cfg.threshold, logits=gl, aux_loss_coeff=cfg.aux_loss_coeff)
+    assert float(g["aux_loss"].item()) == pytest.approx(ref["aux_loss"], rel=1e-9)
+    for key in ("dw_router", "dbias"):
+        got = g[key].cpu().numpy().astype(np.float64)
+        err = np.abs(got - ref[key]).max() / np.abs(ref[key]).max()
+        assert err <= 1e-4, f"{key}: {err:.3e}"
+    dx = P.decode(cfg, g["dx"])   # bf16 output: one rounding
+    err = np.abs(dx - ref["dx"]).max() / np.abs(ref["dx"]).max()
+    assert err <= 8e-3, f"dx: {err:.3e}"
+    for key in ("dw_gate", "dw_up", "dw_down"):
+        if g[key] is not None:
+            assert not g[key].view(torch.int16).any(), f"{key} must be zero"
