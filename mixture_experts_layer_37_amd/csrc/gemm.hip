@@ -459,6 +459,80 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
       }
       return;
     }
+    if constexpr (EPI == EPI_SWIGLU_BWD) {
+      // The float32 dh tile leaves through LDS (the two stages, free after the barrier
+      // above), 64 rows at a time, and is read back in row order: each lane then loads the
+      // saved g and u and stores dg and du as 16-byte pieces of whole 512-byte row segments,
+      // instead of 8-byte pieces scattered over 32 rows per instruction. 16-byte chunk c of
+      // LDS row r (1 KB) sits at c ^ (r & 31). LDS-only barriers.
+      constexpr int kRowB = 1024;
+      // Tile coordinates and lane index pass through empty asm, so no address below is
+      // computed (and held in registers) across the k-loop.
+      int e_row0 = row0, e_nt = n_t, e_mrows = mrows, e_e = e, e_lane = lane, e_tid = tid;
+      asm volatile("" : "+s"(e_row0), "+s"(e_nt), "+s"(e_mrows), "+s"(e_e));
+      asm volatile("" : "+v"(e_lane), "+v"(e_tid));
+      // aux rows: the C rows themselves, or (aux_off given) the compact rows of a layout
+      // without padding: row r of expert e maps to r - offsets[e] + aux_off[e], and pad rows
+      // to the expert's last row (their dh is zero)
+      int a_lo = 0, a_hi = 0;
+      if (aux_off != nullptr) {
+        a_lo = aux_off[e_e];
+        a_hi = aux_off[e_e + 1];
+      }
+      const int e_first = s_off[e_e];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        char* buf = (char*)((i & 1) ? stage1 : stage0);
+        const int lr = wm * 32 + (e_lane & 31);   // row of this lane's outputs in the block
+        const int lh = e_lane >> 5;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int chunk = wn * 32 + j * 8 + 2 * q + lh;   // columns 4 chunk .. 4 chunk + 3
+            *(float4*)(buf + lr * kRowB + ((chunk ^ (lr & 31)) << 4)) =
+                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                            acc[i][j][4 * q + 3]);
+          }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int gi = r * 256 + e_tid;   // 8-column group of the 64 x 256 block
+          const int row = gi >> 5, cg = gi & 31;
+          const int m = (row < 32 ? 0 : 128) + i * 32 + (row & 31);
+          if (m >= e_mrows) continue;
+          const char* lrow = buf + row * kRowB;
+          const float4 d0 = *(const float4*)(lrow + (((2 * cg) ^ (row & 31)) << 4));
+          const float4 d1 = *(const float4*)(lrow + (((2 * cg + 1) ^ (row & 31)) << 4));
+          size_t ar = (size_t)(e_row0 + m);
+          if (aux_off != nullptr) ar = (size_t)max(min(e_row0 + m - e_first + a_lo, a_hi - 1), a_lo);
+          const bf16_t* arow = aux + ar * ldaux + e_nt * 256 + cg * 8;
+          const uint4 gw = *(const uint4*)arow;
+          const uint4 uw = *(const uint4*)(arow + N);
+          const float dh[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+          float g[8], u[8], dg[8], du[8];
+          unpack4(make_uint2(gw.x, gw.y), g);
+          unpack4(make_uint2(gw.z, gw.w), g + 4);
+          unpack4(make_uint2(uw.x, uw.y), u);
+          unpack4(make_uint2(uw.z, uw.w), u + 4);
+          // dg = dh u silu'(g), du = dh silu(g)
+#pragma unroll
+          for (int s = 0; s < 8; ++s) {
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g[s]));
+            dg[s] = dh[s] * u[s] * (sg * (1.0f + g[s] * (1.0f - sg)));
+            du[s] = dh[s] * g[s] * sg;
+          }
+          bf16_t* crow = C + (size_t)(e_row0 + m) * ldc + e_nt * 256 + cg * 8;
+          const uint2 dg0 = pack4(dg), dg1 = pack4(dg + 4);
+          const uint2 du0 = pack4(du), du1 = pack4(du + 4);
+          *(uint4*)crow = make_uint4(dg0.x, dg0.y, dg1.x, dg1.y);
+          *(uint4*)(crow + N) = make_uint4(du0.x, du0.y, du1.x, du1.y);
+        }
+      }
+      // every wave is done reading the stages before the next tile's DMA refills them
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = wm * 128 + i * 32 + l32;
@@ -515,21 +589,6 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
 #pragma unroll
               for (int s = 0; s < 4; ++s) gv[s] = gelu_f(hv[s]);
               *(uint2*)(C2 + (size_t)(row0 + m) * N + col) = pack4(gv);
-            } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-              // hv = dh; with g, u the saved pre-activations: dg = dh u silu'(g),
-              // du = dh silu(g)
-              float g[4], u[4], dg[4], du[4];
-              unpack4(*(const uint2*)(arow + col), g);
-              unpack4(*(const uint2*)(arow + N + col), u);
-#pragma unroll
-              for (int s = 0; s < 4; ++s) {
-                const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g[s]));
-                dg[s] = hv[s] * u[s] * (sg * (1.0f + g[s] * (1.0f - sg)));
-                du[s] = hv[s] * g[s] * sg;
-              }
-              *(uint2*)(crow + col) = pack4(dg);
-              *(uint2*)(crow + N + col) = pack4(du);
-              continue;
             } else if constexpr (EPI == EPI_GELU_BWD) {
               // hv = dh; with a the saved pre-activation: da = dh gelu'(a)
               float a[4];
