@@ -29,6 +29,12 @@
  *     device->host synchronisation (moe_read_device_status excepted) and keep no global
  *     mutable state, so they are safe to call from several host threads. Calls that share
  *     one workspace must be ordered on one stream.
+ *   - Alignment: every tensor of the layer dtype (x, w_router in bf16, w_gate, w_up,
+ *     w_down and their packed forms, x_perm, h, y_perm, out, dout, dx and the weight
+ *     gradients) and the workspaces ws / bws must be 16-byte aligned, since the kernels move
+ *     them in 16-byte pieces; float32 and int32 arrays (logits, gate weights and bias, ids,
+ *     row maps, counts, offsets, dw_router) need 4 bytes, and an fp32 w_router 4 bytes.
+ *     A pointer that breaks this is MOE_ERR_INVALID_ARG.
  *   - Argument errors are reported synchronously, before any HIP call, as a moe_status;
  *     nothing aborts or prints. A failed kernel launch returns MOE_ERR_HIP and the HIP
  *     error code is kept per host thread (moe_last_hip_error).
@@ -62,7 +68,7 @@ typedef enum moe_status {
 enum { MOE_DTYPE_BF16 = 0, MOE_DTYPE_F32 = 1 };
 enum { MOE_ACT_SWIGLU = 0, MOE_ACT_GELU = 1 };
 /* device status flags (moe_read_device_status) */
-enum { MOE_FLAG_BAD_INDEX = 1, MOE_FLAG_NONFINITE_LOGIT = 2 };
+enum { MOE_FLAG_BAD_INDEX = 1, MOE_FLAG_NONFINITE_LOGIT = 2, MOE_FLAG_STALE_SAVED = 4 };
 enum { MOE_MAX_EXPERTS = 256, MOE_MAX_TOPK = 16 };
 /* routing rules (moe_config.routing) */
 enum { MOE_ROUTE_TOPK = 0, MOE_ROUTE_THRESHOLD = 1 };
@@ -243,13 +249,19 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
  *                  logits)
  *   bws, bws_bytes backward scratch, at least moe_backward_workspace_size bytes
  *   saved          nonzero: that call was moe_forward_train with this bws, which kept the
- *                  up-projection's pre-activations there; zero: they are recomputed here
+ *                  up-projection's pre-activations there; zero: they are recomputed here.
+ *                  Precondition of saved != 0: no other call built a permutation in ws
+ *                  after that moe_forward_train (moe_forward, moe_forward_train,
+ *                  moe_permute). Every permutation advances a generation counter in ws
+ *                  and moe_forward_train records its value in bws; when they differ the
+ *                  backward raises MOE_FLAG_STALE_SAVED (moe_read_device_status, which = 4)
+ *                  and its gradients are not to be used
  *   dout [T,H] bf16 in; dx [T,H] bf16 out; dw_router [H,E] float32 out; dgate_bias [E]
  *   float32 out or NULL; dw_gate (SwiGLU only; NULL for GELU), dw_up [E,H,I] and dw_down
  *   [E,I,H] bf16 out (float32 accumulation, rounded once)
  * bf16 layers with I a multiple of 256 only (else MOE_ERR_UNSUPPORTED). Expert rows are
- * regrouped in a padded row space (each expert's rows rounded up to a multiple of 128) and
- * the up-projection is recomputed (its pre-activations are not kept by moe_forward). */
+ * regrouped in a padded row space (each expert's rows rounded up to a multiple of 128); with
+ * saved = 0 the up-projection is recomputed there. */
 moe_status moe_backward_workspace_size(const moe_config* cfg, size_t* bytes);
 moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_router,
                         const void* w_gate, const void* w_up, const void* w_down,
@@ -285,8 +297,9 @@ enum {
 moe_status moe_workspace_view(const moe_config* cfg, void* ws, int32_t which, void** dev_ptr,
                               size_t* bytes);
 
-/* OR of the device flags raised by the last moe_route (which = 1), the last moe_permute
- * (which = 2) or both (which = 3) that used this workspace; moe_forward runs both.
+/* OR of the device flags raised by the last moe_route (which bit 1), the last moe_permute
+ * (bit 2) and the last moe_backward (bit 4: MOE_FLAG_STALE_SAVED) that used this workspace;
+ * which in [1, 7] selects any mix of them (moe_forward runs route and permute).
  * Synchronises `stream`. */
 moe_status moe_read_device_status(const moe_config* cfg, void* ws, int32_t which,
                                   moe_stream_t stream, int32_t* flags);

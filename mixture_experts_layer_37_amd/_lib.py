@@ -20,7 +20,7 @@ LIB_PATH = os.environ.get("MOE_LIB_PATH") or os.path.join(
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_DTYPE_BF16, MOE_DTYPE_F32 = 0, 1
 MOE_ACT_SWIGLU, MOE_ACT_GELU = 0, 1
-MOE_FLAG_BAD_INDEX, MOE_FLAG_NONFINITE_LOGIT = 1, 2
+MOE_FLAG_BAD_INDEX, MOE_FLAG_NONFINITE_LOGIT, MOE_FLAG_STALE_SAVED = 1, 2, 4
 MOE_ROUTE_TOPK, MOE_ROUTE_THRESHOLD = 0, 1
 MOE_WEIGHTS_PLAIN, MOE_WEIGHTS_PACKED = 0, 1
 MOE_WEIGHT_GATE, MOE_WEIGHT_UP, MOE_WEIGHT_DOWN = 0, 1, 2

@@ -13,10 +13,16 @@ namespace moe {
 
 constexpr int kPadRows = 128;
 
-// poff[E+1]: padded row offsets from the kept offsets (clamped to [0, max_rows]).
+// poff[E+1]: padded row offsets from the kept offsets (clamped to [0, max_rows]). With saved
+// pre-activations (gen_saved != null), bflag records whether they were kept by the training
+// forward of the workspace's latest permutation (0) or not (4: stale).
 __global__ void bwd_pad_offsets_kernel(const int32_t* __restrict__ offsets,
-                                       int32_t* __restrict__ poff, int E, int max_rows) {
+                                       int32_t* __restrict__ poff, int E, int max_rows,
+                                       const int32_t* __restrict__ gen,
+                                       const int32_t* __restrict__ gen_saved,
+                                       int32_t* __restrict__ bflag) {
   if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  bflag[0] = (gen_saved != nullptr && gen_saved[0] != gen[0]) ? 4 /* MOE_FLAG_STALE_SAVED */ : 0;
   int acc = 0, prev = min(max(offsets[0], 0), max_rows);
   poff[0] = 0;
   for (int e = 0; e < E; ++e) {
@@ -402,10 +408,12 @@ __global__ __launch_bounds__(256) void bwd_wrouter_sum_kernel(
 int bwd_padded_rows(int T, int k, int E) { return T * k + E * (kPadRows - 1); }
 
 hipError_t launch_bwd_prepare(const bf16_t* x, const int32_t* offsets, const int32_t* row_token,
-                              int32_t* poff, int32_t* prow_token, bf16_t* xP, int T, int H,
-                              int E, int k, hipStream_t s) {
+                              int32_t* poff, int32_t* prow_token, bf16_t* xP,
+                              const int32_t* gen, const int32_t* gen_saved, int32_t* bflag,
+                              int T, int H, int E, int k, hipStream_t s) {
   const int prows = bwd_padded_rows(T, k, E);
-  hipLaunchKernelGGL(bwd_pad_offsets_kernel, dim3(1), dim3(64), 0, s, offsets, poff, E, T * k);
+  hipLaunchKernelGGL(bwd_pad_offsets_kernel, dim3(1), dim3(64), 0, s, offsets, poff, E, T * k,
+                     gen, gen_saved, bflag);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(bwd_pad_rows_kernel, dim3((prows + 3) / 4), dim3(256), 0, s,

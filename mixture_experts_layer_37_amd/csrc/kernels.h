@@ -32,10 +32,13 @@ hipError_t launch_route_topk(const float* logits, int32_t* topk_idx, float* topk
 
 // ---- permute (permute.hip)
 int permute_count_blocks(int T);
+// gen (may be null): the workspace's permutation generation, advanced by one; gen_copy (may
+// be null): receives the new value (a training forward's record of it)
 hipError_t launch_permute(const void* x, int elem_bytes, const int32_t* topk_idx, void* x_perm,
                           int32_t* counts, int32_t* offsets, int32_t* row_token,
-                          int32_t* slot_row, int32_t* hist, int32_t* flags, int T, int H,
-                          int E, int k, int cap, hipStream_t s);
+                          int32_t* slot_row, int32_t* hist, int32_t* flags, int32_t* gen,
+                          int32_t* gen_copy, int T, int H, int E, int k, int cap,
+                          hipStream_t s);
 
 // ---- grouped expert GEMMs (gemm.hip)
 // Epilogues: SWIGLU h = silu(g) u; GELU h = gelu(a); NONE the product itself; GU the gate
@@ -88,9 +91,12 @@ hipError_t launch_wgrad_bf16_packed(const bf16_t* a, int lda, const bf16_t* pb, 
 // ---- backward pass (backward.hip): padded row space, multiples of 128 rows per expert
 int bwd_padded_rows(int T, int k, int E);
 int bwd_wrouter_chunks(int T);
+// gen / gen_saved (gen_saved may be null: no saved pre-activations): bflag = 4 (stale saved
+// pre-activations) when they differ, else 0
 hipError_t launch_bwd_prepare(const bf16_t* x, const int32_t* offsets, const int32_t* row_token,
-                              int32_t* poff, int32_t* prow_token, bf16_t* xP, int T, int H,
-                              int E, int k, hipStream_t s);
+                              int32_t* poff, int32_t* prow_token, bf16_t* xP,
+                              const int32_t* gen, const int32_t* gen_saved, int32_t* bflag,
+                              int T, int H, int E, int k, hipStream_t s);
 // dst[r] = src[compact row of padded row r] for r < poff[E] (rows of `row_vecs` 16-byte
 // vectors; pad rows repeat the expert's last kept row).
 hipError_t launch_bwd_pad_copy(const bf16_t* src, bf16_t* dst, const int32_t* offsets,

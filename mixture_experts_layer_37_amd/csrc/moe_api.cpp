@@ -25,7 +25,7 @@ thread_local int g_last_hip_error = 0;
 
 enum Region {
   R_WT, R_LOGITS, R_TOPK_IDX, R_TOPK_W, R_ROUTE_FLAGS, R_HIST, R_PERM_FLAGS, R_COUNTS,
-  R_OFFSETS, R_SLOT_ROW, R_ROW_TOKEN, R_H, R_Y_PERM, R_SPLIT, R_AUX_LOSS, R_NUM
+  R_OFFSETS, R_SLOT_ROW, R_ROW_TOKEN, R_H, R_Y_PERM, R_SPLIT, R_AUX_LOSS, R_GEN, R_NUM
 };
 
 struct Layout {
@@ -62,6 +62,9 @@ Layout layout_of(const moe_config* c) {
   // float32 partial tiles of GEMM 2's split-K tail (bf16 path)
   L.size[R_SPLIT] = c->dtype == MOE_DTYPE_BF16 ? moe::kSplitPartialBytes : 0;
   L.size[R_AUX_LOSS] = 8;   // float64
+  // [0] permutation generation (advanced by every permutation built in this workspace),
+  // [1] backward flags (MOE_FLAG_STALE_SAVED)
+  L.size[R_GEN] = 8;
   size_t o = 0;
   for (int r = 0; r < R_NUM; ++r) {
     L.off[r] = o;
@@ -79,7 +82,7 @@ template <typename P> P* region(void* ws, const Layout& L, Region r) {
 // expert), the recomputed activations and the gradients on their way.
 enum BRegion {
   B_POFF, B_PROW, B_XP, B_GU, B_H, B_DY, B_DGU, B_DXP, B_DL, B_DW, B_SPLIT, B_WRPART, B_BPART,
-  B_XPK, B_DYPK, B_AUXP, B_AUXG, B_NUM
+  B_XPK, B_DYPK, B_AUXP, B_AUXG, B_GEN, B_NUM
 };
 
 struct BLayout {
@@ -113,6 +116,8 @@ BLayout blayout_of(const moe_config* c) {
   // auxiliary load-balancing loss: per-block probability sums and per-expert gradients
   L.size[B_AUXP] = c->aux_loss_coeff > 0 ? (size_t)moe::bwd_aux_blocks(c->tokens) * E * 8 : 0;
   L.size[B_AUXG] = c->aux_loss_coeff > 0 ? E * 8 : 0;
+  // the workspace generation of the training forward whose pre-activations B_GU holds
+  L.size[B_GEN] = 4;
   size_t o = 0;
   for (int r = 0; r < B_NUM; ++r) {
     L.off[r] = o;
@@ -226,15 +231,17 @@ moe_status do_route(const moe_config* c, const void* x, const void* w_router, co
       moe::launch_route_topk(logits, idx, w, flags, T, E, k, renorm, thr, delta, s));
 }
 
+// gen_copy (may be null): where a training forward records the new permutation generation
 moe_status do_permute(const moe_config* c, const void* x, const int32_t* idx, void* x_perm,
                       int32_t* counts, int32_t* offsets, int32_t* row_token, int32_t* slot_row,
-                      void* ws, hipStream_t s) {
+                      void* ws, hipStream_t s, int32_t* gen_copy = nullptr) {
   const Layout L = layout_of(c);
   const int cap = capacity_of(c);
   return hip_status(moe::launch_permute(
       x, (int)esize(c), idx, x_perm, counts, offsets, row_token, slot_row,
-      region<int32_t>(ws, L, R_HIST), region<int32_t>(ws, L, R_PERM_FLAGS), c->tokens, c->hidden,
-      c->experts, c->top_k, cap < c->tokens ? cap : c->tokens, s));
+      region<int32_t>(ws, L, R_HIST), region<int32_t>(ws, L, R_PERM_FLAGS),
+      region<int32_t>(ws, L, R_GEN), gen_copy, c->tokens, c->hidden, c->experts, c->top_k,
+      cap < c->tokens ? cap : c->tokens, s));
 }
 
 // GEMM 1. `a` is x_perm (row_token == nullptr) or the token matrix x read through
@@ -312,7 +319,7 @@ moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
   if (cfg->tokens == 0) return MOE_OK;   // empty batch: nothing to read or write
   if (x != nullptr) {
     MOE_TRY(need(x, 16));
-    MOE_TRY(need(w_router, cfg->dtype == MOE_DTYPE_BF16 ? 2 : 4));
+    MOE_TRY(need(w_router, cfg->dtype == MOE_DTYPE_BF16 ? 16 : 4));
     if (gate_bias != nullptr) MOE_TRY(need(gate_bias, 4));
   }
   MOE_TRY(need(logits, 4));
@@ -450,7 +457,7 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
   MOE_TRY(check_cfg(cfg));
   if (cfg->tokens == 0) return MOE_OK;   // empty batch: nothing to read or write
   MOE_TRY(need(x, 16));
-  MOE_TRY(need(w_router, cfg->dtype == MOE_DTYPE_BF16 ? 2 : 4));
+  MOE_TRY(need(w_router, cfg->dtype == MOE_DTYPE_BF16 ? 16 : 4));
   if (gate_bias != nullptr) MOE_TRY(need(gate_bias, 4));
   if (cfg->activation == MOE_ACT_SWIGLU) MOE_TRY(need(w_gate, 16));
   MOE_TRY(need(w_up, 16));
@@ -483,7 +490,7 @@ moe_status moe_forward_train(const moe_config* cfg, const void* x, const void* w
   MOE_TRY(check_backward_cfg(cfg));
   if (cfg->tokens == 0) return MOE_OK;   // empty batch: nothing to read or write
   MOE_TRY(need(x, 16));
-  MOE_TRY(need(w_router, 2));
+  MOE_TRY(need(w_router, 16));
   if (gate_bias != nullptr) MOE_TRY(need(gate_bias, 4));
   if (cfg->activation == MOE_ACT_SWIGLU) MOE_TRY(need(w_gate, 16));
   MOE_TRY(need(w_up, 16));
@@ -508,7 +515,8 @@ moe_status moe_forward_train(const moe_config* cfg, const void* x, const void* w
   const int T = cfg->tokens, H = cfg->hidden, I = cfg->inter, E = cfg->experts;
   const int rows = T * cfg->top_k;
   MOE_TRY(do_route(cfg, x, w_router, gate_bias, logits, idx, w, ws, s));
-  MOE_TRY(do_permute(cfg, x, idx, nullptr, counts, offsets, row_token, slot_row, ws, s));
+  MOE_TRY(do_permute(cfg, x, idx, nullptr, counts, offsets, row_token, slot_row, ws, s,
+                     bregion<int32_t>(bws, B, B_GEN)));
   // GEMM 1 keeping the pre-activations for the backward: [g | u] (GELU: a) into bws, h as usual
   if (cfg->activation == MOE_ACT_SWIGLU)
     MOE_TRY(hip_status(moe::launch_gemm_bf16(
@@ -584,8 +592,12 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
   const bf16_t* wd = (const bf16_t*)w_down;
 
   // padded row maps and the token rows in padded expert-major order
+  // (with saved pre-activations, also whether they belong to the latest permutation of ws)
+  int32_t* gen = region<int32_t>(ws, L, R_GEN);
   MOE_TRY(hip_status(moe::launch_bwd_prepare((const bf16_t*)x, offsets, row_token, poff, prow,
-                                             xP, T, H, E, k, s)));
+                                             xP, gen, saved ? bregion<int32_t>(bws, B, B_GEN)
+                                                            : nullptr,
+                                             gen + 1, T, H, E, k, s)));
   // the up-projection's pre-activations: kept by moe_forward_train (compact rows, in bws), or
   // recomputed here in the padded row space together with h (GELU: a and h)
   if (saved) {   // h of the forward (ws), moved into the padded rows for dW_down
@@ -668,18 +680,20 @@ moe_status moe_workspace_view(const moe_config* cfg, void* ws, int32_t which, vo
 moe_status moe_read_device_status(const moe_config* cfg, void* ws, int32_t which,
                                   moe_stream_t stream, int32_t* flags) {
   MOE_TRY(check_cfg(cfg));
-  if (ws == nullptr || flags == nullptr || which < 1 || which > 3) return MOE_ERR_INVALID_ARG;
+  if (ws == nullptr || flags == nullptr || which < 1 || which > 7) return MOE_ERR_INVALID_ARG;
   *flags = 0;
   if (cfg->tokens == 0) return MOE_OK;
   const Layout L = layout_of(cfg);
   const hipStream_t s = (hipStream_t)stream;
   std::vector<int32_t> host;
   int32_t acc = 0;
-  for (int part = 1; part <= 2; ++part) {
+  for (int part = 1; part <= 4; part <<= 1) {
     if (!(which & part)) continue;
-    const Region r = part == 1 ? R_ROUTE_FLAGS : R_PERM_FLAGS;
-    host.assign(L.size[r] / 4, 0);
-    MOE_TRY(hip_status(hipMemcpyAsync(host.data(), region<void>(ws, L, r), L.size[r],
+    // route: one word per 16 tokens; permute: one per count block; backward: word 1 of R_GEN
+    const Region r = part == 1 ? R_ROUTE_FLAGS : part == 2 ? R_PERM_FLAGS : R_GEN;
+    const size_t off = part == 4 ? 4 : 0, bytes = part == 4 ? 4 : L.size[r];
+    host.assign(bytes / 4, 0);
+    MOE_TRY(hip_status(hipMemcpyAsync(host.data(), region<char>(ws, L, r) + off, bytes,
                                       hipMemcpyDeviceToHost, s)));
     MOE_TRY(hip_status(hipStreamSynchronize(s)));
     for (int32_t v : host) acc |= v;

@@ -11,6 +11,9 @@
 //             (-1, an empty slot of threshold routing, is dropped silently).
 //   scan   -- one block: per expert, exclusive prefix over the count blocks (in place),
 //             pre-capacity counts, kept = min(count, C), and the kept offsets (a scan over E).
+//             It also advances the workspace's permutation generation (and, for a training
+//             forward, records it beside the saved pre-activations), so a backward can tell
+//             whether the pre-activations it is handed belong to the latest permutation.
 //   gather -- one wave per token: row = offsets[e] + block prefix + in-block rank, kept iff
 //             below C; writes slot_row / row_token and copies the token row once into each
 //             of its kept rows with 16-byte loads and stores, all loads of a chunk in
@@ -90,9 +93,15 @@ __global__ __launch_bounds__(1024) void permute_count_kernel(const int32_t* __re
 __global__ __launch_bounds__(256) void permute_scan_kernel(int32_t* __restrict__ hist,
                                                            int32_t* __restrict__ counts,
                                                            int32_t* __restrict__ offsets, int NB,
-                                                           int E, int cap) {
+                                                           int E, int cap, int32_t* gen,
+                                                           int32_t* gen_copy) {
   __shared__ int wsum[4];
   const int e = threadIdx.x, wave = e >> 6, lane = e & 63;
+  if (e == 0 && gen != nullptr) {
+    const int g = gen[0] + 1;
+    gen[0] = g;
+    if (gen_copy != nullptr) gen_copy[0] = g;
+  }
   int run = 0;
   if (e < E) {
     int b = 0;
@@ -200,15 +209,15 @@ __global__ __launch_bounds__(256) void permute_rows_kernel(
 
 hipError_t launch_permute(const void* x, int elem_bytes, const int32_t* topk_idx, void* x_perm,
                           int32_t* counts, int32_t* offsets, int32_t* row_token,
-                          int32_t* slot_row, int32_t* hist, int32_t* flags, int T, int H, int E,
-                          int k, int cap, hipStream_t s) {
+                          int32_t* slot_row, int32_t* hist, int32_t* flags, int32_t* gen,
+                          int32_t* gen_copy, int T, int H, int E, int k, int cap, hipStream_t s) {
   const int NB = permute_count_blocks(T);
   hipLaunchKernelGGL(permute_count_kernel, dim3(NB), dim3(kCountBlockTokens), 0, s, topk_idx,
                      hist, slot_row, flags, T, E, k);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(256), 0, s, hist, counts, offsets, NB, E,
-                     cap);
+                     cap, gen, gen_copy);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (x_perm == nullptr) {

@@ -123,6 +123,8 @@ def test_forward_argument_errors(lib):
     assert call_forward(lib, c, need - 1) == L.MOE_ERR_WORKSPACE
     assert call_forward(lib, c, need, x=None) == L.MOE_ERR_INVALID_ARG
     assert call_forward(lib, c, need, x=FAKE + 8) == L.MOE_ERR_INVALID_ARG      # misaligned
+    # the bf16 router weight moves in 16-byte pieces: 2-byte alignment is not enough
+    assert call_forward(lib, c, need, wr=FAKE + 2) == L.MOE_ERR_INVALID_ARG
     assert call_forward(lib, c, need, wg=None) == L.MOE_ERR_INVALID_ARG         # SwiGLU needs it
     assert call_forward(lib, c, need, ws=None) == L.MOE_ERR_INVALID_ARG
     assert call_forward(lib, c, need, out=None) == L.MOE_ERR_INVALID_ARG
@@ -140,6 +142,10 @@ def test_stage_argument_errors(lib):
     _, need = ws_size(lib, c)
     assert lib.moe_route(cp, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, need, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_route(cp, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 16, None) == L.MOE_ERR_WORKSPACE
+    assert lib.moe_route(cp, FAKE, FAKE + 8, None, FAKE, FAKE, FAKE, FAKE, need, None) == L.MOE_ERR_INVALID_ARG
+    # logits as the input (x == NULL): the router weight is not read, so not checked
+    assert lib.moe_route(ctypes.byref(cfg_of(tokens=0)), None, None, None, FAKE, FAKE, FAKE, FAKE,
+                         need, None) == L.MOE_OK
     assert lib.moe_permute(cp, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_expert_up(cp, FAKE, FAKE, None, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_expert_down(cp, FAKE, None, FAKE, FAKE, None, 0, None) == L.MOE_ERR_INVALID_ARG
@@ -150,9 +156,12 @@ def test_stage_argument_errors(lib):
     assert lib.moe_combine(ctypes.byref(cfg_of(top_k=0)), FAKE, FAKE, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG
     f = ctypes.c_int32(5)
     assert lib.moe_read_device_status(cp, FAKE, 0, None, ctypes.byref(f)) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_read_device_status(cp, FAKE, 8, None, ctypes.byref(f)) == L.MOE_ERR_INVALID_ARG
     c0 = cfg_of(tokens=0)
-    assert lib.moe_read_device_status(ctypes.byref(c0), FAKE, 3, None, ctypes.byref(f)) == L.MOE_OK
-    assert f.value == 0
+    for which in range(1, 8):    # route (1), permute (2), backward (4), any mix
+        f.value = 5
+        assert lib.moe_read_device_status(ctypes.byref(c0), FAKE, which, None, ctypes.byref(f)) == L.MOE_OK
+        assert f.value == 0
 
 
 def test_workspace_views(lib):

@@ -143,6 +143,33 @@ def test_saved_preactivations_match_recompute(name):
         assert torch.equal(ga[k].view(torch.uint8), gb[k].view(torch.uint8)), k
 
 
+def test_stale_saved_preactivations_are_flagged():
+    """moe_backward(saved = 1) after another permutation was built in the workspace (here a
+    plain moe_forward between moe_forward_train and the backward) raises
+    MOE_FLAG_STALE_SAVED; the regular order raises nothing, and the flag is re-evaluated by
+    every backward."""
+    cfg = CASES["swiglu"]
+    inp = make_inputs(cfg, seed=11)
+    layer = MoELayer(cfg, inp)
+    x = to_device(cfg, inp["x"])
+    dout = to_device(cfg, f32_to_bf16_bits(
+        np.random.default_rng(7).standard_normal((cfg.tokens, cfg.hidden)).astype(np.float32)))
+    layer.forward_train(x)
+    layer.backward(x, dout)
+    assert layer.device_status(4) == 0
+    layer.forward_train(x)
+    out = torch.empty_like(x)
+    L.moe_forward(layer.c, x, layer.w_router, layer.bias, layer.fw_gate, layer.fw_up,
+                  layer.fw_down, out, layer.ws, None)
+    layer._saved = True            # the caller still believes the saved pre-activations hold
+    layer.backward(x, dout)
+    assert layer.device_status(4) == L.MOE_FLAG_STALE_SAVED
+    assert layer.device_status(3) == 0
+    layer.forward_train(x)
+    layer.backward(x, dout)
+    assert layer.device_status(4) == 0
+
+
 AUX_CASES = {
     "topk": C.SMALL.with_(name="aux_topk", tokens=700, hidden=512, inter=256, experts=8,
                           top_k=2, aux_loss_coeff=0.1),

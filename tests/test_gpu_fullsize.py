@@ -1,6 +1,6 @@
 """GPU parity at the full sizes of the five workloads, in the launch configuration the
-bench times: routing and the permutation on every token, expert outputs and the layer
-output on sampled tokens."""
+bench times (packed expert weights for the bf16 layers): routing and the permutation, every
+kept y_perm row, the combine and the layer output, on every token."""
 import pytest
 import torch
 
@@ -11,20 +11,34 @@ import parity as P
 
 pytestmark = pytest.mark.gpu
 
-SAMPLE = {"tiny": None, "small": 48, "mixtral": 24, "cap32": 12, "fine": 16, "mixtral_threshold": 24}
+WORKLOADS = ["tiny", "small", "mixtral", "cap32", "fine", "mixtral_threshold"]
 
 
-@pytest.mark.parametrize("name", list(SAMPLE))
+@pytest.mark.parametrize("name", WORKLOADS)
 def test_full_size_workload(name):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     cfg = C.get(name)
+    if cfg.dtype == C.BF16:
+        cfg = cfg.with_(weights="packed")
     print(f"[fullsize] {name}: generating inputs", flush=True)
     inputs = make_inputs(cfg, seed=0, threads=16)
     print(f"[fullsize] {name}: running", flush=True)
-    rep, layer = P.full_check(cfg, inputs, tokens_sample=SAMPLE[name])
+    rep, layer = P.full_check(cfg, inputs, tokens_sample=None)
     print(f"[fullsize] {name}: {rep}", flush=True)
-    if cfg.capacity_factor > 0:
+    T = cfg.tokens
+    # every token is compared except the counted exclusions: near ties of the routing
+    # decision, and (capacity only) tokens whose kept/dropped status a flipped near tie
+    # shifted
+    assert rep["compared_tokens"] == T - rep["excluded"]
+    assert rep["excluded"] == rep["excluded_near_tie"] + rep["excluded_keep_shift"]
+    assert rep["excluded_near_tie"] <= max(5, T // 500)
+    assert rep["ffn_rows"] == rep["kept_rows"]          # every kept y_perm row compared
+    if cfg.capacity_factor <= 0:
+        assert rep["excluded_keep_shift"] == 0
+        if cfg.routing == "topk":
+            assert rep["kept_rows"] == T * cfg.top_k
+    else:
         assert rep["dropped"] > 0
     del layer
     torch.cuda.empty_cache()
@@ -33,8 +47,8 @@ def test_full_size_workload(name):
 @pytest.mark.parametrize("name", ["mixtral", "cap32", "fine"])
 def test_full_size_packed_forward_is_bit_identical(name):
     """Full-size workloads on packed weights, in the bench's launch configuration: the output
-    equals the plain-weight forward bit for bit (the plain one is checked against the oracle
-    above). cap32 has 32 experts and a binding capacity, fine 128 experts and an odd number
+    equals the plain-weight forward bit for bit (the packed one is checked against the oracle
+    on every token above). cap32 has 32 experts and a binding capacity, fine 128 experts and an odd number
     of n-tiles in GEMM 1 (I = 1408)."""
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
