@@ -49,13 +49,21 @@ def parse_args():
     return ap.parse_args()
 
 
+GEMM_SOURCES = ("gemm.hip", "packed_kloop.h", "kloop_model.h")
+
+
 def kernel_source_digest(path: str | None = None) -> str:
-    """Digest of the GEMM source with comments and whitespace removed, so that an edit of
-    comments alone keeps the committed counter summary valid."""
-    p = path or os.path.join(ROOT, "mixture_experts_layer_37_amd", "csrc", "gemm.hip")
-    text = re.sub(r"//[^\n]*", "", open(p, encoding="utf-8").read())
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return hashlib.sha256("".join(text.split()).encode()).hexdigest()[:16]
+    """Digest of the GEMM sources (gemm.hip and the k-loop headers it includes, or the one
+    file `path`) with comments and whitespace removed, so that an edit of comments alone
+    keeps the committed counter summary valid."""
+    csrc = os.path.join(ROOT, "mixture_experts_layer_37_amd", "csrc")
+    paths = [path] if path else [os.path.join(csrc, f) for f in GEMM_SOURCES]
+    h = hashlib.sha256()
+    for p in paths:
+        text = re.sub(r"//[^\n]*", "", open(p, encoding="utf-8").read())
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        h.update("".join(text.split()).encode())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(per_launch_flops_unused=None):

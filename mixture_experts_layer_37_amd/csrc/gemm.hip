@@ -52,6 +52,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "packed_kloop.h"
 
 namespace moe {
 
@@ -192,9 +193,6 @@ struct Frags {
   bf16x8 a[4];   // token rows   wm*128 + 32 i + (lane & 31)
   bf16x8 b[4];   // weight columns of the wave's four 32-column blocks
 };
-
-// s_waitcnt immediate: lgkmcnt(0), vmcnt and expcnt left at their maxima (no wait).
-constexpr int kWaitLgkm0 = 0xC07F;
 
 constexpr int kHalf = BK * 128;                  // elements of one B half [64 k][128 n]
 constexpr int kStage = BM * BK + 2 * kHalf;      // elements of one LDS stage (64 KB)
@@ -396,7 +394,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     // track 24 outstanding reads, and without this wait the compiler waits for all of them
     // after issuing the new ones.
     auto phase = [&](const bf16_t* stg, int kk_next, Frags& nxt, const Frags& cur) {
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0Only);
       load_frags(stg, kk_next, nxt);
       mfma16(cur);
       __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);   // the LDS reads
@@ -768,40 +766,12 @@ __global__ __launch_bounds__(256) void pack_weight_kernel(const bf16_t* __restri
   }
 }
 
-__device__ __forceinline__ uint32_t lds_offset(const void* p) {
-  return (uint32_t)(uintptr_t)(const lds_char*)p;
-}
-// The packed kernel's k-loop issues its loads as asm, so the compiler tracks none of them
-// and adds no waits of its own (mixing LDS DMA and register loads, it would wait for all of
-// them in every k-step); the loop waits with explicit counts instead.
-// 16 bytes per lane global -> LDS at lds + 16 l. m0 is written right before the load that
-// reads it, with the one wait state an LDS DMA needs after an SALU write of m0.
-__device__ __forceinline__ void dma16_asm(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(src), "s"(lds) : "memory", "m0");
-}
-// 16 bytes per lane global -> registers, from p + OFF bytes (OFF in the instruction's
-// immediate field, so the slices of one k-step share one address computation).
-template <int OFF>
-__device__ __forceinline__ bf16x8 load16_asm_at(const bf16_t* p) {
-  bf16x8 v;
-  asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "=v"(v) : "v"(p), "n"(OFF) : "memory");
-  return v;
-}
-// Wait until at most N of this wave's loads are in flight. The four fragments pass through
-// the wait, so no instruction that reads them can be scheduled above it.
-template <int N>
-__device__ __forceinline__ void wait_loads(bf16x8* b) {
-  asm volatile("s_waitcnt vmcnt(%4)" : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]) : "n"(N));
-}
-// s_waitcnt immediate: vmcnt(n) and lgkmcnt(0)
-constexpr int wait_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
-
 // Grouped GEMM on packed weights: SWIGLU (P0 gate, P1 up), GELU and NONE (P0), with the
 // tile list, round-by-round order, fused gather and split-K tail of
 // grouped_gemm_bf16_kernel. Wave (wm, wn) computes rows wm*128 .. +127 and the four
 // 32-column blocks j: SwiGLU gate (j < 2) / up (j >= 2) columns wn*64 + 32 (j & 1), else
-// columns wn*128 + 32 j.
+// columns wn*128 + 32 j. The k-loop (token rows by LDS DMA, weight fragments straight into
+// registers, waits derived from its issue order at compile time) is packed_kloop.
 template <int EPI>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ row_token, int a_rows,
@@ -834,9 +804,6 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
     const int m = wm * 128 + l32;
     a_rd[kk] = (uint32_t)(m * BK * 2 + (((kk * 2 + lhi) ^ swz(m)) << 4));
   }
-  struct FragA {
-    bf16x8 a[4];
-  };
   auto load_a = [&](const bf16_t* stg, int kk, FragA& f) {
     const char* st = (const char*)stg;
 #pragma unroll
@@ -874,21 +841,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
       else { P = P0; nb = n_t * 8 + wn * 4 + j; }
       bsrc[j] = P + ((size_t)e * NB + nb) * KS * 512 + lane * 8;
     }
-    // ring of eight k slices of B fragments (slot = slice & 7 within a pair of k-steps)
-    bf16x8 bv[8][4];
-    // Loads each unit issues per wave; the wait counts below are derived from these, so
-    // they stay exact if either changes. An inexact count is not only a wrong result: a
-    // wait that passes early lets the compiler reuse a register that a load still in
-    // flight will overwrite.
-    constexpr int kLB = 4;   // B loads per k slice (one per fragment j)
-    constexpr int kLA = 8;   // A DMA loads per k-step
-    // B slice kk (0..3) of the k-step whose first slice is at base[j] (slices are 1 KB
-    // apart: one address per k-step, the slice in the immediate offset)
-    auto load_b = [&](const bf16_t* const* base, auto kk, int slot) {
-#pragma unroll
-      for (int j = 0; j < kLB; ++j)
-        bv[slot][j] = load16_asm_at<decltype(kk)::value * 1024>(base[j]);
-    };
+    constexpr int kLA = 8;   // A DMA loads per k-step and wave: rows wave * 64 + 8 i + lane / 8
     auto dma_a = [&](int kt, bf16_t* stg) {
       const uint32_t kA = (uint32_t)(kt * BK * 2);
       const uint32_t dst = lds_offset(stg) + wave * kLA * 1024;
@@ -902,94 +855,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    auto mfma16 = [&](const FragA& f, int slot) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[slot][j], f.a[i], acc[i][j], 0,
-                                                              0, 0);
-    };
-    FragA f0, f1;
-    // One k slice: wait for its B fragments, issue the next slice's A reads and (ahead by
-    // one k-step) the B loads of slice s + 4, then the 16 MFMAs.
-    auto phase = [&](const bf16_t* stg, int kk_next, FragA& nxt, const FragA& cur, int slot,
-                     const bf16_t* const* nbase, auto kk, bool ahead, auto wait) {
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-      wait_loads<decltype(wait)::value>(bv[slot]);
-      load_a(stg, kk_next, nxt);
-      if (ahead) load_b(nbase, kk, (slot + 4) & 7);
-      mfma16(cur, slot);
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // the A reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // then the MFMAs
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    // k-step kt on stage `cur` (its B in slots sb .. sb+3). Loads issue in this order
-    // (vector memory loads complete in issue order, the LDS DMA ones included):
-    //   prologue:  A(kb), wait all | B(4kb), B(4kb+1), B(4kb+2), A(kb+1), B(4kb+3)
-    //   step kt-1: ..., A(kt+1), B(4kt+3)
-    //   step kt:   B(4kt+4), B(4kt+5), B(4kt+6) | wait A(kt+1) | A(kt+2), B(4kt+7)
-    // A(kt+2) only if kt+2 < ke, B(4kt+4 ..) only if kt+1 < ke (n1), and A(kt+1) was issued
-    // exactly when n1 holds. Each wait is the number of loads issued after the one it needs.
-    auto kstep = [&](int kt, bf16_t* cur, bf16_t* nxt, int sb, auto refill, auto next) {
-      constexpr int n1 = decltype(next)::value ? 1 : 0;
-      // B(4kt): then B(4kt+1), B(4kt+2), A(kt+1), B(4kt+3)
-      using W0 = std::integral_constant<int, 3 * kLB + n1 * kLA>;
-      // B(4kt+1): then B(4kt+2), A(kt+1), B(4kt+3), B(4kt+4)
-      using W1 = std::integral_constant<int, 2 * kLB + n1 * (kLA + kLB)>;
-      // B(4kt+2): then A(kt+1), B(4kt+3), B(4kt+4), B(4kt+5)
-      using W2 = std::integral_constant<int, kLB + n1 * (kLA + 2 * kLB)>;
-      static_assert(W0::value < 64 && W1::value < 64 && W2::value < 64, "vmcnt is 6 bits");
-      using S0 = std::integral_constant<int, 0>;
-      using S1 = std::integral_constant<int, 1>;
-      using S2 = std::integral_constant<int, 2>;
-      using S3 = std::integral_constant<int, 3>;
-      const bf16_t* nbase[kLB];   // slice 4(kt+1) of each fragment: B(4kt+4) .. B(4kt+7)
-#pragma unroll
-      for (int j = 0; j < kLB; ++j) nbase[j] = bsrc[j] + (size_t)(kt + 1) * 2048;
-      phase(cur, 1, f1, f0, sb + 0, nbase, S0{}, n1, W0{});
-      phase(cur, 2, f0, f1, sb + 1, nbase, S1{}, n1, W1{});
-      phase(cur, 3, f1, f0, sb + 2, nbase, S2{}, n1, W2{});
-      // A(kt+1): then B(4kt+3) .. B(4kt+6)
-      if constexpr (n1) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(4 * kLB));
-      else __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      __builtin_amdgcn_sched_barrier(0);
-      // B(4kt+3): then B(4kt+4) .. B(4kt+6)
-      wait_loads<3 * kLB * n1>(bv[(sb + 3) & 7]);
-      if constexpr (decltype(refill)::value) dma_a(kt + 2, cur);
-      if constexpr (n1) {
-        load_a(nxt, 0, f0);
-        load_b(nbase, S3{}, (sb + 7) & 7);
-      }
-      mfma16(f1, sb + 3);
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    using yes = std::true_type;
-    using no = std::false_type;
-    // prologue: A(kb) landed, then B(4kb) .. B(4kb+2), A(kb+1), B(4kb+3) in flight
-    dma_a(kb, sa0);
-    __builtin_amdgcn_s_waitcnt(0);
-    {
-      const bf16_t* pbase[kLB];   // slice 4kb of each fragment
-#pragma unroll
-      for (int j = 0; j < kLB; ++j) pbase[j] = bsrc[j] + (size_t)kb * 2048;
-      load_b(pbase, std::integral_constant<int, 0>{}, 0);
-      load_b(pbase, std::integral_constant<int, 1>{}, 1);
-      load_b(pbase, std::integral_constant<int, 2>{}, 2);
-      dma_a(kb + 1, sa1);
-      load_b(pbase, std::integral_constant<int, 3>{}, 3);
-    }
-    __syncthreads();
-    load_a(sa0, 0, f0);
-    int kt = kb;   // ke - kb is even
-    for (; kt + 2 < ke; kt += 2) {
-      kstep(kt, sa0, sa1, 0, yes{}, yes{});
-      kstep(kt + 1, sa1, sa0, 4, yes{}, yes{});
-    }
-    kstep(kt, sa0, sa1, 0, no{}, yes{});
-    kstep(kt + 1, sa1, sa0, 4, no{}, no{});
-    __syncthreads();   // every wave is done with both stages before the next tile's DMA
+    packed_kloop<kLA, 4>(kb, ke, sa0, sa1, bsrc, acc, load_a, dma_a);
 
     // Epilogue. acc[i][j][4q+s]: row m = wm*128 + i*32 + l32, column (within the wave's
     // block j) = 8q + 4*lhi + s.
@@ -1162,8 +1028,8 @@ hipError_t launch_gemm_bf16_packed(int epi, const bf16_t* a, const int32_t* row_
 // pairs of k-steps), possibly empty (then C_e = 0); pad rows are zero. Tiles are ordered
 // (expert, m-tile, n-tile) and run round by round: an XCD's blocks share A panels in L2,
 // the XCDs of one round read the same expert's rows, and every block meets every expert in
-// turn, which balances experts of different row counts. The k-loop, its load order and its
-// wait counts are those of grouped_gemm_packed_kernel.
+// turn, which balances experts of different row counts. The k-loop is the one
+// grouped_gemm_packed_kernel runs (packed_kloop), with the transposing A reads.
 // TOUT: C is stored transposed, C_e^T [N][M] (dW_gate / dW_up computed as dg^T x).
 template <bool TOUT>
 __global__ __launch_bounds__(256, 1) void grouped_wgrad_packed_kernel(
@@ -1188,9 +1054,6 @@ __global__ __launch_bounds__(256, 1) void grouped_wgrad_packed_kernel(
     a_rd[i] = (uint32_t)(wm * kHalf * 2) +
               (uint32_t)(krow0 * 256 + ((c32 ^ bswz(krow0)) << 5) + 8 * (lane & 3));
   }
-  struct FragA {
-    bf16x8 a[4];
-  };
   auto load_a = [&](const bf16_t* stg, int kk, FragA& f) {
     const char* st = (const char*)stg + kk * 16 * 256;
 #pragma unroll
@@ -1231,16 +1094,7 @@ __global__ __launch_bounds__(256, 1) void grouped_wgrad_packed_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       bsrc[j] = PB + ((size_t)(n_t * 8 + wn * 4 + j) * ksb + kbase / 16) * 512 + lane * 8;
-    bf16x8 bv[8][4];
-    constexpr int kLB = 4;   // B loads per k slice
-    constexpr int kLA = 8;   // A DMA loads per k-step (4 rows x 2 halves)
-    // B slice kk (0..3) of the k-step whose first slice is at base[j] (slices are 1 KB
-    // apart: one address per k-step, the slice in the immediate offset)
-    auto load_b = [&](const bf16_t* const* base, auto kk, int slot) {
-#pragma unroll
-      for (int j = 0; j < kLB; ++j)
-        bv[slot][j] = load16_asm_at<decltype(kk)::value * 1024>(base[j]);
-    };
+    constexpr int kLA = 8;   // A DMA loads per k-step and wave (4 rows x 2 halves)
     auto dma_a = [&](int kt, bf16_t* stg) {
       const size_t kA = (size_t)kt * BK * lda * 2;
       const uint32_t dst = lds_offset(stg) + wave * 4 * 1024;
@@ -1257,77 +1111,8 @@ __global__ __launch_bounds__(256, 1) void grouped_wgrad_packed_kernel(
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    auto mfma16 = [&](const FragA& f, int slot) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[slot][j], f.a[i], acc[i][j], 0,
-                                                              0, 0);
-    };
-    FragA f0, f1;
-    auto phase = [&](const bf16_t* stg, int kk_next, FragA& nxt, const FragA& cur, int slot,
-                     const bf16_t* const* nbase, auto kk, bool ahead, auto wait) {
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-      wait_loads<decltype(wait)::value>(bv[slot]);
-      load_a(stg, kk_next, nxt);
-      if (ahead) load_b(nbase, kk, (slot + 4) & 7);
-      mfma16(cur, slot);
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // the A reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // then the MFMAs
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    // issue order and wait counts: as grouped_gemm_packed_kernel
-    auto kstep = [&](int kt, bf16_t* cur, bf16_t* nxt, int sb, auto refill, auto next) {
-      constexpr int n1 = decltype(next)::value ? 1 : 0;
-      using W0 = std::integral_constant<int, 3 * kLB + n1 * kLA>;
-      using W1 = std::integral_constant<int, 2 * kLB + n1 * (kLA + kLB)>;
-      using W2 = std::integral_constant<int, kLB + n1 * (kLA + 2 * kLB)>;
-      static_assert(W0::value < 64 && W1::value < 64 && W2::value < 64, "vmcnt is 6 bits");
-      using S0 = std::integral_constant<int, 0>;
-      using S1 = std::integral_constant<int, 1>;
-      using S2 = std::integral_constant<int, 2>;
-      using S3 = std::integral_constant<int, 3>;
-      const bf16_t* nbase[kLB];   // slice 4(kt+1) of each fragment: B(4kt+4) .. B(4kt+7)
-#pragma unroll
-      for (int j = 0; j < kLB; ++j) nbase[j] = bsrc[j] + (size_t)(kt + 1) * 2048;
-      phase(cur, 1, f1, f0, sb + 0, nbase, S0{}, n1, W0{});
-      phase(cur, 2, f0, f1, sb + 1, nbase, S1{}, n1, W1{});
-      phase(cur, 3, f1, f0, sb + 2, nbase, S2{}, n1, W2{});
-      if constexpr (n1) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(4 * kLB));
-      else __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      __builtin_amdgcn_sched_barrier(0);
-      wait_loads<3 * kLB * n1>(bv[(sb + 3) & 7]);
-      if constexpr (decltype(refill)::value) dma_a(kt + 2, cur);
-      if constexpr (n1) {
-        load_a(nxt, 0, f0);
-        load_b(nbase, S3{}, (sb + 7) & 7);
-      }
-      mfma16(f1, sb + 3);
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    using yes = std::true_type;
-    using no = std::false_type;
-    if (KT > 0) {   // KT is even: the padded range is a multiple of 128 rows
-      dma_a(0, sa0);
-      __builtin_amdgcn_s_waitcnt(0);
-      load_b(bsrc, std::integral_constant<int, 0>{}, 0);
-      load_b(bsrc, std::integral_constant<int, 1>{}, 1);
-      load_b(bsrc, std::integral_constant<int, 2>{}, 2);
-      dma_a(1, sa1);
-      load_b(bsrc, std::integral_constant<int, 3>{}, 3);
-      __syncthreads();
-      load_a(sa0, 0, f0);
-      int kt = 0;
-      for (; kt + 2 < KT; kt += 2) {
-        kstep(kt, sa0, sa1, 0, yes{}, yes{});
-        kstep(kt + 1, sa1, sa0, 4, yes{}, yes{});
-      }
-      kstep(kt, sa0, sa1, 0, no{}, yes{});
-      kstep(kt + 1, sa1, sa0, 4, no{}, no{});
-      __syncthreads();
-    }
+    // A fragments come from two transposing reads each: 8 LDS reads per slice
+    if (KT > 0) packed_kloop<kLA, 8>(0, KT, sa0, sa1, bsrc, acc, load_a, dma_a);   // KT even
     // acc[i][j][4q+s]: row m = wm*128 + 32i + l32, column n = wn*128 + 32j + 8q + 4lhi + s
     bf16_t* Ce = C + (size_t)e * M * N;
 #pragma unroll

@@ -1,0 +1,178 @@
+// The k-loop of the packed-operand GEMMs (grouped_gemm_packed_kernel: token rows x packed
+// weights; grouped_wgrad_packed_kernel: activations x packed rows), one implementation for
+// both.
+//
+// Per 16-wide k slice a wave multiplies its four A fragments (from an LDS stage, filled by
+// global->LDS DMA one k-step ahead) by four B fragments that come straight from global memory
+// into registers: each is one 1 KB block of the packed layout, a coalesced 16-byte load per
+// lane, issued one k-step ahead into a ring of eight slices. The loads are inline asm, so
+// the compiler tracks none of them and adds no waits of its own (mixing LDS DMA and
+// register loads, it would wait for all of them once per k-step); the loop instead executes
+// the op lists of kloop_model.h and waits with the counts that model derives and checks at
+// compile time.
+#pragma once
+
+#include <type_traits>
+#include <utility>
+
+#include "common.h"
+#include "kloop_model.h"
+
+namespace moe {
+
+typedef __attribute__((address_space(3))) char lds_char_t;
+
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_char_t*)p;
+}
+// 16 bytes per lane global -> LDS at lds + 16 l. m0 is written right before the load that
+// reads it, with the one wait state an LDS DMA needs after an SALU write of m0.
+__device__ __forceinline__ void dma16_asm(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(lds) : "memory", "m0");
+}
+// 16 bytes per lane global -> registers, from p + OFF bytes (OFF in the instruction's
+// immediate field, so the slices of one k-step share one address computation).
+template <int OFF>
+__device__ __forceinline__ bf16x8 load16_asm_at(const bf16_t* p) {
+  bf16x8 v;
+  asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "=v"(v) : "v"(p), "n"(OFF) : "memory");
+  return v;
+}
+// Wait until at most N of this wave's loads are in flight. The four fragments pass through
+// the wait, so no instruction that reads them can be scheduled above it.
+template <int N>
+__device__ __forceinline__ void wait_loads(bf16x8* b) {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit count");
+  asm volatile("s_waitcnt vmcnt(%4)" : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]) : "n"(N));
+}
+// s_waitcnt immediates: lgkmcnt(0) alone; vmcnt(n) with lgkmcnt(0)
+constexpr int kWaitLgkm0Only = 0xC07F;
+constexpr int wait_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+
+// A fragments of one 16-wide k slice: rows (or columns) 32 i + (lane & 31) of the wave's 128.
+struct FragA {
+  bf16x8 a[4];
+};
+
+template <class F, int... I>
+__device__ __forceinline__ void for_each_op(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+
+// One tile's k-steps [kb, ke) (ke - kb even and >= 2) on the two A stages sa0 / sa1.
+//   kLA      A DMA instructions per k-step and wave (dma_a issues exactly that many)
+//   kAReads  LDS read instructions per load_a (for the scheduling groups)
+//   bsrc[j]  this lane's 16 bytes of B fragment j, slice 0 of k-step 0: slice s of k-step kt
+//            is at bsrc[j] + 2048 kt elements + 1024 s bytes (the packed layout)
+//   load_a(stage, kk, FragA&)  the wave's A fragments of slice kk from an LDS stage
+//   dma_a(kt, stage)           this wave's global->LDS loads of k-step kt
+// acc[i][j] += B fragment j x A fragment i over the k-steps, v_mfma_f32_32x32x16_bf16 (each
+// lane's accumulators then hold four consecutive columns j of one row i).
+template <int kLA, int kAReads, class LoadA, class DmaA>
+__device__ __forceinline__ void packed_kloop(int kb, int ke, bf16_t* sa0, bf16_t* sa1,
+                                             const bf16_t* const* bsrc, f32x16 (&acc)[4][4],
+                                             LoadA&& load_a, DmaA&& dma_a) {
+  using namespace kloop;
+  static_assert(tile_mismatches<kLA>() == 0 && counts_fit<kLA>(),
+                "k-loop wait counts disagree with the issue order");
+  bf16x8 bv[8][kLB];   // ring of eight k slices of B fragments (at most five live)
+  FragA fr[2];         // A fragments of slices of even / odd index
+
+  // B slice kk (0..3) of the k-step whose slice 0 is at base[j]
+  auto load_b = [&](const bf16_t* const* base, auto kk, int slot) {
+#pragma unroll
+    for (int j = 0; j < kLB; ++j)
+      bv[slot][j] = load16_asm_at<decltype(kk)::value * 1024>(base[j]);
+  };
+  auto mfma16 = [&](const FragA& f, int slot) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[slot][j], f.a[i], acc[i][j], 0, 0, 0);
+  };
+
+  // prologue (kPrologue)
+  {
+    const bf16_t* pbase[kLB];   // slice 0 of k-step kb
+#pragma unroll
+    for (int j = 0; j < kLB; ++j) pbase[j] = bsrc[j] + (size_t)kb * 2048;
+    for_each_op(
+        [&](auto I) {
+          constexpr Op op = kPrologue[decltype(I)::value];
+          if constexpr (op.kind == kDmaA) {
+            dma_a(kb + op.arg, op.arg ? sa1 : sa0);
+          } else if constexpr (op.kind == kWaitAll) {
+            __builtin_amdgcn_s_waitcnt(0);
+          } else if constexpr (op.kind == kLoadB) {
+            load_b(pbase, std::integral_constant<int, op.arg>{}, op.arg);
+          } else if constexpr (op.kind == kBarrier) {
+            __syncthreads();
+          } else if constexpr (op.kind == kReadA0) {
+            load_a(sa0, 0, fr[0]);
+          } else {
+            static_assert(op.kind == kDmaA, "op not allowed in the prologue");
+          }
+        },
+        std::make_integer_sequence<int, kPrologueOps>{});
+  }
+
+  // k-step kt on stage `cur` (its B in ring slots sb .. sb + 3), `nxt` in flight; `refill`
+  // (kt + 2 < ke) and `next` (kt + 1 < ke) are compile-time at every call site, so the
+  // steady-state loop carries no branches, which keeps the fragments in VGPRs and the
+  // accumulators in AGPRs.
+  auto kstep = [&](int kt, bf16_t* cur, bf16_t* nxt, int sb, auto refill, auto next) {
+    constexpr bool kNext = decltype(next)::value, kRefill = decltype(refill)::value;
+    const bf16_t* nbase[kLB];   // slice 0 of k-step kt + 1
+#pragma unroll
+    for (int j = 0; j < kLB; ++j) nbase[j] = bsrc[j] + (size_t)(kt + 1) * 2048;
+    for_each_op(
+        [&](auto I) {
+          constexpr int i = decltype(I)::value;
+          constexpr Op op = kStep[i];
+          constexpr int count = wait_count<kLA>(i, kNext, kRefill);
+          if constexpr (op.kind == kLgkm0) {
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0Only);
+          } else if constexpr (op.kind == kWaitB) {
+            wait_loads<count>(bv[(sb + op.arg) & 7]);
+          } else if constexpr (op.kind == kReadA) {
+            load_a(cur, op.arg, fr[op.arg & 1]);
+          } else if constexpr (op.kind == kLoadBNext) {
+            if constexpr (kNext) load_b(nbase, std::integral_constant<int, op.arg>{}, (sb + 4 + op.arg) & 7);
+          } else if constexpr (op.kind == kMfma) {
+            mfma16(fr[op.arg & 1], (sb + op.arg) & 7);
+            if constexpr (op.arg < 3) {   // the slice's A reads, then its MFMAs
+              __builtin_amdgcn_sched_group_barrier(0x100, kAReads, 0);
+              __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          } else if constexpr (op.kind == kWaitANext) {
+            if constexpr (count >= 0) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(count));
+            else __builtin_amdgcn_s_waitcnt(0);
+          } else if constexpr (op.kind == kBarrier) {
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+          } else if constexpr (op.kind == kDmaA2) {
+            if constexpr (kRefill) dma_a(kt + 2, cur);
+          } else if constexpr (op.kind == kReadANext) {
+            if constexpr (kNext) load_a(nxt, 0, fr[0]);
+          } else {
+            static_assert(op.kind == kLgkm0, "op not allowed in a k-step");
+          }
+        },
+        std::make_integer_sequence<int, kStepOps>{});
+  };
+  using yes = std::true_type;
+  using no = std::false_type;
+  int kt = kb;
+  for (; kt + 2 < ke; kt += 2) {
+    kstep(kt, sa0, sa1, 0, yes{}, yes{});
+    kstep(kt + 1, sa1, sa0, 4, yes{}, yes{});
+  }
+  kstep(kt, sa0, sa1, 0, no{}, yes{});
+  kstep(kt + 1, sa1, sa0, 4, no{}, no{});
+  __syncthreads();   // every wave is done with both stages before the next tile's DMA
+}
+
+}  // namespace moe

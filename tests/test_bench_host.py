@@ -27,7 +27,17 @@ def test_digest_ignores_comments_and_whitespace(tmp_path):
                       + "\n/* trailing\n   block comment */\n", encoding="utf-8")
     assert bench.kernel_source_digest(str(edited)) == bench.kernel_source_digest(src)
     changed = tmp_path / "code.hip"
-    changed.write_text(text.replace("constexpr int kLB = 4;", "constexpr int kLB = 2;", 1),
+    assert text.count("constexpr int kLA = 8;") >= 1
+    changed.write_text(text.replace("constexpr int kLA = 8;", "constexpr int kLA = 4;", 1),
                        encoding="utf-8")
     assert bench.kernel_source_digest(str(changed)) != bench.kernel_source_digest(src)
 
+
+
+def test_digest_covers_the_kloop_headers():
+    """The committed counters cover the GEMM's k-loop too, which lives in two headers."""
+    assert set(bench.GEMM_SOURCES) == {"gemm.hip", "packed_kloop.h", "kloop_model.h"}
+    whole = bench.kernel_source_digest()
+    only = bench.kernel_source_digest(os.path.join(ROOT, "mixture_experts_layer_37_amd", "csrc",
+                                                   "gemm.hip"))
+    assert whole != only
