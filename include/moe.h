@@ -27,8 +27,9 @@
  *     are float32; expert ids and row indices are int32 (lshu.cn page, section 5.2).
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null stream), do no
  *     device->host synchronisation (moe_read_device_status excepted) and keep no global
- *     mutable state, so they are safe to call from several host threads. Calls that share
- *     one workspace must be ordered on one stream.
+ *     mutable state (moe_permute_noalloc's fixed scratch excepted), so they are safe to
+ *     call from several host threads. Calls that share one workspace must be ordered on one
+ *     stream.
  *   - Alignment: every tensor of the layer dtype (x, w_router in bf16, w_gate, w_up,
  *     w_down and their packed forms, x_perm, h, y_perm, out, dout, dx and the weight
  *     gradients) and the workspaces ws / bws must be 16-byte aligned, since the kernels move
@@ -162,6 +163,28 @@ moe_status moe_permute(const moe_config* cfg, const void* x, const int32_t* topk
                        void* x_perm, int32_t* expert_counts, int32_t* expert_offsets,
                        int32_t* row_token, int32_t* slot_row, void* ws, size_t ws_bytes,
                        moe_stream_t stream);
+
+/* moe_permute for callers that cannot allocate device memory or hand over a workspace
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same results as moe_permute, bit for bit, with its scratch (the per-block expert
+ * histograms and flags) in a fixed device array inside the library instead of `ws`. It
+ * calls no allocating routine. The array is MOE_NOALLOC_SCRATCH_BYTES per device (each
+ * device that runs this call holds its own copy until the process ends) and this call uses
+ * ceil(T / 1024) * (E + 1) * 4 bytes of it: a larger T or E -> MOE_ERR_WORKSPACE, before any
+ * HIP call. Every call on one device shares that device's array, so calls that overlap on
+ * one device (different streams, or different host threads) race: order them on one
+ * stream. The stream must belong to the current device; the array's device address is
+ * looked up once per device, on the first call there (the library's only global state,
+ * guarded for concurrent first calls).
+ *   x, topk_idx, x_perm (or NULL), expert_counts, expert_offsets, row_token, slot_row:
+ *       as for moe_permute
+ *   flags  [1] int32 out, or NULL: the device flags moe_permute would raise
+ *          (MOE_FLAG_BAD_INDEX), since no workspace holds them for moe_read_device_status */
+enum { MOE_NOALLOC_SCRATCH_BYTES = 1 << 20 };
+moe_status moe_permute_noalloc(const moe_config* cfg, const void* x, const int32_t* topk_idx,
+                               void* x_perm, int32_t* expert_counts, int32_t* expert_offsets,
+                               int32_t* row_token, int32_t* slot_row, int32_t* flags,
+                               moe_stream_t stream);
 
 /* Grouped GEMM 1 with the activation fused: for the rows of each expert e,
  * h = silu(x_perm Wg[e]) * (x_perm Wu[e])  (SwiGLU)   or   h = gelu(x_perm Wu[e])  (GELU)

@@ -33,12 +33,22 @@ hipError_t launch_route_topk(const float* logits, int32_t* topk_idx, float* topk
 // ---- permute (permute.hip)
 int permute_count_blocks(int T);
 // gen (may be null): the workspace's permutation generation, advanced by one; gen_copy (may
-// be null): receives the new value (a training forward's record of it)
+// be null): receives the new value (a training forward's record of it); flag_out (may be
+// null): the OR of the per-block flags
 hipError_t launch_permute(const void* x, int elem_bytes, const int32_t* topk_idx, void* x_perm,
                           int32_t* counts, int32_t* offsets, int32_t* row_token,
                           int32_t* slot_row, int32_t* hist, int32_t* flags, int32_t* gen,
-                          int32_t* gen_copy, int T, int H, int E, int k, int cap,
-                          hipStream_t s);
+                          int32_t* gen_copy, int32_t* flag_out, int T, int H, int E, int k,
+                          int cap, hipStream_t s);
+// The same permutation with its scratch in a file-scope device array of kNoAllocScratchWords
+// int32 words (no workspace, no allocation): permute_noalloc_words(T, E) words are used;
+// more -> hipErrorInvalidValue, before any HIP call. flag_out (may be null) as above.
+constexpr int kNoAllocScratchWords = 1 << 18;   // 1 MiB
+size_t permute_noalloc_words(int T, int E);
+hipError_t launch_permute_noalloc(const void* x, int elem_bytes, const int32_t* topk_idx,
+                                  void* x_perm, int32_t* counts, int32_t* offsets,
+                                  int32_t* row_token, int32_t* slot_row, int32_t* flag_out,
+                                  int T, int H, int E, int k, int cap, hipStream_t s);
 
 // ---- grouped expert GEMMs (gemm.hip)
 // Epilogues: SWIGLU h = silu(g) u; GELU h = gelu(a); NONE the product itself; GU the gate

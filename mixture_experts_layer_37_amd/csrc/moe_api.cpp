@@ -13,6 +13,8 @@
 #include "kernels.h"
 
 // The binding mirrors this layout (explicit 32-bit fields, no implicit padding).
+static_assert(MOE_NOALLOC_SCRATCH_BYTES == moe::kNoAllocScratchWords * 4,
+              "the header states the size of the no-allocation scratch");
 static_assert(sizeof(moe_config) == 64 && offsetof(moe_config, routing) == 40 &&
                   offsetof(moe_config, weight_layout) == 44 &&
                   offsetof(moe_config, threshold) == 48 &&
@@ -240,8 +242,8 @@ moe_status do_permute(const moe_config* c, const void* x, const int32_t* idx, vo
   return hip_status(moe::launch_permute(
       x, (int)esize(c), idx, x_perm, counts, offsets, row_token, slot_row,
       region<int32_t>(ws, L, R_HIST), region<int32_t>(ws, L, R_PERM_FLAGS),
-      region<int32_t>(ws, L, R_GEN), gen_copy, c->tokens, c->hidden, c->experts, c->top_k,
-      cap < c->tokens ? cap : c->tokens, s));
+      region<int32_t>(ws, L, R_GEN), gen_copy, nullptr, c->tokens, c->hidden, c->experts,
+      c->top_k, cap < c->tokens ? cap : c->tokens, s));
 }
 
 // GEMM 1. `a` is x_perm (row_token == nullptr) or the token matrix x read through
@@ -348,6 +350,31 @@ moe_status moe_permute(const moe_config* cfg, const void* x, const int32_t* topk
   MOE_TRY(check_ws(cfg, ws, ws_bytes));
   return do_permute(cfg, x, topk_idx, x_perm, expert_counts, expert_offsets, row_token, slot_row,
                     ws, (hipStream_t)stream);
+}
+
+moe_status moe_permute_noalloc(const moe_config* cfg, const void* x, const int32_t* topk_idx,
+                               void* x_perm, int32_t* expert_counts, int32_t* expert_offsets,
+                               int32_t* row_token, int32_t* slot_row, int32_t* flags,
+                               moe_stream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  if (cfg->tokens == 0) return MOE_OK;   // empty batch: nothing to read or write
+  if (moe::permute_noalloc_words(cfg->tokens, cfg->experts) * 4 > MOE_NOALLOC_SCRATCH_BYTES)
+    return MOE_ERR_WORKSPACE;            // beyond the library's fixed scratch
+  if (x_perm != nullptr) {   // NULL: row maps only
+    MOE_TRY(need(x, 16));
+    MOE_TRY(need(x_perm, 16));
+  }
+  MOE_TRY(need(topk_idx, 4));
+  MOE_TRY(need(expert_counts, 4));
+  MOE_TRY(need(expert_offsets, 4));
+  MOE_TRY(need(row_token, 4));
+  MOE_TRY(need(slot_row, 4));
+  if (flags != nullptr) MOE_TRY(need(flags, 4));
+  const int cap = capacity_of(cfg);
+  return hip_status(moe::launch_permute_noalloc(
+      x, (int)esize(cfg), topk_idx, x_perm, expert_counts, expert_offsets, row_token, slot_row,
+      flags, cfg->tokens, cfg->hidden, cfg->experts, cfg->top_k,
+      cap < cfg->tokens ? cap : cfg->tokens, (hipStream_t)stream));
 }
 
 moe_status moe_expert_up(const moe_config* cfg, const void* x_perm,

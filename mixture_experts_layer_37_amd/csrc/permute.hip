@@ -18,6 +18,9 @@
 //             below C; writes slot_row / row_token and copies the token row once into each
 //             of its kept rows with 16-byte loads and stores, all loads of a chunk in
 //             flight together.
+#include <atomic>
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -90,17 +93,30 @@ __global__ __launch_bounds__(1024) void permute_count_kernel(const int32_t* __re
   if (tid == 0) flags[blockIdx.x] = sbad ? 1 /* MOE_FLAG_BAD_INDEX */ : 0;
 }
 
+// flag_out (may be null): receives the OR of the count blocks' flags.
 __global__ __launch_bounds__(256) void permute_scan_kernel(int32_t* __restrict__ hist,
                                                            int32_t* __restrict__ counts,
                                                            int32_t* __restrict__ offsets, int NB,
                                                            int E, int cap, int32_t* gen,
-                                                           int32_t* gen_copy) {
+                                                           int32_t* gen_copy,
+                                                           const int32_t* __restrict__ flags,
+                                                           int32_t* __restrict__ flag_out) {
   __shared__ int wsum[4];
+  __shared__ int wflag[4];
   const int e = threadIdx.x, wave = e >> 6, lane = e & 63;
   if (e == 0 && gen != nullptr) {
     const int g = gen[0] + 1;
     gen[0] = g;
     if (gen_copy != nullptr) gen_copy[0] = g;
+  }
+  if (flag_out != nullptr) {   // uniform branch: every thread takes part
+    int f = 0;
+    for (int b = e; b < NB; b += blockDim.x) f |= flags[b];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) f |= __shfl_xor(f, o);
+    if (lane == 0) wflag[wave] = f;
+    __syncthreads();
+    if (e == 0) flag_out[0] = wflag[0] | wflag[1] | wflag[2] | wflag[3];
   }
   int run = 0;
   if (e < E) {
@@ -210,14 +226,15 @@ __global__ __launch_bounds__(256) void permute_rows_kernel(
 hipError_t launch_permute(const void* x, int elem_bytes, const int32_t* topk_idx, void* x_perm,
                           int32_t* counts, int32_t* offsets, int32_t* row_token,
                           int32_t* slot_row, int32_t* hist, int32_t* flags, int32_t* gen,
-                          int32_t* gen_copy, int T, int H, int E, int k, int cap, hipStream_t s) {
+                          int32_t* gen_copy, int32_t* flag_out, int T, int H, int E, int k,
+                          int cap, hipStream_t s) {
   const int NB = permute_count_blocks(T);
   hipLaunchKernelGGL(permute_count_kernel, dim3(NB), dim3(kCountBlockTokens), 0, s, topk_idx,
                      hist, slot_row, flags, T, E, k);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(256), 0, s, hist, counts, offsets, NB, E,
-                     cap, gen, gen_copy);
+                     cap, gen, gen_copy, flags, flag_out);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (x_perm == nullptr) {
@@ -235,6 +252,64 @@ hipError_t launch_permute(const void* x, int elem_bytes, const int32_t* topk_idx
   else MOE_GATHER(1);
 #undef MOE_GATHER
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// The permutation without a caller workspace, for callers that cannot allocate device
+// memory (code under graph capture, tight serving loops): its scratch -- the per-block
+// histograms, then the per-block flags -- lives in this file-scope array. Each device that
+// runs it holds its own copy until the process ends; every call on a device shares that
+// copy, so calls that overlap on one device race. Nothing in it needs to start at zero:
+// the count kernel writes every histogram entry and flag word it later reads.
+static __device__ __align__(256) int32_t scratch[kNoAllocScratchWords];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<int32_t*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+// The device address of `scratch` on the current device, looked up once per device (the
+// host-side name of the array is not a device address).
+static hipError_t noalloc_scratch(int32_t** out) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  int32_t* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      void* q = nullptr;
+      err = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+      if (err != hipSuccess) return err;
+      if (q == nullptr) return hipErrorInvalidSymbol;
+      p = static_cast<int32_t*>(q);
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+size_t permute_noalloc_words(int T, int E) {
+  return (size_t)permute_count_blocks(T) * ((size_t)E + 1);
+}
+
+hipError_t launch_permute_noalloc(const void* x, int elem_bytes, const int32_t* topk_idx,
+                                  void* x_perm, int32_t* counts, int32_t* offsets,
+                                  int32_t* row_token, int32_t* slot_row, int32_t* flag_out,
+                                  int T, int H, int E, int k, int cap, hipStream_t s) {
+  if (permute_noalloc_words(T, E) > (size_t)kNoAllocScratchWords) return hipErrorInvalidValue;
+  int32_t* base = nullptr;
+  const hipError_t err = noalloc_scratch(&base);
+  if (err != hipSuccess) return err;
+  const int NB = permute_count_blocks(T);
+  int32_t* hist = base;                        // [NB][E]
+  int32_t* flags = base + (size_t)NB * E;      // [NB]
+  return launch_permute(x, elem_bytes, topk_idx, x_perm, counts, offsets, row_token, slot_row,
+                        hist, flags, nullptr, nullptr, flag_out, T, H, E, k, cap, s);
 }
 
 }  // namespace moe

@@ -240,3 +240,24 @@ def test_packed_weights_are_rejected_by_the_training_entry_points(lib):
     n = ctypes.c_size_t()
     assert lib.moe_backward_workspace_size(ctypes.byref(c), ctypes.byref(n)) == L.MOE_ERR_UNSUPPORTED
     assert ws_size(lib, c)[0] == L.MOE_OK          # the forward takes them
+
+
+def test_permute_noalloc_argument_errors(lib):
+    """The allocation-free permutation: the same argument checks as moe_permute (no
+    workspace), and sizes beyond its fixed scratch are refused before any HIP call."""
+    f = lib.moe_permute_noalloc
+    c = cfg_of()
+    cp = ctypes.byref(c)
+    assert f(cp, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, None, None) == L.MOE_ERR_INVALID_ARG
+    assert f(cp, FAKE, FAKE, FAKE + 8, FAKE, FAKE, FAKE, FAKE, None, None) == L.MOE_ERR_INVALID_ARG
+    assert f(cp, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == L.MOE_ERR_INVALID_ARG
+    assert f(cp, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, None) == L.MOE_ERR_INVALID_ARG
+    assert f(cp, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE + 2, None) == L.MOE_ERR_INVALID_ARG
+    assert f(ctypes.byref(cfg_of(top_k=0)), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None,
+             None) == L.MOE_ERR_INVALID_ARG
+    # ceil(T / 1024) * (E + 1) int32 words of scratch: 1024 blocks x 257 words exceed 1 MiB
+    big = cfg_of(tokens=1 << 20, experts=256, top_k=2)
+    assert f(ctypes.byref(big), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None) == \
+        L.MOE_ERR_WORKSPACE
+    assert f(ctypes.byref(cfg_of(tokens=0)), None, None, None, None, None, None, None, None,
+             None) == L.MOE_OK
