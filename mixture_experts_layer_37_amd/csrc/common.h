@@ -35,8 +35,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return u >> 16;
 }
 
+// Two floats -> two packed bfloat16 (lo in bits 0..15), round to nearest, ties to even: one
+// v_cvt_pk_bf16_f32 on gfx950 (a NaN stays a quiet NaN).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // Element storage helpers: bf16 is stored as raw 16-bit patterns.

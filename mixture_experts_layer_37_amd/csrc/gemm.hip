@@ -813,52 +813,79 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
     }
   };
 
-  auto run_tile = [&](int tile, int kb, int ke, float* part, auto slice) {
-    constexpr bool kSlice = decltype(slice)::value;
-    const TileCoord tc = decode_tile(s_start, s_off, E, __builtin_amdgcn_readfirstlane(tile), BM);
-    const int e = __builtin_amdgcn_readfirstlane(tc.e);
-    const int n_t = __builtin_amdgcn_readfirstlane(tc.n_t);
-    const int row0 = __builtin_amdgcn_readfirstlane(tc.row0);
-    const int mrows = __builtin_amdgcn_readfirstlane(tc.mrows);
-    // A: as grouped_gemm_bf16_kernel (rows past the expert's end re-read its last row)
+  // Where a tile's operands come from: token rows (A, global -> LDS by DMA; with the gather
+  // fused in, rows of x through row_token) and packed weight blocks (B, into registers).
+  struct TileSrc {
+    int n_t, row0, mrows;
     const char* a_src[8];
+    const bf16_t* bsrc[4];
+  };
+  // A tile's coordinates and the token rows of its 8 A DMA loads per wave (rows past the
+  // expert's end re-read its last row, never written back; with the gather fused in, rows
+  // of x through row_token, clamped into [0, a_rows)). The row-map loads are the only
+  // global loads here.
+  struct TileRows {
+    int e, n_t, row0, mrows;
+    int arow[8];
+  };
+  auto tile_rows = [&](int tile, TileRows& r) {
+    // the lane index passes through empty asm, so the per-lane pieces below are computed
+    // for each tile rather than hoisted and held across the k-loop
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+    const TileCoord tc = decode_tile(s_start, s_off, E, __builtin_amdgcn_readfirstlane(tile), BM);
+    r.e = __builtin_amdgcn_readfirstlane(tc.e);
+    r.n_t = __builtin_amdgcn_readfirstlane(tc.n_t);
+    r.row0 = __builtin_amdgcn_readfirstlane(tc.row0);
+    r.mrows = __builtin_amdgcn_readfirstlane(tc.mrows);
+    // all eight row-map loads in flight together, then clamped
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int r = wave * 64 + i * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ swz(r);
-      const int rr = row0 + min(r, mrows - 1);
-      const size_t arow = row_token != nullptr ? (size_t)min(max(row_token[rr], 0), a_rows - 1)
-                                               : (size_t)rr;
-      a_src[i] = (const char*)(A + arow * K) + c * 16;
+      const int rr = r.row0 + min(wave * 64 + i * 8 + (lane >> 3), r.mrows - 1);
+      r.arow[i] = row_token != nullptr ? row_token[rr] : rr;
+    }
+    if (row_token != nullptr) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) r.arow[i] = min(max(r.arow[i], 0), a_rows - 1);
+    }
+  };
+  auto tile_src = [&](const TileRows& r, TileSrc& t) {
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+    t.n_t = r.n_t;
+    t.row0 = r.row0;
+    t.mrows = r.mrows;
+    // A: this lane's 16-byte chunk of row arow[i], at its swizzled place
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int rl = wave * 64 + i * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ swz(rl);
+      t.a_src[i] = (const char*)(A + (size_t)r.arow[i] * K) + c * 16;
     }
     // B fragment j of k slice s: this lane's 16 bytes of block (nb_j, s)
-    const bf16_t* bsrc[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const bf16_t* P;
       int nb;
-      if (kTwoMat) { P = j < 2 ? P0 : P1; nb = n_t * 4 + wn * 2 + (j & 1); }
-      else { P = P0; nb = n_t * 8 + wn * 4 + j; }
-      bsrc[j] = P + ((size_t)e * NB + nb) * KS * 512 + lane * 8;
+      if (kTwoMat) { P = j < 2 ? P0 : P1; nb = r.n_t * 4 + wn * 2 + (j & 1); }
+      else { P = P0; nb = r.n_t * 8 + wn * 4 + j; }
+      t.bsrc[j] = P + ((size_t)r.e * NB + nb) * KS * 512 + lane * 8;
     }
-    constexpr int kLA = 8;   // A DMA loads per k-step and wave: rows wave * 64 + 8 i + lane / 8
-    auto dma_a = [&](int kt, bf16_t* stg) {
-      const uint32_t kA = (uint32_t)(kt * BK * 2);
-      const uint32_t dst = lds_offset(stg) + wave * kLA * 1024;
-#pragma unroll
-      for (int i = 0; i < kLA; ++i) dma16_asm(a_src[i] + kA, dst + i * 1024);
+  };
+  constexpr int kLA = 8;   // A DMA loads per k-step and wave: rows wave * 64 + 8 i + lane / 8
+  auto dma_for = [&](const TileSrc& t) {
+    return [&t, wave](int kt, bf16_t* stg, int i) {   // DMA instruction i of k-step kt
+      dma16_asm(t.a_src[i] + (uint32_t)(kt * BK * 2), lds_offset(stg) + (wave * kLA + i) * 1024);
     };
-    f32x16 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    packed_kloop<kLA, 4>(kb, ke, sa0, sa1, bsrc, acc, load_a, dma_a);
+  };
 
-    // Epilogue. acc[i][j][4q+s]: row m = wm*128 + i*32 + l32, column (within the wave's
-    // block j) = 8q + 4*lhi + s.
+  // The tile's output from its accumulators (a slice of the split-K tail: a float32 partial
+  // tile instead). Each kind has its own call site, so each gets its own register allocation.
+  auto epilogue = [&](f32x16 (&acc)[4][4], int n_t, int row0, int mrows, float* part,
+                      auto slice) {
+    constexpr bool kSlice = decltype(slice)::value;
+    // acc[i][j][4q+s]: row m = wm*128 + i*32 + l32, column (within the wave's block j) =
+    // 8q + 4*lhi + s.
     if constexpr (kSlice) {   // float32 partial tile [BM][256], valid rows only
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -920,37 +947,46 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       return;
     }
+    // SwiGLU: h = silu(gate) * up, the gate and up columns of one output side by side in
+    // the accumulators (j and j + 2)
+    int e_lane = lane;
+    asm volatile("" : "+v"(e_lane));
+    const int l32 = e_lane & 31, lhi = e_lane >> 5;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = wm * 128 + i * 32 + l32;
       if (m >= mrows) continue;
       bf16_t* crow = C + (size_t)(row0 + m) * N;
-      if constexpr (kTwoMat) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int col = n_t * 128 + wn * 64 + j * 32 + 8 * q + 4 * lhi;
-            float hv[4];
+        for (int q = 0; q < 4; ++q) {
+          const int col = n_t * 128 + wn * 64 + j * 32 + 8 * q + 4 * lhi;
+          float hv[4];
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-              hv[s] = silu_f(acc[i][j][4 * q + s]) * acc[i][j + 2][4 * q + s];
-            *(uint2*)(crow + col) = pack4(hv);
-          }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int col = n_t * 256 + wn * 128 + j * 32 + 8 * q + 4 * lhi;
-            float hv[4];
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-              hv[s] = EPI == EPI_GELU ? gelu_f(acc[i][j][4 * q + s]) : acc[i][j][4 * q + s];
-            *(uint2*)(crow + col) = pack4(hv);
-          }
-      }
+          for (int s = 0; s < 4; ++s)
+            hv[s] = silu_f(acc[i][j][4 * q + s]) * acc[i][j + 2][4 * q + s];
+          *(uint2*)(crow + col) = pack4(hv);
+        }
     }
+  };
+
+  // One tile at a time: its loads, k-loop and epilogue (the single-matrix epilogues stage
+  // their output through the two A stages, so the next tile's DMA waits for them).
+  auto run_tile = [&](int tile, int kb, int ke, float* part, auto slice) {
+    TileRows r;
+    tile_rows(tile, r);
+    TileSrc t;
+    tile_src(r, t);
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    packed_kloop<kLA, 4>(kb, ke, sa0, sa1, t.bsrc, acc, load_a, dma_for(t));
+    epilogue(acc, t.n_t, t.row0, t.mrows, part, slice);
   };
 
   for (int base = 0; base < plan.full; base += gridDim.x) {
@@ -1095,14 +1131,11 @@ __global__ __launch_bounds__(256, 1) void grouped_wgrad_packed_kernel(
     for (int j = 0; j < 4; ++j)
       bsrc[j] = PB + ((size_t)(n_t * 8 + wn * 4 + j) * ksb + kbase / 16) * 512 + lane * 8;
     constexpr int kLA = 8;   // A DMA loads per k-step and wave (4 rows x 2 halves)
-    auto dma_a = [&](int kt, bf16_t* stg) {
+    // DMA instruction q of k-step kt: row group q / 2, half q & 1
+    auto dma_a = [&](int kt, bf16_t* stg, int q) {
       const size_t kA = (size_t)kt * BK * lda * 2;
       const uint32_t dst = lds_offset(stg) + wave * 4 * 1024;
-#pragma unroll
-      for (int i = 0; i < kLA / 2; ++i) {
-        dma16_asm(a_src[i] + kA, dst + i * 1024);
-        dma16_asm(a_src[i] + kA + 256, dst + kHalf * 2 + i * 1024);
-      }
+      dma16_asm(a_src[q >> 1] + kA + (q & 1) * 256, dst + (q & 1) * kHalf * 2 + (q >> 1) * 1024);
     };
     f32x16 acc[4][4];
 #pragma unroll

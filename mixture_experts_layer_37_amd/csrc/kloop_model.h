@@ -10,13 +10,16 @@
 // landing load then overwrites (a memory-safety bug, not only a wrong result); one too low
 // only waits longer.
 //
-// The loop executes the op lists below (kPrologue once per tile, kStep once per k-step), and
-// every count it uses comes from wait_count(), which simulates the steady state: the previous
-// k-step's loads, then this one's up to the wait. tile_checks() then replays whole tiles of 2
-// to 10 k-steps from their prologue, with each step's own predicates (a next k-step exists,
-// a refill of the current stage exists), and the static_asserts at the bottom require every
-// wait of every step to equal the load count that replay finds. A change to the op lists
-// re-derives the counts; a count that no longer matches the replay fails the build.
+// The loop executes the op lists below (kPrologue, which only issues a tile's first loads;
+// kStart, which waits for its first stage; kStep once per k-step), and every count it uses
+// comes from wait_count() / start_count(), which simulate the steady state: the previous
+// k-step's loads, then this one's up to the wait. tile_mismatches() then replays whole tiles
+// of 2 to 10 k-steps from their prologue, with each step's own predicates (a next k-step
+// exists, a refill of the current stage exists), and the static_asserts at the bottom
+// require every wait of every step to equal the load count that replay finds. A change to
+// the op lists re-derives the counts; a count that no longer matches the replay fails the
+// build. Global stores issued between tiles (the previous tile's epilogue) can only make the
+// waits stricter, never let one pass early, since loads complete in order among themselves.
 //
 // Plain constexpr C++ (no HIP): it also compiles with a host compiler.
 #pragma once
@@ -27,10 +30,10 @@ namespace kloop {
 constexpr int kLB = 4;   // B loads per 16-wide k slice (one 1 KB block per fragment j)
 
 enum Kind : int {
-  // prologue only
+  // prologue (issue only) and start
   kDmaA,        // A DMA of k-step kb + arg into stage arg
-  kWaitAll,     // s_waitcnt 0
   kLoadB,       // B slice arg (0..3) of k-step kb into ring slot arg
+  kWaitA0,      // wait for A(kb) (and this wave's LDS operations)
   kReadA0,      // LDS reads of A slice 0 of stage 0
   // k-step kt on stage `cur` (its B slices in ring slots sb .. sb + 3)
   kLgkm0,       // wait for this wave's LDS reads
@@ -49,13 +52,16 @@ struct Op {
   int arg;
 };
 
-// Once per tile: A(kb) lands first, then B slices 0..2 of kb, A(kb + 1), B slice 3, in this
-// order; the k-steps below then find their loads one k-step ahead.
+// Once per tile, issue only: A(kb), B slices 0..2 of kb, A(kb + 1), B slice 3, in this
+// order (a k-step's own load order, so the first k-step's waits are the steady state's);
+// the k-steps below then find their loads one k-step ahead.
 constexpr Op kPrologue[] = {
-    {kDmaA, 0},  {kWaitAll, 0}, {kLoadB, 0}, {kLoadB, 1}, {kLoadB, 2},
-    {kDmaA, 1},  {kLoadB, 3},   {kBarrier, 0}, {kReadA0, 0},
+    {kDmaA, 0}, {kLoadB, 0}, {kLoadB, 1}, {kLoadB, 2}, {kDmaA, 1}, {kLoadB, 3},
 };
 constexpr int kPrologueOps = sizeof(kPrologue) / sizeof(kPrologue[0]);
+// Then the first stage lands and is published.
+constexpr Op kStart[] = {{kWaitA0, 0}, {kBarrier, 0}, {kReadA0, 0}};
+constexpr int kStartOps = sizeof(kStart) / sizeof(kStart[0]);
 
 // One k-step: three slices, each waiting for its B fragments, issuing the next slice's A
 // reads and (one k-step ahead) the B loads of slice s + 4, then running its MFMAs; then the
@@ -129,19 +135,38 @@ constexpr int wait_count(int i, bool next, bool refill) {
   return loads_after<kLA>(seq, n, want);
 }
 
+// The prologue's loads in issue order; returns their number.
+constexpr int prologue_loads(Load* seq) {
+  int n = 0;
+  for (int j = 0; j < kPrologueOps; ++j) {
+    const Op& op = kPrologue[j];
+    if (op.kind == kDmaA) seq[n++] = Load{true, op.arg};
+    if (op.kind == kLoadB) seq[n++] = Load{false, op.arg};
+  }
+  return n;
+}
+
+// The count of kWaitA0: the loads the prologue issues after A(kb).
+template <int kLA>
+constexpr int start_count() {
+  Load seq[kPrologueOps] = {};
+  const int n = prologue_loads(seq);
+  return loads_after<kLA>(seq, n, Load{true, 0});
+}
+
 // Replay of whole tiles of 2 .. 10 k-steps (the real predicates of every step, the real
-// prologue): the number of waits whose count differs from what the replay finds.
+// prologue and start): the number of waits whose count differs from what the replay finds.
 template <int kLA>
 constexpr int tile_mismatches() {
   int bad = 0;
   for (int nsteps = 2; nsteps <= 10; nsteps += 2) {
     Load seq[kPrologueOps + 10 * kStepOps] = {};
-    int n = 0;
-    for (int j = 0; j < kPrologueOps; ++j) {
-      const Op& op = kPrologue[j];
-      if (op.kind == kDmaA) seq[n++] = Load{true, op.arg};
-      if (op.kind == kLoadB) seq[n++] = Load{false, op.arg};
-      if (op.kind == kWaitAll) n = 0;   // nothing in flight after it
+    int n = prologue_loads(seq);
+    for (int j = 0; j < kStartOps; ++j) {
+      if (kStart[j].kind == kWaitA0) {
+        const int need = loads_after<kLA>(seq, n, Load{true, 0});
+        if (need < 0 || need != start_count<kLA>()) ++bad;
+      }
     }
     for (int kt = 0; kt < nsteps; ++kt) {
       const bool next = kt + 1 < nsteps, refill = kt + 2 < nsteps;
@@ -164,6 +189,7 @@ constexpr int tile_mismatches() {
 // vmcnt is a 6-bit field: every count the loop can use must fit.
 template <int kLA>
 constexpr bool counts_fit() {
+  if (start_count<kLA>() > 63) return false;
   for (int i = 0; i < kStepOps; ++i)
     for (int m = 0; m < 4; ++m) {
       const int c = wait_count<kLA>(i, m & 1, m & 2);
@@ -176,14 +202,16 @@ constexpr bool counts_fit() {
 // 3 kLB + kLA = 20 before slice 0's MFMAs, 2 kLB + kLA + kLB = 20 before slice 1's and
 // kLB + kLA + 2 kLB = 20 before slice 2's when a next k-step exists (12, 8 and 4 in the last
 // step), 4 kLB = 16 for the next stage before the barrier and 3 kLB = 12 for slice 3 after it
-// (0 in the last step).
+// (0 in the last step); 3 kLB + kLA + kLB = 24 loads follow A(kb) in the prologue.
 static_assert(tile_mismatches<8>() == 0, "k-loop wait counts disagree with the issue order");
 static_assert(counts_fit<8>(), "k-loop wait count exceeds the 6-bit vmcnt field");
-static_assert(wait_count<8>(1, true, true) == 3 * kLB + 8 && wait_count<8>(6, true, true) == 20 &&
-                  wait_count<8>(11, true, true) == 20 && wait_count<8>(15, true, true) == 4 * kLB &&
-                  wait_count<8>(17, true, true) == 3 * kLB && wait_count<8>(1, false, false) == 3 * kLB &&
-                  wait_count<8>(17, false, false) == 0 && wait_count<8>(15, false, false) == -1,
-              "k-loop wait counts");
+static_assert(wait_count<8>(1, true, true) == 20 && wait_count<8>(6, true, true) == 20 &&
+                  wait_count<8>(11, true, true) == 20 && wait_count<8>(15, true, true) == 16 &&
+                  wait_count<8>(17, true, true) == 12 && wait_count<8>(1, false, false) == 12 &&
+                  wait_count<8>(6, false, false) == 8 && wait_count<8>(11, false, false) == 4 &&
+                  wait_count<8>(15, false, false) == -1 && wait_count<8>(17, false, false) == 0 &&
+                  start_count<8>() == 24,
+              "the documented k-loop wait counts");
 
 }  // namespace kloop
 }  // namespace moe

@@ -60,41 +60,38 @@ __device__ __forceinline__ void for_each_op(F&& f, std::integer_sequence<int, I.
   (f(std::integral_constant<int, I>{}), ...);
 }
 
-// One tile's k-steps [kb, ke) (ke - kb even and >= 2) on the two A stages sa0 / sa1.
-//   kLA      A DMA instructions per k-step and wave (dma_a issues exactly that many)
+// The k-loop of one tile:
+//   prologue(kb, ...)  issues A(kb), B slices 0..2 of kb, A(kb + 1), B slice 3 (kPrologue)
+//   run(kb, ke, ...)   waits for A(kb), publishes it (kStart), then runs k-steps [kb, ke)
+//                      (ke - kb even and >= 2) and ends with a barrier, after which both
+//                      stages are free and no load of this wave is in flight
+// Template and call arguments:
+//   kLA      A DMA instructions per k-step and wave
 //   kAReads  LDS read instructions per load_a (for the scheduling groups)
 //   bsrc[j]  this lane's 16 bytes of B fragment j, slice 0 of k-step 0: slice s of k-step kt
 //            is at bsrc[j] + 2048 kt elements + 1024 s bytes (the packed layout)
 //   load_a(stage, kk, FragA&)  the wave's A fragments of slice kk from an LDS stage
-//   dma_a(kt, stage)           this wave's global->LDS loads of k-step kt
+//   dma_a(kt, stage, i)        this wave's global->LDS load i (0 .. kLA-1) of k-step kt
 // acc[i][j] += B fragment j x A fragment i over the k-steps, v_mfma_f32_32x32x16_bf16 (each
 // lane's accumulators then hold four consecutive columns j of one row i).
-template <int kLA, int kAReads, class LoadA, class DmaA>
-__device__ __forceinline__ void packed_kloop(int kb, int ke, bf16_t* sa0, bf16_t* sa1,
-                                             const bf16_t* const* bsrc, f32x16 (&acc)[4][4],
-                                             LoadA&& load_a, DmaA&& dma_a) {
-  using namespace kloop;
-  static_assert(tile_mismatches<kLA>() == 0 && counts_fit<kLA>(),
+template <int kLA, int kAReads>
+struct PackedKLoop {
+  static_assert(kloop::tile_mismatches<kLA>() == 0 && kloop::counts_fit<kLA>(),
                 "k-loop wait counts disagree with the issue order");
-  bf16x8 bv[8][kLB];   // ring of eight k slices of B fragments (at most five live)
-  FragA fr[2];         // A fragments of slices of even / odd index
+  bf16x8 bv[8][kloop::kLB];   // ring of eight k slices of B fragments (at most five live)
+  FragA fr[2];                // A fragments of slices of even / odd index
 
   // B slice kk (0..3) of the k-step whose slice 0 is at base[j]
-  auto load_b = [&](const bf16_t* const* base, auto kk, int slot) {
+  template <int KK>
+  __device__ __forceinline__ void load_b(const bf16_t* const* base, int slot) {
 #pragma unroll
-    for (int j = 0; j < kLB; ++j)
-      bv[slot][j] = load16_asm_at<decltype(kk)::value * 1024>(base[j]);
-  };
-  auto mfma16 = [&](const FragA& f, int slot) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[slot][j], f.a[i], acc[i][j], 0, 0, 0);
-  };
+    for (int j = 0; j < kloop::kLB; ++j) bv[slot][j] = load16_asm_at<KK * 1024>(base[j]);
+  }
 
-  // prologue (kPrologue)
-  {
+  template <class DmaA>
+  __device__ __forceinline__ void prologue(int kb, bf16_t* sa0, bf16_t* sa1,
+                                           const bf16_t* const* bsrc, DmaA&& dma_a) {
+    using namespace kloop;
     const bf16_t* pbase[kLB];   // slice 0 of k-step kb
 #pragma unroll
     for (int j = 0; j < kLB; ++j) pbase[j] = bsrc[j] + (size_t)kb * 2048;
@@ -102,15 +99,10 @@ __device__ __forceinline__ void packed_kloop(int kb, int ke, bf16_t* sa0, bf16_t
         [&](auto I) {
           constexpr Op op = kPrologue[decltype(I)::value];
           if constexpr (op.kind == kDmaA) {
-            dma_a(kb + op.arg, op.arg ? sa1 : sa0);
-          } else if constexpr (op.kind == kWaitAll) {
-            __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+            for (int q = 0; q < kLA; ++q) dma_a(kb + op.arg, op.arg ? sa1 : sa0, q);
           } else if constexpr (op.kind == kLoadB) {
-            load_b(pbase, std::integral_constant<int, op.arg>{}, op.arg);
-          } else if constexpr (op.kind == kBarrier) {
-            __syncthreads();
-          } else if constexpr (op.kind == kReadA0) {
-            load_a(sa0, 0, fr[0]);
+            load_b<op.arg>(pbase, op.arg);
           } else {
             static_assert(op.kind == kDmaA, "op not allowed in the prologue");
           }
@@ -118,61 +110,128 @@ __device__ __forceinline__ void packed_kloop(int kb, int ke, bf16_t* sa0, bf16_t
         std::make_integer_sequence<int, kPrologueOps>{});
   }
 
-  // k-step kt on stage `cur` (its B in ring slots sb .. sb + 3), `nxt` in flight; `refill`
-  // (kt + 2 < ke) and `next` (kt + 1 < ke) are compile-time at every call site, so the
-  // steady-state loop carries no branches, which keeps the fragments in VGPRs and the
-  // accumulators in AGPRs.
-  auto kstep = [&](int kt, bf16_t* cur, bf16_t* nxt, int sb, auto refill, auto next) {
-    constexpr bool kNext = decltype(next)::value, kRefill = decltype(refill)::value;
-    const bf16_t* nbase[kLB];   // slice 0 of k-step kt + 1
+  // kStart, then the k-steps [kb, ke) and a barrier.
+  template <class LoadA, class DmaA>
+  __device__ __forceinline__ void run(int kb, int ke, bf16_t* sa0, bf16_t* sa1,
+                                      const bf16_t* const* bsrc, f32x16 (&acc)[4][4],
+                                      LoadA&& load_a, DmaA&& dma_a) {
+    using namespace kloop;
+    auto mfma16 = [&](const FragA& f, int slot) {
 #pragma unroll
-    for (int j = 0; j < kLB; ++j) nbase[j] = bsrc[j] + (size_t)(kt + 1) * 2048;
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[slot][j], f.a[i], acc[i][j], 0, 0, 0);
+    };
+    // The k-step's last part, kDmaA2, kReadANext, kLoadBNext 3 and kMfma 3, runs as one
+    // pinned sequence: one memory instruction after each of the slice's 16 MFMAs, in the op
+    // list's order (the A refill DMA, the next stage's A reads, the B loads), so their issue
+    // hides under the MFMAs instead of holding the MFMA pipe idle in front of them. The
+    // order of the loads, all the model sees, is unchanged.
+    static_assert(kStep[kStepOps - 5].kind == kWaitB && kStep[kStepOps - 5].arg == 3 &&
+                      kStep[kStepOps - 4].kind == kDmaA2 && kStep[kStepOps - 3].kind == kReadANext &&
+                      kStep[kStepOps - 2].kind == kLoadBNext && kStep[kStepOps - 2].arg == 3 &&
+                      kStep[kStepOps - 1].kind == kMfma && kStep[kStepOps - 1].arg == 3,
+                  "the k-step ends with the sequence that runs interleaved");
     for_each_op(
         [&](auto I) {
-          constexpr int i = decltype(I)::value;
-          constexpr Op op = kStep[i];
-          constexpr int count = wait_count<kLA>(i, kNext, kRefill);
-          if constexpr (op.kind == kLgkm0) {
-            __builtin_amdgcn_s_waitcnt(kWaitLgkm0Only);
-          } else if constexpr (op.kind == kWaitB) {
-            wait_loads<count>(bv[(sb + op.arg) & 7]);
-          } else if constexpr (op.kind == kReadA) {
-            load_a(cur, op.arg, fr[op.arg & 1]);
-          } else if constexpr (op.kind == kLoadBNext) {
-            if constexpr (kNext) load_b(nbase, std::integral_constant<int, op.arg>{}, (sb + 4 + op.arg) & 7);
-          } else if constexpr (op.kind == kMfma) {
-            mfma16(fr[op.arg & 1], (sb + op.arg) & 7);
-            if constexpr (op.arg < 3) {   // the slice's A reads, then its MFMAs
-              __builtin_amdgcn_sched_group_barrier(0x100, kAReads, 0);
-              __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-          } else if constexpr (op.kind == kWaitANext) {
-            if constexpr (count >= 0) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(count));
-            else __builtin_amdgcn_s_waitcnt(0);
+          constexpr Op op = kStart[decltype(I)::value];
+          if constexpr (op.kind == kWaitA0) {
+            __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(start_count<kLA>()));
           } else if constexpr (op.kind == kBarrier) {
             __syncthreads();
-            __builtin_amdgcn_sched_barrier(0);
-          } else if constexpr (op.kind == kDmaA2) {
-            if constexpr (kRefill) dma_a(kt + 2, cur);
-          } else if constexpr (op.kind == kReadANext) {
-            if constexpr (kNext) load_a(nxt, 0, fr[0]);
+          } else if constexpr (op.kind == kReadA0) {
+            load_a(sa0, 0, fr[0]);
           } else {
-            static_assert(op.kind == kLgkm0, "op not allowed in a k-step");
+            static_assert(op.kind == kWaitA0, "op not allowed in the start");
           }
         },
-        std::make_integer_sequence<int, kStepOps>{});
-  };
-  using yes = std::true_type;
-  using no = std::false_type;
-  int kt = kb;
-  for (; kt + 2 < ke; kt += 2) {
-    kstep(kt, sa0, sa1, 0, yes{}, yes{});
-    kstep(kt + 1, sa1, sa0, 4, yes{}, yes{});
+        std::make_integer_sequence<int, kStartOps>{});
+
+    // k-step kt on stage `cur` (its B in ring slots sb .. sb + 3), `nxt` in flight; `refill`
+    // (kt + 2 < ke) and `next` (kt + 1 < ke) are compile-time at every call site, so the
+    // steady-state loop carries no branches, which keeps the fragments in VGPRs and the
+    // accumulators in AGPRs.
+    auto kstep = [&](int kt, bf16_t* cur, bf16_t* nxt, int sb, auto refill, auto next) {
+      constexpr bool kNext = decltype(next)::value, kRefill = decltype(refill)::value;
+      const bf16_t* nbase[kLB];   // slice 0 of k-step kt + 1
+#pragma unroll
+      for (int j = 0; j < kLB; ++j) nbase[j] = bsrc[j] + (size_t)(kt + 1) * 2048;
+      for_each_op(
+          [&](auto I) {
+            constexpr int i = decltype(I)::value;
+            constexpr Op op = kStep[i];
+            constexpr int count = wait_count<kLA>(i, kNext, kRefill);
+            if constexpr (op.kind == kLgkm0) {
+              __builtin_amdgcn_s_waitcnt(kWaitLgkm0Only);
+            } else if constexpr (op.kind == kWaitB) {
+              wait_loads<count>(bv[(sb + op.arg) & 7]);
+            } else if constexpr (op.kind == kReadA) {
+              load_a(cur, op.arg, fr[op.arg & 1]);
+            } else if constexpr (op.kind == kLoadBNext && op.arg < 3) {
+              if constexpr (kNext) load_b<op.arg>(nbase, (sb + 4 + op.arg) & 7);
+            } else if constexpr (op.kind == kMfma && op.arg < 3) {
+              mfma16(fr[op.arg & 1], (sb + op.arg) & 7);
+              __builtin_amdgcn_sched_group_barrier(0x100, kAReads, 0);   // the slice's A reads,
+              __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);        // then its MFMAs
+              __builtin_amdgcn_sched_barrier(0);
+            } else if constexpr (op.kind == kLoadBNext) {
+              // kLoadBNext 3: done in the kDmaA2 sequence
+            } else if constexpr (op.kind == kWaitANext) {
+              if constexpr (count >= 0) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(count));
+              else __builtin_amdgcn_s_waitcnt(0);
+            } else if constexpr (op.kind == kBarrier) {
+              __syncthreads();
+              __builtin_amdgcn_sched_barrier(0);
+            } else if constexpr (op.kind == kDmaA2) {
+              // kDmaA2, kReadANext, kLoadBNext 3, kMfma 3 (see above)
+              const bf16x8* b3 = bv[(sb + 3) & 7];
+              const int slot7 = (sb + 7) & 7;
+#pragma unroll
+              for (int m = 0; m < 16; ++m) {
+                acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    b3[m & 3], fr[1].a[m >> 2], acc[m >> 2][m & 3], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                constexpr int kDmas = kRefill ? kLA : 0;
+                if (m < kDmas) {
+                  dma_a(kt + 2, cur, m);
+                } else if (m == kDmas) {
+                  if constexpr (kNext) load_a(nxt, 0, fr[0]);
+                } else if (m < kDmas + 1 + kLB) {
+                  if constexpr (kNext)
+                    bv[slot7][m - kDmas - 1] = load16_asm_at<3 * 1024>(nbase[m - kDmas - 1]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+              }
+            } else if constexpr (op.kind == kReadANext || op.kind == kMfma) {
+              // kReadANext, kMfma 3: done in the kDmaA2 sequence
+            } else {
+              static_assert(op.kind == kLgkm0, "op not allowed in a k-step");
+            }
+          },
+          std::make_integer_sequence<int, kStepOps>{});
+    };
+    using yes = std::true_type;
+    using no = std::false_type;
+    int kt = kb;
+    for (; kt + 2 < ke; kt += 2) {
+      kstep(kt, sa0, sa1, 0, yes{}, yes{});
+      kstep(kt + 1, sa1, sa0, 4, yes{}, yes{});
+    }
+    kstep(kt, sa0, sa1, 0, no{}, yes{});
+    kstep(kt + 1, sa1, sa0, 4, no{}, no{});
+    __syncthreads();   // every wave is done with both stages before the next tile's DMA
   }
-  kstep(kt, sa0, sa1, 0, no{}, yes{});
-  kstep(kt + 1, sa1, sa0, 4, no{}, no{});
-  __syncthreads();   // every wave is done with both stages before the next tile's DMA
+};
+
+// prologue immediately followed by run: one tile with nothing in between.
+template <int kLA, int kAReads, class LoadA, class DmaA>
+__device__ __forceinline__ void packed_kloop(int kb, int ke, bf16_t* sa0, bf16_t* sa1,
+                                             const bf16_t* const* bsrc, f32x16 (&acc)[4][4],
+                                             LoadA&& load_a, DmaA&& dma_a) {
+  PackedKLoop<kLA, kAReads> loop;
+  loop.prologue(kb, sa0, sa1, bsrc, dma_a);
+  loop.run(kb, ke, sa0, sa1, bsrc, acc, load_a, dma_a);
 }
 
 }  // namespace moe

@@ -48,8 +48,12 @@ PERTURBATIONS = {
     "second_last_step_plus_one": (
         COUNT_LINE, "  return loads_after<kLA>(seq, n, want) + (next && !refill ? 1 : 0);\n}"),
     # the prologue issues B slice 3 before A(kb + 1): the steady-state counts no longer hold
-    # for the first k-step
-    "prologue_order": ("{kDmaA, 1},  {kLoadB, 3},", "{kLoadB, 3},  {kDmaA, 1},"),
+    # for the first k-step (its wait for A(kb + 1) would pass with that stage in flight)
+    "prologue_order": ("{kLoadB, 2}, {kDmaA, 1}, {kLoadB, 3},",
+                       "{kLoadB, 2}, {kLoadB, 3}, {kDmaA, 1},"),
+    # the first stage's wait counted one load too many
+    "start_plus_one": ("  return loads_after<kLA>(seq, n, Load{true, 0});\n}",
+                       "  return loads_after<kLA>(seq, n, Load{true, 0}) + 1;\n}"),
     # a k-step that issues the next B slice before waiting for its own: the derived counts
     # change, and the documented numbers no longer match
     "step_order": ("{kLgkm0, 0}, {kWaitB, 0}, {kReadA, 1}, {kLoadBNext, 0}, {kMfma, 0},",
