@@ -44,6 +44,14 @@ def parse_args():
                     help="time a training step instead: moe_forward then moe_backward")
     ap.add_argument("--weights", choices=("packed", "plain"), default="packed",
                     help="expert weight layout of the timed forward (bf16)")
+    ap.add_argument("--no-extra-workloads", action="store_true",
+                    help="time the headline workload only")
+    ap.add_argument("--extra-steps", type=int, default=20,
+                    help="timed steps of each of the other workloads")
+    ap.add_argument("--extra-warmup", type=int, default=5)
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the clock reading (a 1.6 s GEMM-1 loop per workload), e.g. "
+                         "under a profiler")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -84,13 +92,86 @@ def measured_traffic(per_launch_flops_unused=None):
         return None
 
 
-def main():
-    args = parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU layout "
-              "is described in the design notes and is not run here.", file=sys.stderr)
-        sys.exit(2)
+EXTRA_WORKLOADS = ("small", "cap32", "fine", "mixtral_threshold")
 
+
+def step_stats(ms):
+    """mean, median, min and p90 of per-step times (ms)."""
+    import numpy as np
+    a = np.asarray(ms, dtype=np.float64)
+    return {"mean": float(a.mean()), "median": float(np.median(a)), "min": float(a.min()),
+            "p90": float(np.percentile(a, 90))}
+
+
+def gemm_clock(launch, seconds=1.6, settle=0.8):
+    """The GPU's graphics clock while GEMM 1 runs back to back: `launch` is enqueued for
+    `seconds` while a thread samples amdsmi's current per-XCD gfx clocks (the readings
+    refresh a few times a second); samples from the first `settle` seconds are dropped.
+    Returns the mean over samples and XCDs (MHz), the per-XCD means and the sample count, or
+    None where amdsmi cannot read the device."""
+    import threading
+    import torch
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handle = amdsmi.amdsmi_get_processor_handles()[0]
+        amdsmi.amdsmi_get_gpu_metrics_info(handle)
+    except Exception:
+        return None
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            t = time.perf_counter()
+            try:
+                clks = amdsmi.amdsmi_get_gpu_metrics_info(handle).get("current_gfxclks")
+                if isinstance(clks, list):
+                    clks = [float(v) for v in clks if isinstance(v, (int, float))]
+                    if clks:
+                        samples.append((t, clks))
+            except Exception:
+                pass
+            stop.wait(0.05)
+
+    torch.cuda.synchronize()
+    th = threading.Thread(target=sampler, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        launch()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()   # keep the queue short so the loop ends on time
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    use = [c for t, c in samples if t - t0 >= settle]
+    amdsmi.amdsmi_shut_down()
+    if not use:
+        return None
+    nx = min(len(c) for c in use)
+    per_xcd = [sum(c[i] for c in use) / len(use) for i in range(nx)]
+    return {"mhz": sum(per_xcd) / nx, "per_xcd_mhz": [round(v) for v in per_xcd],
+            "samples": len(use), "launches": n}
+
+
+def add_measured(rec, peaks):
+    """The record's fractions against what this device sustains (measured_peaks)."""
+    if peaks is None:
+        return
+    rec["grouped_gemm_frac_of_measured"] = rec["_ffn_tflops"] / peaks["mfma_bf16_tflops"]
+    rec["hbm_frac_of_measured"] = {n: v * PEAK_HBM_GBS / peaks["hbm_copy_gbs"]
+                                   for n, v in rec["hbm_frac"].items()}
+    if "materialised_permute" in rec:
+        rec["materialised_permute"]["hbm_frac_of_measured"] = (
+            rec["materialised_permute"]["hbm_frac"] * PEAK_HBM_GBS / peaks["hbm_copy_gbs"])
+
+
+def run_workload(name, args, steps, warmup, headline, peaks=None):
+    """Times `steps` forward steps of one workload (after `warmup`) and returns its record;
+    the headline workload also carries the roofline, the plain-weight context, the
+    materialised permute, the router against a one-pass read and the CPU baseline."""
     import numpy as np
     import torch
 
@@ -99,10 +180,8 @@ def main():
     from mixture_experts_layer_37_amd.inputs import make_inputs
     from mixture_experts_layer_37_amd.layer import MoELayer, to_device
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    torch.cuda.set_device(0)
-    cfg = C.get(args.config)
-    if cfg.dtype == C.BF16 and not args.backward:
+    cfg = C.get(name)
+    if cfg.dtype == C.BF16:
         cfg = cfg.with_(weights=args.weights)
     T, H, I, E, k = cfg.tokens, cfg.hidden, cfg.inter, cfg.experts, cfg.top_k
     print(f"[bench] {cfg.name}: generating inputs", file=sys.stderr, flush=True)
@@ -113,8 +192,6 @@ def main():
     c = layer.c
     ws = layer.ws
     edt = x.dtype
-    if args.backward:
-        return backward_bench(args, cfg, layer, x)
     logits = torch.empty((T, E), dtype=torch.float32, device=dev)
     idx = torch.empty((T, k), dtype=torch.int32, device=dev)
     w = torch.empty((T, k), dtype=torch.float32, device=dev)
@@ -127,12 +204,13 @@ def main():
     out = torch.empty_like(x)
     stream = torch.cuda.current_stream()
     names = ["route", "permute", "gemm_up", "gemm_down", "combine"]
+    packed = cfg.weights == "packed"
 
     def step(ev=None, plain=False):
         # the path moe_forward runs: the permute writes the row maps only and GEMM 1 reads
         # the token rows in place through them
         cw = layer.c_plain if plain else c
-        wg, wu, wd = ((layer.w_gate, layer.w_up, layer.w_down) if plain
+        wg, wu, wd = ((layer.w_gate, layer.w_up, layer.w_down) if plain or not packed
                       else (layer.fw_gate, layer.fw_up, layer.fw_down))
         if ev: ev[0].record(stream)
         L.moe_route(cw, x, layer.w_router, layer.bias, logits, idx, w, ws, stream)
@@ -146,128 +224,200 @@ def main():
         L.moe_combine(cw, y, sr, w, out, stream)
         if ev: ev[5].record(stream)
 
-    if args.calib_copy_mib > 0:
-        n = args.calib_copy_mib << 20
-        a = torch.empty(n, dtype=torch.uint8, device=dev)
-        b = torch.empty(n, dtype=torch.uint8, device=dev)
+    def timed_steps(n, plain=False):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(n):
+            step(ev[s], plain=plain)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / n
+        per_step = [e[0].elapsed_time(e[5]) for e in ev]
+        stages = {nm: float(np.median([e[i].elapsed_time(e[i + 1]) for e in ev])) * 1e3
+                  for i, nm in enumerate(names)}
+        return wall, per_step, stages
+
+    if headline and args.calib_copy_mib > 0:
+        nb = args.calib_copy_mib << 20
+        a = torch.empty(nb, dtype=torch.uint8, device=dev)
+        b = torch.empty(nb, dtype=torch.uint8, device=dev)
         a.fill_(1)
         torch.cuda.synchronize()
         b.copy_(a)
         torch.cuda.synchronize()
         del a, b
 
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
+    print(f"[bench] {cfg.name}: warmup {warmup}", file=sys.stderr, flush=True)
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(events[s])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    stage_ms = {n: float(np.mean([events[s][i].elapsed_time(events[s][i + 1])
-                                  for s in range(args.steps)])) for i, n in enumerate(names)}
-    plain = None
-    if cfg.weights == "packed":
-        # context: the same steps on the plain row-major weights (bit-identical output)
-        n_plain = max(2, args.steps // 2)
-        for _ in range(2):
-            step(plain=True)
-        pev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_plain)]
-        torch.cuda.synchronize()
-        p0 = time.perf_counter()
-        for s in range(n_plain):
-            step(pev[s], plain=True)
-        torch.cuda.synchronize()
-        plain = {"ms_per_step": (time.perf_counter() - p0) * 1e3 / n_plain, "steps": n_plain,
-                 "stages_us": {n: 1e3 * float(np.mean([pev[s][i].elapsed_time(pev[s][i + 1])
-                                                       for s in range(n_plain)]))
-                               for i, n in enumerate(names)}}
-        step()   # leave the packed step's results in place for the checks below
-        torch.cuda.synchronize()
+    print(f"[bench] {cfg.name}: timing {steps} steps", file=sys.stderr, flush=True)
+    wall_ms, per_step, stages_us = timed_steps(steps)
+    stats = step_stats(per_step)
 
     n_kept = int(offs[-1].item())
     up_flops = (4 if cfg.activation == C.SWIGLU else 2) * n_kept * H * I
     down_flops = 2 * n_kept * H * I
     ffn_flops = up_flops + down_flops
     total_flops = 2 * T * H * E + ffn_flops
-    up_tflops = up_flops / (stage_ms["gemm_up"] * 1e-3) / 1e12
-    ffn_tflops = ffn_flops / ((stage_ms["gemm_up"] + stage_ms["gemm_down"]) * 1e-3) / 1e12
+    up_tflops = up_flops / (stages_us["gemm_up"] * 1e-6) / 1e12
+    ffn_tflops = ffn_flops / ((stages_us["gemm_up"] + stages_us["gemm_down"]) * 1e-6) / 1e12
     es = 2 if cfg.dtype == C.BF16 else 4
     # algorithmic bytes of the bandwidth-bound steps (the permute moves index data only: its
     # row gather is fused into GEMM 1)
     route_bytes = T * H * es + H * E * es + T * E * 4 + T * k * 8
     permute_bytes = T * k * 4 * 4
     combine_bytes = n_kept * H * es + T * H * es + T * k * 8
+    hbm = {"route": route_bytes / (stages_us["route"] * 1e-6) / 1e9 / PEAK_HBM_GBS,
+           "permute_row_maps": permute_bytes / (stages_us["permute"] * 1e-6) / 1e9 / PEAK_HBM_GBS,
+           "combine": combine_bytes / (stages_us["combine"] * 1e-6) / 1e9 / PEAK_HBM_GBS}
+    rec = {"workload": cfg.description, "tokens": T, "hidden": H, "inter": I, "experts": E,
+           "top_k": k, "routing": cfg.routing, "capacity_factor": cfg.capacity_factor,
+           "kept_rows": n_kept, "steps": steps, "warmup": warmup,
+           "ms_per_step": stats, "ms_per_step_wall_mean": wall_ms,
+           "tokens_per_s": T / (stats["median"] * 1e-3),
+           "stages_us": stages_us,
+           "gemm_up_frac_of_peak": up_tflops / PEAK_BF16_TFLOPS,
+           "grouped_gemm_frac_of_peak": ffn_tflops / PEAK_BF16_TFLOPS,
+           "layer_tflops": total_flops / (stats["median"] * 1e-3) / 1e12,
+           "hbm_frac": hbm}
+    rec["_ffn_tflops"] = ffn_tflops
+    add_measured(rec, peaks)
+    wg, wu = ((layer.fw_gate, layer.fw_up) if packed else (layer.w_gate, layer.w_up))
+    rec["gemm_clock"] = None if args.no_clock else gemm_clock(
+        lambda: L.moe_expert_up_rows(c, x, rt, offs, wg, wu, h, stream))
+    if not headline:
+        rec["device_flags"] = L.moe_read_device_status(c, ws, 3, stream)
+        return rec
+
+    # the headline's extras
+    rec["_wall_ms"] = wall_ms
+    rec["_up_flops"], rec["_up_tflops"] = up_flops, up_tflops
+    rec["weights"] = ("packed once at load (moe_pack_expert_weight)" if packed
+                      else "plain row-major")
+    rec["activation"] = cfg.activation
+    rec["threshold"] = ((cfg.threshold if cfg.threshold > 0 else 1.0 / E)
+                        if cfg.routing == "threshold" else None)
+    if packed:
+        # context: the same steps on the plain row-major weights (bit-identical output)
+        n_plain = max(2, steps // 2)
+        for _ in range(2):
+            step(plain=True)
+        pw, pst, pstages = timed_steps(n_plain, plain=True)
+        rec["plain_weights"] = {"ms_per_step": step_stats(pst), "steps": n_plain,
+                                "stages_us": pstages}
+        step()   # leave the packed step's results in place for the checks below
+        torch.cuda.synchronize()
+    rec["materialised_permute"] = materialised_permute(L, c, x, idx, counts, offs, rt, sr, ws,
+                                                       stream, T, H, k, n_kept, es)
+    rd = one_pass_read_us(stream, x, T * H * es, step)
+    if rd is not None:
+        # the router against a plain one-pass read of the same token matrix, each timed
+        # right after a full step (the same cache state): 1.0 = as fast as reading x
+        rec["route_vs_one_pass_read"] = {
+            "read_us": rd, "route_us": stages_us["route"],
+            "read_gbs": T * H * es / (rd * 1e-6) / 1e9, "frac": rd / stages_us["route"]}
+    rec["device_flags"] = L.moe_read_device_status(c, ws, 3, stream)
+    if not args.no_cpu_baseline:
+        rec["_cpu_baseline"] = cpu_baseline(cfg, inp, out, logits, idx, args.cpu_sample_tokens,
+                                            rec)
+    return rec
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU layout "
+              "is described in the design notes and is not run here.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from mixture_experts_layer_37_amd import configs as C
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    if args.backward:
+        from mixture_experts_layer_37_amd.inputs import make_inputs
+        from mixture_experts_layer_37_amd.layer import MoELayer, to_device
+        cfg = C.get(args.config)
+        inp = make_inputs(cfg, seed=args.seed, threads=16)
+        layer = MoELayer(cfg, inp)
+        return backward_bench(args, cfg, layer, to_device(cfg, inp["x"]))
+
+    stream = torch.cuda.current_stream()
+    head = run_workload(args.config, args, args.steps, args.warmup, True)
+    torch.cuda.empty_cache()
+    peaks = measured_peaks(stream)   # after the headline, so its load does not precede it
+    add_measured(head, peaks)
+    cfg = C.get(args.config)
+    # the headline: whole-step wall time over the K timed steps, as the step contract says
+    ms_per_step = head.pop("_wall_ms")
+    up_flops, up_tflops = head.pop("_up_flops"), head.pop("_up_tflops")
+    cpu = head.pop("_cpu_baseline", None)
     # the committed counter summary covers GEMM 1 (packed weights) of the Mixtral top-2
     # workload only
-    traffic = (measured_traffic() if cfg.name == "mixtral" and cfg.weights == "packed"
+    traffic = (measured_traffic() if cfg.name == "mixtral" and args.weights == "packed"
                else None)
     result = {
         "metric": METRIC,
-        "value": T / (ms_per_step * 1e-3),
+        "value": cfg.tokens / (ms_per_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "ms_per_step_stats": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if cfg.dtype == C.BF16 else "f32",
         "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) weights)",
-        "config": {"workload": cfg.description, "tokens": T, "hidden": H, "inter": I,
-                   "experts": E, "top_k": k, "capacity_factor": cfg.capacity_factor,
-                   "activation": cfg.activation, "routing": cfg.routing,
-                   "threshold": (cfg.threshold if cfg.threshold > 0 else 1.0 / E)
-                   if cfg.routing == "threshold" else None, "kept_rows": n_kept,
-                   "weights": ("packed once at load (moe_pack_expert_weight)"
-                               if cfg.weights == "packed" else "plain row-major")},
+        "config": {"workload": head["workload"], "tokens": head["tokens"],
+                   "hidden": head["hidden"], "inter": head["inter"],
+                   "experts": head["experts"], "top_k": head["top_k"],
+                   "capacity_factor": head["capacity_factor"],
+                   "activation": head["activation"], "routing": head["routing"],
+                   "threshold": head["threshold"], "kept_rows": head["kept_rows"],
+                   "weights": head["weights"]},
         "roofline": {"kernel": ("grouped_gemm_packed_kernel<SwiGLU> (moe_expert_up_rows)"
-                                if cfg.weights == "packed" else
+                                if args.weights == "packed" else
                                 "grouped_gemm_bf16_kernel<SwiGLU> (moe_expert_up_rows)"),
                      "bound": "mfma", "achieved": up_tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": up_tflops / PEAK_BF16_TFLOPS,
                      "traffic": traffic, "algorithmic_flops": up_flops},
-        "grouped_gemm_frac_of_peak": ffn_tflops / PEAK_BF16_TFLOPS,
-        "layer_tflops": total_flops / (ms_per_step * 1e-3) / 1e12,
-        "stages_us": {n: v * 1e3 for n, v in stage_ms.items()},
-        "hbm_frac": {"route": route_bytes / (stage_ms["route"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                     "permute_row_maps": permute_bytes / (stage_ms["permute"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                     "combine": combine_bytes / (stage_ms["combine"] * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        "grouped_gemm_frac_of_peak": head["grouped_gemm_frac_of_peak"],
+        "layer_tflops": head["layer_tflops"],
+        "stages_us": head["stages_us"],
+        "hbm_frac": head["hbm_frac"],
+        "gemm_clock": head["gemm_clock"],
     }
-    if plain is not None:
-        result["plain_weights"] = plain
-    result["materialised_permute"] = materialised_permute(L, c, x, idx, counts, offs, rt, sr, ws,
-                                                          stream, T, H, k, n_kept, es)
-    peaks = measured_peaks(stream)
+    for key in ("plain_weights", "materialised_permute", "hbm_frac_of_measured",
+                "grouped_gemm_frac_of_measured",
+                "route_vs_one_pass_read", "device_flags", "parity"):
+        if key in head:
+            result[key] = head[key]
     result["measured_peaks"] = peaks
     if peaks is not None:
         result["roofline"]["peak_measured"] = peaks["mfma_bf16_tflops"]
         result["roofline"]["frac_of_measured"] = up_tflops / peaks["mfma_bf16_tflops"]
-        result["hbm_frac_of_measured"] = {
-            n: v * PEAK_HBM_GBS / peaks["hbm_copy_gbs"] for n, v in result["hbm_frac"].items()}
-        result["materialised_permute"]["hbm_frac_of_measured"] = (
-            result["materialised_permute"]["hbm_frac"] * PEAK_HBM_GBS / peaks["hbm_copy_gbs"])
-
-    rd = one_pass_read_us(stream, x, T * H * es, step)
-    if rd is not None:
-        # the router against a plain one-pass read of the same token matrix, each timed
-        # right after a full step (the same cache state): 1.0 = as fast as reading x
-        result["route_vs_one_pass_read"] = {
-            "read_us": rd, "route_us": stage_ms["route"] * 1e3,
-            "read_gbs": T * H * es / (rd * 1e-6) / 1e9,
-            "frac": rd / (stage_ms["route"] * 1e3)}
-
-    result["device_flags"] = L.moe_read_device_status(c, ws, 3, stream)
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, inp, out, logits, idx, args.cpu_sample_tokens,
-                                              result)
+    # every workload of the layer, each timed on its own (the headline's entry repeats it)
+    workloads = {cfg.name: {k: v for k, v in head.items()
+                            if k not in ("plain_weights", "materialised_permute",
+                                         "route_vs_one_pass_read", "parity")}}
+    for rec in [head] + list(workloads.values()):
+        rec.pop("_ffn_tflops", None)
+    if not args.no_extra_workloads:
+        for name in EXTRA_WORKLOADS:
+            if name == cfg.name:
+                continue
+            rec = run_workload(name, args, args.extra_steps, args.extra_warmup, False, peaks)
+            rec.pop("_ffn_tflops", None)
+            workloads[name] = rec
+            torch.cuda.empty_cache()
+    result["workloads"] = workloads
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 

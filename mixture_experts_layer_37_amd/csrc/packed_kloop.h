@@ -123,16 +123,6 @@ struct PackedKLoop {
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[slot][j], f.a[i], acc[i][j], 0, 0, 0);
     };
-    // The k-step's last part, kDmaA2, kReadANext, kLoadBNext 3 and kMfma 3, runs as one
-    // pinned sequence: one memory instruction after each of the slice's 16 MFMAs, in the op
-    // list's order (the A refill DMA, the next stage's A reads, the B loads), so their issue
-    // hides under the MFMAs instead of holding the MFMA pipe idle in front of them. The
-    // order of the loads, all the model sees, is unchanged.
-    static_assert(kStep[kStepOps - 5].kind == kWaitB && kStep[kStepOps - 5].arg == 3 &&
-                      kStep[kStepOps - 4].kind == kDmaA2 && kStep[kStepOps - 3].kind == kReadANext &&
-                      kStep[kStepOps - 2].kind == kLoadBNext && kStep[kStepOps - 2].arg == 3 &&
-                      kStep[kStepOps - 1].kind == kMfma && kStep[kStepOps - 1].arg == 3,
-                  "the k-step ends with the sequence that runs interleaved");
     for_each_op(
         [&](auto I) {
           constexpr Op op = kStart[decltype(I)::value];
@@ -168,15 +158,18 @@ struct PackedKLoop {
               wait_loads<count>(bv[(sb + op.arg) & 7]);
             } else if constexpr (op.kind == kReadA) {
               load_a(cur, op.arg, fr[op.arg & 1]);
-            } else if constexpr (op.kind == kLoadBNext && op.arg < 3) {
+            } else if constexpr (op.kind == kLoadBNext) {
               if constexpr (kNext) load_b<op.arg>(nbase, (sb + 4 + op.arg) & 7);
             } else if constexpr (op.kind == kMfma && op.arg < 3) {
               mfma16(fr[op.arg & 1], (sb + op.arg) & 7);
               __builtin_amdgcn_sched_group_barrier(0x100, kAReads, 0);   // the slice's A reads,
               __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);        // then its MFMAs
               __builtin_amdgcn_sched_barrier(0);
-            } else if constexpr (op.kind == kLoadBNext) {
-              // kLoadBNext 3: done in the kDmaA2 sequence
+            } else if constexpr (op.kind == kMfma) {
+              // slice 3: scheduled by the compiler among the refill and next-stage loads
+              // (pinning one load after each MFMA here made the 32 CUs of an XCD share less
+              // of their operands in L2: a third more fabric traffic in GEMM 1, no faster)
+              mfma16(fr[1], (sb + 3) & 7);
             } else if constexpr (op.kind == kWaitANext) {
               if constexpr (count >= 0) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(count));
               else __builtin_amdgcn_s_waitcnt(0);
@@ -184,27 +177,12 @@ struct PackedKLoop {
               __syncthreads();
               __builtin_amdgcn_sched_barrier(0);
             } else if constexpr (op.kind == kDmaA2) {
-              // kDmaA2, kReadANext, kLoadBNext 3, kMfma 3 (see above)
-              const bf16x8* b3 = bv[(sb + 3) & 7];
-              const int slot7 = (sb + 7) & 7;
+              if constexpr (kRefill) {
 #pragma unroll
-              for (int m = 0; m < 16; ++m) {
-                acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    b3[m & 3], fr[1].a[m >> 2], acc[m >> 2][m & 3], 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
-                constexpr int kDmas = kRefill ? kLA : 0;
-                if (m < kDmas) {
-                  dma_a(kt + 2, cur, m);
-                } else if (m == kDmas) {
-                  if constexpr (kNext) load_a(nxt, 0, fr[0]);
-                } else if (m < kDmas + 1 + kLB) {
-                  if constexpr (kNext)
-                    bv[slot7][m - kDmas - 1] = load16_asm_at<3 * 1024>(nbase[m - kDmas - 1]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
+                for (int q = 0; q < kLA; ++q) dma_a(kt + 2, cur, q);
               }
-            } else if constexpr (op.kind == kReadANext || op.kind == kMfma) {
-              // kReadANext, kMfma 3: done in the kDmaA2 sequence
+            } else if constexpr (op.kind == kReadANext) {
+              if constexpr (kNext) load_a(nxt, 0, fr[0]);
             } else {
               static_assert(op.kind == kLgkm0, "op not allowed in a k-step");
             }
