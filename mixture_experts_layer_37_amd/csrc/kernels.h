@@ -32,6 +32,10 @@ hipError_t launch_route_topk(const float* logits, int32_t* topk_idx, float* topk
 
 // ---- permute (permute.hip)
 int permute_count_blocks(int T);
+// Batches of at most this many count blocks (65536 tokens) get the scan and their row maps
+// from one launch after the count (permute_scan_rows_kernel), each block reading the whole
+// histogram table.
+constexpr int kMapsMaxBlocks = 64;
 // gen (may be null): the workspace's permutation generation, advanced by one; gen_copy (may
 // be null): receives the new value (a training forward's record of it); flag_out (may be
 // null): the OR of the per-block flags

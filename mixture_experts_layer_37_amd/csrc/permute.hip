@@ -3,8 +3,10 @@
 // 算子优化实战": a per-expert mask feeds SparseGather, and sparse data is kept CSR-style;
 // lshu.cn/news/82007, section 4: npu_moe_token_preprocess reorders the tokens).
 //
-// Three launches, no float and no global atomics (without an x_perm destination the third
-// only computes the row maps, for a GEMM that gathers token rows itself):
+// No float and no global atomics. Three launches; for the row maps only (no x_perm
+// destination, for a GEMM that gathers token rows itself) on a batch of at most
+// kMapsMaxBlocks count blocks, two: the count, then permute_scan_rows_kernel, in which every
+// block does the scan itself from the histogram table and writes its own tokens' rows.
 //   count  -- 1024 tokens per block. Per wave and expert a 64-bit lane mask (LDS OR);
 //             popcounts give the block's per-expert histogram and each assignment's rank
 //             inside the block in token order. Invalid or repeated ids are dropped, flagged
@@ -223,6 +225,112 @@ __global__ __launch_bounds__(256) void permute_rows_kernel(
   }
 }
 
+// The scan and the row maps in one launch (no x_perm), after the count kernel, for batches
+// of at most kMapsMaxBlocks count blocks. A block of 256 threads owns 256 tokens of one
+// count block; every block reads the whole [NB][E] histogram table and derives from it, in
+// the scan kernel's order, each expert's pre-capacity count, kept offsets and the prefix
+// over the count blocks before its own, so no block waits for another. Block 0 writes
+// counts and offsets, advances the generation and gathers the flag words; every block then
+// turns its tokens' in-block ranks (slot_row, from the count kernel) into rows, as the rows
+// kernel does, with all of a token's slot loads in flight together.
+static_assert(kCountBlockTokens % 256 == 0, "a 256-token block lies in one count block");
+__global__ __launch_bounds__(256) void permute_scan_rows_kernel(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ hist,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ row_token,
+    int32_t* __restrict__ slot_row, const int32_t* __restrict__ flags, int32_t* gen,
+    int32_t* gen_copy, int32_t* __restrict__ flag_out, int T, int E, int k, int cap) {
+  __shared__ int before[kMaxExperts];   // assignments of earlier count blocks, per expert
+  __shared__ int off[kMaxExperts + 1];
+  __shared__ int wsum[4];
+  __shared__ int wflag[4];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int t = blockIdx.x * blockDim.x + tid;
+  const int cb = (blockIdx.x * blockDim.x) / kCountBlockTokens;   // this block's count block
+  const int NB = (T + kCountBlockTokens - 1) / kCountBlockTokens;
+  // expert tid: the prefix over count blocks < cb and the batch total
+  int total = 0;
+  if (tid < E) {
+    int pre = 0, ob = 0;
+    for (; ob + 8 <= NB; ob += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = hist[(size_t)(ob + u) * E + tid];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        pre += ob + u < cb ? v[u] : 0;
+        total += v[u];
+      }
+    }
+    for (; ob < NB; ++ob) {
+      const int v = hist[(size_t)ob * E + tid];
+      pre += ob < cb ? v : 0;
+      total += v;
+    }
+    before[tid] = pre;
+  }
+  // this thread's token: its slots' in-block ranks and ids, all loads in flight together
+  int r[kMaxTopK], ev[kMaxTopK];
+  if (t < T) {
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+      if (j < k) {
+        r[j] = slot_row[(size_t)t * k + j];
+        ev[j] = idx[(size_t)t * k + j];
+      }
+  }
+  // exclusive scan of min(total, cap) over E <= 256 experts (one per thread)
+  const int kept = tid < E ? min(total, cap) : 0;
+  int incl = kept;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int n = __shfl_up(incl, o);
+    if (lane >= o) incl += n;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  // block 0: the OR of the count blocks' flag words
+  int f = 0;
+  if (blockIdx.x == 0 && flag_out != nullptr)
+    for (int ob = tid; ob < NB; ob += blockDim.x) f |= flags[ob];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) f |= __shfl_xor(f, o);
+  if (lane == 0) wflag[wave] = f;
+  __syncthreads();
+  {
+    int pre = 0;
+    for (int w = 0; w < wave; ++w) pre += wsum[w];
+    incl += pre;
+    if (tid < E) off[tid] = incl - kept;
+    if (tid == E - 1) off[E] = incl;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    if (tid < E) counts[tid] = total;
+    for (int e = tid; e <= E; e += blockDim.x) offsets[e] = off[e];
+    if (tid == 0) {
+      if (gen != nullptr) {
+        const int g = gen[0] + 1;
+        gen[0] = g;
+        if (gen_copy != nullptr) gen_copy[0] = g;
+      }
+      if (flag_out != nullptr) flag_out[0] = wflag[0] | wflag[1] | wflag[2] | wflag[3];
+    }
+  }
+  if (t < T) {
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (j < k) {
+        int row = -1;
+        if (r[j] >= 0) {
+          const int pos = before[ev[j]] + r[j];
+          if (pos < cap) row = off[ev[j]] + pos;
+        }
+        slot_row[(size_t)t * k + j] = row;
+        if (row >= 0) row_token[row] = t;
+      }
+    }
+  }
+}
+
 hipError_t launch_permute(const void* x, int elem_bytes, const int32_t* topk_idx, void* x_perm,
                           int32_t* counts, int32_t* offsets, int32_t* row_token,
                           int32_t* slot_row, int32_t* hist, int32_t* flags, int32_t* gen,
@@ -233,6 +341,12 @@ hipError_t launch_permute(const void* x, int elem_bytes, const int32_t* topk_idx
                      hist, slot_row, flags, T, E, k);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (x_perm == nullptr && NB <= kMapsMaxBlocks) {
+    hipLaunchKernelGGL(permute_scan_rows_kernel, dim3((T + 255) / 256), dim3(256), 0, s,
+                       topk_idx, hist, counts, offsets, row_token, slot_row, flags, gen, gen_copy,
+                       flag_out, T, E, k, cap);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(256), 0, s, hist, counts, offsets, NB, E,
                      cap, gen, gen_copy, flags, flag_out);
   err = hipGetLastError();

@@ -501,3 +501,48 @@ def test_threshold_rows_flow_through_permute_without_flags():
     print(f"[threshold] experts per token: mean {kept.mean():.2f}, min {kept.min()}, "
           f"max {kept.max()}", flush=True)
     assert kept.min() >= 1 and kept.max() <= cfg.experts - 1
+
+
+# The row maps come from the count and one scan-and-rows launch on batches of up to 65536
+# tokens (64 count blocks), and from the three-launch count / scan / rows path above that;
+# with an x_perm destination the three-launch path (its third launch the gather) always
+# runs. Both against the oracle's permutation, and the two paths against each other, on
+# batches on both sides of the boundary, with capacity drops, empty (-1) slots and invalid
+# ids.
+@pytest.mark.parametrize("T,E,k,cf", [(1100, 6, 3, 0.7), (9000, 16, 2, 0.0),
+                                      (65536, 8, 2, 1.1), (65537, 64, 4, 0.9),
+                                      (70000, 16, 2, 0.0), (40000, 128, 8, 0.0),
+                                      (5000, 256, 16, 1.0)])
+def test_row_map_paths_agree(T, E, k, cf):
+    cfg = C.SMALL.with_(tokens=T, hidden=256, inter=256, experts=E, top_k=k,
+                        capacity_factor=cf)
+    rng = np.random.default_rng(T + E)
+    idx = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    idx[rng.random((T, k)) < 0.02] = -1                 # empty slots
+    idx[3, 0] = E                                       # out of range
+    idx[T - 1, k - 1] = idx[T - 1, 0] if k > 1 else -2  # repeated (or negative)
+    c = L.cconfig(cfg)
+    ws = torch.empty(L.moe_workspace_size(c), dtype=torch.uint8, device="cuda")
+    xd = torch.zeros((T, 256), dtype=torch.bfloat16, device="cuda")
+    idd = torch.from_numpy(idx).cuda()
+    out = {}
+    for tag, xp in (("maps", None),
+                    ("gather", torch.empty((T * k, 256), dtype=torch.bfloat16, device="cuda"))):
+        counts = torch.full((E,), -9, dtype=torch.int32, device="cuda")
+        offs = torch.full((E + 1,), -9, dtype=torch.int32, device="cuda")
+        rt = torch.full((T * k,), -9, dtype=torch.int32, device="cuda")
+        sr = torch.full((T, k), -9, dtype=torch.int32, device="cuda")
+        print(f"[permute] T={T} E={E} k={k} cf={cf} path={tag}", flush=True)
+        L.moe_permute(c, xd, idd, xp, counts, offs, rt, sr, ws)
+        flag = L.moe_read_device_status(c, ws, 2)
+        out[tag] = [a.cpu().numpy() for a in (counts, offs, rt, sr)] + [flag]
+    cap = O.capacity(cf, T, k, E) if cf > 0 else T
+    counts, offs, rt, sr, flag = out["maps"]
+    P.check_permute(cfg, None, idx, cap, counts, offs, sr, rt)
+    assert flag == L.MOE_FLAG_BAD_INDEX
+    n = int(offs[-1])
+    for a, b in zip(out["maps"][:3], out["gather"][:3]):
+        np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(out["maps"][3], out["gather"][3])
+    np.testing.assert_array_equal(out["maps"][2][:n], out["gather"][2][:n])
+    assert out["gather"][4] == flag
