@@ -213,7 +213,8 @@ def run_workload(name, args, steps, warmup, headline, peaks=None):
         wg, wu, wd = ((layer.w_gate, layer.w_up, layer.w_down) if plain or not packed
                       else (layer.fw_gate, layer.fw_up, layer.fw_down))
         if ev: ev[0].record(stream)
-        L.moe_route(cw, x, layer.w_router, layer.bias, logits, idx, w, ws, stream)
+        L.moe_route(cw, x, layer.w_router if plain else layer.fw_router, layer.bias, logits,
+                    idx, w, ws, stream)
         if ev: ev[1].record(stream)
         L.moe_permute(cw, x, idx, None, counts, offs, rt, sr, ws, stream)
         if ev: ev[2].record(stream)

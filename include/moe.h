@@ -73,9 +73,9 @@ enum { MOE_FLAG_BAD_INDEX = 1, MOE_FLAG_NONFINITE_LOGIT = 2, MOE_FLAG_STALE_SAVE
 enum { MOE_MAX_EXPERTS = 256, MOE_MAX_TOPK = 16 };
 /* routing rules (moe_config.routing) */
 enum { MOE_ROUTE_TOPK = 0, MOE_ROUTE_THRESHOLD = 1 };
-/* expert weight layouts (moe_config.weight_layout) and weights (moe_pack_expert_weight) */
-enum { MOE_WEIGHTS_PLAIN = 0, MOE_WEIGHTS_PACKED = 1 };
-enum { MOE_WEIGHT_GATE = 0, MOE_WEIGHT_UP = 1, MOE_WEIGHT_DOWN = 2 };
+/* weight layouts (moe_config.weight_layout, bit flags) and weights (moe_pack_expert_weight) */
+enum { MOE_WEIGHTS_PLAIN = 0, MOE_WEIGHTS_PACKED = 1, MOE_ROUTER_PACKED = 2 };
+enum { MOE_WEIGHT_GATE = 0, MOE_WEIGHT_UP = 1, MOE_WEIGHT_DOWN = 2, MOE_WEIGHT_ROUTER = 3 };
 
 typedef struct moe_config {
   int32_t tokens;            /* T >= 0 */
@@ -100,14 +100,16 @@ typedef struct moe_config {
                                 contributes zero (intelliparadigm.com page, section 3.2.1:
                                 keep the experts scoring above delta, default 1/E, then
                                 renormalise) */
-  int32_t weight_layout;     /* MOE_WEIGHTS_PLAIN (0, the default): w_gate, w_up, w_down
+  int32_t weight_layout;     /* bit flags; MOE_WEIGHTS_PLAIN (0, the default): every weight
                                 in the row-major layouts below. MOE_WEIGHTS_PACKED (bf16
-                                only): the same tensors as written by
+                                only): w_gate, w_up, w_down as written by
                                 moe_pack_expert_weight, for the forward entry points
                                 (moe_expert_up, moe_expert_up_rows, moe_expert_down,
-                                moe_grouped_ffn, moe_forward); the backward and
-                                moe_forward_train need plain weights
-                                (MOE_ERR_UNSUPPORTED). Other values: MOE_ERR_INVALID_ARG */
+                                moe_grouped_ffn, moe_forward). MOE_ROUTER_PACKED (bf16
+                                only): w_router as written by moe_pack_expert_weight
+                                (MOE_WEIGHT_ROUTER), for moe_route and moe_forward. The
+                                backward and moe_forward_train need plain weights (either
+                                bit: MOE_ERR_UNSUPPORTED). Other bits: MOE_ERR_INVALID_ARG */
   double threshold;          /* delta of MOE_ROUTE_THRESHOLD; <= 0 means 1/E; not NaN */
   double aux_loss_coeff;     /* >= 0, not NaN. > 0: moe_backward also differentiates the
                                 auxiliary load-balancing loss coeff * E * sum_e f_e P_e (f_e:
@@ -133,7 +135,9 @@ moe_status moe_capacity(const moe_config* cfg, int32_t* capacity);
 /* Gate GEMM + softmax + top-k + weights (gitcode page, "核心代码解析": routing_module_,
  * TopKRouting; hnwysp.cn page, section 2.1: top-k routing; section 4.1: softmax first).
  *   x         [T,H] dtype, or NULL: then `logits` is an INPUT and only top-k runs
- *   w_router  [H,E] dtype (ignored when x == NULL)
+ *   w_router  [H,E] dtype, or with MOE_ROUTER_PACKED in weight_layout the same weight as
+ *             written by moe_pack_expert_weight (MOE_WEIGHT_ROUTER; 16-byte aligned);
+ *             ignored when x == NULL. The two give bit-identical results
  *   gate_bias [E] float32 or NULL, added to the logits before softmax and selection
  *   logits    [T,E] float32: output (input when x == NULL)
  *   topk_idx  [T,k] int32 out: experts in descending logit order, lower index first on ties
@@ -227,18 +231,31 @@ moe_status moe_grouped_ffn(const moe_config* cfg, const void* x_perm,
                            const void* w_down, void* y_perm, void* ws, size_t ws_bytes,
                            moe_stream_t stream);
 
-/* Repack one expert weight tensor for MOE_WEIGHTS_PACKED (bf16 only; once, when weights
- * are loaded: inference weights are constant). which = MOE_WEIGHT_GATE or MOE_WEIGHT_UP
- * (w [E,H,I]; gate: SwiGLU only) or MOE_WEIGHT_DOWN (w [E,I,H]); for w [E,K,N], `packed`
- * (same byte size, must not overlap w) receives, for each expert e, 32-column block nb and
- * 16-row slice ks, a 1 KB block whose 16-byte chunk l (0..63) holds
- *   w[e][16 ks + 8 (l >> 5) + q][32 nb + (l & 31)],  q = 0..7,
- * blocks ordered [e][nb][ks]: chunk l is lane l's operand of one 32x32x16 bf16 MFMA, so the
- * packed GEMMs load weights straight into registers. The packed GEMMs give bit-identical
- * results to the plain ones (the summation order is unchanged). Asynchronous on `stream`;
- * a bad `which` or overlapping buffers -> MOE_ERR_INVALID_ARG. */
+/* Repack one weight tensor for MOE_WEIGHTS_PACKED or MOE_ROUTER_PACKED (bf16 only; once,
+ * when weights are loaded: inference weights are constant; the pages likewise store their
+ * weights in the matrix unit's own NZ format, lshu.cn page, section 5.1). `packed` must
+ * hold moe_packed_weight_bytes(cfg, which) bytes, be 16-byte aligned and not overlap w.
+ *   which = MOE_WEIGHT_GATE or MOE_WEIGHT_UP (w [E,H,I]; gate: SwiGLU only) or
+ *   MOE_WEIGHT_DOWN (w [E,I,H]): for w [E,K,N], `packed` (the same byte size) receives, for
+ *   each expert e, 32-column block nb and 16-row slice ks, a 1 KB block whose 16-byte chunk
+ *   l (0..63) holds
+ *     w[e][16 ks + 8 (l >> 5) + q][32 nb + (l & 31)],  q = 0..7,
+ *   blocks ordered [e][nb][ks]: chunk l is lane l's operand of one 32x32x16 bf16 MFMA, so
+ *   the packed GEMMs load weights straight into registers.
+ *   which = MOE_WEIGHT_ROUTER (w = w_router [H,E]): `packed` receives, for each group g of
+ *   16 experts (EP / 16 groups, EP the smallest of 32, 64, 128, 256 that is >= E) and
+ *   32-row slice s, a 1 KB block whose 16-byte chunk l holds
+ *     w[32 s + 8 (l >> 4) + q][16 g + (l & 15)],  q = 0..7 (0 for experts >= E),
+ *   blocks ordered [g][s]: lane l's operand of one 16x16x32 bf16 MFMA of the gate GEMM.
+ * Results with packed weights are bit-identical to plain ones (the summation order is
+ * unchanged). Asynchronous on `stream`; a bad `which` or overlapping buffers ->
+ * MOE_ERR_INVALID_ARG. */
 moe_status moe_pack_expert_weight(const moe_config* cfg, int32_t which, const void* w,
                                   void* packed, moe_stream_t stream);
+
+/* Bytes of moe_pack_expert_weight's output for `which` (0 for a bad which or config):
+ * E*H*I*2 for the expert weights, EP*H*2 for the router. */
+size_t moe_packed_weight_bytes(const moe_config* cfg, int32_t which);
 
 /* Weighted combine back to token order (lshu.cn page, section 4,
  * npu_moe_token_postprocess; the pages aggregate with an atomic scatter-add, this library

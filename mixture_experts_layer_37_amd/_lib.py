@@ -22,15 +22,15 @@ MOE_DTYPE_BF16, MOE_DTYPE_F32 = 0, 1
 MOE_ACT_SWIGLU, MOE_ACT_GELU = 0, 1
 MOE_FLAG_BAD_INDEX, MOE_FLAG_NONFINITE_LOGIT, MOE_FLAG_STALE_SAVED = 1, 2, 4
 MOE_ROUTE_TOPK, MOE_ROUTE_THRESHOLD = 0, 1
-MOE_WEIGHTS_PLAIN, MOE_WEIGHTS_PACKED = 0, 1
-MOE_WEIGHT_GATE, MOE_WEIGHT_UP, MOE_WEIGHT_DOWN = 0, 1, 2
+MOE_WEIGHTS_PLAIN, MOE_WEIGHTS_PACKED, MOE_ROUTER_PACKED = 0, 1, 2
+MOE_WEIGHT_GATE, MOE_WEIGHT_UP, MOE_WEIGHT_DOWN, MOE_WEIGHT_ROUTER = 0, 1, 2, 3
 (MOE_WS_LOGITS, MOE_WS_TOPK_IDX, MOE_WS_TOPK_W, MOE_WS_COUNTS, MOE_WS_OFFSETS, MOE_WS_SLOT_ROW,
  MOE_WS_ROW_TOKEN, MOE_WS_X_PERM, MOE_WS_H, MOE_WS_Y_PERM, MOE_WS_AUX_LOSS) = range(11)
 
 EXPORTS = ("moe_workspace_size", "moe_capacity", "moe_route", "moe_permute",
            "moe_permute_noalloc", "moe_expert_up",
            "moe_expert_up_rows", "moe_expert_down", "moe_grouped_ffn",
-           "moe_pack_expert_weight", "moe_combine",
+           "moe_pack_expert_weight", "moe_packed_weight_bytes", "moe_combine",
            "moe_forward", "moe_forward_train", "moe_backward_workspace_size", "moe_backward",
            "moe_workspace_view", "moe_read_device_status", "moe_status_string",
            "moe_last_hip_error")
@@ -91,6 +91,8 @@ def lib():
             f = getattr(L, name)
             f.argtypes = args
             f.restype = c_int32
+        L.moe_packed_weight_bytes.argtypes = [cfgp, c_int32]
+        L.moe_packed_weight_bytes.restype = c_size_t
         L.moe_status_string.argtypes = [c_int32]
         L.moe_status_string.restype = c_char_p
         L.moe_last_hip_error.argtypes = []
@@ -107,8 +109,8 @@ def cconfig(cfg: MoEConfig, tokens: int | None = None) -> CConfig:
                    renormalize=1 if cfg.renormalize else 0,
                    capacity_factor=float(cfg.capacity_factor),
                    routing=MOE_ROUTE_THRESHOLD if cfg.routing == "threshold" else MOE_ROUTE_TOPK,
-                   weight_layout=(MOE_WEIGHTS_PACKED if cfg.weights == "packed"
-                                  else MOE_WEIGHTS_PLAIN),
+                   weight_layout=(MOE_WEIGHTS_PACKED | MOE_ROUTER_PACKED
+                                  if cfg.weights == "packed" else MOE_WEIGHTS_PLAIN),
                    threshold=float(cfg.threshold),
                    aux_loss_coeff=float(cfg.aux_loss_coeff))
 
@@ -205,6 +207,10 @@ def moe_grouped_ffn(cfg, x_perm, expert_offsets, w_gate, w_up, w_down, y_perm, w
 def moe_pack_expert_weight(cfg, which: int, w, packed, stream=None):
     _check("moe_pack_expert_weight", lib().moe_pack_expert_weight(
         ctypes.byref(_as_cfg(cfg)), which, _ptr(w), _ptr(packed), _stream(stream)))
+
+
+def moe_packed_weight_bytes(cfg, which: int) -> int:
+    return int(lib().moe_packed_weight_bytes(ctypes.byref(_as_cfg(cfg)), which))
 
 
 def moe_combine(cfg, y_perm, slot_row, topk_w, out, stream=None):

@@ -19,10 +19,12 @@ hipError_t launch_route_bf16(const bf16_t* x, const bf16_t* wt, const float* bia
                              int T, int H, int E, int k, int renorm, int thr, double delta,
                              hipStream_t s);
 bool route_lds_fits(int H, int E);
-hipError_t launch_route_bf16_lds(const bf16_t* x, const bf16_t* w_router, const float* bias,
-                                 float* logits, int32_t* topk_idx, float* topk_w, int32_t* flags,
-                                 int T, int H, int E, int k, int renorm, int thr, double delta,
-                                 int cus, hipStream_t s);
+// the streaming router: w_router [H][E] as it is, or (w_router == nullptr) wt, the same
+// weight in launch_router_pack's layout
+hipError_t launch_route_bf16_lds(const bf16_t* x, const bf16_t* w_router, const bf16_t* wt,
+                                 const float* bias, float* logits, int32_t* topk_idx,
+                                 float* topk_w, int32_t* flags, int T, int H, int E, int k,
+                                 int renorm, int thr, double delta, int cus, hipStream_t s);
 int device_cus();
 hipError_t launch_route_logits_f32(const float* x, const float* w_router, const float* bias,
                                    float* logits, int T, int H, int E, hipStream_t s);

@@ -145,10 +145,10 @@ moe_status check_cfg(const moe_config* c) {
     return MOE_ERR_INVALID_ARG;
   if (std::isnan(c->threshold)) return MOE_ERR_INVALID_ARG;
   if (!(c->aux_loss_coeff >= 0.0) || std::isinf(c->aux_loss_coeff)) return MOE_ERR_INVALID_ARG;
-  if (c->weight_layout != MOE_WEIGHTS_PLAIN && c->weight_layout != MOE_WEIGHTS_PACKED)
+  if ((c->weight_layout & ~(MOE_WEIGHTS_PACKED | MOE_ROUTER_PACKED)) != 0)
     return MOE_ERR_INVALID_ARG;
   if (c->dtype != MOE_DTYPE_BF16 && c->dtype != MOE_DTYPE_F32) return MOE_ERR_UNSUPPORTED;
-  if (c->weight_layout == MOE_WEIGHTS_PACKED && c->dtype != MOE_DTYPE_BF16)
+  if (c->weight_layout != MOE_WEIGHTS_PLAIN && c->dtype != MOE_DTYPE_BF16)
     return MOE_ERR_UNSUPPORTED;
   if (c->activation != MOE_ACT_SWIGLU && c->activation != MOE_ACT_GELU) return MOE_ERR_UNSUPPORTED;
   if (c->experts > MOE_MAX_EXPERTS || c->top_k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
@@ -216,14 +216,22 @@ moe_status do_route(const moe_config* c, const void* x, const void* w_router, co
   if (x == nullptr)
     return hip_status(
         moe::launch_route_topk(logits, idx, w, flags, T, E, k, renorm, thr, delta, s));
+  // a router weight packed at load time (MOE_ROUTER_PACKED) is already in the MFMA operand
+  // order the routers read; a plain one goes to the streaming router as it is, or is
+  // packed into the workspace for the general router
+  const bool packed = (c->weight_layout & MOE_ROUTER_PACKED) != 0;
   if (c->dtype == MOE_DTYPE_BF16 && moe::route_lds_fits(H, E))
-    return hip_status(moe::launch_route_bf16_lds((const moe::bf16_t*)x,
-                                                 (const moe::bf16_t*)w_router, bias, logits,
-                                                 idx, w, flags, T, H, E, k, renorm, thr,
-                                                 delta, moe::device_cus(), s));
+    return hip_status(moe::launch_route_bf16_lds(
+        (const moe::bf16_t*)x, packed ? nullptr : (const moe::bf16_t*)w_router,
+        packed ? (const moe::bf16_t*)w_router : nullptr, bias, logits, idx, w, flags, T, H, E,
+        k, renorm, thr, delta, moe::device_cus(), s));
   if (c->dtype == MOE_DTYPE_BF16) {
-    moe::bf16_t* wt = region<moe::bf16_t>(ws, L, R_WT);
-    MOE_TRY(hip_status(moe::launch_router_pack((const moe::bf16_t*)w_router, wt, H, E, s)));
+    const moe::bf16_t* wt = (const moe::bf16_t*)w_router;
+    if (!packed) {
+      moe::bf16_t* wp = region<moe::bf16_t>(ws, L, R_WT);
+      MOE_TRY(hip_status(moe::launch_router_pack((const moe::bf16_t*)w_router, wp, H, E, s)));
+      wt = wp;
+    }
     return hip_status(moe::launch_route_bf16((const moe::bf16_t*)x, wt, bias, logits, idx, w,
                                              flags, T, H, E, k, renorm, thr, delta, s));
   }
@@ -255,7 +263,7 @@ moe_status do_up(const moe_config* c, const void* a, const int32_t* row_token,
   const int epi = swiglu ? moe::EPI_SWIGLU : moe::EPI_GELU;
   const int rows = c->tokens * c->top_k;
   const int a_rows = row_token != nullptr ? c->tokens : rows;
-  if (c->weight_layout == MOE_WEIGHTS_PACKED)
+  if (c->weight_layout & MOE_WEIGHTS_PACKED)
     return hip_status(moe::launch_gemm_bf16_packed(
         epi, (const moe::bf16_t*)a, row_token, a_rows, offsets,
         (const moe::bf16_t*)(swiglu ? w_gate : w_up), (const moe::bf16_t*)w_up,
@@ -275,7 +283,7 @@ moe_status do_up(const moe_config* c, const void* a, const int32_t* row_token,
 moe_status do_down(const moe_config* c, const void* h, const int32_t* offsets,
                    const void* w_down, void* y, float* partial, hipStream_t s) {
   const int rows = c->tokens * c->top_k;
-  if (c->weight_layout == MOE_WEIGHTS_PACKED)
+  if (c->weight_layout & MOE_WEIGHTS_PACKED)
     return hip_status(moe::launch_gemm_bf16_packed(
         moe::EPI_NONE, (const moe::bf16_t*)h, nullptr, rows, offsets,
         (const moe::bf16_t*)w_down, nullptr, (moe::bf16_t*)y, partial, c->experts, c->inter,
@@ -441,10 +449,31 @@ moe_status moe_grouped_ffn(const moe_config* cfg, const void* x_perm,
   return do_down(cfg, h, expert_offsets, w_down, y_perm, region<float>(ws, L, R_SPLIT), s);
 }
 
+size_t moe_packed_weight_bytes(const moe_config* cfg, int32_t which) {
+  if (cfg == nullptr || check_cfg(cfg) != MOE_OK || cfg->dtype != MOE_DTYPE_BF16) return 0;
+  if (which == MOE_WEIGHT_ROUTER)
+    return (size_t)moe::route_padded_experts(cfg->experts) * cfg->hidden * 2;
+  if (which == MOE_WEIGHT_GATE && cfg->activation != MOE_ACT_SWIGLU) return 0;
+  if (which == MOE_WEIGHT_GATE || which == MOE_WEIGHT_UP || which == MOE_WEIGHT_DOWN)
+    return (size_t)cfg->experts * cfg->hidden * cfg->inter * 2;
+  return 0;
+}
+
 moe_status moe_pack_expert_weight(const moe_config* cfg, int32_t which, const void* w,
                                   void* packed, moe_stream_t stream) {
   MOE_TRY(check_cfg(cfg));
   if (cfg->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (which == MOE_WEIGHT_ROUTER) {
+    MOE_TRY(need(w, 2));
+    MOE_TRY(need(packed, 16));
+    const size_t wbytes = (size_t)cfg->hidden * cfg->experts * 2;
+    const size_t pbytes = moe_packed_weight_bytes(cfg, which);
+    const char* wb = (const char*)w;
+    const char* pb = (const char*)packed;
+    if (pb < wb + wbytes && wb < pb + pbytes) return MOE_ERR_INVALID_ARG;   // no overlap
+    return hip_status(moe::launch_router_pack((const moe::bf16_t*)w, (moe::bf16_t*)packed,
+                                              cfg->hidden, cfg->experts, (hipStream_t)stream));
+  }
   int K, N;
   if (which == MOE_WEIGHT_GATE || which == MOE_WEIGHT_UP) {
     K = cfg->hidden;

@@ -518,7 +518,8 @@ bool route_lds_fits(int H, int E) {
 
 template <int KMAX>
 __global__ __launch_bounds__(512, 1) void route_stream_kernel(
-    const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, const float* __restrict__ bias,
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, const bf16_t* __restrict__ wt,
+    const float* __restrict__ bias,
     float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     int32_t* __restrict__ flags, int T, int H, int E, int k, int renorm, int thr, double delta) {
   constexpr int BT = 32, LDR = 17;
@@ -550,35 +551,49 @@ __global__ __launch_bounds__(512, 1) void route_stream_kernel(
       __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)(dst + i * 512), 16, 0, 0);
     }
   };
-  // The wave's slice of the router weight is contiguous in W[H, E] (hs * E elements, at
-  // most one buffer). It is DMA'd into the wave's second buffer ahead of the first x
-  // sub-chunk; once it has landed (all but the 8 newest DMA instructions done), the MFMA
-  // operands of every k-step (8 consecutive k of expert lane & 15; zeros for experts
-  // >= E) are read from LDS into registers, after which the buffer is free for x.
+  // The MFMA operands of every k-step of the wave's slice (8 consecutive k of expert
+  // lane & 15 per lane; zeros for experts >= E) go into registers before the stream starts.
+  //   - A packed router weight (wt, launch_router_pack's layout, packed once at load time):
+  //     k-step st is one contiguous 1 KB block of expert group 0, one 16-byte load per lane
+  //     of a live expert (the block's zeros for experts >= E are not fetched), issued
+  //     together and ahead of the first x sub-chunk. Measured as fast as the plain path:
+  //     the wait for the weights is latency either way.
+  //   - A plain one: the slice is contiguous in W[H, E] (hs * E elements, at most one
+  //     buffer). It is DMA'd into the wave's second buffer ahead of the first x sub-chunk;
+  //     once it has landed (all but the 8 newest DMA instructions done), the operands are
+  //     read from LDS, after which the buffer is free for x.
   const int n = lane & 15;
   const bool live = n < E;
-  bf16_t* wsl = xb1 + wave * kRouteBufElems;
-  const int wchunks = hs * E / 8;                 // 16-byte chunks of the slice
-  const int wdma = (wchunks + 63) / 64;           // 1 KB DMA instructions (<= 8)
-  const bf16_t* wsrc = w + (size_t)kbase * E;
-  for (int i = 0; i < wdma; ++i) {
-    const bf16_t* src = wsrc + (size_t)min(i * 64 + lane, wchunks - 1) * 8;
-    __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)(wsl + i * 512), 16, 0, 0);
-  }
-  dma(0, xb0);
-  __builtin_amdgcn_s_waitcnt(wait_vmcnt(8));   // the weight slice has landed
   bf16x8 wf[kRouteMaxSteps];
+  if (wt != nullptr) {
+    const bf16x8* src = (const bf16x8*)wt + (size_t)(kbase / 32) * 64 + lane;
 #pragma unroll
-  for (int st = 0; st < kRouteMaxSteps; ++st) {
-    v8i16 v = {};
-    if (st < nsteps && live) {
-      const bf16_t* p = wsl + (st * 32 + 8 * (lane >> 4)) * E + n;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = (short)p[i * E];
+    for (int st = 0; st < kRouteMaxSteps; ++st)
+      wf[st] = (st < nsteps && live) ? src[st * 64] : bf16x8{};   // dead lanes load nothing
+    dma(0, xb0);
+  } else {
+    bf16_t* wsl = xb1 + wave * kRouteBufElems;
+    const int wchunks = hs * E / 8;                 // 16-byte chunks of the slice
+    const int wdma = (wchunks + 63) / 64;           // 1 KB DMA instructions (<= 8)
+    const bf16_t* wsrc = w + (size_t)kbase * E;
+    for (int i = 0; i < wdma; ++i) {
+      const bf16_t* src = wsrc + (size_t)min(i * 64 + lane, wchunks - 1) * 8;
+      __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)(wsl + i * 512), 16, 0, 0);
     }
-    wf[st] = __builtin_bit_cast(bf16x8, v);
+    dma(0, xb0);
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(8));   // the weight slice has landed
+#pragma unroll
+    for (int st = 0; st < kRouteMaxSteps; ++st) {
+      v8i16 v = {};
+      if (st < nsteps && live) {
+        const bf16_t* p = wsl + (st * 32 + 8 * (lane >> 4)) * E + n;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = (short)p[i * E];
+      }
+      wf[st] = __builtin_bit_cast(bf16x8, v);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // the weight slice has been read out
   }
-  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // the weight slice has been read out
 
   f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
   auto compute = [&](int j, const bf16_t* set) {
@@ -651,14 +666,14 @@ __global__ __launch_bounds__(512, 1) void route_stream_kernel(
   }
 }
 
-hipError_t launch_route_bf16_lds(const bf16_t* x, const bf16_t* w_router, const float* bias,
-                                 float* logits, int32_t* idx, float* w, int32_t* flags, int T,
-                                 int H, int E, int k, int renorm, int thr, double delta,
-                                 int cus, hipStream_t s) {
+hipError_t launch_route_bf16_lds(const bf16_t* x, const bf16_t* w_router, const bf16_t* wt,
+                                 const float* bias, float* logits, int32_t* idx, float* w,
+                                 int32_t* flags, int T, int H, int E, int k, int renorm, int thr,
+                                 double delta, int cus, hipStream_t s) {
   (void)cus;
   const dim3 grid((T + 31) / 32), block(64 * kRouteWaves);
 #define MOE_ROUTE_STREAM(KM)                                                                    \
-  hipLaunchKernelGGL((route_stream_kernel<KM>), grid, block, 0, s, x, w_router, bias, logits, idx, \
+  hipLaunchKernelGGL((route_stream_kernel<KM>), grid, block, 0, s, x, w_router, wt, bias, logits, idx, \
                      w, flags, T, H, E, k, renorm, thr, delta)
   if (k <= 1) MOE_ROUTE_STREAM(1);
   else if (k <= 2) MOE_ROUTE_STREAM(2);

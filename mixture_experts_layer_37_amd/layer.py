@@ -36,15 +36,17 @@ def from_device(t: torch.Tensor) -> np.ndarray:
     return t.numpy()
 
 
-def pack_weights(c, w_gate, w_up, w_down, stream=None):
-    """Packed copies of the expert weights (moe_pack_expert_weight; w_gate may be None)."""
+def pack_weights(c, w_gate, w_up, w_down, w_router=None, stream=None):
+    """Packed copies of the expert weights and, if given, of the router weight
+    (moe_pack_expert_weight; w_gate may be None)."""
     out = []
     for which, w in ((L.MOE_WEIGHT_GATE, w_gate), (L.MOE_WEIGHT_UP, w_up),
-                     (L.MOE_WEIGHT_DOWN, w_down)):
+                     (L.MOE_WEIGHT_DOWN, w_down), (L.MOE_WEIGHT_ROUTER, w_router)):
         if w is None:
             out.append(None)
             continue
-        p = torch.empty_like(w)
+        p = torch.empty(L.moe_packed_weight_bytes(c, which) // 2, dtype=w.dtype,
+                        device=w.device)
         L.moe_pack_expert_weight(c, which, w, p, stream)
         out.append(p)
     return tuple(out)
@@ -53,7 +55,7 @@ def pack_weights(c, w_gate, w_up, w_down, stream=None):
 class MoELayer:
     """Holds device weights and one workspace; ``forward`` calls moe_forward.
 
-    With ``cfg.weights == "packed"`` the expert weights are also repacked once
+    With ``cfg.weights == "packed"`` the expert and router weights are also repacked once
     (moe_pack_expert_weight) and the forward runs on the packed copies (``fw_*``); the
     training forward and the backward use the plain ones (``w_*``)."""
 
@@ -69,16 +71,17 @@ class MoELayer:
         self.w_up = to_device(cfg, inputs["w_up"], device)
         self.w_down = to_device(cfg, inputs["w_down"], device)
         self.fw_gate, self.fw_up, self.fw_down = self.w_gate, self.w_up, self.w_down
+        self.fw_router = self.w_router
         if cfg.weights == "packed":
-            self.fw_gate, self.fw_up, self.fw_down = pack_weights(self.c, self.w_gate, self.w_up,
-                                                                  self.w_down)
+            self.fw_gate, self.fw_up, self.fw_down, self.fw_router = pack_weights(
+                self.c, self.w_gate, self.w_up, self.w_down, self.w_router)
         self.ws = torch.empty(L.moe_workspace_size(self.c), dtype=torch.uint8, device=device)
 
     def forward(self, x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
         self._saved = False
         if out is None:
             out = torch.empty_like(x)
-        L.moe_forward(self.c, x, self.w_router, self.bias, self.fw_gate, self.fw_up,
+        L.moe_forward(self.c, x, self.fw_router, self.bias, self.fw_gate, self.fw_up,
                       self.fw_down, out, self.ws, stream)
         return out
 

@@ -159,7 +159,7 @@ def test_stale_saved_preactivations_are_flagged():
     assert layer.device_status(4) == 0
     layer.forward_train(x)
     out = torch.empty_like(x)
-    L.moe_forward(layer.c, x, layer.w_router, layer.bias, layer.fw_gate, layer.fw_up,
+    L.moe_forward(layer.c, x, layer.fw_router, layer.bias, layer.fw_gate, layer.fw_up,
                   layer.fw_down, out, layer.ws, None)
     layer._saved = True            # the caller still believes the saved pre-activations hold
     layer.backward(x, dout)

@@ -1,7 +1,7 @@
-"""Packed expert weights (moe_pack_expert_weight, MOE_WEIGHTS_PACKED): the packed layout
-against its definition in include/moe.h, the packed GEMMs and forward against the plain ones
-bit for bit (the packed kernels add in the same order), and the packed forward against the
-oracle."""
+"""Packed weights (moe_pack_expert_weight; MOE_WEIGHTS_PACKED, MOE_ROUTER_PACKED): the packed
+layouts against their definitions in include/moe.h, the packed GEMMs, routers and forward
+against the plain ones bit for bit (the packed kernels add in the same order), and the
+packed forward against the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -40,7 +40,7 @@ def test_pack_layout_matches_definition(activation):
                         activation=activation)
     inp = make_inputs(cfg, seed=11)
     layer = MoELayer(cfg, inp)
-    pg, pu, pd = pack_weights(layer.c, layer.w_gate, layer.w_up, layer.w_down)
+    pg, pu, pd, _ = pack_weights(layer.c, layer.w_gate, layer.w_up, layer.w_down)
     torch.cuda.synchronize()
     for name, packed, plain in (("gate", pg, inp["w_gate"]), ("up", pu, inp["w_up"]),
                                 ("down", pd, inp["w_down"])):
@@ -54,6 +54,76 @@ def test_pack_layout_matches_definition(activation):
         with pytest.raises(L.MoEError):
             L.moe_pack_expert_weight(layer.c, L.MOE_WEIGHT_GATE, layer.w_up,
                                      torch.empty_like(layer.w_up))
+
+
+def router_packed_by_definition(w: np.ndarray, EP: int) -> np.ndarray:
+    """w_router [H,E] (bf16 bits) -> [EP/16, H/32, 64, 8]: chunk l of block (g, s) holds
+    w[32 s + 8 (l >> 4) + q][16 g + (l & 15)], q = 0..7, zero for experts >= E."""
+    H, E = w.shape
+    wp = np.zeros((H, EP), dtype=w.dtype)
+    wp[:, :E] = w
+    v = wp.reshape(H // 32, 4, 8, EP // 16, 16)             # [s, h, q, g, c]
+    return v.transpose(3, 0, 1, 4, 2).reshape(EP // 16, H // 32, 64, 8)
+
+
+@pytest.mark.parametrize("E", [1, 8, 12, 32, 100, 256])
+def test_router_pack_layout_matches_definition(E):
+    cfg = C.SMALL.with_(tokens=64, hidden=512, inter=256, experts=E, top_k=1)
+    inp = make_inputs(cfg, seed=5, weights=False)
+    c = L.cconfig(cfg)
+    w = to_device(cfg, inp["w_router"])
+    nbytes = L.moe_packed_weight_bytes(c, L.MOE_WEIGHT_ROUTER)
+    EP = 32 if E <= 32 else 64 if E <= 64 else 128 if E <= 128 else 256
+    assert nbytes == EP * 512 * 2
+    p = torch.full((nbytes // 2,), 7, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    L.moe_pack_expert_weight(c, L.MOE_WEIGHT_ROUTER, w, p)
+    torch.cuda.synchronize()
+    got = from_device(p).reshape(-1)
+    assert np.array_equal(got, router_packed_by_definition(inp["w_router"], EP).reshape(-1))
+
+
+# The streaming router (E <= 16, H a multiple of 1024) and the general one (the other gates),
+# top-k and threshold routing: routing from the packed router weight is bit-identical to
+# routing from the plain one (the general router packs a plain weight per call into the same
+# layout; the streaming one reads it from LDS in the same order).
+@pytest.mark.parametrize("T,H,E,k,routing", [(1000, 1024, 12, 3, "topk"),
+                                             (777, 2048, 16, 4, "topk"),
+                                             (8192, 4096, 8, 2, "topk"),
+                                             (900, 4096, 8, 8, "threshold"),
+                                             (700, 512, 32, 2, "topk"),
+                                             (600, 256, 64, 4, "topk"),
+                                             (500, 2048, 128, 8, "topk"),
+                                             (300, 256, 256, 16, "threshold")])
+def test_packed_router_is_bit_identical(T, H, E, k, routing):
+    cfg = C.SMALL.with_(tokens=T, hidden=H, inter=256, experts=E, top_k=k, routing=routing,
+                        bias=("normal", 1.0))
+    inp = make_inputs(cfg, seed=T + E, weights=False)
+    x = to_device(cfg, inp["x"])
+    w = to_device(cfg, inp["w_router"])
+    bias = to_device(cfg, inp["bias"])
+    c = L.cconfig(cfg)
+    cp = L.cconfig(cfg)
+    cp.weight_layout = L.MOE_ROUTER_PACKED
+    wp = torch.empty(L.moe_packed_weight_bytes(c, L.MOE_WEIGHT_ROUTER) // 2,
+                     dtype=torch.bfloat16, device="cuda")
+    L.moe_pack_expert_weight(c, L.MOE_WEIGHT_ROUTER, w, wp)
+    out = {}
+    for tag, cc, ww in (("plain", c, w), ("packed", cp, wp)):
+        ws = torch.empty(L.moe_workspace_size(cc), dtype=torch.uint8, device="cuda")
+        lg = torch.empty((T, E), dtype=torch.float32, device="cuda")
+        idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        tw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        print(f"[router] T={T} H={H} E={E} k={k} {routing} {tag}", flush=True)
+        L.moe_route(cc, x, ww, bias, lg, idx, tw, ws)
+        torch.cuda.synchronize()
+        out[tag] = (lg.cpu(), idx.cpu(), tw.cpu(), L.moe_read_device_status(cc, ws, 1))
+    a, b = out["plain"], out["packed"]
+    assert torch.equal(a[0].view(torch.int32), b[0].view(torch.int32))
+    assert torch.equal(a[1], b[1])
+    assert torch.equal(a[2].view(torch.int32), b[2].view(torch.int32))
+    assert a[3] == b[3] == 0
+    if T == 8192:   # the Mixtral gate: also against the oracle's fp64 logits
+        P.check_route_from_logits(a[0].numpy(), a[1].numpy(), a[2].numpy(), cfg)
 
 
 # Expert row counts around the 256-row m-tile (none, one, 127, 128, 129, 255, 256, 257, 384,
