@@ -27,7 +27,9 @@
 namespace moe {
 namespace kloop {
 
-constexpr int kLB = 4;   // B loads per 16-wide k slice (one 1 KB block per fragment j)
+// Every function below takes kLA, the A DMA instructions per k-step and wave, and kLB, the
+// B loads per 16-wide k slice (one 1 KB block per weight fragment: 4 in the 2 x 2 wave
+// layout, 2 in the 1 x 4 one).
 
 enum Kind : int {
   // prologue (issue only) and start
@@ -84,7 +86,7 @@ struct Load {
 };
 
 // Loads (counted in instructions) issued after `want` in seq[0, n); -1 if it was never issued.
-template <int kLA>
+template <int kLA, int kLB>
 constexpr int loads_after(const Load* seq, int n, Load want) {
   int after = 0;
   for (int i = n - 1; i >= 0; --i) {
@@ -124,7 +126,7 @@ constexpr bool awaited(const Op& op, int kt, bool next, Load& want) {
 // The count the loop uses at op i of a k-step with these predicates, from the steady state:
 // the previous k-step (which always had a next one, and had a refill exactly when this one
 // has a next) followed by this step's ops before i. -1 for a wait-for-everything op.
-template <int kLA>
+template <int kLA, int kLB>
 constexpr int wait_count(int i, bool next, bool refill) {
   Load seq[2 * kStepOps] = {};
   int n = 0;
@@ -132,7 +134,7 @@ constexpr int wait_count(int i, bool next, bool refill) {
   for (int j = 0; j < i; ++j) n += issue(kStep[j], 0, next, refill, seq + n);
   Load want{false, 0};
   if (!awaited(kStep[i], 0, next, want)) return -1;
-  return loads_after<kLA>(seq, n, want);
+  return loads_after<kLA, kLB>(seq, n, want);
 }
 
 // The prologue's loads in issue order; returns their number.
@@ -147,16 +149,16 @@ constexpr int prologue_loads(Load* seq) {
 }
 
 // The count of kWaitA0: the loads the prologue issues after A(kb).
-template <int kLA>
+template <int kLA, int kLB>
 constexpr int start_count() {
   Load seq[kPrologueOps] = {};
   const int n = prologue_loads(seq);
-  return loads_after<kLA>(seq, n, Load{true, 0});
+  return loads_after<kLA, kLB>(seq, n, Load{true, 0});
 }
 
 // Replay of whole tiles of 2 .. 10 k-steps (the real predicates of every step, the real
 // prologue and start): the number of waits whose count differs from what the replay finds.
-template <int kLA>
+template <int kLA, int kLB>
 constexpr int tile_mismatches() {
   int bad = 0;
   for (int nsteps = 2; nsteps <= 10; nsteps += 2) {
@@ -164,8 +166,8 @@ constexpr int tile_mismatches() {
     int n = prologue_loads(seq);
     for (int j = 0; j < kStartOps; ++j) {
       if (kStart[j].kind == kWaitA0) {
-        const int need = loads_after<kLA>(seq, n, Load{true, 0});
-        if (need < 0 || need != start_count<kLA>()) ++bad;
+        const int need = loads_after<kLA, kLB>(seq, n, Load{true, 0});
+        if (need < 0 || need != start_count<kLA, kLB>()) ++bad;
       }
     }
     for (int kt = 0; kt < nsteps; ++kt) {
@@ -174,10 +176,10 @@ constexpr int tile_mismatches() {
         const Op& op = kStep[i];
         Load want{false, 0};
         if (awaited(op, kt, next, want)) {
-          const int need = loads_after<kLA>(seq, n, want);
-          if (need < 0 || need != wait_count<kLA>(i, next, refill)) ++bad;
+          const int need = loads_after<kLA, kLB>(seq, n, want);
+          if (need < 0 || need != wait_count<kLA, kLB>(i, next, refill)) ++bad;
         } else if (op.kind == kWaitANext) {
-          if (wait_count<kLA>(i, next, refill) != -1) ++bad;   // the last step waits for all
+          if (wait_count<kLA, kLB>(i, next, refill) != -1) ++bad;   // the last step waits for all
         }
         n += issue(op, kt, next, refill, seq + n);
       }
@@ -187,31 +189,41 @@ constexpr int tile_mismatches() {
 }
 
 // vmcnt is a 6-bit field: every count the loop can use must fit.
-template <int kLA>
+template <int kLA, int kLB>
 constexpr bool counts_fit() {
-  if (start_count<kLA>() > 63) return false;
+  if (start_count<kLA, kLB>() > 63) return false;
   for (int i = 0; i < kStepOps; ++i)
     for (int m = 0; m < 4; ++m) {
-      const int c = wait_count<kLA>(i, m & 1, m & 2);
+      const int c = wait_count<kLA, kLB>(i, m & 1, m & 2);
       if (c > 63) return false;
     }
   return true;
 }
 
-// The counts in numbers (both kernels issue kLA = 8 A DMA instructions per k-step):
-// 3 kLB + kLA = 20 before slice 0's MFMAs, 2 kLB + kLA + kLB = 20 before slice 1's and
-// kLB + kLA + 2 kLB = 20 before slice 2's when a next k-step exists (12, 8 and 4 in the last
-// step), 4 kLB = 16 for the next stage before the barrier and 3 kLB = 12 for slice 3 after it
-// (0 in the last step); 3 kLB + kLA + kLB = 24 loads follow A(kb) in the prologue.
-static_assert(tile_mismatches<8>() == 0, "k-loop wait counts disagree with the issue order");
-static_assert(counts_fit<8>(), "k-loop wait count exceeds the 6-bit vmcnt field");
-static_assert(wait_count<8>(1, true, true) == 20 && wait_count<8>(6, true, true) == 20 &&
-                  wait_count<8>(11, true, true) == 20 && wait_count<8>(15, true, true) == 16 &&
-                  wait_count<8>(17, true, true) == 12 && wait_count<8>(1, false, false) == 12 &&
-                  wait_count<8>(6, false, false) == 8 && wait_count<8>(11, false, false) == 4 &&
-                  wait_count<8>(15, false, false) == -1 && wait_count<8>(17, false, false) == 0 &&
-                  start_count<8>() == 24,
+// The counts in numbers, for kLA = 8 A DMA instructions per k-step (both kernels) and kLB
+// = 4 B loads per slice (the 2 x 2 wave layout): 3 kLB + kLA = 20 before slice 0's MFMAs,
+// 2 kLB + kLA + kLB = 20 before slice 1's and kLB + kLA + 2 kLB = 20 before slice 2's when a
+// next k-step exists (12, 8 and 4 in the last step), 4 kLB = 16 for the next stage before
+// the barrier and 3 kLB = 12 for slice 3 after it (0 in the last step); 3 kLB + kLA + kLB =
+// 24 loads follow A(kb) in the prologue. With kLB = 2 (the 1 x 4 layout) the same formulas
+// give 14, 14, 14 (6, 4, 2), 8, 6 (0) and 16.
+static_assert(tile_mismatches<8, 4>() == 0, "k-loop wait counts disagree with the issue order");
+static_assert(counts_fit<8, 4>(), "k-loop wait count exceeds the 6-bit vmcnt field");
+static_assert(wait_count<8, 4>(1, true, true) == 20 && wait_count<8, 4>(6, true, true) == 20 &&
+                  wait_count<8, 4>(11, true, true) == 20 && wait_count<8, 4>(15, true, true) == 16 &&
+                  wait_count<8, 4>(17, true, true) == 12 && wait_count<8, 4>(1, false, false) == 12 &&
+                  wait_count<8, 4>(6, false, false) == 8 && wait_count<8, 4>(11, false, false) == 4 &&
+                  wait_count<8, 4>(15, false, false) == -1 && wait_count<8, 4>(17, false, false) == 0 &&
+                  start_count<8, 4>() == 24,
               "the documented k-loop wait counts");
+static_assert(tile_mismatches<8, 2>() == 0 && counts_fit<8, 2>(),
+              "k-loop wait counts disagree with the issue order (1 x 4 layout)");
+static_assert(wait_count<8, 2>(1, true, true) == 14 && wait_count<8, 2>(6, true, true) == 14 &&
+                  wait_count<8, 2>(11, true, true) == 14 && wait_count<8, 2>(15, true, true) == 8 &&
+                  wait_count<8, 2>(17, true, true) == 6 && wait_count<8, 2>(1, false, false) == 6 &&
+                  wait_count<8, 2>(6, false, false) == 4 && wait_count<8, 2>(11, false, false) == 2 &&
+                  wait_count<8, 2>(17, false, false) == 0 && start_count<8, 2>() == 16,
+              "the documented k-loop wait counts (1 x 4 layout)");
 
 }  // namespace kloop
 }  // namespace moe

@@ -39,20 +39,26 @@ __device__ __forceinline__ bf16x8 load16_asm_at(const bf16_t* p) {
   asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "=v"(v) : "v"(p), "n"(OFF) : "memory");
   return v;
 }
-// Wait until at most N of this wave's loads are in flight. The four fragments pass through
-// the wait, so no instruction that reads them can be scheduled above it.
-template <int N>
+// Wait until at most N of this wave's loads are in flight. The slice's NB fragments pass
+// through the wait, so no instruction that reads them can be scheduled above it.
+template <int N, int NB>
 __device__ __forceinline__ void wait_loads(bf16x8* b) {
   static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit count");
-  asm volatile("s_waitcnt vmcnt(%4)" : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]) : "n"(N));
+  static_assert(NB == 2 || NB == 4, "two or four fragments per slice");
+  if constexpr (NB == 4)
+    asm volatile("s_waitcnt vmcnt(%4)" : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]) : "n"(N));
+  else
+    asm volatile("s_waitcnt vmcnt(%2)" : "+v"(b[0]), "+v"(b[1]) : "n"(N));
 }
 // s_waitcnt immediates: lgkmcnt(0) alone; vmcnt(n) with lgkmcnt(0)
 constexpr int kWaitLgkm0Only = 0xC07F;
 constexpr int wait_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
 
-// A fragments of one 16-wide k slice: rows (or columns) 32 i + (lane & 31) of the wave's 128.
+// A fragments of one 16-wide k slice: rows (or columns) 32 i + (lane & 31) of the wave's
+// 32 NA.
+template <int NA>
 struct FragA {
-  bf16x8 a[4];
+  bf16x8 a[NA];
 };
 
 template <class F, int... I>
@@ -68,24 +74,27 @@ __device__ __forceinline__ void for_each_op(F&& f, std::integer_sequence<int, I.
 // Template and call arguments:
 //   kLA      A DMA instructions per k-step and wave
 //   kAReads  LDS read instructions per load_a (for the scheduling groups)
+//   kLB, kNA B and A fragments per slice: 4 and 4 for a wave's 128 x 128 of the 2 x 2
+//            layout, 2 and 8 for its 256 x 64 of the 1 x 4 one
 //   bsrc[j]  this lane's 16 bytes of B fragment j, slice 0 of k-step 0: slice s of k-step kt
 //            is at bsrc[j] + 2048 kt elements + 1024 s bytes (the packed layout)
 //   load_a(stage, kk, FragA&)  the wave's A fragments of slice kk from an LDS stage
 //   dma_a(kt, stage, i)        this wave's global->LDS load i (0 .. kLA-1) of k-step kt
 // acc[i][j] += B fragment j x A fragment i over the k-steps, v_mfma_f32_32x32x16_bf16 (each
 // lane's accumulators then hold four consecutive columns j of one row i).
-template <int kLA, int kAReads>
+template <int kLA, int kAReads, int kLB = 4, int kNA = 4>
 struct PackedKLoop {
-  static_assert(kloop::tile_mismatches<kLA>() == 0 && kloop::counts_fit<kLA>(),
+  static_assert(kLB * kNA == 16, "16 MFMAs per slice: 256 accumulator registers");
+  static_assert(kloop::tile_mismatches<kLA, kLB>() == 0 && kloop::counts_fit<kLA, kLB>(),
                 "k-loop wait counts disagree with the issue order");
-  bf16x8 bv[8][kloop::kLB];   // ring of eight k slices of B fragments (at most five live)
-  FragA fr[2];                // A fragments of slices of even / odd index
+  bf16x8 bv[8][kLB];          // ring of eight k slices of B fragments (at most five live)
+  FragA<kNA> fr[2];           // A fragments of slices of even / odd index
 
   // B slice kk (0..3) of the k-step whose slice 0 is at base[j]
   template <int KK>
   __device__ __forceinline__ void load_b(const bf16_t* const* base, int slot) {
 #pragma unroll
-    for (int j = 0; j < kloop::kLB; ++j) bv[slot][j] = load16_asm_at<KK * 1024>(base[j]);
+    for (int j = 0; j < kLB; ++j) bv[slot][j] = load16_asm_at<KK * 1024>(base[j]);
   }
 
   template <class DmaA>
@@ -113,21 +122,21 @@ struct PackedKLoop {
   // kStart, then the k-steps [kb, ke) and a barrier.
   template <class LoadA, class DmaA>
   __device__ __forceinline__ void run(int kb, int ke, bf16_t* sa0, bf16_t* sa1,
-                                      const bf16_t* const* bsrc, f32x16 (&acc)[4][4],
+                                      const bf16_t* const* bsrc, f32x16 (&acc)[kNA][kLB],
                                       LoadA&& load_a, DmaA&& dma_a) {
     using namespace kloop;
-    auto mfma16 = [&](const FragA& f, int slot) {
+    auto mfma16 = [&](const FragA<kNA>& f, int slot) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kNA; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < kLB; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[slot][j], f.a[i], acc[i][j], 0, 0, 0);
     };
     for_each_op(
         [&](auto I) {
           constexpr Op op = kStart[decltype(I)::value];
           if constexpr (op.kind == kWaitA0) {
-            __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(start_count<kLA>()));
+            __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(start_count<kLA, kLB>()));
           } else if constexpr (op.kind == kBarrier) {
             __syncthreads();
           } else if constexpr (op.kind == kReadA0) {
@@ -151,11 +160,11 @@ struct PackedKLoop {
           [&](auto I) {
             constexpr int i = decltype(I)::value;
             constexpr Op op = kStep[i];
-            constexpr int count = wait_count<kLA>(i, kNext, kRefill);
+            constexpr int count = wait_count<kLA, kLB>(i, kNext, kRefill);
             if constexpr (op.kind == kLgkm0) {
               __builtin_amdgcn_s_waitcnt(kWaitLgkm0Only);
             } else if constexpr (op.kind == kWaitB) {
-              wait_loads<count>(bv[(sb + op.arg) & 7]);
+              wait_loads<count, kLB>(bv[(sb + op.arg) & 7]);
             } else if constexpr (op.kind == kReadA) {
               load_a(cur, op.arg, fr[op.arg & 1]);
             } else if constexpr (op.kind == kLoadBNext) {
@@ -203,11 +212,11 @@ struct PackedKLoop {
 };
 
 // prologue immediately followed by run: one tile with nothing in between.
-template <int kLA, int kAReads, class LoadA, class DmaA>
+template <int kLA, int kAReads, int kLB = 4, int kNA = 4, class LoadA, class DmaA>
 __device__ __forceinline__ void packed_kloop(int kb, int ke, bf16_t* sa0, bf16_t* sa1,
-                                             const bf16_t* const* bsrc, f32x16 (&acc)[4][4],
+                                             const bf16_t* const* bsrc, f32x16 (&acc)[kNA][kLB],
                                              LoadA&& load_a, DmaA&& dma_a) {
-  PackedKLoop<kLA, kAReads> loop;
+  PackedKLoop<kLA, kAReads, kLB, kNA> loop;
   loop.prologue(kb, sa0, sa1, bsrc, dma_a);
   loop.run(kb, ke, sa0, sa1, bsrc, acc, load_a, dma_a);
 }

@@ -37,23 +37,23 @@ def test_model_compiles():
     assert rc == 0, err
 
 
-COUNT_LINE = "  return loads_after<kLA>(seq, n, want);\n}"
+COUNT_LINE = "  return loads_after<kLA, kLB>(seq, n, want);\n}"
 
 PERTURBATIONS = {
     # every count the loop uses one too high (a wait that passes with its load in flight)
-    "count_plus_one": (COUNT_LINE, "  return loads_after<kLA>(seq, n, want) + 1;\n}"),
+    "count_plus_one": (COUNT_LINE, "  return loads_after<kLA, kLB>(seq, n, want) + 1;\n}"),
     # one too low
-    "count_minus_one": (COUNT_LINE, "  return loads_after<kLA>(seq, n, want) - 1;\n}"),
+    "count_minus_one": (COUNT_LINE, "  return loads_after<kLA, kLB>(seq, n, want) - 1;\n}"),
     # only the counts of the step before the last (next k-step, no refill) one too high
     "second_last_step_plus_one": (
-        COUNT_LINE, "  return loads_after<kLA>(seq, n, want) + (next && !refill ? 1 : 0);\n}"),
+        COUNT_LINE, "  return loads_after<kLA, kLB>(seq, n, want) + (next && !refill ? 1 : 0);\n}"),
     # the prologue issues B slice 3 before A(kb + 1): the steady-state counts no longer hold
     # for the first k-step (its wait for A(kb + 1) would pass with that stage in flight)
     "prologue_order": ("{kLoadB, 2}, {kDmaA, 1}, {kLoadB, 3},",
                        "{kLoadB, 2}, {kLoadB, 3}, {kDmaA, 1},"),
     # the first stage's wait counted one load too many
-    "start_plus_one": ("  return loads_after<kLA>(seq, n, Load{true, 0});\n}",
-                       "  return loads_after<kLA>(seq, n, Load{true, 0}) + 1;\n}"),
+    "start_plus_one": ("  return loads_after<kLA, kLB>(seq, n, Load{true, 0});\n}",
+                       "  return loads_after<kLA, kLB>(seq, n, Load{true, 0}) + 1;\n}"),
     # a k-step that issues the next B slice before waiting for its own: the derived counts
     # change, and the documented numbers no longer match
     "step_order": ("{kLgkm0, 0}, {kWaitB, 0}, {kReadA, 1}, {kLoadBNext, 0}, {kMfma, 0},",
