@@ -75,7 +75,8 @@ __device__ __forceinline__ void for_each_op(F&& f, std::integer_sequence<int, I.
 //   kLA      A DMA instructions per k-step and wave
 //   kAReads  LDS read instructions per load_a (for the scheduling groups)
 //   kLB, kNA B and A fragments per slice: 4 and 4 for a wave's 128 x 128 of the 2 x 2
-//            layout, 2 and 8 for its 256 x 64 of the 1 x 4 one
+//            layout, 2 and 8 for its 256 x 64 of the 1 x 4 one (2 and 4 for a tile of at
+//            most 128 rows)
 //   bsrc[j]  this lane's 16 bytes of B fragment j, slice 0 of k-step 0: slice s of k-step kt
 //            is at bsrc[j] + 2048 kt elements + 1024 s bytes (the packed layout)
 //   load_a(stage, kk, FragA&)  the wave's A fragments of slice kk from an LDS stage
@@ -84,7 +85,7 @@ __device__ __forceinline__ void for_each_op(F&& f, std::integer_sequence<int, I.
 // lane's accumulators then hold four consecutive columns j of one row i).
 template <int kLA, int kAReads, int kLB = 4, int kNA = 4>
 struct PackedKLoop {
-  static_assert(kLB * kNA == 16, "16 MFMAs per slice: 256 accumulator registers");
+  static_assert(kLB * kNA <= 16, "at most 16 MFMAs per slice: 256 accumulator registers");
   static_assert(kloop::tile_mismatches<kLA, kLB>() == 0 && kloop::counts_fit<kLA, kLB>(),
                 "k-loop wait counts disagree with the issue order");
   bf16x8 bv[8][kLB];          // ring of eight k slices of B fragments (at most five live)
