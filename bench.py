@@ -483,7 +483,8 @@ def backward_bench(args, cfg, layer, x):
 
 def measured_peaks(stream):
     """What this device sustains, from the library's probes (libmoe_peaks.so): an MFMA-only
-    loop (bf16 v_mfma_f32_32x32x16, no memory traffic; 4 blocks of 4 waves per CU) and a
+    loop (bf16 v_mfma_f32_32x32x16, no memory traffic) at the packed GEMMs' occupancy, one
+    block of 4 waves per CU (one wave per SIMD; 4 blocks per CU sustain ~15% less), and a
     1 GiB device-to-device streaming copy (bytes read + written). None if not built."""
     import ctypes
     import torch
@@ -495,7 +496,7 @@ def measured_peaks(stream):
     lib.moe_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                   ctypes.c_void_p]
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    blocks, iters = 4 * cus, 4000
+    blocks, iters = cus, 16000
     sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
     nbytes = 1 << 30
     src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")

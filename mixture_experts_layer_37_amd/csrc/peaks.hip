@@ -14,7 +14,9 @@ using moe::u32x4;
 
 // Each wave runs 8 independent accumulation chains of v_mfma_f32_32x32x16_bf16 on register
 // operands (no memory traffic in the loop); 8 chains keep the MFMA pipe busy despite the
-// dependent-issue latency of each chain.
+// dependent-issue latency of each chain. Launched with one block (one wave per SIMD) per CU,
+// as the packed GEMMs run, it issues at ~96% of the nominal per-cycle rate; more waves per
+// SIMD contend and sustain less.
 __global__ __launch_bounds__(256) void peak_mfma_kernel(float* __restrict__ sink, int iters) {
   const int lane = threadIdx.x & 63;
   bf16x8 a, b;
