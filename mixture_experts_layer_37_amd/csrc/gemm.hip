@@ -62,39 +62,88 @@ constexpr int kXcds = 8;
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
-// Per-expert tile starts for tiles of BMt rows x NT column tiles; returns total tiles.
-// Uses s_start[0..E] and s_off[0..E] in LDS; 256 threads, E <= 256. Offsets are clamped
-// to [0, max_rows] and empty ranges count as empty, so no offsets content can send a tile
-// outside the row buffers.
-template <int BMt>
+// Tile order of the grouped GEMMs. Each expert owns ceil(rows / BMt) * NT tiles, n-tile
+// major, m-tile minor. Experts fall into two classes: "wide" ones, and "small" ones whose
+// rows fit in 128 (one m-tile: their tiles stream the expert's weights for few rows, while
+// a wide expert's tiles are MFMA-bound and share weight panels across m-tiles through L2).
+// The tile list holds the wide experts' tiles first (experts in index order), then the
+// small ones'. A launch takes its tiles in rounds of the grid, XCD x the x-th run of `run`
+// tiles of each round, one tile per block; the merged order below gives, while both classes
+// last, XCD x the wide class in rounds r with r + x even and the small class in the others.
+// So in every round half the XCDs stream weights while the others run MFMAs, and every block
+// takes both classes in turn (a fixed class per XCD left half the chip idle at the end).
+// With no small expert (or no wide one) the merged order is the list order.
+constexpr int kSmallRows = 128;
+
+// Per-expert tile starts in that list; returns the total. s_perm[slot] is the expert in
+// list slot `slot`, s_start[slot] its first tile, n_wide the wide experts' tiles (the
+// second part starts there). Uses s_start, s_perm, s_off [0..E] and s_wsum[4] in LDS; 256
+// threads, E <= 256. Offsets are clamped to [0, max_rows] and empty ranges count as empty,
+// so no offsets content can send a tile outside the row buffers. kClasses = false keeps
+// every expert in the first part (index order, no merge).
+template <int BMt, bool kClasses>
 __device__ __forceinline__ int build_tile_starts(const int32_t* __restrict__ offsets, int E,
                                                  int NT, int max_rows, int* s_start,
-                                                 int* s_off, int* s_wsum) {
+                                                 int* s_perm, int* s_off, int* s_wsum,
+                                                 int& n_wide) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  int tiles = 0;
+  // exclusive scan of v over the block's 256 threads (4 waves)
+  auto block_scan = [&](int v, int& total) {
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int n = __shfl_up(incl, o);
+      if (lane >= o) incl += n;
+    }
+    if (lane == 63) s_wsum[wave] = incl;
+    __syncthreads();
+    int pre = 0;
+    for (int w = 0; w < wave; ++w) pre += s_wsum[w];
+    total = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
+    __syncthreads();
+    return incl + pre - v;
+  };
   for (int i = tid; i <= E; i += blockDim.x) s_off[i] = min(max(offsets[i], 0), max_rows);
   __syncthreads();
+  const int m = tid < E ? max(s_off[tid + 1] - s_off[tid], 0) : 0;
+  const int small = (kClasses && tid < E && m > 0 && m <= kSmallRows) ? 1 : 0;
+  int n_small = 0;
+  const int small_before = block_scan(small, n_small);
+  if (tid < E) s_perm[small ? (E - n_small) + small_before : tid - small_before] = tid;
+  __syncthreads();
+  int tiles = 0;
   if (tid < E) {
-    const int m = max(s_off[tid + 1] - s_off[tid], 0);
-    tiles = ((m + BMt - 1) / BMt) * NT;
+    const int e = s_perm[tid];
+    const int me = max(s_off[e + 1] - s_off[e], 0);
+    tiles = ((me + BMt - 1) / BMt) * NT;
   }
-  int incl = tiles;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int n = __shfl_up(incl, o);
-    if (lane >= o) incl += n;
-  }
-  if (lane == 63) s_wsum[wave] = incl;
+  int total = 0;
+  const int before = block_scan(tiles, total);
+  if (tid < E) s_start[tid] = before;
+  if (tid == 0) s_start[E] = total;
   __syncthreads();
-  int pre = 0;
-  for (int w = 0; w < wave; ++w) pre += s_wsum[w];
-  if (tid < E) s_start[tid + 1] = incl + pre;
-  if (tid == 0) s_start[0] = 0;
-  __syncthreads();
-  return s_start[E];
+  n_wide = __builtin_amdgcn_readfirstlane(s_start[E - n_small]);   // the small part's start
+  return __builtin_amdgcn_readfirstlane(total);
 }
 
-// Largest e in [0, E) with s_start[e] <= tile (experts without tiles have equal starts).
+// List index of merged position p. Runs of `run` tiles, kXcds runs per round: for rounds
+// r < R the run of XCD x is the (4 r + x / 2)-th run of the wide part [0, nw) if r + x is
+// even, else that run of the small part [nw, total); R = the whole rounds both parts can
+// fill. Then the rest of the wide part, then the rest of the small part.
+__device__ __forceinline__ int merged_tile(int p, int nw, int total, int run) {
+  constexpr int kHalf = kXcds / 2;
+  const int R = min(nw / (kHalf * run), (total - nw) / (kHalf * run));
+  if (p < kXcds * run * R) {
+    const int c = p / run, o = p - c * run;
+    const int r = c / kXcds, x = c - r * kXcds;
+    const int idx = (kHalf * r + (x >> 1)) * run + o;
+    return ((r + x) & 1) ? nw + idx : idx;
+  }
+  const int q = p - kXcds * run * R, rest_w = nw - kHalf * run * R;
+  return q < rest_w ? kHalf * run * R + q : nw + kHalf * run * R + (q - rest_w);
+}
+
+// Largest slot in [0, E) with s_start[slot] <= tile (experts without tiles have equal starts).
 __device__ __forceinline__ int find_expert(const int* s_start, int E, int tile) {
   int lo = 0, hi = E - 1;
   while (lo < hi) {
@@ -108,14 +157,18 @@ __device__ __forceinline__ int find_expert(const int* s_start, int E, int tile) 
 struct TileCoord {
   int e, row0, mrows, n_t;
 };
-__device__ __forceinline__ TileCoord decode_tile(const int* s_start, const int* s_off, int E,
-                                                 int tile, int BMt) {
+// The tile at merged position p.
+__device__ __forceinline__ TileCoord decode_tile(const int* s_start, const int* s_perm,
+                                                 const int* s_off, int E, int nw, int total,
+                                                 int run, int p, int BMt) {
   TileCoord t;
-  t.e = find_expert(s_start, E, tile);
+  const int tile = merged_tile(p, nw, total, run);
+  const int slot = find_expert(s_start, E, tile);
+  t.e = s_perm[slot];
   const int row_beg = s_off[t.e];
   const int m_e = s_off[t.e + 1] - row_beg;   // > 0: the expert owns this tile
   const int mt_e = (m_e + BMt - 1) / BMt;
-  const int rem = tile - s_start[t.e];
+  const int rem = tile - s_start[slot];
   t.n_t = rem / mt_e;
   const int m_t = rem - t.n_t * mt_e;
   t.row0 = row_beg + m_t * BMt;
@@ -211,6 +264,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) bf16_t stage0[kStage];
   __shared__ __attribute__((aligned(1024))) bf16_t stage1[kStage];
   __shared__ int s_start[kMaxExperts + 1];
+  __shared__ int s_perm[kMaxExperts];
   __shared__ int s_off[kMaxExperts + 1];
   __shared__ int s_wsum[4];
 
@@ -226,7 +280,9 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   const size_t ldc = kPairOut ? 2 * (size_t)N : (size_t)N;
   const size_t ldaux = (EPI == EPI_SWIGLU_BWD) ? 2 * (size_t)N : (size_t)N;
   const int NT = N / OUTN;
-  const int total = build_tile_starts<BM>(offsets, E, NT, max_rows, s_start, s_off, s_wsum);
+  int n_wide = 0;
+  const int total =
+      build_tile_starts<BM, true>(offsets, E, NT, max_rows, s_start, s_perm, s_off, s_wsum, n_wide);
 
   const int xcd = blockIdx.x % kXcds, li = blockIdx.x / kXcds;
   const int nper = gridDim.x / kXcds;
@@ -301,7 +357,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   // each gets its own register allocation.
   auto run_tile = [&](int tile, int kb, int ke, float* part, auto slice) {
     constexpr bool kSlice = decltype(slice)::value;
-    const TileCoord tc = decode_tile(s_start, s_off, E, __builtin_amdgcn_readfirstlane(tile), BM);
+    const TileCoord tc = decode_tile(s_start, s_perm, s_off, E, n_wide, total, nper,
+                                      __builtin_amdgcn_readfirstlane(tile), BM);
     const int e = __builtin_amdgcn_readfirstlane(tc.e);
     const int n_t = __builtin_amdgcn_readfirstlane(tc.n_t);
     const int row0 = __builtin_amdgcn_readfirstlane(tc.row0);
@@ -637,14 +694,18 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
                                                             bf16_t* __restrict__ C, int E, int K,
                                                             int N, int max_rows, int grid) {
   __shared__ int s_start[kMaxExperts + 1];
+  __shared__ int s_perm[kMaxExperts];
   __shared__ int s_off[kMaxExperts + 1];
   __shared__ int s_wsum[4];
-  const int total = build_tile_starts<BM>(offsets, E, N / 256, max_rows, s_start, s_off, s_wsum);
+  int n_wide = 0;
+  const int total = build_tile_starts<BM, true>(offsets, E, N / 256, max_rows, s_start, s_perm,
+                                                s_off, s_wsum, n_wide);
   const SplitPlan plan = split_plan(total, grid, K / BK, true);
   const int tid = threadIdx.x;
   for (int w = blockIdx.x; w < plan.tail * (BM / 8); w += gridDim.x) {
     const int ti = w / (BM / 8);
-    const TileCoord tc = decode_tile(s_start, s_off, E, plan.full + ti, BM);
+    const TileCoord tc = decode_tile(s_start, s_perm, s_off, E, n_wide, total, grid / kXcds,
+                                      plan.full + ti, BM);
     const int r = (w % (BM / 8)) * 8 + (tid >> 5);
     if (r >= tc.mrows) continue;
     const int c8 = (tid & 31) * 8;
@@ -782,6 +843,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
   __shared__ __attribute__((aligned(1024))) bf16_t sa0[BM * BK];
   __shared__ __attribute__((aligned(1024))) bf16_t sa1[BM * BK];
   __shared__ int s_start[kMaxExperts + 1];
+  __shared__ int s_perm[kMaxExperts];
   __shared__ int s_off[kMaxExperts + 1];
   __shared__ int s_wsum[4];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -789,7 +851,9 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
   constexpr bool kTwoMat = EPI == EPI_SWIGLU;
   constexpr int OUTN = kTwoMat ? 128 : 256;
   const int NT = N / OUTN, NB = N / 32, KS = K / 16;
-  const int total = build_tile_starts<BM>(offsets, E, NT, max_rows, s_start, s_off, s_wsum);
+  int n_wide = 0;
+  const int total =
+      build_tile_starts<BM, true>(offsets, E, NT, max_rows, s_start, s_perm, s_off, s_wsum, n_wide);
   const int xcd = blockIdx.x % kXcds, li = blockIdx.x / kXcds;
   const int nper = gridDim.x / kXcds;
   const int KT = K / BK;
@@ -838,7 +902,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
     // for each tile rather than hoisted and held across the k-loop
     int lane = threadIdx.x & 63;
     asm volatile("" : "+v"(lane));
-    const TileCoord tc = decode_tile(s_start, s_off, E, __builtin_amdgcn_readfirstlane(tile), BM);
+    const TileCoord tc = decode_tile(s_start, s_perm, s_off, E, n_wide, total, nper,
+                                      __builtin_amdgcn_readfirstlane(tile), BM);
     r.e = __builtin_amdgcn_readfirstlane(tc.e);
     r.n_t = __builtin_amdgcn_readfirstlane(tc.n_t);
     r.row0 = __builtin_amdgcn_readfirstlane(tc.row0);
@@ -1222,14 +1287,18 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
     const float* __restrict__ W1, float* __restrict__ C, int E, int K, int N, int max_rows) {
   __shared__ float As[FT][FT + 1], B0[FT][FT + 1], B1[FT][FT + 1];
   __shared__ int s_start[kMaxExperts + 1];
+  __shared__ int s_perm[kMaxExperts];
   __shared__ int s_off[kMaxExperts + 1];
   __shared__ int s_wsum[4];
-  const int total = build_tile_starts<FT>(offsets, E, 1, max_rows, s_start, s_off, s_wsum);
+  int n_wide = 0;
+  const int total = build_tile_starts<FT, false>(offsets, E, 1, max_rows, s_start, s_perm, s_off,
+                                                 s_wsum, n_wide);
   const int tile = blockIdx.x;
   if (tile >= total) return;
-  const int e = find_expert(s_start, E, tile);
+  const int slot = find_expert(s_start, E, tile);   // list order is expert order here
+  const int e = s_perm[slot];
   const int row_beg = s_off[e], m_e = s_off[e + 1] - row_beg;
-  const int m_t = tile - s_start[e];
+  const int m_t = tile - s_start[slot];
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   const int row = m_t * FT + ty;            // within the expert
   const int col = blockIdx.y * FT + tx;
