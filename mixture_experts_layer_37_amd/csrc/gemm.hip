@@ -895,6 +895,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
   struct TileRows {
     int e, n_t, row0, mrows;
     int alone;   // the expert has at most 128 rows: this is its only m-tile
+    int tiny;    // ... and at most 64
     int arow[8];
   };
   auto tile_rows = [&](int tile, TileRows& r) {
@@ -908,7 +909,9 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
     r.n_t = __builtin_amdgcn_readfirstlane(tc.n_t);
     r.row0 = __builtin_amdgcn_readfirstlane(tc.row0);
     r.mrows = __builtin_amdgcn_readfirstlane(tc.mrows);
-    r.alone = __builtin_amdgcn_readfirstlane(s_off[r.e + 1] - s_off[r.e]) <= 128;
+    const int rows_e = __builtin_amdgcn_readfirstlane(s_off[r.e + 1] - s_off[r.e]);
+    r.alone = rows_e <= 128;
+    r.tiny = rows_e <= 64;
     // all eight row-map loads in flight together, then clamped
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -1049,9 +1052,11 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
   // One tile at a time: its loads, k-loop and epilogue (the single-matrix epilogues stage
   // their output through the two A stages, so the next tile's DMA waits for them).
   // The tile of an expert with at most 128 rows runs the same loads, waits and barriers
-  // with only the first 4 A fragments: half the MFMAs and fragment reads, no accumulator for
-  // rows that are all padding. Each row class is its own instantiation of the k-loop, so
-  // neither carries a branch inside it. (An expert's last, partial m-tile beside full ones
+  // with only the first 4 A fragments (at most 64 rows: the first 2): a half (a quarter) of
+  // the MFMAs and fragment reads, no accumulator for rows that are all padding. Each row
+  // class is its own instantiation of the k-loop, so none carries a branch inside it. The
+  // quarter class pays where small-expert tiles run beside large-expert ones (GEMM 2 of the
+  // 32-expert workload 3-4% faster). (An expert's last, partial m-tile beside full ones
   // stays on the full path: finishing early, it pulled its block out of step with the
   // blocks sharing its weight panel through L2, measured 2-4% slower on Mixtral.)
   auto run_rows = [&](const TileSrc& t, int kb, int ke, float* part, auto slice, auto na) {
@@ -1072,7 +1077,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
     TileSrc t;
     tile_src(r, t);
     if (!r.alone) run_rows(t, kb, ke, part, slice, std::integral_constant<int, kNA>{});
-    else run_rows(t, kb, ke, part, slice, std::integral_constant<int, kNA / 2>{});
+    else if (!r.tiny) run_rows(t, kb, ke, part, slice, std::integral_constant<int, kNA / 2>{});
+    else run_rows(t, kb, ke, part, slice, std::integral_constant<int, kNA / 4>{});
   };
 
   for (int base = 0; base < plan.full; base += gridDim.x) {

@@ -166,6 +166,55 @@ def test_packed_gemms_are_bit_identical(activation):
     assert np.isfinite(hf).all()
 
 
+# Experts of every row class (none; at most 64 rows; at most 128; more), enough of the
+# small ones and of the large ones' m-tiles that, at a 256-block grid, both GEMMs take tiles
+# in the merged order that alternates the two classes by round and XCD (GEMM 1: 306 tiles of
+# each class; GEMM 2: 136 of each, 16 of them in the split-K tail).
+MIXED_ROWS = [0, 1, 2, 5, 7, 17, 31, 32, 33, 50, 63, 64, 65, 90, 100, 120, 127, 128,
+              129, 255, 256, 257, 384, 600, 700, 1000]
+
+
+def test_interleaved_tile_order_matches_oracle():
+    """Both GEMMs over experts of all row classes, outputs pre-filled with NaN: every row of
+    h and y written, packed and plain kernels bit-identical, y against the oracle's FFN."""
+    import oracle as O
+    from mixture_experts_layer_37_amd.inputs import as_float
+    E, T = len(MIXED_ROWS), sum(MIXED_ROWS)
+    cfg = C.SMALL.with_(name="mixed_rows", tokens=T, hidden=2048, inter=2304, experts=E,
+                        top_k=1, bias=None)
+    print(f"[case] interleaved tile order rows {MIXED_ROWS}", flush=True)
+    inp = make_inputs(cfg, seed=21)
+    layer = MoELayer(cfg.with_(weights="packed"), inp)
+    x = to_device(cfg, inp["x"])
+    offs_np = np.concatenate([[0], np.cumsum(MIXED_ROWS)]).astype(np.int32)
+    offs = torch.from_numpy(offs_np).cuda()
+    I, H = cfg.inter, cfg.hidden
+    out = {}
+    for tag, c, wg, wu, wd in (("plain", layer.c_plain, layer.w_gate, layer.w_up, layer.w_down),
+                               ("packed", layer.c, layer.fw_gate, layer.fw_up, layer.fw_down)):
+        h = torch.full((T, I), float("nan"), dtype=x.dtype, device="cuda")
+        y1 = torch.full((T, H), float("nan"), dtype=x.dtype, device="cuda")
+        y2 = torch.full((T, H), float("nan"), dtype=x.dtype, device="cuda")
+        L.moe_expert_up(c, x, offs, wg, wu, h)
+        L.moe_expert_down(c, h, offs, wd, y1, layer.ws)     # split-K tail
+        L.moe_expert_down(c, h, offs, wd, y2)               # every tile whole
+        out[tag] = (h, y1, y2)
+    torch.cuda.synchronize()
+    for a, b, what in zip(out["plain"], out["packed"], ("h", "y (split)", "y")):
+        assert torch.equal(bits(a), bits(b)), what
+    x32 = as_float(cfg, inp["x"]).astype(np.float64)
+    wg, wu, wd = P.oracle_weights(cfg, inp)
+    for y in out["packed"][1:]:
+        got = P.decode(cfg, y)
+        assert np.isfinite(got).all(), "a row of y was not written"
+        ref = np.zeros_like(got)
+        for e in range(E):
+            r0, r1 = int(offs_np[e]), int(offs_np[e + 1])
+            if r1 > r0:
+                ref[r0:r1] = O.expert_ffn(x32[r0:r1], wg[e], wu[e], wd[e], cfg.activation)
+        P.assert_layer_close(got, ref, "y")
+
+
 PACKED_CASES = {
     "bf16_ragged": C.SMALL.with_(name="bf16_ragged", tokens=2000, hidden=512, inter=768),
     "bf16_gelu": C.SMALL.with_(name="bf16_gelu", tokens=600, hidden=256, inter=512,
