@@ -73,7 +73,24 @@ __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 // So in every round half the XCDs stream weights while the others run MFMAs, and every block
 // takes both classes in turn (a fixed class per XCD left half the chip idle at the end).
 // With no small expert (or no wide one) the merged order is the list order.
+//
+// Paired ragged ends (kPairs; GEMM 1 with SwiGLU on packed weights): a wide expert whose
+// last m-tile holds at most 128 rows gives that m-tile one tile per PAIR of n-tiles, 128
+// rows by both n-tiles' columns: the MFMAs of a full tile, so it ends with the blocks that
+// share its weight panels, where a half-height tile per n-tile ended early and pulled its
+// block out of step with them. Within the expert, n-tile pair q holds the full-height
+// m-tiles of n-tile 2q, those of 2q + 1, then the pair tile; an odd last n-tile keeps a
+// half-height tile of its own.
 constexpr int kSmallRows = 128;
+
+// Tiles of one expert of m rows: one per m-tile and n-tile, except for a paired ragged end.
+template <int BMt, bool kPairs>
+__device__ __forceinline__ int expert_tiles(int m, int NT) {
+  if (!kPairs || m <= kSmallRows) return ((m + BMt - 1) / BMt) * NT;
+  const int rem = m % BMt;
+  const int mw = m / BMt + (rem > kSmallRows ? 1 : 0);   // full-height m-tiles
+  return mw * NT + (rem > 0 && rem <= kSmallRows ? (NT + 1) / 2 : 0);
+}
 
 // Per-expert tile starts in that list; returns the total. s_perm[slot] is the expert in
 // list slot `slot`, s_start[slot] its first tile, n_wide the wide experts' tiles (the
@@ -81,7 +98,7 @@ constexpr int kSmallRows = 128;
 // threads, E <= 256. Offsets are clamped to [0, max_rows] and empty ranges count as empty,
 // so no offsets content can send a tile outside the row buffers. kClasses = false keeps
 // every expert in the first part (index order, no merge).
-template <int BMt, bool kClasses>
+template <int BMt, bool kClasses, bool kPairs = false>
 __device__ __forceinline__ int build_tile_starts(const int32_t* __restrict__ offsets, int E,
                                                  int NT, int max_rows, int* s_start,
                                                  int* s_perm, int* s_off, int* s_wsum,
@@ -115,7 +132,7 @@ __device__ __forceinline__ int build_tile_starts(const int32_t* __restrict__ off
   if (tid < E) {
     const int e = s_perm[tid];
     const int me = max(s_off[e + 1] - s_off[e], 0);
-    tiles = ((me + BMt - 1) / BMt) * NT;
+    tiles = expert_tiles<BMt, kPairs>(me, NT);
   }
   int total = 0;
   const int before = block_scan(tiles, total);
@@ -153,24 +170,43 @@ __device__ __forceinline__ int find_expert(const int* s_start, int E, int tile) 
   return lo;
 }
 
-// Where a tile sits: its expert, first row, valid rows and n-tile.
+// Where a tile sits: its expert, first row, valid rows and n-tile (pair: n-tiles n_t and
+// n_t + 1, at most 128 rows).
 struct TileCoord {
-  int e, row0, mrows, n_t;
+  int e, row0, mrows, n_t, pair;
 };
-// The tile at merged position p.
+// The tile at merged position p (NT: n-tiles per m-tile).
+template <bool kPairs = false>
 __device__ __forceinline__ TileCoord decode_tile(const int* s_start, const int* s_perm,
                                                  const int* s_off, int E, int nw, int total,
-                                                 int run, int p, int BMt) {
+                                                 int run, int p, int BMt, int NT) {
   TileCoord t;
   const int tile = merged_tile(p, nw, total, run);
   const int slot = find_expert(s_start, E, tile);
   t.e = s_perm[slot];
   const int row_beg = s_off[t.e];
   const int m_e = s_off[t.e + 1] - row_beg;   // > 0: the expert owns this tile
-  const int mt_e = (m_e + BMt - 1) / BMt;
   const int rem = tile - s_start[slot];
-  t.n_t = rem / mt_e;
-  const int m_t = rem - t.n_t * mt_e;
+  t.pair = 0;
+  int m_t;
+  const int ragged = m_e % BMt;
+  if (!kPairs || m_e <= kSmallRows || ragged == 0 || ragged > kSmallRows) {
+    const int mt_e = (m_e + BMt - 1) / BMt;
+    t.n_t = rem / mt_e;
+    m_t = rem - t.n_t * mt_e;
+  } else {
+    const int mw = m_e / BMt;            // full-height m-tiles; the ragged end is m-tile mw
+    const int blk = 2 * mw + 1;          // tiles of one n-tile pair
+    const int q = rem / blk, o = rem - q * blk;
+    if (q < NT / 2) {
+      t.n_t = 2 * q + (o < 2 * mw ? o / mw : 0);
+      m_t = o < 2 * mw ? o % mw : mw;
+      t.pair = o >= 2 * mw;
+    } else {                             // the odd last n-tile: its m-tiles, then its end
+      t.n_t = NT - 1;
+      m_t = o;
+    }
+  }
   t.row0 = row_beg + m_t * BMt;
   t.mrows = min(BMt, m_e - m_t * BMt);
   return t;
@@ -358,7 +394,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   auto run_tile = [&](int tile, int kb, int ke, float* part, auto slice) {
     constexpr bool kSlice = decltype(slice)::value;
     const TileCoord tc = decode_tile(s_start, s_perm, s_off, E, n_wide, total, nper,
-                                      __builtin_amdgcn_readfirstlane(tile), BM);
+                                      __builtin_amdgcn_readfirstlane(tile), BM, NT);
     const int e = __builtin_amdgcn_readfirstlane(tc.e);
     const int n_t = __builtin_amdgcn_readfirstlane(tc.n_t);
     const int row0 = __builtin_amdgcn_readfirstlane(tc.row0);
@@ -705,7 +741,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   for (int w = blockIdx.x; w < plan.tail * (BM / 8); w += gridDim.x) {
     const int ti = w / (BM / 8);
     const TileCoord tc = decode_tile(s_start, s_perm, s_off, E, n_wide, total, grid / kXcds,
-                                      plan.full + ti, BM);
+                                      plan.full + ti, BM, N / 256);
     const int r = (w % (BM / 8)) * 8 + (tid >> 5);
     if (r >= tc.mrows) continue;
     const int c8 = (tid & 31) * 8;
@@ -849,11 +885,12 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   constexpr bool kTwoMat = EPI == EPI_SWIGLU;
+  constexpr bool kPairs = EPI == EPI_SWIGLU;   // paired ragged ends (no split-K here)
   constexpr int OUTN = kTwoMat ? 128 : 256;
   const int NT = N / OUTN, NB = N / 32, KS = K / 16;
   int n_wide = 0;
-  const int total =
-      build_tile_starts<BM, true>(offsets, E, NT, max_rows, s_start, s_perm, s_off, s_wsum, n_wide);
+  const int total = build_tile_starts<BM, true, kPairs>(offsets, E, NT, max_rows, s_start, s_perm,
+                                                        s_off, s_wsum, n_wide);
   const int xcd = blockIdx.x % kXcds, li = blockIdx.x / kXcds;
   const int nper = gridDim.x / kXcds;
   const int KT = K / BK;
@@ -886,16 +923,20 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
   struct TileSrc {
     int n_t, row0, mrows;
     const char* a_src[8];
-    const bf16_t* bsrc[kNB];
+    const bf16_t* bsrc[2 * kNB];   // a pair tile: both n-tiles' fragments
   };
   // A tile's coordinates and the token rows of its 8 A DMA loads per wave (rows past the
   // expert's end re-read its last row, never written back; with the gather fused in, rows
   // of x through row_token, clamped into [0, a_rows)). The row-map loads are the only
   // global loads here.
+  // Row classes: full height (8 A fragments); half (4) and quarter (2) height for a tile
+  // whose rows are all of an expert of at most 128 and 64 rows (and, with paired ragged
+  // ends, for the ragged end of an odd last n-tile); a pair tile (4 A fragments by both
+  // n-tiles' weight fragments).
+  enum { kFull = 0, kHalfRows = 1, kQuarterRows = 2, kPairTile = 3 };
   struct TileRows {
     int e, n_t, row0, mrows;
-    int alone;   // the expert has at most 128 rows: this is its only m-tile
-    int tiny;    // ... and at most 64
+    int cls;
     int arow[8];
   };
   auto tile_rows = [&](int tile, TileRows& r) {
@@ -903,15 +944,21 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
     // for each tile rather than hoisted and held across the k-loop
     int lane = threadIdx.x & 63;
     asm volatile("" : "+v"(lane));
-    const TileCoord tc = decode_tile(s_start, s_perm, s_off, E, n_wide, total, nper,
-                                      __builtin_amdgcn_readfirstlane(tile), BM);
+    const TileCoord tc = decode_tile<kPairs>(s_start, s_perm, s_off, E, n_wide, total, nper,
+                                              __builtin_amdgcn_readfirstlane(tile), BM, NT);
     r.e = __builtin_amdgcn_readfirstlane(tc.e);
     r.n_t = __builtin_amdgcn_readfirstlane(tc.n_t);
     r.row0 = __builtin_amdgcn_readfirstlane(tc.row0);
     r.mrows = __builtin_amdgcn_readfirstlane(tc.mrows);
     const int rows_e = __builtin_amdgcn_readfirstlane(s_off[r.e + 1] - s_off[r.e]);
-    r.alone = rows_e <= 128;
-    r.tiny = rows_e <= 64;
+    // the rows that decide the height: the expert's if it has a single m-tile; with paired
+    // ragged ends, the tile's (the ragged end of an odd last n-tile)
+    const int hrows = (kPairs && rows_e > kSmallRows) ? r.mrows : rows_e;
+    r.cls = (kPairs && tc.pair) ? kPairTile
+            : hrows <= 64       ? kQuarterRows
+            : hrows <= 128      ? kHalfRows
+                                : kFull;
+    r.cls = __builtin_amdgcn_readfirstlane(r.cls);
     // all eight row-map loads in flight together, then clamped
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -937,13 +984,15 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
       t.a_src[i] = (const char*)(A + (size_t)r.arow[i] * K) + c * 16;
     }
     // B fragment j of k slice s: this lane's 16 bytes of block (nb_j, s). SwiGLU: j = 0 the
-    // gate block, j = 1 the up block of the same 32 output columns.
+    // gate block, j = 1 the up block of the same 32 output columns (a pair tile: j = 2, 3
+    // the same for n-tile n_t + 1).
 #pragma unroll
-    for (int j = 0; j < kNB; ++j) {
+    for (int j = 0; j < 2 * kNB; ++j) {
       const bf16_t* P;
       int nb;
-      if (kTwoMat) { P = j == 0 ? P0 : P1; nb = r.n_t * 4 + wn; }
-      else { P = P0; nb = r.n_t * 8 + wn * 2 + j; }
+      if (kTwoMat) { P = (j & 1) == 0 ? P0 : P1; nb = (r.n_t + (j >> 1)) * 4 + wn; }
+      else { P = P0; nb = r.n_t * 8 + wn * 2 + (j & 1); }
+      if (j >= kNB && !(kPairs && r.cls == kPairTile)) nb = 0;   // not loaded
       t.bsrc[j] = P + ((size_t)r.e * NB + nb) * KS * 512 + lane * 8;
     }
   };
@@ -1071,13 +1120,41 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
     packed_kloop<kLA, NA, kNB, NA>(kb, ke, sa0, sa1, t.bsrc, acc, load_a, dma_for(t));
     epilogue(acc, t.n_t, t.row0, t.mrows, part, slice);
   };
+  // A pair tile: 4 A fragments by 4 weight fragments per slice (the k-loop's 2 x 2 form,
+  // the MFMAs of a full tile), then each n-tile's outputs through the SwiGLU epilogue.
+  auto run_pair = [&](const TileSrc& t, int kb, int ke) {
+    f32x16 acc[kNA / 2][2 * kNB];
+#pragma unroll
+    for (int i = 0; i < kNA / 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2 * kNB; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    packed_kloop<kLA, kNA / 2, 2 * kNB, kNA / 2>(kb, ke, sa0, sa1, t.bsrc, acc, load_a,
+                                                  dma_for(t));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      f32x16 half[kNA / 2][kNB];
+#pragma unroll
+      for (int i = 0; i < kNA / 2; ++i)
+#pragma unroll
+        for (int j = 0; j < kNB; ++j) half[i][j] = acc[i][h * kNB + j];
+      epilogue(half, t.n_t + h, t.row0, t.mrows, nullptr, std::false_type{});
+    }
+  };
   auto run_tile = [&](int tile, int kb, int ke, float* part, auto slice) {
     TileRows r;
     tile_rows(tile, r);
     TileSrc t;
     tile_src(r, t);
-    if (!r.alone) run_rows(t, kb, ke, part, slice, std::integral_constant<int, kNA>{});
-    else if (!r.tiny) run_rows(t, kb, ke, part, slice, std::integral_constant<int, kNA / 2>{});
+    if constexpr (kPairs) {
+      if (r.cls == kPairTile) {
+        run_pair(t, kb, ke);
+        return;
+      }
+    }
+    if (r.cls == kFull) run_rows(t, kb, ke, part, slice, std::integral_constant<int, kNA>{});
+    else if (r.cls == kHalfRows) run_rows(t, kb, ke, part, slice, std::integral_constant<int, kNA / 2>{});
     else run_rows(t, kb, ke, part, slice, std::integral_constant<int, kNA / 4>{});
   };
 
