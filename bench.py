@@ -203,40 +203,58 @@ def run_workload(name, args, steps, warmup, headline, peaks=None):
     y = torch.empty((T * k, H), dtype=edt, device=dev)
     out = torch.empty_like(x)
     stream = torch.cuda.current_stream()
-    names = ["route", "permute", "gemm_up", "gemm_down", "combine"]
+    names = ["route_permute", "gemm_up", "gemm_down", "combine"]
     packed = cfg.weights == "packed"
 
     def step(ev=None, plain=False):
-        # the path moe_forward runs: the permute writes the row maps only and GEMM 1 reads
-        # the token rows in place through them
+        # the path moe_forward runs: route and the permutation's row maps in one call (the
+        # count step inside the streaming router), then GEMM 1 reading the token rows in
+        # place through the maps
         cw = layer.c_plain if plain else c
         wg, wu, wd = ((layer.w_gate, layer.w_up, layer.w_down) if plain or not packed
                       else (layer.fw_gate, layer.fw_up, layer.fw_down))
         if ev: ev[0].record(stream)
-        L.moe_route(cw, x, layer.w_router if plain else layer.fw_router, layer.bias, logits,
-                    idx, w, ws, stream)
+        L.moe_route_permute(cw, x, layer.w_router if plain else layer.fw_router, layer.bias,
+                            logits, idx, w, counts, offs, rt, sr, ws, stream)
         if ev: ev[1].record(stream)
-        L.moe_permute(cw, x, idx, None, counts, offs, rt, sr, ws, stream)
-        if ev: ev[2].record(stream)
         L.moe_expert_up_rows(cw, x, rt, offs, wg, wu, h, stream)
-        if ev: ev[3].record(stream)
+        if ev: ev[2].record(stream)
         L.moe_expert_down(cw, h, offs, wd, y, ws, stream)
-        if ev: ev[4].record(stream)
+        if ev: ev[3].record(stream)
         L.moe_combine(cw, y, sr, w, out, stream)
-        if ev: ev[5].record(stream)
+        if ev: ev[4].record(stream)
 
     def timed_steps(n, plain=False):
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n)]
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+              for _ in range(n)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for s in range(n):
             step(ev[s], plain=plain)
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) * 1e3 / n
-        per_step = [e[0].elapsed_time(e[5]) for e in ev]
+        per_step = [e[0].elapsed_time(e[-1]) for e in ev]
         stages = {nm: float(np.median([e[i].elapsed_time(e[i + 1]) for e in ev])) * 1e3
                   for i, nm in enumerate(names)}
         return wall, per_step, stages
+
+    def route_and_permute_alone(reps=7):
+        """moe_route and moe_permute (row maps) as separate calls, each rep right after a
+        full step (the cache state of the timed steps): median µs of each."""
+        r_us, p_us = [], []
+        for _ in range(reps):
+            step()
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(stream)
+            L.moe_route(c, x, layer.fw_router if packed else layer.w_router, layer.bias, logits,
+                        idx, w, ws, stream)
+            e[1].record(stream)
+            L.moe_permute(c, x, idx, None, counts, offs, rt, sr, ws, stream)
+            e[2].record(stream)
+            torch.cuda.synchronize()
+            r_us.append(e[0].elapsed_time(e[1]) * 1e3)
+            p_us.append(e[1].elapsed_time(e[2]) * 1e3)
+        return float(np.median(r_us)), float(np.median(p_us))
 
     if headline and args.calib_copy_mib > 0:
         nb = args.calib_copy_mib << 20
@@ -255,6 +273,9 @@ def run_workload(name, args, steps, warmup, headline, peaks=None):
     print(f"[bench] {cfg.name}: timing {steps} steps", file=sys.stderr, flush=True)
     wall_ms, per_step, stages_us = timed_steps(steps)
     stats = step_stats(per_step)
+    # the router and the permutation each on its own (moe_route, moe_permute), for their
+    # bandwidth figures; the step runs them as one call (stages_us.route_permute)
+    stages_us["route"], stages_us["permute"] = route_and_permute_alone()
 
     n_kept = int(offs[-1].item())
     up_flops = (4 if cfg.activation == C.SWIGLU else 2) * n_kept * H * I

@@ -168,6 +168,20 @@ moe_status moe_permute(const moe_config* cfg, const void* x, const int32_t* topk
                        int32_t* row_token, int32_t* slot_row, void* ws, size_t ws_bytes,
                        moe_stream_t stream);
 
+/* moe_route followed by moe_permute's row maps (x_perm NULL), as moe_forward runs them,
+ * with the same arguments, meanings and results, bit for bit (gitcode page, routing_module_
+ * then SparseGather's per-expert grouping; lshu.cn page, section 4, the token reordering
+ * after routing). For a bf16 gate of at most 16 experts (the streaming router) the
+ * permutation's count step runs inside the router and the whole takes two launches
+ * instead of three; otherwise it is the two calls one after the other. The device flags
+ * of both steps land where moe_read_device_status reads them (which = 1 and 2).
+ *   x may be NULL (logits an INPUT), as for moe_route */
+moe_status moe_route_permute(const moe_config* cfg, const void* x, const void* w_router,
+                             const float* gate_bias, float* logits, int32_t* topk_idx,
+                             float* topk_w, int32_t* expert_counts, int32_t* expert_offsets,
+                             int32_t* row_token, int32_t* slot_row, void* ws, size_t ws_bytes,
+                             moe_stream_t stream);
+
 /* moe_permute for callers that cannot allocate device memory or hand over a workspace
  * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * the same results as moe_permute, bit for bit, with its scratch (the per-block expert

@@ -28,7 +28,7 @@ MOE_WEIGHT_GATE, MOE_WEIGHT_UP, MOE_WEIGHT_DOWN, MOE_WEIGHT_ROUTER = 0, 1, 2, 3
  MOE_WS_ROW_TOKEN, MOE_WS_X_PERM, MOE_WS_H, MOE_WS_Y_PERM, MOE_WS_AUX_LOSS) = range(11)
 
 EXPORTS = ("moe_workspace_size", "moe_capacity", "moe_route", "moe_permute",
-           "moe_permute_noalloc", "moe_expert_up",
+           "moe_route_permute", "moe_permute_noalloc", "moe_expert_up",
            "moe_expert_up_rows", "moe_expert_down", "moe_grouped_ffn",
            "moe_pack_expert_weight", "moe_packed_weight_bytes", "moe_combine",
            "moe_forward", "moe_forward_train", "moe_backward_workspace_size", "moe_backward",
@@ -71,6 +71,7 @@ def lib():
             "moe_capacity": [cfgp, POINTER(c_int32)],
             "moe_route": [cfgp, vp, vp, vp, vp, vp, vp, vp, c_size_t, vp],
             "moe_permute": [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, c_size_t, vp],
+            "moe_route_permute": [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, c_size_t, vp],
             "moe_permute_noalloc": [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
             "moe_expert_up": [cfgp, vp, vp, vp, vp, vp, vp],
             "moe_expert_up_rows": [cfgp, vp, vp, vp, vp, vp, vp, vp],
@@ -170,6 +171,14 @@ def moe_permute(cfg, x, topk_idx, x_perm, expert_counts, expert_offsets, row_tok
         ctypes.byref(_as_cfg(cfg)), _ptr(x), _ptr(topk_idx), _ptr(x_perm), _ptr(expert_counts),
         _ptr(expert_offsets), _ptr(row_token), _ptr(slot_row), _ptr(ws), _nbytes(ws),
         _stream(stream)))
+
+
+def moe_route_permute(cfg, x, w_router, gate_bias, logits, topk_idx, topk_w, expert_counts,
+                      expert_offsets, row_token, slot_row, ws, stream=None):
+    _check("moe_route_permute", lib().moe_route_permute(
+        ctypes.byref(_as_cfg(cfg)), _ptr(x), _ptr(w_router), _ptr(gate_bias), _ptr(logits),
+        _ptr(topk_idx), _ptr(topk_w), _ptr(expert_counts), _ptr(expert_offsets), _ptr(row_token),
+        _ptr(slot_row), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def moe_permute_noalloc(cfg, x, topk_idx, x_perm, expert_counts, expert_offsets, row_token,

@@ -19,12 +19,19 @@ hipError_t launch_route_bf16(const bf16_t* x, const bf16_t* wt, const float* bia
                              int T, int H, int E, int k, int renorm, int thr, double delta,
                              hipStream_t s);
 bool route_lds_fits(int H, int E);
+// Tokens per block of the streaming router, which is also the count block of the
+// permutation it can count (cnt_hist / cnt_rank below).
+constexpr int kRouteCountTokens = 32;
 // the streaming router: w_router [H][E] as it is, or (w_router == nullptr) wt, the same
-// weight in launch_router_pack's layout
+// weight in launch_router_pack's layout. cnt_hist (may be null: no count): the
+// permutation's count step as well, per block of kRouteCountTokens tokens the per-expert
+// assignment counts into cnt_hist [ceil(T / 32)][E], and each slot's rank among its block's
+// assignments to its expert (token order; -1 for an empty slot) into cnt_rank [T][k]
 hipError_t launch_route_bf16_lds(const bf16_t* x, const bf16_t* w_router, const bf16_t* wt,
                                  const float* bias, float* logits, int32_t* topk_idx,
-                                 float* topk_w, int32_t* flags, int T, int H, int E, int k,
-                                 int renorm, int thr, double delta, int cus, hipStream_t s);
+                                 float* topk_w, int32_t* flags, int32_t* cnt_hist,
+                                 int32_t* cnt_rank, int T, int H, int E, int k, int renorm,
+                                 int thr, double delta, int cus, hipStream_t s);
 int device_cus();
 hipError_t launch_route_logits_f32(const float* x, const float* w_router, const float* bias,
                                    float* logits, int T, int H, int E, hipStream_t s);
@@ -46,6 +53,18 @@ hipError_t launch_permute(const void* x, int elem_bytes, const int32_t* topk_idx
                           int32_t* slot_row, int32_t* hist, int32_t* flags, int32_t* gen,
                           int32_t* gen_copy, int32_t* flag_out, int T, int H, int E, int k,
                           int cap, hipStream_t s);
+// The row maps of the permutation whose count step the streaming router did
+// (launch_route_bf16_lds with cnt_hist): one launch, permute_scan_rows_kernel over count
+// blocks of kRouteCountTokens tokens. slot_row holds the router's ranks on entry and the
+// rows on return; perm_flags (the count kernel's flag words, ceil(T / 1024) of them) are
+// cleared, since the router's ids are valid by construction. At most kRoutedMaxBlocks
+// count blocks.
+constexpr int kRoutedMaxBlocks = 8192;
+hipError_t launch_permute_routed(const int32_t* topk_idx, const int32_t* cnt_hist,
+                                 int32_t* counts, int32_t* offsets, int32_t* row_token,
+                                 int32_t* slot_row, int32_t* perm_flags, int32_t* gen,
+                                 int32_t* gen_copy, int T, int E, int k, int cap,
+                                 hipStream_t s);
 // The same permutation with its scratch in a file-scope device array of kNoAllocScratchWords
 // int32 words (no workspace, no allocation): permute_noalloc_words(T, E) words are used;
 // more -> hipErrorInvalidValue, before any HIP call. flag_out (may be null) as above.

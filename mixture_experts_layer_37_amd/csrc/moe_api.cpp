@@ -40,6 +40,14 @@ constexpr size_t kAlign = 256;
 
 size_t esize(const moe_config* c) { return c->dtype == MOE_DTYPE_BF16 ? 2 : 4; }
 
+// Whether route and permute run as two launches (moe_route_permute, moe_forward): the
+// streaming router counts the permutation's assignments itself, per block of 32 tokens.
+bool routed_count(const moe_config* c) {
+  return c->dtype == MOE_DTYPE_BF16 && moe::route_lds_fits(c->hidden, c->experts) &&
+         (c->tokens + moe::kRouteCountTokens - 1) / moe::kRouteCountTokens <=
+             moe::kRoutedMaxBlocks;
+}
+
 Layout layout_of(const moe_config* c) {
   const size_t T = (size_t)c->tokens, H = (size_t)c->hidden, I = (size_t)c->inter;
   const size_t E = (size_t)c->experts, k = (size_t)c->top_k, es = esize(c);
@@ -53,7 +61,9 @@ Layout layout_of(const moe_config* c) {
   L.size[R_TOPK_IDX] = N * 4;
   L.size[R_TOPK_W] = N * 4;
   L.size[R_ROUTE_FLAGS] = ((T + moe::kRouteFlagGroup - 1) / moe::kRouteFlagGroup) * 4;
-  L.size[R_HIST] = NB * E * 4;
+  // the count kernel's histogram table, or the router's (one row per 32 tokens)
+  const size_t NBR = (T + moe::kRouteCountTokens - 1) / moe::kRouteCountTokens;
+  L.size[R_HIST] = (routed_count(c) ? NBR : NB) * E * 4;
   L.size[R_PERM_FLAGS] = NB * 4;
   L.size[R_COUNTS] = E * 4;
   L.size[R_OFFSETS] = (E + 1) * 4;
@@ -223,8 +233,8 @@ moe_status do_route(const moe_config* c, const void* x, const void* w_router, co
   if (c->dtype == MOE_DTYPE_BF16 && moe::route_lds_fits(H, E))
     return hip_status(moe::launch_route_bf16_lds(
         (const moe::bf16_t*)x, packed ? nullptr : (const moe::bf16_t*)w_router,
-        packed ? (const moe::bf16_t*)w_router : nullptr, bias, logits, idx, w, flags, T, H, E,
-        k, renorm, thr, delta, moe::device_cus(), s));
+        packed ? (const moe::bf16_t*)w_router : nullptr, bias, logits, idx, w, flags, nullptr,
+        nullptr, T, H, E, k, renorm, thr, delta, moe::device_cus(), s));
   if (c->dtype == MOE_DTYPE_BF16) {
     const moe::bf16_t* wt = (const moe::bf16_t*)w_router;
     if (!packed) {
@@ -252,6 +262,36 @@ moe_status do_permute(const moe_config* c, const void* x, const int32_t* idx, vo
       region<int32_t>(ws, L, R_HIST), region<int32_t>(ws, L, R_PERM_FLAGS),
       region<int32_t>(ws, L, R_GEN), gen_copy, nullptr, c->tokens, c->hidden, c->experts,
       c->top_k, cap < c->tokens ? cap : c->tokens, s));
+}
+
+// Route, then the permutation's row maps (no x_perm). With the streaming router the count
+// step runs in the router's epilogue and one more launch builds the maps; otherwise the
+// two steps as moe_route and moe_permute run them. Same results either way.
+moe_status do_route_permute(const moe_config* c, const void* x, const void* w_router,
+                            const float* bias, float* logits, int32_t* idx, float* w,
+                            int32_t* counts, int32_t* offsets, int32_t* row_token,
+                            int32_t* slot_row, void* ws, hipStream_t s,
+                            int32_t* gen_copy = nullptr) {
+  if (x == nullptr || !routed_count(c)) {
+    MOE_TRY(do_route(c, x, w_router, bias, logits, idx, w, ws, s));
+    return do_permute(c, x, idx, nullptr, counts, offsets, row_token, slot_row, ws, s,
+                      gen_copy);
+  }
+  const Layout L = layout_of(c);
+  const int T = c->tokens, H = c->hidden, E = c->experts, k = c->top_k;
+  const int thr = c->routing == MOE_ROUTE_THRESHOLD;
+  const double delta = c->threshold > 0 ? c->threshold : 1.0 / (double)E;
+  const bool packed = (c->weight_layout & MOE_ROUTER_PACKED) != 0;
+  int32_t* hist = region<int32_t>(ws, L, R_HIST);
+  MOE_TRY(hip_status(moe::launch_route_bf16_lds(
+      (const moe::bf16_t*)x, packed ? nullptr : (const moe::bf16_t*)w_router,
+      packed ? (const moe::bf16_t*)w_router : nullptr, bias, logits, idx, w,
+      region<int32_t>(ws, L, R_ROUTE_FLAGS), hist, slot_row, T, H, E, k, c->renormalize != 0,
+      thr, delta, moe::device_cus(), s)));
+  const int cap = capacity_of(c);
+  return hip_status(moe::launch_permute_routed(
+      idx, hist, counts, offsets, row_token, slot_row, region<int32_t>(ws, L, R_PERM_FLAGS),
+      region<int32_t>(ws, L, R_GEN), gen_copy, T, E, k, cap < T ? cap : T, s));
 }
 
 // GEMM 1. `a` is x_perm (row_token == nullptr) or the token matrix x read through
@@ -358,6 +398,30 @@ moe_status moe_permute(const moe_config* cfg, const void* x, const int32_t* topk
   MOE_TRY(check_ws(cfg, ws, ws_bytes));
   return do_permute(cfg, x, topk_idx, x_perm, expert_counts, expert_offsets, row_token, slot_row,
                     ws, (hipStream_t)stream);
+}
+
+moe_status moe_route_permute(const moe_config* cfg, const void* x, const void* w_router,
+                             const float* gate_bias, float* logits, int32_t* topk_idx,
+                             float* topk_w, int32_t* expert_counts, int32_t* expert_offsets,
+                             int32_t* row_token, int32_t* slot_row, void* ws, size_t ws_bytes,
+                             moe_stream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  if (cfg->tokens == 0) return MOE_OK;   // empty batch: nothing to read or write
+  if (x != nullptr) {
+    MOE_TRY(need(x, 16));
+    MOE_TRY(need(w_router, cfg->dtype == MOE_DTYPE_BF16 ? 16 : 4));
+    if (gate_bias != nullptr) MOE_TRY(need(gate_bias, 4));
+  }
+  MOE_TRY(need(logits, 4));
+  MOE_TRY(need(topk_idx, 4));
+  MOE_TRY(need(topk_w, 4));
+  MOE_TRY(need(expert_counts, 4));
+  MOE_TRY(need(expert_offsets, 4));
+  MOE_TRY(need(row_token, 4));
+  MOE_TRY(need(slot_row, 4));
+  MOE_TRY(check_ws(cfg, ws, ws_bytes));
+  return do_route_permute(cfg, x, w_router, gate_bias, logits, topk_idx, topk_w, expert_counts,
+                          expert_offsets, row_token, slot_row, ws, (hipStream_t)stream);
 }
 
 moe_status moe_permute_noalloc(const moe_config* cfg, const void* x, const int32_t* topk_idx,
@@ -531,9 +595,9 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
   int32_t* row_token = region<int32_t>(ws, L, R_ROW_TOKEN);
   void* h = region<void>(ws, L, R_H);
   void* y = region<void>(ws, L, R_Y_PERM);
-  MOE_TRY(do_route(cfg, x, w_router, gate_bias, logits, idx, w, ws, s));
   // the permutation's row maps only: GEMM 1 gathers the token rows itself
-  MOE_TRY(do_permute(cfg, x, idx, nullptr, counts, offsets, row_token, slot_row, ws, s));
+  MOE_TRY(do_route_permute(cfg, x, w_router, gate_bias, logits, idx, w, counts, offsets,
+                           row_token, slot_row, ws, s));
   MOE_TRY(do_up(cfg, x, row_token, offsets, w_gate, w_up, h, s));
   MOE_TRY(do_down(cfg, h, offsets, w_down, y, region<float>(ws, L, R_SPLIT), s));
   return do_combine(cfg, y, slot_row, w, out, s);
@@ -570,9 +634,8 @@ moe_status moe_forward_train(const moe_config* cfg, const void* x, const void* w
   moe::bf16_t* gu = bregion<moe::bf16_t>(bws, B, B_GU);
   const int T = cfg->tokens, H = cfg->hidden, I = cfg->inter, E = cfg->experts;
   const int rows = T * cfg->top_k;
-  MOE_TRY(do_route(cfg, x, w_router, gate_bias, logits, idx, w, ws, s));
-  MOE_TRY(do_permute(cfg, x, idx, nullptr, counts, offsets, row_token, slot_row, ws, s,
-                     bregion<int32_t>(bws, B, B_GEN)));
+  MOE_TRY(do_route_permute(cfg, x, w_router, gate_bias, logits, idx, w, counts, offsets,
+                           row_token, slot_row, ws, s, bregion<int32_t>(bws, B, B_GEN)));
   // GEMM 1 keeping the pre-activations for the backward: [g | u] (GELU: a) into bws, h as usual
   if (cfg->activation == MOE_ACT_SWIGLU)
     MOE_TRY(hip_status(moe::launch_gemm_bf16(

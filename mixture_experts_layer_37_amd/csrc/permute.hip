@@ -225,50 +225,40 @@ __global__ __launch_bounds__(256) void permute_rows_kernel(
   }
 }
 
-// The scan and the row maps in one launch (no x_perm), after the count kernel, for batches
-// of at most kMapsMaxBlocks count blocks. A block of 256 threads owns 256 tokens of one
-// count block; every block reads the whole [NB][E] histogram table and derives from it, in
-// the scan kernel's order, each expert's pre-capacity count, kept offsets and the prefix
-// over the count blocks before its own, so no block waits for another. Block 0 writes
-// counts and offsets, advances the generation and gathers the flag words; every block then
-// turns its tokens' in-block ranks (slot_row, from the count kernel) into rows, as the rows
-// kernel does, with all of a token's slot loads in flight together.
+// The scan and the row maps in one launch (no x_perm), after the count step, for batches
+// of at most kMapsMaxBlocks count blocks of the count kernel (CB = kCountBlockTokens) or
+// kRoutedMaxBlocks of the streaming router (CB = kRouteCountTokens). A block of 256 threads
+// owns 256 tokens; every block reads the whole [NB][E] histogram table and derives from
+// it, in the scan kernel's order, each expert's pre-capacity count, kept offsets and the
+// prefix over the count blocks before each of its tokens' own, so no block waits for
+// another. Block 0 writes counts and offsets, advances the generation and gathers the flag
+// words (after the router's count, which raises none: clears them); every block then turns
+// its tokens' in-block ranks (slot_row, from the count step) into rows, as the rows kernel
+// does, with all of a token's slot loads in flight together.
 static_assert(kCountBlockTokens % 256 == 0, "a 256-token block lies in one count block");
+static_assert(256 % kRouteCountTokens == 0, "a 256-token block holds whole router blocks");
+constexpr int kRoutedExperts = 16;   // the streaming router's gates: E <= 16
+template <int CB>
 __global__ __launch_bounds__(256) void permute_scan_rows_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ hist,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ row_token,
-    int32_t* __restrict__ slot_row, const int32_t* __restrict__ flags, int32_t* gen,
+    int32_t* __restrict__ slot_row, int32_t* __restrict__ flags, int32_t* gen,
     int32_t* gen_copy, int32_t* __restrict__ flag_out, int T, int E, int k, int cap) {
-  __shared__ int before[kMaxExperts];   // assignments of earlier count blocks, per expert
+  constexpr bool kRouted = CB == kRouteCountTokens;
+  constexpr int kLocal = kRouted ? 256 / CB : 1;   // count blocks a block's tokens span
+  // assignments of earlier count blocks, per local count block and expert
+  __shared__ int before[kLocal][kRouted ? kRoutedExperts : kMaxExperts];
+  __shared__ int red[kRouted ? 2 * 256 : 1];                   // partial sums per reducer
+  __shared__ int loc[kLocal][kRouted ? kRoutedExperts : 1];   // the block's own table rows
+  __shared__ int tab[kRouted ? 256 * kRoutedExperts : 1];     // 256 rows of the table
   __shared__ int off[kMaxExperts + 1];
   __shared__ int wsum[4];
   __shared__ int wflag[4];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int t = blockIdx.x * blockDim.x + tid;
-  const int cb = (blockIdx.x * blockDim.x) / kCountBlockTokens;   // this block's count block
-  const int NB = (T + kCountBlockTokens - 1) / kCountBlockTokens;
-  // expert tid: the prefix over count blocks < cb and the batch total
-  int total = 0;
-  if (tid < E) {
-    int pre = 0, ob = 0;
-    for (; ob + 8 <= NB; ob += 8) {
-      int v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = hist[(size_t)(ob + u) * E + tid];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        pre += ob + u < cb ? v[u] : 0;
-        total += v[u];
-      }
-    }
-    for (; ob < NB; ++ob) {
-      const int v = hist[(size_t)ob * E + tid];
-      pre += ob < cb ? v : 0;
-      total += v;
-    }
-    before[tid] = pre;
-  }
+  const int NB = (T + CB - 1) / CB;
   // this thread's token: its slots' in-block ranks and ids, all loads in flight together
+  // (issued first: they land while the histogram table is read)
   int r[kMaxTopK], ev[kMaxTopK];
   if (t < T) {
 #pragma unroll
@@ -277,6 +267,84 @@ __global__ __launch_bounds__(256) void permute_scan_rows_kernel(
         r[j] = slot_row[(size_t)t * k + j];
         ev[j] = idx[(size_t)t * k + j];
       }
+  }
+  int total = 0;
+  if constexpr (!kRouted) {
+    // expert tid: the prefix over count blocks < cb and the batch total
+    const int cb = (blockIdx.x * blockDim.x) / CB;   // this block's count block
+    if (tid < E) {
+      int pre = 0, ob = 0;
+      for (; ob + 8 <= NB; ob += 8) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = hist[(size_t)(ob + u) * E + tid];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          pre += ob + u < cb ? v[u] : 0;
+          total += v[u];
+        }
+      }
+      for (; ob < NB; ++ob) {
+        const int v = hist[(size_t)ob * E + tid];
+        pre += ob < cb ? v : 0;
+        total += v;
+      }
+      before[0][tid] = pre;
+    }
+  } else {
+    // Many small count blocks. The table goes through LDS 256 rows at a time (coalesced
+    // loads); thread (g, e), g < G = 256 / E, sums rows g, g + G, ... of each piece for expert
+    // e, over the rows before this block's first count block b0 and over all rows; the G
+    // partial sums of each expert are then added. The block's own kLocal rows go to LDS beside, for
+    // the prefix inside the block.
+    const int b0 = blockIdx.x * kLocal;
+    if (tid < kLocal * E) {
+      const int c = tid / E, e = tid - c * E;
+      loc[c][e] = b0 + c < NB ? hist[(size_t)(b0 + c) * E + e] : 0;
+    }
+    int pre = 0, tot = 0;
+    const int G = 256 / E;                    // reducers per expert
+    const int g = tid / E, e = tid - g * E;   // reducer (g, e) for tid < G E
+    for (int base = 0; base < NB; base += 256) {
+      const int rows = min(256, NB - base);
+      int v[kRoutedExperts];   // all of this thread's loads in flight together
+#pragma unroll
+      for (int u = 0; u < kRoutedExperts; ++u) {
+        const int i = tid + u * 256;
+        v[u] = i < rows * E ? hist[(size_t)base * E + i] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < kRoutedExperts; ++u)
+        if (tid + u * 256 < rows * E) tab[tid + u * 256] = v[u];
+      __syncthreads();
+      if (tid < G * E) {
+#pragma unroll 4
+        for (int rr = g; rr < rows; rr += G) {
+          const int x = tab[rr * E + e];
+          tot += x;
+          pre += base + rr < b0 ? x : 0;
+        }
+      }
+      __syncthreads();
+    }
+    if (tid < G * E) {
+      red[tid] = pre;
+      red[256 + tid] = tot;
+    }
+    __syncthreads();
+    // local count block c (tid / E), expert e: the prefix before b0 plus rows b0 .. b0 + c - 1
+    if (tid < kLocal * E) {
+      const int c = tid / E, ee = tid - c * E;
+      int p = 0;
+#pragma unroll 8
+      for (int gg = 0; gg < G; ++gg) p += red[gg * E + ee];
+      for (int cc = 0; cc < c; ++cc) p += loc[cc][ee];
+      before[c][ee] = p;
+    }
+    if (tid < E) {
+#pragma unroll 8
+      for (int gg = 0; gg < G; ++gg) total += red[256 + gg * E + tid];
+    }
   }
   // exclusive scan of min(total, cap) over E <= 256 experts (one per thread)
   const int kept = tid < E ? min(total, cap) : 0;
@@ -287,10 +355,17 @@ __global__ __launch_bounds__(256) void permute_scan_rows_kernel(
     if (lane >= o) incl += n;
   }
   if (lane == 63) wsum[wave] = incl;
-  // block 0: the OR of the count blocks' flag words
+  // block 0: the OR of the count blocks' flag words (after the router's count: none, and
+  // the count kernel's words are cleared)
   int f = 0;
-  if (blockIdx.x == 0 && flag_out != nullptr)
-    for (int ob = tid; ob < NB; ob += blockDim.x) f |= flags[ob];
+  if constexpr (!kRouted) {
+    if (blockIdx.x == 0 && flag_out != nullptr)
+      for (int ob = tid; ob < NB; ob += blockDim.x) f |= flags[ob];
+  } else {
+    if (blockIdx.x == 0)
+      for (int ob = tid; ob < (T + kCountBlockTokens - 1) / kCountBlockTokens; ob += blockDim.x)
+        flags[ob] = 0;
+  }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) f |= __shfl_xor(f, o);
   if (lane == 0) wflag[wave] = f;
@@ -321,7 +396,7 @@ __global__ __launch_bounds__(256) void permute_scan_rows_kernel(
       if (j < k) {
         int row = -1;
         if (r[j] >= 0) {
-          const int pos = before[ev[j]] + r[j];
+          const int pos = before[kRouted ? tid / CB : 0][ev[j]] + r[j];
           if (pos < cap) row = off[ev[j]] + pos;
         }
         slot_row[(size_t)t * k + j] = row;
@@ -342,9 +417,9 @@ hipError_t launch_permute(const void* x, int elem_bytes, const int32_t* topk_idx
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (x_perm == nullptr && NB <= kMapsMaxBlocks) {
-    hipLaunchKernelGGL(permute_scan_rows_kernel, dim3((T + 255) / 256), dim3(256), 0, s,
-                       topk_idx, hist, counts, offsets, row_token, slot_row, flags, gen, gen_copy,
-                       flag_out, T, E, k, cap);
+    hipLaunchKernelGGL(permute_scan_rows_kernel<kCountBlockTokens>, dim3((T + 255) / 256),
+                       dim3(256), 0, s, topk_idx, hist, counts, offsets, row_token, slot_row,
+                       flags, gen, gen_copy, flag_out, T, E, k, cap);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(256), 0, s, hist, counts, offsets, NB, E,
@@ -365,6 +440,19 @@ hipError_t launch_permute(const void* x, int elem_bytes, const int32_t* topk_idx
   else if (row_vecs >= 128) MOE_GATHER(2);
   else MOE_GATHER(1);
 #undef MOE_GATHER
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_routed(const int32_t* topk_idx, const int32_t* cnt_hist,
+                                 int32_t* counts, int32_t* offsets, int32_t* row_token,
+                                 int32_t* slot_row, int32_t* perm_flags, int32_t* gen,
+                                 int32_t* gen_copy, int T, int E, int k, int cap,
+                                 hipStream_t s) {
+  if (E > kRoutedExperts || (T + kRouteCountTokens - 1) / kRouteCountTokens > kRoutedMaxBlocks)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(permute_scan_rows_kernel<kRouteCountTokens>, dim3((T + 255) / 256),
+                     dim3(256), 0, s, topk_idx, cnt_hist, counts, offsets, row_token, slot_row,
+                     perm_flags, gen, gen_copy, nullptr, T, E, k, cap);
   return hipGetLastError();
 }
 

@@ -40,8 +40,7 @@ __device__ __forceinline__ int order_key(float f) {
 // Returns true if a logit is not finite.
 template <int KMAX>
 __device__ bool topk_token(const float* L, int E, int k, int renorm, int thr, double delta,
-                           int32_t* idx_out,
-                           float* w_out) {
+                           int32_t* idx_out, float* w_out, int* ids = nullptr) {
   int key[KMAX];
   int id[KMAX];
 #pragma unroll
@@ -107,6 +106,7 @@ __device__ bool topk_token(const float* L, int E, int k, int renorm, int thr, do
       idx_out[j] = -1;
       w_out[j] = 0.f;
     }
+    if (ids != nullptr) ids[j] = j < cnt ? id[j] : -1;   // what idx_out now holds (-1 past k)
   }
   return nonfinite;
 }
@@ -521,8 +521,9 @@ __global__ __launch_bounds__(512, 1) void route_stream_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, const bf16_t* __restrict__ wt,
     const float* __restrict__ bias,
     float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    int32_t* __restrict__ flags, int T, int H, int E, int k, int renorm, int thr, double delta) {
-  constexpr int BT = 32, LDR = 17;
+    int32_t* __restrict__ flags, int32_t* __restrict__ cnt_hist, int32_t* __restrict__ cnt_rank,
+    int T, int H, int E, int k, int renorm, int thr, double delta) {
+  constexpr int BT = kRouteCountTokens, LDR = 17;   // tokens per block
   // Two buffer sets in two distinct LDS objects, so the compiler can tell a DMA into one
   // from reads of the other.
   __shared__ __attribute__((aligned(1024))) bf16_t xb0[kRouteWaves * kRouteBufElems];
@@ -655,26 +656,56 @@ __global__ __launch_bounds__(512, 1) void route_stream_kernel(
   if (tid < 64) {
     bool nf = false;
     const int t = t0 + tid;
+    int ev[KMAX];   // this token's ids as written (-1: empty slot or no token)
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) ev[j] = -1;
     if (tid < BT && t < T)
       nf = topk_token<KMAX>(lg + tid * LDR, E, k, renorm, thr, delta, topk_idx + (size_t)t * k,
-                            topk_w + (size_t)t * k);
+                            topk_w + (size_t)t * k, ev);
     const unsigned long long m = __ballot(nf);
     const int ngroups = (T + kRouteFlagGroup - 1) / kRouteFlagGroup;
     if (tid < 2 && blockIdx.x * 2 + tid < ngroups)
       flags[blockIdx.x * 2 + tid] =
           ((m >> (16 * tid)) & 0xffffull) ? 2 /* MOE_FLAG_NONFINITE_LOGIT */ : 0;
+    if (cnt_hist != nullptr) {
+      // The permutation's count step for this block's 32 tokens (one count block): per
+      // expert, the number of its assignments, and each slot's rank among them in token
+      // order. Lane tid holds token t0 + tid; its ids are distinct, in [0, E) or -1 (an empty
+      // slot of threshold routing: rank -1, dropped like the count kernel drops it).
+      const bool live = tid < BT && t < T;
+      int rk[KMAX];
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) rk[j] = -1;
+      const unsigned long long below = (1ull << tid) - 1ull;
+      for (int e = 0; e < E; ++e) {
+        bool has = false;
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) has |= ev[j] == e;
+        const unsigned long long me = __ballot(has);
+        if (tid == 0) cnt_hist[(size_t)blockIdx.x * E + e] = (int)__popcll(me);
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+          if (ev[j] == e) rk[j] = (int)__popcll(me & below);
+      }
+      if (live) {
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+          if (j < k) cnt_rank[(size_t)t * k + j] = rk[j];
+      }
+    }
   }
 }
 
 hipError_t launch_route_bf16_lds(const bf16_t* x, const bf16_t* w_router, const bf16_t* wt,
                                  const float* bias, float* logits, int32_t* idx, float* w,
-                                 int32_t* flags, int T, int H, int E, int k, int renorm, int thr,
-                                 double delta, int cus, hipStream_t s) {
+                                 int32_t* flags, int32_t* cnt_hist, int32_t* cnt_rank, int T,
+                                 int H, int E, int k, int renorm, int thr, double delta, int cus,
+                                 hipStream_t s) {
   (void)cus;
-  const dim3 grid((T + 31) / 32), block(64 * kRouteWaves);
+  const dim3 grid((T + kRouteCountTokens - 1) / kRouteCountTokens), block(64 * kRouteWaves);
 #define MOE_ROUTE_STREAM(KM)                                                                    \
   hipLaunchKernelGGL((route_stream_kernel<KM>), grid, block, 0, s, x, w_router, wt, bias, logits, idx, \
-                     w, flags, T, H, E, k, renorm, thr, delta)
+                     w, flags, cnt_hist, cnt_rank, T, H, E, k, renorm, thr, delta)
   if (k <= 1) MOE_ROUTE_STREAM(1);
   else if (k <= 2) MOE_ROUTE_STREAM(2);
   else if (k <= 4) MOE_ROUTE_STREAM(4);

@@ -150,6 +150,16 @@ def test_stage_argument_errors(lib):
     assert lib.moe_route(ctypes.byref(cfg_of(tokens=0)), None, None, None, FAKE, FAKE, FAKE, FAKE,
                          need, None) == L.MOE_OK
     assert lib.moe_permute(cp, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == L.MOE_ERR_INVALID_ARG
+    # route + row maps: every output required, the workspace checked, an empty batch a no-op
+    rp = lib.moe_route_permute
+    for miss in range(4, 11):   # logits, idx, weights, counts, offsets, row_token, slot_row
+        args = [cp, FAKE, FAKE, None] + [FAKE] * 7 + [FAKE, need, None]
+        args[miss] = None
+        assert rp(*args) == L.MOE_ERR_INVALID_ARG, miss
+    assert rp(cp, FAKE, FAKE + 8, None, *([FAKE] * 7), FAKE, need, None) == L.MOE_ERR_INVALID_ARG
+    assert rp(cp, FAKE, FAKE, None, *([FAKE] * 7), FAKE, 16, None) == L.MOE_ERR_WORKSPACE
+    assert rp(ctypes.byref(cfg_of(tokens=0)), None, None, None, *([None] * 7), None, 0,
+              None) == L.MOE_OK
     assert lib.moe_expert_up(cp, FAKE, FAKE, None, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_expert_down(cp, FAKE, None, FAKE, FAKE, None, 0, None) == L.MOE_ERR_INVALID_ARG
     # a workspace is optional for GEMM 2, but one that is given must be large enough

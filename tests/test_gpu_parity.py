@@ -546,3 +546,58 @@ def test_row_map_paths_agree(T, E, k, cf):
     np.testing.assert_array_equal(out["maps"][3], out["gather"][3])
     np.testing.assert_array_equal(out["maps"][2][:n], out["gather"][2][:n])
     assert out["gather"][4] == flag
+
+
+# moe_route_permute (the count step inside the streaming router, two launches) against
+# moe_route then moe_permute on the same inputs: every output bit for bit, and the flags.
+# The streaming router's cases: a whole Mixtral gate, ragged token blocks, capacity drops,
+# threshold routing with empty slots, 16 experts, T beyond one 65536-token map batch, a
+# single token; then a 32-expert gate, which takes the two calls inside it.
+@pytest.mark.parametrize("T,H,E,k,routing,cf", [(8192, 4096, 8, 2, "topk", 0.0),
+                                                (1000, 1024, 12, 3, "topk", 0.7),
+                                                (5000, 2048, 16, 4, "threshold", 0.0),
+                                                (777, 4096, 8, 8, "threshold", 0.9),
+                                                (33, 1024, 5, 1, "topk", 0.0),
+                                                (70000, 1024, 8, 2, "topk", 1.1),
+                                                (1, 1024, 8, 2, "topk", 0.0),
+                                                (600, 512, 32, 4, "topk", 0.8)])
+def test_route_permute_matches_route_then_permute(T, H, E, k, routing, cf):
+    cfg = C.SMALL.with_(tokens=T, hidden=H, inter=256, experts=E, top_k=k, routing=routing,
+                        capacity_factor=cf, bias=("normal", 1.0))
+    inp = make_inputs(cfg, seed=T + 3 * E, weights=False)
+    x = to_device(cfg, inp["x"])
+    w = to_device(cfg, inp["w_router"])
+    bias = to_device(cfg, inp["bias"])
+    c = L.cconfig(cfg)
+    out = {}
+    for tag in ("separate", "fused"):
+        ws = torch.empty(L.moe_workspace_size(c), dtype=torch.uint8, device="cuda")
+        lg = torch.full((T, E), -9.0, dtype=torch.float32, device="cuda")
+        idx = torch.full((T, k), -9, dtype=torch.int32, device="cuda")
+        tw = torch.full((T, k), -9.0, dtype=torch.float32, device="cuda")
+        counts = torch.full((E,), -9, dtype=torch.int32, device="cuda")
+        offs = torch.full((E + 1,), -9, dtype=torch.int32, device="cuda")
+        rt = torch.full((T * k,), -9, dtype=torch.int32, device="cuda")
+        sr = torch.full((T, k), -9, dtype=torch.int32, device="cuda")
+        # raise the permutation's bad-id flag in this workspace first: the call under test
+        # must leave its own flags, not this one
+        bad = torch.full((T, k), E, dtype=torch.int32, device="cuda")
+        L.moe_permute(c, None, bad, None, counts, offs, rt, sr, ws)
+        assert L.moe_read_device_status(c, ws, 2) == L.MOE_FLAG_BAD_INDEX
+        print(f"[route_permute] T={T} H={H} E={E} k={k} {routing} cf={cf} {tag}", flush=True)
+        if tag == "separate":
+            L.moe_route(c, x, w, bias, lg, idx, tw, ws)
+            L.moe_permute(c, None, idx, None, counts, offs, rt, sr, ws)
+        else:
+            L.moe_route_permute(c, x, w, bias, lg, idx, tw, counts, offs, rt, sr, ws)
+        torch.cuda.synchronize()
+        out[tag] = ([a.cpu() for a in (lg, idx, tw, counts, offs, rt, sr)],
+                    L.moe_read_device_status(c, ws, 1), L.moe_read_device_status(c, ws, 2))
+    (a, fa1, fa2), (b, fb1, fb2) = out["separate"], out["fused"]
+    for u, v, what in zip(a, b, ("logits", "idx", "weights", "counts", "offsets", "row_token",
+                                 "slot_row")):
+        if u.dtype == torch.float32:
+            u, v = u.view(torch.int32), v.view(torch.int32)
+        assert torch.equal(u, v), what
+    assert fa1 == fb1 and fa2 == fb2 == 0
+    assert int(a[4][-1]) > 0 and int(a[4][-1]) == int((a[6] >= 0).sum())
