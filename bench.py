@@ -57,13 +57,13 @@ def parse_args():
     return ap.parse_args()
 
 
-GEMM_SOURCES = ("gemm.hip", "packed_kloop.h", "kloop_model.h")
+GEMM_SOURCES = ("gemm.hip", "packed_kloop.h", "kloop_model.h", "tile_order.h")
 
 
 def kernel_source_digest(path: str | None = None) -> str:
-    """Digest of the GEMM sources (gemm.hip and the k-loop headers it includes, or the one
-    file `path`) with comments and whitespace removed, so that an edit of comments alone
-    keeps the committed counter summary valid."""
+    """Digest of the GEMM sources (gemm.hip and the k-loop and tile-order headers it
+    includes, or the one file `path`) with comments and whitespace removed, so that an edit
+    of comments alone keeps the committed counter summary valid."""
     csrc = os.path.join(ROOT, "mixture_experts_layer_37_amd", "csrc")
     paths = [path] if path else [os.path.join(csrc, f) for f in GEMM_SOURCES]
     h = hashlib.sha256()

@@ -53,44 +53,16 @@
 #include "common.h"
 #include "kernels.h"
 #include "packed_kloop.h"
+#include "tile_order.h"
 
 namespace moe {
 
 constexpr int BM = 256;
 constexpr int BK = 64;
-constexpr int kXcds = 8;
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
-// Tile order of the grouped GEMMs. Each expert owns ceil(rows / BMt) * NT tiles, n-tile
-// major, m-tile minor. Experts fall into two classes: "wide" ones, and "small" ones whose
-// rows fit in 128 (one m-tile: their tiles stream the expert's weights for few rows, while
-// a wide expert's tiles are MFMA-bound and share weight panels across m-tiles through L2).
-// The tile list holds the wide experts' tiles first (experts in index order), then the
-// small ones'. A launch takes its tiles in rounds of the grid, XCD x the x-th run of `run`
-// tiles of each round, one tile per block; the merged order below gives, while both classes
-// last, XCD x the wide class in rounds r with r + x even and the small class in the others.
-// So in every round half the XCDs stream weights while the others run MFMAs, and every block
-// takes both classes in turn (a fixed class per XCD left half the chip idle at the end).
-// With no small expert (or no wide one) the merged order is the list order.
-//
-// Paired ragged ends (kPairs; GEMM 1 with SwiGLU on packed weights): a wide expert whose
-// last m-tile holds at most 128 rows gives that m-tile one tile per PAIR of n-tiles, 128
-// rows by both n-tiles' columns: the MFMAs of a full tile, so it ends with the blocks that
-// share its weight panels, where a half-height tile per n-tile ended early and pulled its
-// block out of step with them. Within the expert, n-tile pair q holds the full-height
-// m-tiles of n-tile 2q, those of 2q + 1, then the pair tile; an odd last n-tile keeps a
-// half-height tile of its own.
-constexpr int kSmallRows = 128;
-
-// Tiles of one expert of m rows: one per m-tile and n-tile, except for a paired ragged end.
-template <int BMt, bool kPairs>
-__device__ __forceinline__ int expert_tiles(int m, int NT) {
-  if (!kPairs || m <= kSmallRows) return ((m + BMt - 1) / BMt) * NT;
-  const int rem = m % BMt;
-  const int mw = m / BMt + (rem > kSmallRows ? 1 : 0);   // full-height m-tiles
-  return mw * NT + (rem > 0 && rem <= kSmallRows ? (NT + 1) / 2 : 0);
-}
+// The tile order itself (classes, merged order, paired ragged ends) is tile_order.h's.
 
 // Per-expert tile starts in that list; returns the total. s_perm[slot] is the expert in
 // list slot `slot`, s_start[slot] its first tile, n_wide the wide experts' tiles (the
@@ -132,7 +104,7 @@ __device__ __forceinline__ int build_tile_starts(const int32_t* __restrict__ off
   if (tid < E) {
     const int e = s_perm[tid];
     const int me = max(s_off[e + 1] - s_off[e], 0);
-    tiles = expert_tiles<BMt, kPairs>(me, NT);
+    tiles = expert_tiles(me, NT, BMt, kPairs);
   }
   int total = 0;
   const int before = block_scan(tiles, total);
@@ -141,33 +113,6 @@ __device__ __forceinline__ int build_tile_starts(const int32_t* __restrict__ off
   __syncthreads();
   n_wide = __builtin_amdgcn_readfirstlane(s_start[E - n_small]);   // the small part's start
   return __builtin_amdgcn_readfirstlane(total);
-}
-
-// List index of merged position p. Runs of `run` tiles, kXcds runs per round: for rounds
-// r < R the run of XCD x is the (4 r + x / 2)-th run of the wide part [0, nw) if r + x is
-// even, else that run of the small part [nw, total); R = the whole rounds both parts can
-// fill. Then the rest of the wide part, then the rest of the small part.
-__device__ __forceinline__ int merged_tile(int p, int nw, int total, int run) {
-  constexpr int kHalf = kXcds / 2;
-  const int R = min(nw / (kHalf * run), (total - nw) / (kHalf * run));
-  if (p < kXcds * run * R) {
-    const int c = p / run, o = p - c * run;
-    const int r = c / kXcds, x = c - r * kXcds;
-    const int idx = (kHalf * r + (x >> 1)) * run + o;
-    return ((r + x) & 1) ? nw + idx : idx;
-  }
-  const int q = p - kXcds * run * R, rest_w = nw - kHalf * run * R;
-  return q < rest_w ? kHalf * run * R + q : nw + kHalf * run * R + (q - rest_w);
-}
-
-// Largest slot in [0, E) with s_start[slot] <= tile (experts without tiles have equal starts).
-__device__ __forceinline__ int find_expert(const int* s_start, int E, int tile) {
-  int lo = 0, hi = E - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (s_start[mid] <= tile) lo = mid; else hi = mid - 1;
-  }
-  return lo;
 }
 
 // Where a tile sits: its expert, first row, valid rows and n-tile (pair: n-tiles n_t and
@@ -186,27 +131,10 @@ __device__ __forceinline__ TileCoord decode_tile(const int* s_start, const int* 
   t.e = s_perm[slot];
   const int row_beg = s_off[t.e];
   const int m_e = s_off[t.e + 1] - row_beg;   // > 0: the expert owns this tile
-  const int rem = tile - s_start[slot];
-  t.pair = 0;
-  int m_t;
-  const int ragged = m_e % BMt;
-  if (!kPairs || m_e <= kSmallRows || ragged == 0 || ragged > kSmallRows) {
-    const int mt_e = (m_e + BMt - 1) / BMt;
-    t.n_t = rem / mt_e;
-    m_t = rem - t.n_t * mt_e;
-  } else {
-    const int mw = m_e / BMt;            // full-height m-tiles; the ragged end is m-tile mw
-    const int blk = 2 * mw + 1;          // tiles of one n-tile pair
-    const int q = rem / blk, o = rem - q * blk;
-    if (q < NT / 2) {
-      t.n_t = 2 * q + (o < 2 * mw ? o / mw : 0);
-      m_t = o < 2 * mw ? o % mw : mw;
-      t.pair = o >= 2 * mw;
-    } else {                             // the odd last n-tile: its m-tiles, then its end
-      t.n_t = NT - 1;
-      m_t = o;
-    }
-  }
+  const TileInExpert te = tile_in_expert(m_e, tile - s_start[slot], NT, BMt, kPairs);
+  t.n_t = te.n_t;
+  t.pair = te.pair;
+  const int m_t = te.m_t;
   t.row0 = row_beg + m_t * BMt;
   t.mrows = min(BMt, m_e - m_t * BMt);
   return t;

@@ -35,8 +35,10 @@ def test_digest_ignores_comments_and_whitespace(tmp_path):
 
 
 def test_digest_covers_the_kloop_headers():
-    """The committed counters cover the GEMM's k-loop too, which lives in two headers."""
-    assert set(bench.GEMM_SOURCES) == {"gemm.hip", "packed_kloop.h", "kloop_model.h"}
+    """The committed counters cover the GEMM's k-loop and tile order too, which live in three
+    headers."""
+    assert set(bench.GEMM_SOURCES) == {"gemm.hip", "packed_kloop.h", "kloop_model.h",
+                                       "tile_order.h"}
     whole = bench.kernel_source_digest()
     only = bench.kernel_source_digest(os.path.join(ROOT, "mixture_experts_layer_37_amd", "csrc",
                                                    "gemm.hip"))
