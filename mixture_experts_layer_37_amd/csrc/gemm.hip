@@ -69,9 +69,8 @@ __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 // second part starts there). Uses s_start, s_perm, s_off [0..E] and s_wsum[4] in LDS; 256
 // threads, E <= 256. Offsets are clamped to [0, max_rows] and empty ranges count as empty,
 // so no offsets content can send a tile outside the row buffers. kClasses = false keeps
-// every expert in the first part (index order, no merge). kPairs: the pairing threshold
-// (full-height m-tiles an expert needs for a paired ragged end; 0: no pairs).
-template <int BMt, bool kClasses, int kPairs = 0>
+// every expert in the first part (index order, no merge).
+template <int BMt, bool kClasses, bool kPairs = false>
 __device__ __forceinline__ int build_tile_starts(const int32_t* __restrict__ offsets, int E,
                                                  int NT, int max_rows, int* s_start,
                                                  int* s_perm, int* s_off, int* s_wsum,
@@ -119,10 +118,10 @@ __device__ __forceinline__ int build_tile_starts(const int32_t* __restrict__ off
 // Where a tile sits: its expert, first row, valid rows and n-tile (pair: n-tiles n_t and
 // n_t + 1, at most 128 rows).
 struct TileCoord {
-  int e, row0, mrows, n_t, pair, odd_end;
+  int e, row0, mrows, n_t, pair;
 };
 // The tile at merged position p (NT: n-tiles per m-tile).
-template <int kPairs = 0>
+template <bool kPairs = false>
 __device__ __forceinline__ TileCoord decode_tile(const int* s_start, const int* s_perm,
                                                  const int* s_off, int E, int nw, int total,
                                                  int run, int p, int BMt, int NT) {
@@ -135,7 +134,6 @@ __device__ __forceinline__ TileCoord decode_tile(const int* s_start, const int* 
   const TileInExpert te = tile_in_expert(m_e, tile - s_start[slot], NT, BMt, kPairs);
   t.n_t = te.n_t;
   t.pair = te.pair;
-  t.odd_end = te.odd_end;
   const int m_t = te.m_t;
   t.row0 = row_beg + m_t * BMt;
   t.mrows = min(BMt, m_e - m_t * BMt);
@@ -246,14 +244,9 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   const size_t ldc = kPairOut ? 2 * (size_t)N : (size_t)N;
   const size_t ldaux = (EPI == EPI_SWIGLU_BWD) ? 2 * (size_t)N : (size_t)N;
   const int NT = N / OUTN;
-  // GEMM 2 takes the packed kernel's paired ragged ends (the same tile list and split-K
-  // plan, so both kernels split the same tiles the same way and stay bit-identical); a pair
-  // tile runs here as its two n-tiles. Without a split the tile list changes no output
-  // element's sum, so the other epilogues keep the plain list.
-  constexpr int kPairs = (EPI == EPI_NONE && !BT) ? kPairMinFullDown : 0;
   int n_wide = 0;
-  const int total = build_tile_starts<BM, true, kPairs>(offsets, E, NT, max_rows, s_start, s_perm,
-                                                        s_off, s_wsum, n_wide);
+  const int total =
+      build_tile_starts<BM, true>(offsets, E, NT, max_rows, s_start, s_perm, s_off, s_wsum, n_wide);
 
   const int xcd = blockIdx.x % kXcds, li = blockIdx.x / kXcds;
   const int nper = gridDim.x / kXcds;
@@ -326,10 +319,12 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   // One work item: tile `tile`, k-steps [kb, ke). A slice item (GEMM 2's split-K tail)
   // writes a float32 partial tile instead of bf16 rows. Each kind has its own call site, so
   // each gets its own register allocation.
-  auto run_sub = [&](const TileCoord& tc, int h, int kb, int ke, float* part, auto slice) {
+  auto run_tile = [&](int tile, int kb, int ke, float* part, auto slice) {
     constexpr bool kSlice = decltype(slice)::value;
+    const TileCoord tc = decode_tile(s_start, s_perm, s_off, E, n_wide, total, nper,
+                                      __builtin_amdgcn_readfirstlane(tile), BM, NT);
     const int e = __builtin_amdgcn_readfirstlane(tc.e);
-    const int n_t = __builtin_amdgcn_readfirstlane(tc.n_t + h);
+    const int n_t = __builtin_amdgcn_readfirstlane(tc.n_t);
     const int row0 = __builtin_amdgcn_readfirstlane(tc.row0);
     const int mrows = __builtin_amdgcn_readfirstlane(tc.mrows);
     // B halves: base pointers (uniform) of columns [0,128) and [128,256) of the tile
@@ -627,21 +622,6 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     }
   };
 
-  // A pair tile's second n-tile writes its partial (a slice item) at rows 128 .. 255 of the
-  // partial tile, where the packed kernel puts it; the tile is decoded again for it rather
-  // than held across the first half's k-loop.
-  auto run_tile = [&](int tile, int kb, int ke, float* part, auto slice) {
-    const TileCoord tc = decode_tile<kPairs>(s_start, s_perm, s_off, E, n_wide, total, nper,
-                                             __builtin_amdgcn_readfirstlane(tile), BM, NT);
-    run_sub(tc, 0, kb, ke, part, slice);
-    if constexpr (kPairs > 0) {
-      const TileCoord t2 = decode_tile<kPairs>(s_start, s_perm, s_off, E, n_wide, total, nper,
-                                               __builtin_amdgcn_readfirstlane(tile), BM, NT);
-      if (__builtin_amdgcn_readfirstlane(t2.pair))
-        run_sub(t2, 1, kb, ke, part != nullptr ? part + (BM / 2) * 256 : nullptr, slice);
-    }
-  };
-
   // Whole tiles round by round, then at most one split slice per block. Round r covers
   // tiles [r G, (r + 1) G) of the list; XCD x takes the x-th eighth of it, one tile per
   // block.
@@ -673,7 +653,6 @@ int device_cus() {
 // slice order, of the float32 partials). Re-derives the launch's tile list and split plan
 // from the same offsets and grid size. Block work item: 8 rows of one tile, 32 threads per
 // row, 8 columns per thread.
-template <int kPairs>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial,
                                                             const int32_t* __restrict__ offsets,
                                                             bf16_t* __restrict__ C, int E, int K,
@@ -683,18 +662,16 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   __shared__ int s_off[kMaxExperts + 1];
   __shared__ int s_wsum[4];
   int n_wide = 0;
-  const int total = build_tile_starts<BM, true, kPairs>(offsets, E, N / 256, max_rows, s_start,
-                                                        s_perm, s_off, s_wsum, n_wide);
+  const int total = build_tile_starts<BM, true>(offsets, E, N / 256, max_rows, s_start, s_perm,
+                                                s_off, s_wsum, n_wide);
   const SplitPlan plan = split_plan(total, grid, K / BK, true);
   const int tid = threadIdx.x;
   for (int w = blockIdx.x; w < plan.tail * (BM / 8); w += gridDim.x) {
     const int ti = w / (BM / 8);
-    const TileCoord tc = decode_tile<kPairs>(s_start, s_perm, s_off, E, n_wide, total,
-                                             grid / kXcds, plan.full + ti, BM, N / 256);
-    const int r = (w % (BM / 8)) * 8 + (tid >> 5);   // row of the partial tile
-    // a pair tile: rows 128 .. 255 hold its second n-tile
-    const int h = tc.pair ? r / (BM / 2) : 0, m = tc.pair ? r % (BM / 2) : r;
-    if (m >= tc.mrows) continue;
+    const TileCoord tc = decode_tile(s_start, s_perm, s_off, E, n_wide, total, grid / kXcds,
+                                      plan.full + ti, BM, N / 256);
+    const int r = (w % (BM / 8)) * 8 + (tid >> 5);
+    if (r >= tc.mrows) continue;
     const int c8 = (tid & 31) * 8;
     float acc[8];
 #pragma unroll
@@ -705,7 +682,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
       acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
       acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
     }
-    *(uint4*)(C + (size_t)(tc.row0 + m) * N + (tc.n_t + h) * 256 + c8) =
+    *(uint4*)(C + (size_t)(tc.row0 + r) * N + tc.n_t * 256 + c8) =
         make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
                    pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
   }
@@ -743,8 +720,8 @@ hipError_t launch_gemm_bf16(int epi, const bf16_t* a, const int32_t* row_token, 
   if (split) {
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(splitk_reduce_kernel<kPairMinFullDown>, dim3(1024), dim3(256), 0, s, partial, offsets, c,
-                       E, K, N, max_rows, grid);
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(1024), dim3(256), 0, s, partial, offsets, c, E,
+                       K, N, max_rows, grid);
   }
   return hipGetLastError();
 }
@@ -775,8 +752,8 @@ hipError_t launch_gemm_bf16_bt(int epi, const bf16_t* a, const int32_t* offsets,
   if (split) {
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(splitk_reduce_kernel<0>, dim3(1024), dim3(256), 0, s, partial, offsets, c,
-                       E, K, N, max_rows, grid);
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(1024), dim3(256), 0, s, partial, offsets, c, E,
+                       K, N, max_rows, grid);
   }
   return hipGetLastError();
 }
@@ -836,8 +813,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   constexpr bool kTwoMat = EPI == EPI_SWIGLU;
-  // paired ragged ends: GEMM 1 from one full m-tile, GEMM 2 from three (tile_order.h)
-  constexpr int kPairs = EPI == EPI_SWIGLU ? kPairMinFullUp : EPI == EPI_NONE ? kPairMinFullDown : 0;
+  constexpr bool kPairs = EPI == EPI_SWIGLU;   // paired ragged ends (no split-K here)
   constexpr int OUTN = kTwoMat ? 128 : 256;
   const int NT = N / OUTN, NB = N / 32, KS = K / 16;
   int n_wide = 0;
@@ -903,12 +879,10 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
     r.row0 = __builtin_amdgcn_readfirstlane(tc.row0);
     r.mrows = __builtin_amdgcn_readfirstlane(tc.mrows);
     const int rows_e = __builtin_amdgcn_readfirstlane(s_off[r.e + 1] - s_off[r.e]);
-    // the rows that decide the height: the expert's if it has a single m-tile, the tile's
-    // for the ragged end of a paired expert's odd last n-tile; every other tile of a wide
-    // expert runs at full height (a half-height tile beside its full siblings pulled its
-    // block out of step with the blocks sharing its weight panel)
-    const int hrows = rows_e <= kSmallRows ? rows_e : tc.odd_end ? r.mrows : BM;
-    r.cls = (kPairs > 0 && tc.pair) ? kPairTile
+    // the rows that decide the height: the expert's if it has a single m-tile; with paired
+    // ragged ends, the tile's (the ragged end of an odd last n-tile)
+    const int hrows = (kPairs && rows_e > kSmallRows) ? r.mrows : rows_e;
+    r.cls = (kPairs && tc.pair) ? kPairTile
             : hrows <= 64       ? kQuarterRows
             : hrows <= 128      ? kHalfRows
                                 : kFull;
@@ -938,15 +912,15 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
       t.a_src[i] = (const char*)(A + (size_t)r.arow[i] * K) + c * 16;
     }
     // B fragment j of k slice s: this lane's 16 bytes of block (nb_j, s). SwiGLU: j = 0 the
-    // gate block, j = 1 the up block of the same 32 output columns; otherwise column blocks
-    // 2 wn and 2 wn + 1 of the tile (a pair tile: j = 2, 3 the same for n-tile n_t + 1).
+    // gate block, j = 1 the up block of the same 32 output columns (a pair tile: j = 2, 3
+    // the same for n-tile n_t + 1).
 #pragma unroll
     for (int j = 0; j < 2 * kNB; ++j) {
       const bf16_t* P;
       int nb;
       if (kTwoMat) { P = (j & 1) == 0 ? P0 : P1; nb = (r.n_t + (j >> 1)) * 4 + wn; }
-      else { P = P0; nb = (r.n_t + (j >> 1)) * 8 + wn * 2 + (j & 1); }
-      if (j >= kNB && !(kPairs > 0 && r.cls == kPairTile)) nb = 0;   // not loaded
+      else { P = P0; nb = r.n_t * 8 + wn * 2 + (j & 1); }
+      if (j >= kNB && !(kPairs && r.cls == kPairTile)) nb = 0;   // not loaded
       t.bsrc[j] = P + ((size_t)r.e * NB + nb) * KS * 512 + lane * 8;
     }
   };
@@ -1075,9 +1049,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
     epilogue(acc, t.n_t, t.row0, t.mrows, part, slice);
   };
   // A pair tile: 4 A fragments by 4 weight fragments per slice (the k-loop's 2 x 2 form,
-  // the MFMAs of a full tile), then each n-tile's outputs through the tile epilogue (a
-  // slice item: the second n-tile's partial at rows 128 .. 255 of the partial tile).
-  auto run_pair = [&](const TileSrc& t, int kb, int ke, float* part, auto slice) {
+  // the MFMAs of a full tile), then each n-tile's outputs through the SwiGLU epilogue.
+  auto run_pair = [&](const TileSrc& t, int kb, int ke) {
     f32x16 acc[kNA / 2][2 * kNB];
 #pragma unroll
     for (int i = 0; i < kNA / 2; ++i)
@@ -1094,8 +1067,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
       for (int i = 0; i < kNA / 2; ++i)
 #pragma unroll
         for (int j = 0; j < kNB; ++j) half[i][j] = acc[i][h * kNB + j];
-      epilogue(half, t.n_t + h, t.row0, t.mrows,
-               part != nullptr ? part + h * (BM / 2) * 256 : nullptr, slice);
+      epilogue(half, t.n_t + h, t.row0, t.mrows, nullptr, std::false_type{});
     }
   };
   auto run_tile = [&](int tile, int kb, int ke, float* part, auto slice) {
@@ -1103,9 +1075,9 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
     tile_rows(tile, r);
     TileSrc t;
     tile_src(r, t);
-    if constexpr (kPairs > 0) {
+    if constexpr (kPairs) {
       if (r.cls == kPairTile) {
-        run_pair(t, kb, ke, part, slice);
+        run_pair(t, kb, ke);
         return;
       }
     }
@@ -1170,8 +1142,8 @@ hipError_t launch_gemm_bf16_packed(int epi, const bf16_t* a, const int32_t* row_
   if (split) {
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(splitk_reduce_kernel<kPairMinFullDown>, dim3(1024), dim3(256), 0, s, partial, offsets, c,
-                       E, K, N, max_rows, grid);
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(1024), dim3(256), 0, s, partial, offsets, c, E,
+                       K, N, max_rows, grid);
   }
   return hipGetLastError();
 }

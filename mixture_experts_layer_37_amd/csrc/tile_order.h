@@ -15,17 +15,13 @@
 // XCD left half the chip idle at the end). With no small expert (or no wide one) the merged
 // order is the list order.
 //
-// Paired ragged ends (`pair_min_full` > 0): a wide expert with at least pair_min_full
-// full-height m-tiles whose last m-tile holds at most kSmallRows rows gives that m-tile one
-// tile per PAIR of n-tiles, kSmallRows rows by both n-tiles' columns: the MFMAs of a full
-// tile, so it ends with the blocks that share its weight panels, where a half-height tile per
-// n-tile ended early and pulled its block out of step with them. Within the expert, n-tile
-// pair q holds the full-height m-tiles of n-tile 2q, those of 2q + 1, then the pair tile; an
-// odd last n-tile keeps a half-height tile of its own. GEMM 1 (SwiGLU, packed weights) pairs
-// from one full m-tile (kPairMinFullUp). GEMM 2 (no activation, plain and packed weights)
-// pairs from three (kPairMinFullDown): a pair tile streams two weight panels for 128 rows,
-// which pays on experts with many m-tiles (Mixtral +1.2-1.6%) and cost the 32-expert
-// workload's two-m-tile experts 6.8% when they paired too.
+// Paired ragged ends (`pairs`; GEMM 1 with SwiGLU on packed weights): a wide expert whose last
+// m-tile holds at most kSmallRows rows gives that m-tile one tile per PAIR of n-tiles,
+// kSmallRows rows by both n-tiles' columns: the MFMAs of a full tile, so it ends with the
+// blocks that share its weight panels, where a half-height tile per n-tile ended early and
+// pulled its block out of step with them. Within the expert, n-tile pair q holds the
+// full-height m-tiles of n-tile 2q, those of 2q + 1, then the pair tile; an odd last n-tile
+// keeps a half-height tile of its own.
 //
 // Plain constexpr C++ (implicitly host and device functions under hipcc): a host compiler
 // runs the same code in the CPU tests.
@@ -35,19 +31,13 @@ namespace moe {
 
 constexpr int kXcds = 8;          // XCDs of the chip, each with its own L2
 constexpr int kSmallRows = 128;   // rows of a small expert / of a pairable ragged end
-constexpr int kPairMinFullUp = 1;     // GEMM 1: pair from one full-height m-tile
-constexpr int kPairMinFullDown = 3;   // GEMM 2: pair from three
-
-// Whether an expert of m rows has a paired ragged end (pair_min_full 0: no pairs).
-constexpr bool paired_end(int m, int BMt, int pair_min_full) {
-  return pair_min_full > 0 && m > kSmallRows && m % BMt > 0 && m % BMt <= kSmallRows &&
-         m / BMt >= pair_min_full;
-}
 
 // Tiles of one expert of m rows: one per m-tile and n-tile, except for a paired ragged end.
-constexpr int expert_tiles(int m, int NT, int BMt, int pair_min_full) {
-  if (!paired_end(m, BMt, pair_min_full)) return ((m + BMt - 1) / BMt) * NT;
-  return (m / BMt) * NT + (NT + 1) / 2;   // full-height m-tiles, then the ragged end
+constexpr int expert_tiles(int m, int NT, int BMt, bool pairs) {
+  if (!pairs || m <= kSmallRows) return ((m + BMt - 1) / BMt) * NT;
+  const int rem = m % BMt;
+  const int mw = m / BMt + (rem > kSmallRows ? 1 : 0);   // full-height m-tiles
+  return mw * NT + (rem > 0 && rem <= kSmallRows ? (NT + 1) / 2 : 0);
 }
 
 // List index of merged position p. Runs of `run` tiles, kXcds runs per round: for rounds
@@ -78,15 +68,15 @@ constexpr int find_expert(const int* s_start, int E, int tile) {
   return lo;
 }
 
-// Tile `rem` of an expert of m_e > 0 rows: its n-tile, m-tile, whether it is a pair tile
-// (n-tiles n_t and n_t + 1), and whether it is the ragged end of an odd last n-tile of a
-// paired expert (which runs at half height; every other tile of a wide expert at full).
+// Tile `rem` of an expert of m_e > 0 rows: its n-tile, m-tile and whether it is a pair tile
+// (n-tiles n_t and n_t + 1).
 struct TileInExpert {
-  int n_t, m_t, pair, odd_end;
+  int n_t, m_t, pair;
 };
-constexpr TileInExpert tile_in_expert(int m_e, int rem, int NT, int BMt, int pair_min_full) {
-  TileInExpert t{0, 0, 0, 0};
-  if (!paired_end(m_e, BMt, pair_min_full)) {
+constexpr TileInExpert tile_in_expert(int m_e, int rem, int NT, int BMt, bool pairs) {
+  TileInExpert t{0, 0, 0};
+  const int ragged = m_e % BMt;
+  if (!pairs || m_e <= kSmallRows || ragged == 0 || ragged > kSmallRows) {
     const int mt_e = (m_e + BMt - 1) / BMt;
     t.n_t = rem / mt_e;
     t.m_t = rem - t.n_t * mt_e;
@@ -102,7 +92,6 @@ constexpr TileInExpert tile_in_expert(int m_e, int rem, int NT, int BMt, int pai
   } else {                             // the odd last n-tile: its m-tiles, then its end
     t.n_t = NT - 1;
     t.m_t = o;
-    t.odd_end = o == mw;
   }
   return t;
 }

@@ -168,12 +168,10 @@ def test_packed_gemms_are_bit_identical(activation):
 
 # Experts of every row class (none; at most 64 rows; at most 128; more), enough of the
 # small ones and of the large ones' m-tiles that, at a 256-block grid, both GEMMs take tiles
-# in the merged order that alternates the two classes by round and XCD (GEMM 1: 423 large-
-# and 306 small-class tiles; GEMM 2: 200 and 136). Ragged ends that pair in GEMM 1 (from one
-# full m-tile: 257, 384, 800, 1100) and in GEMM 2 (from three: 800, 1100), the latter with
-# pair tiles in GEMM 2's split-K tail (80 tiles in two slices).
+# in the merged order that alternates the two classes by round and XCD (GEMM 1: 306 tiles of
+# each class; GEMM 2: 136 of each, 16 of them in the split-K tail).
 MIXED_ROWS = [0, 1, 2, 5, 7, 17, 31, 32, 33, 50, 63, 64, 65, 90, 100, 120, 127, 128,
-              129, 255, 256, 257, 384, 600, 700, 800, 1000, 1100]
+              129, 255, 256, 257, 384, 600, 700, 1000]
 
 
 def test_interleaved_tile_order_matches_oracle():

@@ -1,11 +1,10 @@
 """The grouped GEMMs' tile order (csrc/tile_order.h: the two expert classes and their merged
-order, the paired ragged ends with their threshold) checked on the CPU: the same header the
-kernels compile, built with g++ into a checker that walks every launch position of many
-expert-size mixes and requires every output block (expert, m-tile, n-tile) to be covered by
-exactly one tile, pair tiles to hold at most 128 rows and two existing n-tiles of an expert
-with at least the threshold's full-height m-tiles, the odd-end flag only on the ragged end
-of a paired expert's odd last n-tile, and the merged order to be a permutation of the list.
-A planted mistake in the pair decoding, the threshold or the merged order fails it."""
+order, the paired ragged ends) checked on the CPU: the same header the kernels compile,
+built with g++ into a checker that walks every launch position of many expert-size mixes
+and requires every output block (expert, m-tile, n-tile) to be covered by exactly one tile,
+pair tiles to hold at most 128 rows and two existing n-tiles, and the merged order to be a
+permutation of the list. A planted mistake in the pair decoding or in the merged order
+fails it."""
 import os
 import shutil
 import subprocess
@@ -43,9 +42,7 @@ int main() {
     const int NT = 1 + rnd(20);
     const int runs[] = {1, 2, 8, 32, 64};
     const int run = runs[rnd(5)];
-    const int pair_choices[] = {0, 1, 3, kPairMinFullUp, kPairMinFullDown};
-    const int pairs = pair_choices[rnd(5)];
-    const bool classes = rnd(4) != 0;
+    const bool pairs = rnd(4) != 0, classes = rnd(4) != 0;
     std::vector<int> m(E);
     for (int e = 0; e < E; ++e) {
       switch (rnd(7)) {
@@ -78,15 +75,7 @@ int main() {
       const TileInExpert t = tile_in_expert(m[e], tile - start[slot], NT, BMt, pairs);
       const int mrows = m[e] - t.m_t * BMt < BMt ? m[e] - t.m_t * BMt : BMt;
       if (t.n_t < 0 || t.n_t >= NT || t.m_t < 0 || mrows <= 0) return fail("tile outside the expert", E, NT, run, pairs, classes);
-      if (t.pair && (t.n_t + 1 >= NT || mrows > kSmallRows || !pairs || m[e] / BMt < pairs))
-        return fail("bad pair tile", E, NT, run, pairs, classes);
-      if (t.odd_end && (t.pair || NT % 2 == 0 || t.n_t != NT - 1 || mrows > kSmallRows ||
-                        !pairs || m[e] / BMt < pairs || t.m_t != m[e] / BMt))
-        return fail("bad odd end", E, NT, run, pairs, classes);
-      // a paired expert's ragged end is a pair tile or the odd end, never a plain tile
-      if (pairs && m[e] > kSmallRows && m[e] / BMt >= pairs && m[e] % BMt > 0 &&
-          m[e] % BMt <= kSmallRows && t.m_t == m[e] / BMt && !t.pair && !t.odd_end)
-        return fail("unpaired ragged end", E, NT, run, pairs, classes);
+      if (t.pair && (t.n_t + 1 >= NT || mrows > kSmallRows || !pairs)) return fail("bad pair tile", E, NT, run, pairs, classes);
       const int mt_e = (m[e] + BMt - 1) / BMt;
       for (int h = 0; h <= t.pair; ++h)
         if (cov[e][(t.n_t + h) * mt_e + t.m_t]++) return fail("block covered twice", E, NT, run, pairs, classes);
@@ -137,14 +126,11 @@ PLANTED = {
     "pair_block_size": ("const int blk = 2 * mw + 1;", "const int blk = 2 * mw;"),
     # the odd last n-tile's ragged end counted as a pair tile
     "odd_tail_pair": ("    t.n_t = NT - 1;\n    t.m_t = o;", "    t.n_t = NT - 1;\n    t.m_t = o;\n    t.pair = o == mw;"),
-    # the odd last n-tile's ragged end left out of the tile count
-    "odd_tail_count": ("return (m / BMt) * NT + (NT + 1) / 2;", "return (m / BMt) * NT + NT / 2;"),
-    # the threshold ignored (every expert with a short ragged end paired)
-    "threshold_ignored": ("         m / BMt >= pair_min_full;", "         m / BMt >= 1;"),
-    # the odd end not flagged (it would run at full height)
-    "odd_end_unflagged": ("    t.odd_end = o == mw;", "    t.odd_end = 0;"),
     # the interleave gives the same class to both XCD parities
     "interleave_parity": ("return ((r + x) & 1) ? nw + idx : idx;", "return (r & 1) ? nw + idx : idx;"),
+    # a ragged end of exactly kSmallRows rows left out of the pairs (and of the tile count)
+    "boundary_rows": ("return mw * NT + (rem > 0 && rem <= kSmallRows ? (NT + 1) / 2 : 0);",
+                      "return mw * NT + (rem > 0 && rem < kSmallRows ? (NT + 1) / 2 : 0);"),
 }
 
 
