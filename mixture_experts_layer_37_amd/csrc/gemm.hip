@@ -860,11 +860,17 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
   // Row classes: full height (8 A fragments); half (4) and quarter (2) height for a tile
   // whose rows are all of an expert of at most 128 and 64 rows (and, with paired ragged
   // ends, for the ragged end of an odd last n-tile); a pair tile (4 A fragments by both
-  // n-tiles' weight fragments).
-  enum { kFull = 0, kHalfRows = 1, kQuarterRows = 2, kPairTile = 3 };
+  // n-tiles' weight fragments), and in an expert of at most 64 rows a quarter-height pair
+  // tile (2 A fragments by both n-tiles' weight fragments).
+  enum { kFull = 0, kHalfRows = 1, kQuarterRows = 2, kPairTile = 3, kPairQuarter = 4 };
+  // A DMA loads per k-step and wave of a class: its 32 NA rows, 8 per load, over 4 waves
+  // (rows past the expert's end are not loaded for a tile of fewer A fragments)
+  auto a_loads = [](int cls) {
+    return cls == kFull ? 8 : (cls == kQuarterRows || cls == kPairQuarter) ? 2 : 4;
+  };
   struct TileRows {
     int e, n_t, row0, mrows;
-    int cls;
+    int cls, la;
     int arow[8];
   };
   auto tile_rows = [&](int tile, TileRows& r) {
@@ -882,16 +888,17 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
     // the rows that decide the height: the expert's if it has a single m-tile; with paired
     // ragged ends, the tile's (the ragged end of an odd last n-tile)
     const int hrows = (kPairs && rows_e > kSmallRows) ? r.mrows : rows_e;
-    r.cls = (kPairs && tc.pair) ? kPairTile
+    r.cls = (kPairs && tc.pair) ? (rows_e <= 64 ? kPairQuarter : kPairTile)
             : hrows <= 64       ? kQuarterRows
             : hrows <= 128      ? kHalfRows
                                 : kFull;
     r.cls = __builtin_amdgcn_readfirstlane(r.cls);
-    // all eight row-map loads in flight together, then clamped
+    r.la = a_loads(r.cls);
+    // all the row-map loads in flight together, then clamped
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int rr = r.row0 + min(wave * 64 + i * 8 + (lane >> 3), r.mrows - 1);
-      r.arow[i] = row_token != nullptr ? row_token[rr] : rr;
+      const int rr = r.row0 + min(wave * 8 * r.la + i * 8 + (lane >> 3), r.mrows - 1);
+      r.arow[i] = row_token != nullptr && i < r.la ? row_token[rr] : rr;
     }
     if (row_token != nullptr) {
 #pragma unroll
@@ -907,7 +914,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
     // A: this lane's 16-byte chunk of row arow[i], at its swizzled place
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int rl = wave * 64 + i * 8 + (lane >> 3);
+      const int rl = wave * 8 * r.la + i * 8 + (lane >> 3);
       const int c = (lane & 7) ^ swz(rl);
       t.a_src[i] = (const char*)(A + (size_t)r.arow[i] * K) + c * 16;
     }
@@ -920,14 +927,16 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
       int nb;
       if (kTwoMat) { P = (j & 1) == 0 ? P0 : P1; nb = (r.n_t + (j >> 1)) * 4 + wn; }
       else { P = P0; nb = r.n_t * 8 + wn * 2 + (j & 1); }
-      if (j >= kNB && !(kPairs && r.cls == kPairTile)) nb = 0;   // not loaded
+      if (j >= kNB && !(kPairs && r.cls >= kPairTile)) nb = 0;   // not loaded
       t.bsrc[j] = P + ((size_t)r.e * NB + nb) * KS * 512 + lane * 8;
     }
   };
-  constexpr int kLA = 8;   // A DMA loads per k-step and wave: rows wave * 64 + 8 i + lane / 8
-  auto dma_for = [&](const TileSrc& t) {
-    return [&t, wave](int kt, bf16_t* stg, int i) {   // DMA instruction i of k-step kt
-      dma16_asm(t.a_src[i] + (uint32_t)(kt * BK * 2), lds_offset(stg) + (wave * kLA + i) * 1024);
+  // DMA instruction i of k-step kt for a class of LA loads per k-step and wave: rows
+  // wave * 8 LA + 8 i + lane / 8, each at row * 128 bytes of the stage
+  auto dma_for = [&](const TileSrc& t, auto la) {
+    constexpr int LA = decltype(la)::value;
+    return [&t, wave](int kt, bf16_t* stg, int i) {
+      dma16_asm(t.a_src[i] + (uint32_t)(kt * BK * 2), lds_offset(stg) + (wave * LA + i) * 1024);
     };
   };
 
@@ -1045,26 +1054,29 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
       for (int j = 0; j < kNB; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    packed_kloop<kLA, NA, kNB, NA>(kb, ke, sa0, sa1, t.bsrc, acc, load_a, dma_for(t));
+    packed_kloop<NA, NA, kNB, NA>(kb, ke, sa0, sa1, t.bsrc, acc, load_a,
+                                  dma_for(t, std::integral_constant<int, NA>{}));
     epilogue(acc, t.n_t, t.row0, t.mrows, part, slice);
   };
-  // A pair tile: 4 A fragments by 4 weight fragments per slice (the k-loop's 2 x 2 form,
-  // the MFMAs of a full tile), then each n-tile's outputs through the SwiGLU epilogue.
-  auto run_pair = [&](const TileSrc& t, int kb, int ke) {
-    f32x16 acc[kNA / 2][2 * kNB];
+  // A pair tile: NA (4, or 2 for an expert of at most 64 rows) A fragments by 4 weight
+  // fragments per slice (the k-loop's 2 x 2 form; at 4, the MFMAs of a full tile), then
+  // each n-tile's outputs through the SwiGLU epilogue.
+  auto run_pair = [&](const TileSrc& t, int kb, int ke, auto na) {
+    constexpr int NA = decltype(na)::value;
+    f32x16 acc[NA][2 * kNB];
 #pragma unroll
-    for (int i = 0; i < kNA / 2; ++i)
+    for (int i = 0; i < NA; ++i)
 #pragma unroll
       for (int j = 0; j < 2 * kNB; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    packed_kloop<kLA, kNA / 2, 2 * kNB, kNA / 2>(kb, ke, sa0, sa1, t.bsrc, acc, load_a,
-                                                  dma_for(t));
+    packed_kloop<NA, NA, 2 * kNB, NA>(kb, ke, sa0, sa1, t.bsrc, acc, load_a,
+                                      dma_for(t, std::integral_constant<int, NA>{}));
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      f32x16 half[kNA / 2][kNB];
+      f32x16 half[NA][kNB];
 #pragma unroll
-      for (int i = 0; i < kNA / 2; ++i)
+      for (int i = 0; i < NA; ++i)
 #pragma unroll
         for (int j = 0; j < kNB; ++j) half[i][j] = acc[i][h * kNB + j];
       epilogue(half, t.n_t + h, t.row0, t.mrows, nullptr, std::false_type{});
@@ -1077,7 +1089,11 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
     tile_src(r, t);
     if constexpr (kPairs) {
       if (r.cls == kPairTile) {
-        run_pair(t, kb, ke);
+        run_pair(t, kb, ke, std::integral_constant<int, kNA / 2>{});
+        return;
+      }
+      if (r.cls == kPairQuarter) {
+        run_pair(t, kb, ke, std::integral_constant<int, kNA / 4>{});
         return;
       }
     }

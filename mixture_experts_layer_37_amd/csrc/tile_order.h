@@ -15,13 +15,15 @@
 // XCD left half the chip idle at the end). With no small expert (or no wide one) the merged
 // order is the list order.
 //
-// Paired ragged ends (`pairs`; GEMM 1 with SwiGLU on packed weights): a wide expert whose last
+// Paired ragged ends (`pairs`; GEMM 1 with SwiGLU on packed weights): an expert whose last
 // m-tile holds at most kSmallRows rows gives that m-tile one tile per PAIR of n-tiles,
-// kSmallRows rows by both n-tiles' columns: the MFMAs of a full tile, so it ends with the
-// blocks that share its weight panels, where a half-height tile per n-tile ended early and
-// pulled its block out of step with them. Within the expert, n-tile pair q holds the
-// full-height m-tiles of n-tile 2q, those of 2q + 1, then the pair tile; an odd last n-tile
-// keeps a half-height tile of its own.
+// kSmallRows rows by both n-tiles' columns. In a wide expert that is the MFMAs of a full
+// tile, so it ends with the blocks that share its weight panels, where a half-height tile
+// per n-tile ended early and pulled its block out of step with them. A small expert's
+// m-tile is its ragged end too: its pair tiles stream two weight panels at once, twice the
+// weight bytes in flight per k-step of a half-height tile, which waits on memory. Within
+// the expert, n-tile pair q holds the full-height m-tiles of n-tile 2q, those of 2q + 1
+// (none in a small expert), then the pair tile; an odd last n-tile keeps a tile of its own.
 //
 // Plain constexpr C++ (implicitly host and device functions under hipcc): a host compiler
 // runs the same code in the CPU tests.
@@ -34,7 +36,7 @@ constexpr int kSmallRows = 128;   // rows of a small expert / of a pairable ragg
 
 // Tiles of one expert of m rows: one per m-tile and n-tile, except for a paired ragged end.
 constexpr int expert_tiles(int m, int NT, int BMt, bool pairs) {
-  if (!pairs || m <= kSmallRows) return ((m + BMt - 1) / BMt) * NT;
+  if (!pairs || m <= 0) return ((m + BMt - 1) / BMt) * NT;
   const int rem = m % BMt;
   const int mw = m / BMt + (rem > kSmallRows ? 1 : 0);   // full-height m-tiles
   return mw * NT + (rem > 0 && rem <= kSmallRows ? (NT + 1) / 2 : 0);
@@ -76,13 +78,15 @@ struct TileInExpert {
 constexpr TileInExpert tile_in_expert(int m_e, int rem, int NT, int BMt, bool pairs) {
   TileInExpert t{0, 0, 0};
   const int ragged = m_e % BMt;
-  if (!pairs || m_e <= kSmallRows || ragged == 0 || ragged > kSmallRows) {
+  if (!pairs || ragged == 0 || ragged > kSmallRows) {
     const int mt_e = (m_e + BMt - 1) / BMt;
     t.n_t = rem / mt_e;
     t.m_t = rem - t.n_t * mt_e;
     return t;
   }
-  const int mw = m_e / BMt;            // full-height m-tiles; the ragged end is m-tile mw
+  // full-height m-tiles (0 in a small expert; then o < 2 mw never holds, so no division by
+  // zero below); the ragged end is m-tile mw
+  const int mw = m_e / BMt;
   const int blk = 2 * mw + 1;          // tiles of one n-tile pair
   const int q = rem / blk, o = rem - q * blk;
   if (q < NT / 2) {

@@ -122,8 +122,9 @@ def test_tile_order_covers_every_block_once():
 
 
 PLANTED = {
-    # a pair block one tile short: the pair tile of one n-tile pair lands on the next pair
-    "pair_block_size": ("const int blk = 2 * mw + 1;", "const int blk = 2 * mw;"),
+    # a pair block one tile too long: each n-tile pair's tiles drift into the next pair's
+    # (one tile short instead divides by zero for a small expert, whose block is one tile)
+    "pair_block_size": ("const int blk = 2 * mw + 1;", "const int blk = 2 * mw + 2;"),
     # the odd last n-tile's ragged end counted as a pair tile
     "odd_tail_pair": ("    t.n_t = NT - 1;\n    t.m_t = o;", "    t.n_t = NT - 1;\n    t.m_t = o;\n    t.pair = o == mw;"),
     # the interleave gives the same class to both XCD parities
