@@ -45,7 +45,7 @@ def parse_args():
     ap.add_argument("--weights", choices=("packed", "plain"), default="packed",
                     help="expert weight layout of the timed forward (bf16)")
     ap.add_argument("--no-extra-workloads", action="store_true",
-                    help="time the headline workload only")
+                    help="time the headline workload only (and skip the vendor BLAS reference)")
     ap.add_argument("--extra-steps", type=int, default=20,
                     help="timed steps of each of the other workloads")
     ap.add_argument("--extra-warmup", type=int, default=5)
@@ -420,6 +420,9 @@ def main():
         if key in head:
             result[key] = head[key]
     result["measured_peaks"] = peaks
+    if not args.no_extra_workloads and cfg.dtype == C.BF16:
+        result["vendor_gemm"] = vendor_gemm_reference(cfg, stream, head["stages_us"])
+        torch.cuda.empty_cache()
     if peaks is not None:
         result["roofline"]["peak_measured"] = peaks["mfma_bf16_tflops"]
         result["roofline"]["frac_of_measured"] = up_tflops / peaks["mfma_bf16_tflops"]
@@ -542,6 +545,43 @@ def measured_peaks(stream):
     ms_copy = timed(lambda: lib.moe_peak_copy(src.data_ptr(), dst.data_ptr(), nbytes, sh))
     return {"mfma_bf16_tflops": blocks * 4 * iters * 8 * 32768 / (ms_mfma * 1e-3) / 1e12,
             "hbm_copy_gbs": 2 * nbytes / (ms_copy * 1e-3) / 1e9}
+
+
+def vendor_gemm_reference(cfg, stream, stages_us, reps=7):
+    """The ROCm BLAS (torch.bmm) on the same two expert products with the rows split evenly,
+    T*k/E per expert, bf16, contiguous operands: GEMM 1's x_e [R, H] x [H, 2I] (gate and up
+    side by side, no activation) and GEMM 2's h_e [R, I] x [I, H]. A reference beside the
+    grouped GEMMs (which also gather x, apply SwiGLU and take the routed, uneven rows); the
+    layer never calls it. Median of `reps` after two warm-up calls."""
+    import torch
+    E, H, I = cfg.experts, cfg.hidden, cfg.inter
+    R = cfg.tokens * cfg.top_k // E
+    gen = torch.Generator(device="cuda").manual_seed(0)
+
+    def med_us(fn):
+        for _ in range(2):
+            fn()
+        ts = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        return sorted(ts)[len(ts) // 2]
+
+    out = {"library": "torch.bmm (ROCm BLAS)", "rows_per_expert": R}
+    for key, K, N, stage in (("gemm_up", H, 2 * I, "gemm_up"), ("gemm_down", I, H, "gemm_down")):
+        a = torch.randn(E, R, K, device="cuda", dtype=torch.bfloat16, generator=gen)
+        b = torch.randn(E, K, N, device="cuda", dtype=torch.bfloat16, generator=gen) * K ** -0.5
+        us = med_us(lambda: torch.bmm(a, b))
+        del a, b
+        tflops = 2.0 * E * R * K * N / (us * 1e-6) / 1e12
+        out[key] = {"us": us, "tflops": tflops, "frac_of_peak": tflops / PEAK_BF16_TFLOPS,
+                    "grouped_us": stages_us[stage], "grouped_over_vendor": stages_us[stage] / us}
+    return out
 
 
 def one_pass_read_us(stream, buf, nbytes, step, reps=7):

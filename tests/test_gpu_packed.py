@@ -168,21 +168,24 @@ def test_packed_gemms_are_bit_identical(activation):
 
 # Experts of every row class (none; at most 64 rows; at most 128; more), enough of the
 # small ones and of the large ones' m-tiles that, at a 256-block grid, both GEMMs take tiles
-# in the merged order that alternates the two classes by round and XCD (GEMM 1: 306 tiles of
-# each class; GEMM 2: 136 of each, 16 of them in the split-K tail).
+# in the merged order that alternates the two classes by round and XCD. GEMM 1 (small
+# experts and the large ones' short ragged ends in pair tiles): 279 wide and 153 small tiles
+# at I = 2304; at I = 2176 (17 n-tiles) 265 and 153, each small expert's odd last n-tile a
+# tile of its own. GEMM 2: 136 of each class, with a split-K tail.
 MIXED_ROWS = [0, 1, 2, 5, 7, 17, 31, 32, 33, 50, 63, 64, 65, 90, 100, 120, 127, 128,
               129, 255, 256, 257, 384, 600, 700, 1000]
 
 
-def test_interleaved_tile_order_matches_oracle():
+@pytest.mark.parametrize("inter", [2304, 2176])
+def test_interleaved_tile_order_matches_oracle(inter):
     """Both GEMMs over experts of all row classes, outputs pre-filled with NaN: every row of
     h and y written, packed and plain kernels bit-identical, y against the oracle's FFN."""
     import oracle as O
     from mixture_experts_layer_37_amd.inputs import as_float
     E, T = len(MIXED_ROWS), sum(MIXED_ROWS)
-    cfg = C.SMALL.with_(name="mixed_rows", tokens=T, hidden=2048, inter=2304, experts=E,
+    cfg = C.SMALL.with_(name="mixed_rows", tokens=T, hidden=2048, inter=inter, experts=E,
                         top_k=1, bias=None)
-    print(f"[case] interleaved tile order rows {MIXED_ROWS}", flush=True)
+    print(f"[case] interleaved tile order rows {MIXED_ROWS}, I {inter}", flush=True)
     inp = make_inputs(cfg, seed=21)
     layer = MoELayer(cfg.with_(weights="packed"), inp)
     x = to_device(cfg, inp["x"])
