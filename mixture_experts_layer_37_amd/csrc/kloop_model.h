@@ -200,6 +200,67 @@ constexpr bool counts_fit() {
   return true;
 }
 
+// The loop's schedule, as data the loop executes: pairs of steady k-steps while at least two
+// more remain, then the last two. Each entry is {offset from the pair's first k-step, ring
+// base, k-steps left counting this one (capped at 3, the steady state: a next k-step for
+// 2 or more, a refill for 3 or more)}. The B slices of k-step kt sit in ring slots
+// (4 kt + s) mod kRingSlots, so a pair's bases are the constants 0 and 4.
+constexpr int kRingSlots = 8;
+struct StepSlot {
+  int off, sb, r;
+};
+constexpr StepSlot kSteadyPair[] = {{0, 0, 3}, {1, 4, 3}};
+constexpr StepSlot kLastPair[] = {{0, 0, 2}, {1, 4, 1}};
+constexpr int kPairSteps = 2;
+
+// Replay of the schedule over tiles of 2 .. 40 k-steps with the ring's slots: every k-step
+// runs once, in order, with the predicates of its position; every wait for slice s of
+// k-step kt finds that slice in its slot; no load overwrites a slice not yet read; and every
+// slice loaded is read. (A slot loaded and never read would leave an asm output unused, and
+// the compiler may give its registers to another value while the load is in flight.)
+// Returns the number of violations.
+constexpr int schedule_mismatches() {
+  int bad = 0;
+  for (int n = 2; n <= 40; n += 2) {
+    int slot_kt[kRingSlots] = {}, slot_s[kRingSlots] = {};
+    bool unread[kRingSlots] = {}, filled[kRingSlots] = {};
+    auto load = [&](int slot, int kt, int sl) {
+      if (unread[slot]) ++bad;
+      slot_kt[slot] = kt;
+      slot_s[slot] = sl;
+      unread[slot] = true;
+      filled[slot] = true;
+    };
+    for (int j = 0; j < kPrologueOps; ++j)
+      if (kPrologue[j].kind == kLoadB) load(kPrologue[j].arg % kRingSlots, 0, kPrologue[j].arg);
+    int expect = 0;
+    auto run = [&](const StepSlot* t, int kt0) {
+      for (int e = 0; e < kPairSteps; ++e) {
+        const int kt = kt0 + t[e].off, left = n - kt;
+        if (kt != expect++) ++bad;
+        if (t[e].r != (left < 3 ? left : 3)) ++bad;
+        if (t[e].sb != (4 * kt) % kRingSlots) ++bad;
+        for (int sl = 0; sl < 4; ++sl) {
+          const int slot = (t[e].sb + sl) % kRingSlots;
+          if (!filled[slot] || slot_kt[slot] != kt || slot_s[slot] != sl) ++bad;
+          unread[slot] = false;
+          if (t[e].r >= 2) load((t[e].sb + 4 + sl) % kRingSlots, kt + 1, sl);
+        }
+      }
+    };
+    int kt = 0;
+    for (; kt + 2 < n; kt += kPairSteps) run(kSteadyPair, kt);
+    run(kLastPair, kt);
+    if (expect != n) ++bad;
+    for (int q = 0; q < kRingSlots; ++q)
+      if (unread[q]) ++bad;
+  }
+  return bad;
+}
+static_assert(schedule_mismatches() == 0,
+              "the loop's schedule breaks the ring (a slice read before its load, overwritten "
+              "unread, or loaded and never read) or the k-steps' order or predicates");
+
 // The counts in numbers, for kLA = 8 A DMA instructions per k-step (both kernels) and kLB
 // = 4 B loads per slice (the 2 x 2 wave layout): 3 kLB + kLA = 20 before slice 0's MFMAs,
 // 2 kLB + kLA + kLB = 20 before slice 1's and kLB + kLA + 2 kLB = 20 before slice 2's when a

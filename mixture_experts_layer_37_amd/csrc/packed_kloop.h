@@ -88,7 +88,9 @@ struct PackedKLoop {
   static_assert(kLB * kNA <= 16, "at most 16 MFMAs per slice: 256 accumulator registers");
   static_assert(kloop::tile_mismatches<kLA, kLB>() == 0 && kloop::counts_fit<kLA, kLB>(),
                 "k-loop wait counts disagree with the issue order");
-  bf16x8 bv[8][kLB];          // ring of eight k slices of B fragments (at most five live)
+  // ring of k slices of B fragments (at most five live): slice s of k-step kt (counted from
+  // the tile's first) in slot (4 kt + s) mod kloop::kRingSlots
+  bf16x8 bv[kloop::kRingSlots][kLB];
   FragA<kNA> fr[2];           // A fragments of slices of even / odd index
 
   // B slice kk (0..3) of the k-step whose slice 0 is at base[j]
@@ -169,12 +171,16 @@ struct PackedKLoop {
         },
         std::make_integer_sequence<int, kStartOps>{});
 
-    // k-step kt on stage `cur` (its B in ring slots sb .. sb + 3), `nxt` in flight; `refill`
-    // (kt + 2 < ke) and `next` (kt + 1 < ke) are compile-time at every call site, so the
-    // steady-state loop carries no branches, which keeps the fragments in VGPRs and the
-    // accumulators in AGPRs.
-    auto kstep = [&](int kt, bf16_t* cur, bf16_t* nxt, int sb, auto refill, auto next) {
-      constexpr bool kNext = decltype(next)::value, kRefill = decltype(refill)::value;
+    // k-step kt on stage `cur` (its B in ring slots sb .. sb + 3), `nxt` in flight, with R
+    // k-steps left counting itself (capped at 3): a next k-step (kt + 1 < ke) for R >= 2, a
+    // refill of `cur` (kt + 2 < ke) for R >= 3. sb and R are compile-time at every call
+    // site, so the steady-state loop carries no branches and indexes the ring with
+    // constants, which keeps the fragments in VGPRs and the accumulators in AGPRs.
+    constexpr int kMask = kRingSlots - 1;
+    static_assert((kRingSlots & kMask) == 0, "a power-of-two ring");
+    auto kstep = [&](int kt, bf16_t* cur, bf16_t* nxt, auto sbc, auto rem) {
+      constexpr int sb = decltype(sbc)::value, R = decltype(rem)::value;
+      constexpr bool kNext = R >= 2, kRefill = R >= 3;
       const bf16_t* nbase[kLB];   // slice 0 of k-step kt + 1
 #pragma unroll
       for (int j = 0; j < kLB; ++j) nbase[j] = bsrc[j] + (size_t)(kt + 1) * 2048;
@@ -186,13 +192,13 @@ struct PackedKLoop {
             if constexpr (op.kind == kLgkm0) {
               __builtin_amdgcn_s_waitcnt(kWaitLgkm0Only);
             } else if constexpr (op.kind == kWaitB) {
-              wait_loads<count, kLB>(bv[(sb + op.arg) & 7]);
+              wait_loads<count, kLB>(bv[(sb + op.arg) & kMask]);
             } else if constexpr (op.kind == kReadA) {
               load_a(cur, op.arg, fr[op.arg & 1]);
             } else if constexpr (op.kind == kLoadBNext && op.arg < 3) {
-              if constexpr (kNext) load_b<op.arg>(nbase, (sb + 4 + op.arg) & 7);
+              if constexpr (kNext) load_b<op.arg>(nbase, (sb + 4 + op.arg) & kMask);
             } else if constexpr (op.kind == kMfma && op.arg < 3) {
-              mfma16(fr[op.arg & 1], (sb + op.arg) & 7);
+              mfma16(fr[op.arg & 1], (sb + op.arg) & kMask);
               for_each_op([&](auto) {   // one A read, then kM / kAReads MFMAs
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, kM / kAReads, 0);
@@ -213,7 +219,7 @@ struct PackedKLoop {
               // reads spread over its last kAReads MFMAs, then slice 3 + 4 of the next k-step.
               // DMAs and B loads are inline asm, which the compiler does not move MFMAs
               // across; the A reads are ordinary LDS loads placed by the scheduling groups.
-              const bf16x8* b3 = bv[(sb + 3) & 7];
+              const bf16x8* b3 = bv[(sb + 3) & kMask];
               constexpr int kD = kM - kAReads;
               constexpr int kPer = (kLA + kD - 1) / kD;
               constexpr int kDmas = kRefill ? kLA : 0;
@@ -236,22 +242,30 @@ struct PackedKLoop {
                 }, std::make_integer_sequence<int, kAReads>{});
               }
               __builtin_amdgcn_sched_barrier(0);
-              if constexpr (kNext) load_b<3>(nbase, (sb + 7) & 7);
+              if constexpr (kNext) load_b<3>(nbase, (sb + 7) & kMask);
             } else {
               static_assert(op.kind == kLgkm0, "op not allowed in a k-step");
             }
           },
           std::make_integer_sequence<int, kStepOps>{});
     };
-    using yes = std::true_type;
-    using no = std::false_type;
+    // The schedule (kloop_model.h, replayed there against the ring and the k-steps' order):
+    // steady pairs while kt + 2 < ke (ke - kt is even, so both steps of such a pair have a
+    // refill), then the last pair. An entry's stage is sa0 at an even offset.
+    auto run_pair = [&](auto last, int kt0) {
+      constexpr const StepSlot* t = decltype(last)::value ? kLastPair : kSteadyPair;
+      for_each_op(
+          [&](auto I) {
+            constexpr StepSlot e = t[decltype(I)::value];
+            const bool odd = e.off & 1;
+            kstep(kt0 + e.off, odd ? sa1 : sa0, odd ? sa0 : sa1,
+                  std::integral_constant<int, e.sb>{}, std::integral_constant<int, e.r>{});
+          },
+          std::make_integer_sequence<int, kPairSteps>{});
+    };
     int kt = kb;
-    for (; kt + 2 < ke; kt += 2) {
-      kstep(kt, sa0, sa1, 0, yes{}, yes{});
-      kstep(kt + 1, sa1, sa0, 4, yes{}, yes{});
-    }
-    kstep(kt, sa0, sa1, 0, no{}, yes{});
-    kstep(kt + 1, sa1, sa0, 4, no{}, no{});
+    for (; kt + 2 < ke; kt += kPairSteps) run_pair(std::false_type{}, kt);
+    run_pair(std::true_type{}, kt);
     __syncthreads();   // every wave is done with both stages before the next tile's DMA
   }
 };

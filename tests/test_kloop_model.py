@@ -58,6 +58,16 @@ PERTURBATIONS = {
     # change, and the documented numbers no longer match
     "step_order": ("{kLgkm0, 0}, {kWaitB, 0}, {kReadA, 1}, {kLoadBNext, 0}, {kMfma, 0},",
                    "{kLgkm0, 0}, {kLoadBNext, 0}, {kWaitB, 0}, {kReadA, 1}, {kMfma, 0},"),
+    # a ring of 16 slots under the pair schedule: the second step of a pair loads slots
+    # 8..11, which no later step reads (asm outputs left unused while their loads are in
+    # flight), and the next pair reads stale slots
+    "ring_slots": ("constexpr int kRingSlots = 8;", "constexpr int kRingSlots = 16;"),
+    # the second step of a steady pair on the first one's ring base
+    "steady_ring_base": ("constexpr StepSlot kSteadyPair[] = {{0, 0, 3}, {1, 4, 3}};",
+                         "constexpr StepSlot kSteadyPair[] = {{0, 0, 3}, {1, 0, 3}};"),
+    # the step before the last run as a steady one: it would refill a stage past the tile
+    "last_pair_remaining": ("constexpr StepSlot kLastPair[] = {{0, 0, 2}, {1, 4, 1}};",
+                            "constexpr StepSlot kLastPair[] = {{0, 0, 3}, {1, 4, 1}};"),
 }
 
 
