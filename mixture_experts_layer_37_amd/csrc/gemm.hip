@@ -853,10 +853,10 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
     const char* a_src[8];
     const bf16_t* bsrc[2 * kNB];   // a pair tile: both n-tiles' fragments
   };
-  // A tile's coordinates and the token rows of its 8 A DMA loads per wave (rows past the
-  // expert's end re-read its last row, never written back; with the gather fused in, rows
-  // of x through row_token, clamped into [0, a_rows)). The row-map loads are the only
-  // global loads here.
+  // A tile's coordinates and the token rows of its A DMA loads (8, 4 or 2 per wave by row
+  // class; rows past the expert's end re-read its last row, never written back; with the
+  // gather fused in, rows of x through row_token, clamped into [0, a_rows)). The row-map
+  // loads are the only global loads here.
   // Row classes: full height (8 A fragments); half (4) and quarter (2) height for a tile
   // whose rows are all of an expert of at most 128 and 64 rows (and, with paired ragged
   // ends, for the ragged end of an odd last n-tile); a pair tile (4 A fragments by both
@@ -1037,9 +1037,10 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
 
   // One tile at a time: its loads, k-loop and epilogue (the single-matrix epilogues stage
   // their output through the two A stages, so the next tile's DMA waits for them).
-  // The tile of an expert with at most 128 rows runs the same loads, waits and barriers
-  // with only the first 4 A fragments (at most 64 rows: the first 2): a half (a quarter) of
-  // the MFMAs and fragment reads, no accumulator for rows that are all padding. Each row
+  // The tile of an expert with at most 128 rows runs the same weight loads, waits and
+  // barriers with only the first 4 A fragments (at most 64 rows: the first 2) and as many A
+  // DMA loads per wave: a half (a quarter) of the MFMAs, fragment reads and token-row
+  // loads, no accumulator for rows that are all padding. Each row
   // class is its own instantiation of the k-loop, so none carries a branch inside it. The
   // quarter class pays where small-expert tiles run beside large-expert ones (GEMM 2 of the
   // 32-expert workload 3-4% faster). (An expert's last, partial m-tile beside full ones
