@@ -209,6 +209,11 @@ constexpr int kRingSlots = 8;
 struct StepSlot {
   int off, sb, r;
 };
+// The slot a k-step on ring base sb waits on for its slice s, and the slot it loads slice s
+// of the next k-step into; the loop indexes its ring with these, and the replay below
+// checks them.
+constexpr int wait_slot(int sb, int s) { return (sb + s) % kRingSlots; }
+constexpr int next_slot(int sb, int s) { return (sb + 4 + s) % kRingSlots; }
 constexpr StepSlot kSteadyPair[] = {{0, 0, 3}, {1, 4, 3}};
 constexpr StepSlot kLastPair[] = {{0, 0, 2}, {1, 4, 1}};
 constexpr int kPairSteps = 2;
@@ -241,10 +246,10 @@ constexpr int schedule_mismatches() {
         if (t[e].r != (left < 3 ? left : 3)) ++bad;
         if (t[e].sb != (4 * kt) % kRingSlots) ++bad;
         for (int sl = 0; sl < 4; ++sl) {
-          const int slot = (t[e].sb + sl) % kRingSlots;
+          const int slot = wait_slot(t[e].sb, sl);
           if (!filled[slot] || slot_kt[slot] != kt || slot_s[slot] != sl) ++bad;
           unread[slot] = false;
-          if (t[e].r >= 2) load((t[e].sb + 4 + sl) % kRingSlots, kt + 1, sl);
+          if (t[e].r >= 2) load(next_slot(t[e].sb, sl), kt + 1, sl);
         }
       }
     };

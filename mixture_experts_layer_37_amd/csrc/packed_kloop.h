@@ -176,8 +176,6 @@ struct PackedKLoop {
     // refill of `cur` (kt + 2 < ke) for R >= 3. sb and R are compile-time at every call
     // site, so the steady-state loop carries no branches and indexes the ring with
     // constants, which keeps the fragments in VGPRs and the accumulators in AGPRs.
-    constexpr int kMask = kRingSlots - 1;
-    static_assert((kRingSlots & kMask) == 0, "a power-of-two ring");
     auto kstep = [&](int kt, bf16_t* cur, bf16_t* nxt, auto sbc, auto rem) {
       constexpr int sb = decltype(sbc)::value, R = decltype(rem)::value;
       constexpr bool kNext = R >= 2, kRefill = R >= 3;
@@ -192,13 +190,13 @@ struct PackedKLoop {
             if constexpr (op.kind == kLgkm0) {
               __builtin_amdgcn_s_waitcnt(kWaitLgkm0Only);
             } else if constexpr (op.kind == kWaitB) {
-              wait_loads<count, kLB>(bv[(sb + op.arg) & kMask]);
+              wait_loads<count, kLB>(bv[wait_slot(sb, op.arg)]);
             } else if constexpr (op.kind == kReadA) {
               load_a(cur, op.arg, fr[op.arg & 1]);
             } else if constexpr (op.kind == kLoadBNext && op.arg < 3) {
-              if constexpr (kNext) load_b<op.arg>(nbase, (sb + 4 + op.arg) & kMask);
+              if constexpr (kNext) load_b<op.arg>(nbase, next_slot(sb, op.arg));
             } else if constexpr (op.kind == kMfma && op.arg < 3) {
-              mfma16(fr[op.arg & 1], (sb + op.arg) & kMask);
+              mfma16(fr[op.arg & 1], wait_slot(sb, op.arg));
               for_each_op([&](auto) {   // one A read, then kM / kAReads MFMAs
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, kM / kAReads, 0);
@@ -219,7 +217,7 @@ struct PackedKLoop {
               // reads spread over its last kAReads MFMAs, then slice 3 + 4 of the next k-step.
               // DMAs and B loads are inline asm, which the compiler does not move MFMAs
               // across; the A reads are ordinary LDS loads placed by the scheduling groups.
-              const bf16x8* b3 = bv[(sb + 3) & kMask];
+              const bf16x8* b3 = bv[wait_slot(sb, 3)];
               constexpr int kD = kM - kAReads;
               constexpr int kPer = (kLA + kD - 1) / kD;
               constexpr int kDmas = kRefill ? kLA : 0;
@@ -242,7 +240,7 @@ struct PackedKLoop {
                 }, std::make_integer_sequence<int, kAReads>{});
               }
               __builtin_amdgcn_sched_barrier(0);
-              if constexpr (kNext) load_b<3>(nbase, (sb + 7) & kMask);
+              if constexpr (kNext) load_b<3>(nbase, next_slot(sb, 3));
             } else {
               static_assert(op.kind == kLgkm0, "op not allowed in a k-step");
             }

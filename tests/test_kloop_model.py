@@ -62,6 +62,10 @@ PERTURBATIONS = {
     # 8..11, which no later step reads (asm outputs left unused while their loads are in
     # flight), and the next pair reads stale slots
     "ring_slots": ("constexpr int kRingSlots = 8;", "constexpr int kRingSlots = 16;"),
+    # the next k-step's slices loaded two k-steps' worth of slots ahead: the waits then read
+    # slots never loaded
+    "next_slot": ("constexpr int next_slot(int sb, int s) { return (sb + 4 + s) % kRingSlots; }",
+                  "constexpr int next_slot(int sb, int s) { return (sb + 8 + s) % kRingSlots; }"),
     # the second step of a steady pair on the first one's ring base
     "steady_ring_base": ("constexpr StepSlot kSteadyPair[] = {{0, 0, 3}, {1, 4, 3}};",
                          "constexpr StepSlot kSteadyPair[] = {{0, 0, 3}, {1, 0, 3}};"),
