@@ -176,20 +176,20 @@ MIXED_ROWS = [0, 1, 2, 5, 7, 17, 31, 32, 33, 50, 63, 64, 65, 90, 100, 120, 127, 
               129, 255, 256, 257, 384, 600, 700, 1000]
 
 
-@pytest.mark.parametrize("inter", [2304, 2176])
-def test_interleaved_tile_order_matches_oracle(inter):
-    """Both GEMMs over experts of all row classes, outputs pre-filled with NaN: every row of
-    h and y written, packed and plain kernels bit-identical, y against the oracle's FFN."""
+def _check_expert_rows(rows, hidden, inter, seed, label):
+    """Both GEMMs over experts with the given rows (offsets given directly), outputs
+    pre-filled with NaN: every row of h and y written, packed and plain kernels
+    bit-identical (y with and without the split-K tail), y against the oracle's FFN."""
     import oracle as O
     from mixture_experts_layer_37_amd.inputs import as_float
-    E, T = len(MIXED_ROWS), sum(MIXED_ROWS)
-    cfg = C.SMALL.with_(name="mixed_rows", tokens=T, hidden=2048, inter=inter, experts=E,
+    E, T = len(rows), int(sum(rows))
+    cfg = C.SMALL.with_(name="mixed_rows", tokens=T, hidden=hidden, inter=inter, experts=E,
                         top_k=1, bias=None)
-    print(f"[case] interleaved tile order rows {MIXED_ROWS}, I {inter}", flush=True)
-    inp = make_inputs(cfg, seed=21)
+    print(f"[case] {label}: E {E} H {hidden} I {inter} rows {list(rows)}", flush=True)
+    inp = make_inputs(cfg, seed=seed)
     layer = MoELayer(cfg.with_(weights="packed"), inp)
     x = to_device(cfg, inp["x"])
-    offs_np = np.concatenate([[0], np.cumsum(MIXED_ROWS)]).astype(np.int32)
+    offs_np = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
     offs = torch.from_numpy(offs_np).cuda()
     I, H = cfg.inter, cfg.hidden
     out = {}
@@ -216,6 +216,40 @@ def test_interleaved_tile_order_matches_oracle(inter):
             if r1 > r0:
                 ref[r0:r1] = O.expert_ffn(x32[r0:r1], wg[e], wu[e], wd[e], cfg.activation)
         P.assert_layer_close(got, ref, "y")
+
+
+@pytest.mark.parametrize("inter", [2304, 2176])
+def test_interleaved_tile_order_matches_oracle(inter):
+    _check_expert_rows(MIXED_ROWS, 2048, inter, 21, "interleaved tile order")
+
+
+def _random_rows(rng, E):
+    """Rows per expert drawn across every tile class: none, at most 64, at most 128, one
+    ragged m-tile above 128, whole m-tiles plus a pairable (<= 128) or a full-height ragged
+    end, and whole m-tiles only."""
+    rows = []
+    for _ in range(E):
+        c = rng.choice(7, p=[0.1, 0.25, 0.15, 0.1, 0.2, 0.1, 0.1])
+        k = int(rng.integers(1, 4))
+        rows.append([0, int(rng.integers(1, 65)), int(rng.integers(65, 129)),
+                     int(rng.integers(129, 256)), 256 * k + int(rng.integers(1, 129)),
+                     256 * k + int(rng.integers(129, 256)), 256 * k][c])
+    if sum(rows) == 0:
+        rows[0] = 1
+    return rows
+
+
+# Seeded random expert mixes: expert counts, hidden sizes and intermediate sizes with an odd
+# or even number of 128-wide n-tiles (3, 5, 8, 9), so that small experts' pairs, their odd
+# last n-tiles, the wide experts' paired ragged ends and the split-K tail all occur in
+# mixes no hand list fixes.
+@pytest.mark.parametrize("seed", range(6))
+def test_random_expert_mixes_match_oracle(seed):
+    rng = np.random.default_rng(1000 + seed)
+    E = int(rng.choice([3, 9, 17, 24]))
+    hidden = int(rng.choice([256, 512]))
+    inter = int(rng.choice([384, 640, 1024, 1152]))
+    _check_expert_rows(_random_rows(rng, E), hidden, inter, 50 + seed, f"random mix {seed}")
 
 
 PACKED_CASES = {
