@@ -79,6 +79,35 @@ def test_forward_matches_oracle(name):
         assert rep["dropped"] > 0
 
 
+def _random_config(seed):
+    """A seeded random bf16 layer within the boundary's limits: token count, hidden and
+    intermediate sizes, expert count, k, routing rule, capacity, gate bias, activation and
+    weight renormalisation all drawn."""
+    rng = np.random.default_rng(7000 + seed)
+    act = C.GELU if rng.random() < 0.3 else C.SWIGLU
+    E = int(rng.choice([1, 3, 6, 8, 12, 16, 24, 40, 96]))
+    k = int(rng.integers(1, min(E, 8) + 1))
+    routing = "threshold" if rng.random() < 0.3 else "topk"
+    bias = [None, ("normal", 1.0), ("zipf", 1.1)][int(rng.integers(0, 3))]
+    return C.SMALL.with_(
+        name=f"random_{seed}", tokens=int(rng.integers(1, 2500)),
+        hidden=int(rng.choice([256, 512, 1024, 2048])),
+        inter=int(rng.integers(1, 10)) * (256 if act == C.GELU else 128),
+        experts=E, top_k=k, activation=act, routing=routing, bias=bias,
+        capacity_factor=float(rng.choice([0.0, 0.0, 0.6, 1.0, 1.4])),
+        renormalize=bool(rng.random() < 0.8))
+
+
+# Seeded random layers through moe_forward against the oracle, for combinations the named
+# cases above do not fix (each prints its configuration first).
+@pytest.mark.parametrize("seed", range(6))
+def test_random_layers_match_oracle(seed):
+    cfg = _random_config(seed)
+    print(f"[case] random layer {seed}: {cfg}", flush=True)
+    rep, _ = P.full_check(cfg, make_inputs(cfg, seed=seed))
+    _report(cfg.name, rep)
+
+
 def test_deterministic_bytes():
     cfg = CASES["bf16_many_experts"]
     inp = make_inputs(cfg, seed=3)
