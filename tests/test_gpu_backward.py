@@ -67,7 +67,35 @@ def _need_gpu():
 
 @pytest.mark.parametrize("name", list(CASES))
 def test_backward_matches_oracle(name):
-    cfg = CASES[name]
+    _check_backward(CASES[name], name)
+
+
+def _random_backward_config(seed):
+    """A seeded random bf16 layer within the backward's limits (I a multiple of 256, plain
+    weights): tokens, sizes, experts, k, routing, capacity, gate bias, activation,
+    renormalisation and the auxiliary-loss coefficient all drawn."""
+    rng = np.random.default_rng(9100 + seed)
+    E = int(rng.choice([1, 4, 8, 12, 16, 24, 48]))
+    return C.SMALL.with_(
+        name=f"bwd_random_{seed}", tokens=int(rng.integers(1, 1500)),
+        hidden=int(rng.choice([256, 512, 1024])), inter=256 * int(rng.integers(1, 5)),
+        experts=E, top_k=int(rng.integers(1, min(E, 6) + 1)),
+        activation=C.GELU if rng.random() < 0.3 else C.SWIGLU,
+        routing="threshold" if rng.random() < 0.3 else "topk",
+        bias=[None, ("normal", 1.0), ("zipf", 1.1)][int(rng.integers(0, 3))],
+        capacity_factor=float(rng.choice([0.0, 0.0, 0.7, 1.2])),
+        renormalize=bool(rng.random() < 0.8),
+        aux_loss_coeff=float(rng.choice([0.0, 0.0, 0.01])))
+
+
+# Seeded random layers through moe_forward_train and moe_backward against the oracle's
+# gradients, for combinations the named cases do not fix.
+@pytest.mark.parametrize("seed", range(4))
+def test_random_backward_matches_oracle(seed):
+    _check_backward(_random_backward_config(seed), f"random {seed}")
+
+
+def _check_backward(cfg, name):
     print(f"[case] {name} {cfg}", flush=True)
     inp = make_inputs(cfg, seed=8)
     layer = MoELayer(cfg, inp)
