@@ -38,6 +38,9 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="mixtral")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="token count of the headline workload (a batch sweep); the other "
+                         "workloads keep theirs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     ap.add_argument("--backward", action="store_true",
@@ -183,6 +186,10 @@ def run_workload(name, args, steps, warmup, headline, peaks=None):
     cfg = C.get(name)
     if cfg.dtype == C.BF16:
         cfg = cfg.with_(weights=args.weights)
+    if headline and args.tokens is not None:
+        cfg = cfg.with_(tokens=args.tokens,
+                        description=re.sub(r"^\d+ tokens( \([^)]*\))?", f"{args.tokens} tokens",
+                                           cfg.description))
     T, H, I, E, k = cfg.tokens, cfg.hidden, cfg.inter, cfg.experts, cfg.top_k
     print(f"[bench] {cfg.name}: generating inputs", file=sys.stderr, flush=True)
     inp = make_inputs(cfg, seed=args.seed, threads=16)
@@ -373,6 +380,8 @@ def main():
     peaks = measured_peaks(stream)   # after the headline, so its load does not precede it
     add_measured(head, peaks)
     cfg = C.get(args.config)
+    if args.tokens is not None:
+        cfg = cfg.with_(tokens=args.tokens)
     # the headline: whole-step wall time over the K timed steps, as the step contract says
     ms_per_step = head.pop("_wall_ms")
     up_flops, up_tflops = head.pop("_up_flops"), head.pop("_up_tflops")
@@ -380,7 +389,7 @@ def main():
     # the committed counter summary covers GEMM 1 (packed weights) of the Mixtral top-2
     # workload only
     traffic = (measured_traffic() if cfg.name == "mixtral" and args.weights == "packed"
-               else None)
+               and args.tokens in (None, C.get(args.config).tokens) else None)
     result = {
         "metric": METRIC,
         "value": cfg.tokens / (ms_per_step * 1e-3),
